@@ -1,0 +1,634 @@
+/*
+ * bsp_oracle.c -- CPU oracle for the block-scaled quantization path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, scalar reference
+ * that the HIP library is checked against.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the library never
+ * calls it and shares no code, header or table with it.
+ *
+ * Sources (the pages), cited by title and section:
+ *   [remio]  remio.ai, "Miles Blackwell RL sostituisce l'uniformita BF16 con
+ *            MXFP8 e NVFP4 nativi"
+ *   [hn]     hackernews.jp, "4ビットの教訓: NVFP4 RLにおける安定性とパフォーマンス"
+ *   [lmsys]  alphasignal.ai, "LMSYS Drops Miles, an Open-Source RL Framework"
+ *   [tml]    nopree.com, "End-to-End 4-Bit Training" (Chinese summary)
+ *
+ * Arithmetic convention (the pages only say that the exact, non-fast-math
+ * quantizer path is the contract [remio, "Un quantizzatore condiviso";
+ * lmsys, "The bit-exact quantizer contract"]): IEEE binary32, round to nearest
+ * even, every operation rounded on its own, no contraction unless fmaf() is
+ * written, subnormals kept.  Build with -ffp-contract=off -fno-fast-math.
+ * The GEMM reference is evaluated in binary64 on exactly decoded operands.
+ *
+ * Parity status per function is stated in its comment: every function is
+ * pinned by the tests (worked examples of the pages, library casts, brute
+ * force or closed forms) except where "parity unpinned" is written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* bf16 storage                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 -> f32 is exact: the bf16 bits are the top half of the f32. */
+ORC_API float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* f32 -> bf16, round to nearest even (finite inputs). */
+ORC_API uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E2M1 (FP4).  Value set +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} [tml, 先说为什么难].  */
+/* Code = sign(bit 3) | exponent(2 bits) | mantissa(1 bit).                   */
+/* ------------------------------------------------------------------------ */
+
+static const float kE2M1Mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+ORC_API float orc_e2m1_value(uint8_t code) {
+    float m = kE2M1Mag[code & 7u];
+    return (code & 8u) ? -m : m;
+}
+
+/* Magnitude code of a >= 0: round to nearest, ties to the even code (the one
+ * whose mantissa bit is 0), saturating at 6.  The intervals below are the
+ * midpoints of the value set; closed ends mark the ties that go to an even
+ * code.  Pinned by the worked example 2.25 -> 2 [tml, 第二个决定] and by a
+ * nearest-value search in the tests. */
+static uint8_t e2m1_mag_rne(float a) {
+    if (a <= 0.25f) return 0;
+    if (a < 0.75f) return 1;
+    if (a <= 1.25f) return 2;
+    if (a < 1.75f) return 3;
+    if (a <= 2.5f) return 4;
+    if (a < 3.5f) return 5;
+    if (a <= 5.0f) return 6;
+    return 7;
+}
+
+ORC_API uint8_t orc_e2m1_encode(float v) {
+    uint8_t s = signbit(v) ? 8u : 0u;
+    return s | e2m1_mag_rne(fabsf(v));
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP FP8 E4M3FN: bias 7, max 448, subnormals m * 2^-9, no infinity). */
+/* The pages name the type only [remio; hn]; its definition is the OCP one.  */
+/* ------------------------------------------------------------------------ */
+
+ORC_API float orc_e4m3_value(uint8_t code) {
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    float mag = (e == 0) ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return (code & 0x80u) ? -mag : mag;
+}
+
+/* Round to nearest even with saturation at 448 (sign kept).  Values in
+ * (448, 464] already round to 448; anything larger saturates instead of
+ * producing the NaN code.  Pinned against torch's float8_e4m3fn cast. */
+ORC_API uint8_t orc_e4m3_encode_sat(float y) {
+    uint8_t s = signbit(y) ? 0x80u : 0u;
+    float a = fabsf(y);
+    if (a >= 448.0f) return s | 0x7Eu;
+    if (a < 0.015625f) {                       /* below 2^-6: subnormal grid 2^-9 */
+        float q = nearbyintf(a * 512.0f);      /* exact scaling, RNE to integer */
+        return s | (uint8_t)q;                 /* q == 8 is the code of 2^-6 */
+    }
+    int e;
+    float m = frexpf(a, &e);                   /* a = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                             /* a = (2m) * 2^E, 2m in [1, 2) */
+    float f = nearbyintf((2.0f * m - 1.0f) * 8.0f);   /* exact, then RNE */
+    if (f == 8.0f) { f = 0.0f; E += 1; }
+    return s | (uint8_t)(((E + 7) << 3) | (int)f);
+}
+
+/* ------------------------------------------------------------------------ */
+/* E8M0: code c in [0, 254] stands for 2^(c - 127).                           */
+/* ------------------------------------------------------------------------ */
+
+ORC_API float orc_e8m0_value(uint8_t code) { return ldexpf(1.0f, (int)code - 127); }
+
+/* Shared MXFP8 exponent of a block with absolute maximum `amax`: the smallest
+ * integer k with amax <= 448 * 2^k, so that no element of the block
+ * saturates, kept within [-127, 119].  The pages fix the block (32 E4M3
+ * values, one E8M0 scale) [lmsys, Recipe 1; remio, "Il supporto Miles
+ * Blackwell"] but not how the exponent is chosen; this is the reading that
+ * never clips the block maximum.  The upper bound 119 is the largest k for
+ * which 448 * 2^k is a finite float: above it (block maxima beyond
+ * 1.75 * 2^127, near the bf16 maximum) the block saturates at 448 instead of
+ * dequantizing to infinity.  Written as the search the definition
+ * describes; pinned by an exact integer search and by torch's e8m0 cast. */
+ORC_API int orc_mxfp8_block_exponent(float amax) {
+    if (amax == 0.0f) return -127;
+    int e;
+    (void)frexp((double)amax, &e);
+    int k = e - 12;                            /* well below the answer */
+    while ((double)amax > ldexp(448.0, k)) k++;
+    if (k < -127) k = -127;
+    if (k > 119) k = 119;
+    return k;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 quantization [remio, "Il supporto Miles Blackwell" and "Un           */
+/* quantizzatore condiviso"; hn, ベースラインレシピ; tml, 先说为什么难 and     */
+/* 工程细节].                                                                 */
+/*   16 consecutive values share one E4M3 block scale s; an FP32 outer scale  */
+/*   g covers a wider scope (one token row for activations, one expert's      */
+/*   weight matrix for weights).  Readings (pages silent): g = amax / (6*448) */
+/*   so the scope maximum lands on E2M1 max times E4M3 max;                    */
+/*   s = E4M3(a / (6 g)); elements are scaled by one correctly rounded        */
+/*   reciprocal of eff = s * g; zero or subnormal eff flushes the block.      */
+/* ------------------------------------------------------------------------ */
+
+#define NVFP4_BLOCK 16
+#define MXFP8_BLOCK 32
+#define FLUSH_BELOW 0x1p-126f
+
+/* One candidate block scale with divisor D (6 = standard; 4 = the "4"
+ * candidate of the 4/6 choice).  Writes 16 codes, returns the scale code and
+ * the effective decode scale. */
+static uint8_t nvfp4_block_candidate(const float *xb, float g, float D, uint8_t q[NVFP4_BLOCK],
+                                     float *eff_out) {
+    float a = 0.0f;
+    for (int i = 0; i < NVFP4_BLOCK; i++) {
+        float m = fabsf(xb[i]);
+        if (m > a) a = m;
+    }
+    uint8_t s = 0;
+    float eff = 0.0f;
+    if (g > 0.0f) {
+        float denom = D * g;
+        s = orc_e4m3_encode_sat(a / denom);
+        eff = orc_e4m3_value(s) * g;
+    }
+    if (!(g > 0.0f) || eff < FLUSH_BELOW) {
+        for (int i = 0; i < NVFP4_BLOCK; i++) q[i] = signbit(xb[i]) ? 8u : 0u;
+        *eff_out = 0.0f;
+        return 0;
+    }
+    float r = 1.0f / eff;
+    for (int i = 0; i < NVFP4_BLOCK; i++) q[i] = orc_e2m1_encode(xb[i] * r);
+    *eff_out = eff;
+    return s;
+}
+
+/* Sum of squared reconstruction errors of a candidate, accumulated in index
+ * order with fused multiply-adds: d_i = x_i - value(q_i) * eff. */
+static float nvfp4_block_sse(const float *xb, const uint8_t q[NVFP4_BLOCK], float eff) {
+    float acc = 0.0f;
+    for (int i = 0; i < NVFP4_BLOCK; i++) {
+        float d = fmaf(-orc_e2m1_value(q[i]), eff, xb[i]);
+        acc = fmaf(d, d, acc);
+    }
+    return acc;
+}
+
+/* Quantize one 16-value block under outer scale g.  With mode46 the "4"
+ * candidate replaces the standard "6" one only if its squared error is
+ * strictly lower [tml, 工程细节: choose between two candidate scales to reduce
+ * error; activations only].  Parity of the 4/6 rule is unpinned by the
+ * pages (no worked example); the tests pin it with hand-built blocks. */
+static uint8_t nvfp4_quantize_block(const float *xb, float g, int mode46, uint8_t q[NVFP4_BLOCK]) {
+    float eff6;
+    uint8_t s6 = nvfp4_block_candidate(xb, g, 6.0f, q, &eff6);
+    if (!mode46) return s6;
+    uint8_t q4[NVFP4_BLOCK];
+    float eff4;
+    uint8_t s4 = nvfp4_block_candidate(xb, g, 4.0f, q4, &eff4);
+    float err6 = nvfp4_block_sse(xb, q, eff6);
+    float err4 = nvfp4_block_sse(xb, q4, eff4);
+    if (err4 < err6) {
+        memcpy(q, q4, NVFP4_BLOCK);
+        return s4;
+    }
+    return s6;
+}
+
+/* x: bf16 [M, K] row-major.  rows_per_scale consecutive rows share one outer
+ * scale (1 = per token; N = per expert for E stacked [N, K] matrices; M = per
+ * tensor).  Outputs: codes [M, K/2] (element 2j in the low nibble of byte j),
+ * scales [M, K/16] E4M3, outer [M / rows_per_scale] f32 decode scales. */
+ORC_API void orc_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t rows_per_scale,
+                                int mode46, uint8_t *codes, uint8_t *scales, float *outer) {
+    int64_t nscope = M / rows_per_scale;
+    int64_t nblk = K / NVFP4_BLOCK;
+    /* outer scale per scope: amax over the scope, g = amax / 2688 */
+    for (int64_t sc = 0; sc < nscope; sc++) {
+        float A = 0.0f;
+        for (int64_t r = sc * rows_per_scale; r < (sc + 1) * rows_per_scale; r++)
+            for (int64_t k = 0; k < K; k++) {
+                float m = fabsf(orc_bf16_to_f32(x[r * K + k]));
+                if (m > A) A = m;
+            }
+        outer[sc] = (A == 0.0f) ? 0.0f : A / 2688.0f;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++) {
+        float g = outer[r / rows_per_scale];
+        for (int64_t b = 0; b < nblk; b++) {
+            float xb[NVFP4_BLOCK];
+            uint8_t q[NVFP4_BLOCK];
+            for (int i = 0; i < NVFP4_BLOCK; i++) xb[i] = orc_bf16_to_f32(x[r * K + b * NVFP4_BLOCK + i]);
+            scales[r * nblk + b] = nvfp4_quantize_block(xb, g, mode46, q);
+            for (int i = 0; i < NVFP4_BLOCK; i += 2)
+                codes[r * (K / 2) + (b * NVFP4_BLOCK + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+        }
+    }
+}
+
+static inline uint8_t nvfp4_code_at(const uint8_t *codes, int64_t K, int64_t r, int64_t k) {
+    uint8_t byte = codes[r * (K / 2) + k / 2];
+    return (k & 1) ? (byte >> 4) : (byte & 15u);
+}
+
+/* Dequantize [remio, "Entrambe le ricette"; lmsys, dequantized backward]:
+ * y = value(q) * (s * g), both products in f32 in that order.  out_f32 and/or
+ * out_bf16 (RNE of the f32 result) may be NULL. */
+ORC_API void orc_dequantize_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                  int64_t M, int64_t K, int64_t rows_per_scale, float *out_f32,
+                                  uint16_t *out_bf16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++) {
+        float g = outer[r / rows_per_scale];
+        for (int64_t k = 0; k < K; k++) {
+            float eff = orc_e4m3_value(scales[r * (K / 16) + k / 16]) * g;
+            float y = orc_e2m1_value(nvfp4_code_at(codes, K, r, k)) * eff;
+            if (out_f32) out_f32[r * K + k] = y;
+            if (out_bf16) out_bf16[r * K + k] = orc_f32_to_bf16(y);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 quantization [lmsys, Recipe 1; remio, "Un quantizzatore condiviso"]. */
+/* 32 consecutive values along the reduction axis share one E8M0 scale 2^k;   */
+/* codes are E4M3(x * 2^-k).  Rowwise blocks run along K; the columnwise copy */
+/* is made from the original bf16 with blocks along M and is stored            */
+/* transposed [K, M].  Grouped columnwise copies keep blocks inside one group  */
+/* of rows and pad each group with zero rows to a multiple of 32.             */
+/* ------------------------------------------------------------------------ */
+
+static uint8_t mxfp8_block(const float *xb, uint8_t q[MXFP8_BLOCK]) {
+    float a = 0.0f;
+    for (int i = 0; i < MXFP8_BLOCK; i++) {
+        float m = fabsf(xb[i]);
+        if (m > a) a = m;
+    }
+    int k = orc_mxfp8_block_exponent(a);
+    for (int i = 0; i < MXFP8_BLOCK; i++) q[i] = orc_e4m3_encode_sat(ldexpf(xb[i], -k));
+    return (uint8_t)(k + 127);
+}
+
+ORC_API void orc_quantize_mxfp8_rowwise(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes,
+                                        uint8_t *scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t b = 0; b < K / MXFP8_BLOCK; b++) {
+            float xb[MXFP8_BLOCK];
+            uint8_t q[MXFP8_BLOCK];
+            for (int i = 0; i < MXFP8_BLOCK; i++) xb[i] = orc_bf16_to_f32(x[r * K + b * MXFP8_BLOCK + i]);
+            scales[r * (K / MXFP8_BLOCK) + b] = mxfp8_block(xb, q);
+            memcpy(codes + r * K + b * MXFP8_BLOCK, q, MXFP8_BLOCK);
+        }
+}
+
+/* Padded start column of each group: P[0] = 0, P[g+1] = P[g] + roundup32(n_g). */
+ORC_API void orc_padded_offsets(const int64_t *group_offsets, int64_t G, int64_t *padded) {
+    padded[0] = 0;
+    for (int64_t g = 0; g < G; g++) {
+        int64_t n = group_offsets[g + 1] - group_offsets[g];
+        padded[g + 1] = padded[g] + (n + 31) / 32 * 32;
+    }
+}
+
+/* Columnwise copy.  group_offsets == NULL: one group of all M rows (M must be
+ * a multiple of 32) and ldT == M.  Otherwise column c of the output for group
+ * g, block b, lane i is P[g] + 32 b + i and holds row offsets[g] + 32 b + i
+ * (zero beyond the group).  codesT [K, ldT], scalesT [K, ldT / 32]. */
+ORC_API void orc_quantize_mxfp8_colwise(const uint16_t *x, int64_t M, int64_t K,
+                                        const int64_t *group_offsets, int64_t G, int64_t ldT,
+                                        uint8_t *codesT, uint8_t *scalesT) {
+    int64_t one[2] = {0, M};
+    const int64_t *off = group_offsets ? group_offsets : one;
+    int64_t ng = group_offsets ? G : 1;
+    int64_t *P = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ng + 1));
+    orc_padded_offsets(off, ng, P);
+    for (int64_t g = 0; g < ng; g++) {
+        int64_t r0 = off[g], n = off[g + 1] - off[g];
+        int64_t nb = (n + 31) / 32;
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < K; k++)
+            for (int64_t b = 0; b < nb; b++) {
+                float xb[MXFP8_BLOCK];
+                uint8_t q[MXFP8_BLOCK];
+                for (int i = 0; i < MXFP8_BLOCK; i++) {
+                    int64_t rr = 32 * b + i;
+                    xb[i] = (rr < n) ? orc_bf16_to_f32(x[(r0 + rr) * K + k]) : 0.0f;
+                }
+                scalesT[k * (ldT / 32) + P[g] / 32 + b] = mxfp8_block(xb, q);
+                memcpy(codesT + k * ldT + P[g] + 32 * b, q, MXFP8_BLOCK);
+            }
+    }
+    free(P);
+}
+
+/* MXFP8 dequantize: y = value(q) * 2^k, exact in f32; bf16 is its RNE. */
+ORC_API void orc_dequantize_mxfp8(const uint8_t *codes, const uint8_t *scales, int64_t M, int64_t K,
+                                  float *out_f32, uint16_t *out_bf16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t k = 0; k < K; k++) {
+            int e = (int)scales[r * (K / 32) + k / 32] - 127;
+            float y = ldexpf(orc_e4m3_value(codes[r * K + k]), e);
+            if (out_f32) out_f32[r * K + k] = y;
+            if (out_bf16) out_bf16[r * K + k] = orc_f32_to_bf16(y);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Counter-based RNG: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel    */
+/* Random Numbers: As Easy as 1, 2, 3", SC'11).  Each round multiplies words */
+/* 0 and 2 by the two Philox multipliers, mixes the high halves with the     */
+/* other two words and the key, and swaps; the key is advanced by the Weyl   */
+/* constants between rounds.                                                  */
+/* ------------------------------------------------------------------------ */
+
+ORC_API void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; round++) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c[1] ^ k0;
+        uint32_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+    memcpy(out, c, sizeof c);
+}
+
+/* 16 uniform bits for output element `index` under `seed`: the counter is
+ * (index / 8) in words 0-1, the key is the seed; element index % 8 takes
+ * word (index % 8) / 2, low half for even indices, high half for odd. */
+ORC_API uint16_t orc_sr_bits(uint64_t seed, uint64_t index) {
+    uint64_t blk = index >> 3;
+    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    uint32_t word = w[(index & 7u) >> 1];
+    return (uint16_t)((index & 1u) ? (word >> 16) : (word & 0xFFFFu));
+}
+
+/* Stochastic rounding of v >= 0 onto the E2M1 grid [tml, 第二个决定]: round
+ * up to the next grid value with probability equal to the distance from the
+ * lower neighbour over the gap, so the expectation is kept.  With 16 random
+ * bits u, round up iff u < frac * 65536 (frac is exact in f32).  Values >= 6
+ * saturate to 6. */
+ORC_API uint8_t orc_e2m1_sr_mag(float v, uint16_t u) {
+    if (v >= 6.0f) return 7;
+    int c = 0;
+    while (c < 7 && kE2M1Mag[c + 1] <= v) c++;
+    float lo = kE2M1Mag[c], hi = kE2M1Mag[c + 1];
+    float frac = (v - lo) / (hi - lo);
+    return ((float)u < frac * 65536.0f) ? (uint8_t)(c + 1) : (uint8_t)c;
+}
+
+/* Dequantize -> transpose -> requantize with stochastic rounding
+ * [tml, 第二个决定].  Input: rowwise NVFP4 [M, K] with per-row outer scales.
+ * Output: NVFP4 of the transpose [K, M] (16-blocks now run along M) under a
+ * single outer scale G = max_m g_m (reading: the transposed blocks span 16
+ * tokens, so the per-tensor scale of standard NVFP4 is used; for standard-
+ * mode inputs this is the tensor amax / 2688 up to rounding).  The
+ * intermediate is the f32 dequantized value, not rounded to bf16.  use_sr = 0
+ * rounds to nearest even instead.  The random bits of output element (k, m)
+ * use index k * M + m. */
+ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                      int64_t M, int64_t K, uint64_t seed, int use_sr,
+                                      uint8_t *codesT, uint8_t *scalesT, float *outerT) {
+    float G = 0.0f;
+    for (int64_t m = 0; m < M; m++)
+        if (outer[m] > G) G = outer[m];
+    *outerT = G;
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; k++)
+        for (int64_t j = 0; j < M / 16; j++) {
+            float d[16];
+            float a = 0.0f;
+            for (int i = 0; i < 16; i++) {
+                int64_t m = 16 * j + i;
+                float eff = orc_e4m3_value(scales[m * (K / 16) + k / 16]) * outer[m];
+                d[i] = orc_e2m1_value(nvfp4_code_at(codes, K, m, k)) * eff;
+                if (fabsf(d[i]) > a) a = fabsf(d[i]);
+            }
+            uint8_t s = 0;
+            float eff = 0.0f;
+            if (G > 0.0f) {
+                s = orc_e4m3_encode_sat(a / (6.0f * G));
+                eff = orc_e4m3_value(s) * G;
+            }
+            uint8_t q[16];
+            if (!(G > 0.0f) || eff < FLUSH_BELOW) {
+                s = 0;
+                for (int i = 0; i < 16; i++) q[i] = signbit(d[i]) ? 8u : 0u;
+            } else {
+                float r = 1.0f / eff;
+                for (int i = 0; i < 16; i++) {
+                    float v = fabsf(d[i]) * r;
+                    uint8_t mag = use_sr ? orc_e2m1_sr_mag(v, orc_sr_bits(seed, (uint64_t)(k * M + 16 * j + i)))
+                                         : e2m1_mag_rne(v);
+                    q[i] = (uint8_t)((signbit(d[i]) ? 8u : 0u) | mag);
+                }
+            }
+            scalesT[k * (M / 16) + j] = s;
+            for (int i = 0; i < 16; i += 2)
+                codesT[k * (M / 2) + (16 * j + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block-scaled grouped GEMM reference (binary64 on exact operand values).   */
+/* fmt 0 = NVFP4 (value(q) * s * g), fmt 1 = MXFP8 (value(q) * 2^k).         */
+/* ------------------------------------------------------------------------ */
+
+static double exact_elem(int fmt, const uint8_t *codes, const uint8_t *scales, int64_t K, int64_t r,
+                         int64_t k) {
+    if (fmt == 0) {
+        double v = (double)orc_e2m1_value(nvfp4_code_at(codes, K, r, k));
+        return v * (double)orc_e4m3_value(scales[r * (K / 16) + k / 16]);
+    }
+    double v = (double)orc_e4m3_value(codes[r * K + k]);
+    return ldexp(v, (int)scales[r * (K / 32) + k / 32] - 127);
+}
+
+/* Forward / data-gradient form: C[r, n] = g_A[t] g_B[e] sum_k A[t, k] B_e[n, k]
+ * with t = gather[r] (or r) and e the group holding row r.  Only the rows
+ * listed in `rows` are computed (all rows if rows == NULL, nrows = M).
+ * c and c_abs are [nrows, N]; c_abs holds sum_k |A B| * |g_A g_B| (the scale
+ * of the f32 accumulation error bound). */
+ORC_API void orc_gemm_rowgroup(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
+                               const float *a_outer, const int32_t *a_gather,
+                               const int64_t *group_offsets, int64_t G, int64_t M, int64_t N, int64_t K,
+                               const uint8_t *b_codes, const uint8_t *b_scales, const float *b_outer,
+                               const int64_t *rows, int64_t nrows, double *c, double *c_abs) {
+    (void)M;
+    int64_t b_code_stride = (fmt == 0) ? N * K / 2 : N * K;
+    int64_t b_scale_stride = (fmt == 0) ? N * K / 16 : N * K / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        int64_t e = 0;
+        while (e < G && group_offsets[e + 1] <= r) e++;
+        int64_t t = a_gather ? (int64_t)a_gather[r] : r;
+        double ga = (fmt == 0) ? (double)a_outer[t] : 1.0;
+        double gb = (fmt == 0) ? (double)b_outer[e] : 1.0;
+        double *arow = (double *)malloc(sizeof(double) * (size_t)K);
+        for (int64_t k = 0; k < K; k++) arow[k] = exact_elem(fmt, a_codes, a_scales, K, t, k);
+        const uint8_t *bc = b_codes + e * b_code_stride;
+        const uint8_t *bs = b_scales + e * b_scale_stride;
+        for (int64_t n = 0; n < N; n++) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = arow[k] * exact_elem(fmt, bc, bs, K, n, k);
+                s += p;
+                sa += fabs(p);
+            }
+            c[i * N + n] = s * ga * gb;
+            if (c_abs) c_abs[i * N + n] = sa * fabs(ga * gb);
+        }
+        free(arow);
+    }
+}
+
+/* Weight-gradient form (MXFP8 only): for group g,
+ * C_g[n, c] = sum over the group's padded token columns j of
+ * A[n, P[g] + j] * B[c, P[g] + j], with A [NA, ldk] and B [NB, ldk] the
+ * grouped columnwise copies (padding columns hold zeros).  The (g, n) output
+ * rows to compute are listed in sel (pairs); c and c_abs are [nsel, NB]. */
+ORC_API void orc_gemm_wgrad(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                            const uint8_t *b_scales, const int64_t *group_offsets, int64_t G, int64_t NA,
+                            int64_t NB, int64_t ldk, const int64_t *sel, int64_t nsel, double *c,
+                            double *c_abs) {
+    int64_t *P = (int64_t *)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    orc_padded_offsets(group_offsets, G, P);
+    (void)NA;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nsel; i++) {
+        int64_t g = sel[2 * i], n = sel[2 * i + 1];
+        for (int64_t cc = 0; cc < NB; cc++) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t j = P[g]; j < P[g + 1]; j++) {
+                double p = exact_elem(1, a_codes, a_scales, ldk, n, j) * exact_elem(1, b_codes, b_scales, ldk, cc, j);
+                s += p;
+                sa += fabs(p);
+            }
+            c[i * NB + cc] = s;
+            if (c_abs) c_abs[i * NB + cc] = sa;
+        }
+    }
+    free(P);
+}
+
+/* ------------------------------------------------------------------------ */
+/* SwiGLU between the gate/up and down projections.                          */
+/* The pages give no arithmetic for it; the reading is h = silu(gate) * up    */
+/* with silu(z) = z / (1 + exp(-z)), gate = columns [0, I) and up = columns  */
+/* [I, 2I) of the fused gate/up output, and h stored as bf16 (RNE).  Because  */
+/* h feeds a bit-exact quantizer, exp is fixed to one explicit f32 algorithm  */
+/* (Cody-Waite reduction by ln 2, degree-7 Taylor polynomial, exact 2^n       */
+/* scaling) instead of a libm whose last bit may differ.                      */
+/* ------------------------------------------------------------------------ */
+
+ORC_API float orc_exp_f32(float x) {
+    if (x >= 89.0f) return INFINITY;
+    if (x <= -104.0f) return 0.0f;
+    const float log2e = 1.44269504088896341f;
+    const float ln2_hi = 0.693145751953125f;     /* ln 2 to 16 bits: n * ln2_hi is exact */
+    const float ln2_lo = 1.428606765330187e-06f; /* ln 2 - ln2_hi */
+    float n = nearbyintf(x * log2e);
+    float r = (x - n * ln2_hi) - n * ln2_lo;
+    /* e^r = sum_{j=0..7} r^j / j!, Horner, each step rounded */
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+ORC_API float orc_silu_f32(float z) { return z / (1.0f + orc_exp_f32(-z)); }
+
+/* h13: f32 [R, 2I] (ld = 2I); h: bf16 [R, I]. */
+ORC_API void orc_swiglu(const float *h13, int64_t R, int64_t I, uint16_t *h) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t j = 0; j < I; j++) {
+            float gate = h13[r * 2 * I + j], up = h13[r * 2 * I + I + j];
+            h[r * I + j] = orc_f32_to_bf16(orc_silu_f32(gate) * up);
+        }
+}
+
+ORC_API int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+ORC_API void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Array forms of the scalar codecs, for exhaustive sweeps in the tests. */
+ORC_API void orc_e2m1_encode_array(const float *v, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_e2m1_encode(v[i]);
+}
+
+ORC_API void orc_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_e4m3_encode_sat(v[i]);
+}
+
+ORC_API void orc_mxfp8_block_exponent_array(const float *a, int64_t n, int32_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_mxfp8_block_exponent(a[i]);
+}
+
+ORC_API void orc_f32_to_bf16_array(const float *v, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_f32_to_bf16(v[i]);
+}
+
+ORC_API void orc_exp_f32_array(const float *v, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; i++) out[i] = orc_exp_f32(v[i]);
+}
