@@ -1,0 +1,191 @@
+// bsp_capi.cpp -- the exported C ABI: host-side validation, then launches on
+// the caller's stream.  Validation happens before any HIP call, so a rejected
+// call enqueues nothing and needs no GPU.
+#include <hip/hip_runtime.h>
+
+#include "bsp_internal.hpp"
+
+#define BSP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned16_or_null(const void *p) { return p == nullptr || aligned16(p); }
+
+inline bsp_status hip_status(hipError_t e) { return e == hipSuccess ? BSP_OK : BSP_ERR_HIP; }
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+BSP_EXPORT int bsp_version(void) { return 100; }
+
+BSP_EXPORT const char *bsp_status_string(int status) {
+    switch (status) {
+        case BSP_OK: return "ok";
+        case BSP_ERR_INVALID_ARG: return "invalid argument (null pointer, unknown enum or flag)";
+        case BSP_ERR_SHAPE: return "invalid shape (size not positive or not a multiple of the block)";
+        case BSP_ERR_ALIGNMENT: return "device pointer or leading dimension not 16-byte aligned";
+        case BSP_ERR_UNSUPPORTED: return "unsupported combination";
+        case BSP_ERR_WORKSPACE: return "workspace missing or too small";
+        case BSP_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+BSP_EXPORT bsp_status bsp_nvfp4_sizes(int64_t M, int64_t K, int64_t rows_per_scale, size_t *codes_bytes,
+                                      size_t *scales_bytes, size_t *outer_count) {
+    if (!codes_bytes || !scales_bytes || !outer_count) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || K % 16 || rows_per_scale <= 0 || M % rows_per_scale) return BSP_ERR_SHAPE;
+    *codes_bytes = (size_t)(M * (K / 2));
+    *scales_bytes = (size_t)(M * (K / 16));
+    *outer_count = (size_t)(M / rows_per_scale);
+    return BSP_OK;
+}
+
+BSP_EXPORT bsp_status bsp_mxfp8_sizes(int64_t M, int64_t K, size_t *codes_bytes, size_t *scales_bytes) {
+    if (!codes_bytes || !scales_bytes) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || K % 32) return BSP_ERR_SHAPE;
+    *codes_bytes = (size_t)(M * K);
+    *scales_bytes = (size_t)(M * (K / 32));
+    return BSP_OK;
+}
+
+BSP_EXPORT int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G) {
+    if (M < 0 || G < 1) return -1;
+    return (M + 31 * G + 31) / 32 * 32;
+}
+
+BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
+    (void)M;
+    return 64 * sizeof(float);
+}
+
+BSP_EXPORT size_t bsp_gemm_workspace_size(int mode, int64_t M, int64_t G) {
+    if (M < 0 || G < 1) return 0;
+    if (mode == BSP_GEMM_WGRAD) return (size_t)(G + 1) * sizeof(int64_t);
+    return (size_t)bsp::gemm_tile_count(M, G) * sizeof(int64_t);
+}
+
+BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                                   int64_t rows_per_scale, uint8_t *codes, uint8_t *scales,
+                                                   float *outer, uint32_t flags, void *stream) {
+    if (!x || !codes || !scales || !outer) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_NVFP4_46) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K < 16 || K % 16 || ldx < K || rows_per_scale <= 0 || M % rows_per_scale) return BSP_ERR_SHAPE;
+    if (!aligned16(x) || ldx % 8 || !aligned16(codes) || !aligned16(scales) || !aligned16(outer))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_quantize_nvfp4(x, M, K, ldx, rows_per_scale, codes, scales, outer,
+                                                 (flags & BSP_NVFP4_46) != 0, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
+                                         uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT,
+                                         int64_t ld_colT, const int64_t *group_offsets, int64_t G, uint32_t flags,
+                                         void *stream) {
+    if (!x) return BSP_ERR_INVALID_ARG;
+    if (flags != 0) return BSP_ERR_INVALID_ARG;
+    if ((codes_row == nullptr) != (scales_row == nullptr)) return BSP_ERR_INVALID_ARG;
+    if ((codes_colT == nullptr) != (scales_colT == nullptr)) return BSP_ERR_INVALID_ARG;
+    if (!codes_row && !codes_colT) return BSP_ERR_INVALID_ARG;
+    if (group_offsets && !codes_colT) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K < 32 || K % 32 || ldx < K) return BSP_ERR_SHAPE;
+    if (codes_colT) {
+        if (ld_colT <= 0 || ld_colT % 32) return BSP_ERR_SHAPE;
+        if (group_offsets) {
+            if (G < 1 || G > 2048) return BSP_ERR_SHAPE;
+            if (ld_colT < bsp_mxfp8_grouped_cols(M, G)) return BSP_ERR_SHAPE;
+        } else {
+            if (M % 32 || ld_colT < M) return BSP_ERR_SHAPE;
+        }
+    }
+    if (!aligned16(x) || ldx % 8 || !aligned16_or_null(codes_row) || !aligned16_or_null(scales_row) ||
+        !aligned16_or_null(codes_colT) || !aligned16_or_null(scales_colT) || !aligned16_or_null(group_offsets))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_quantize_mxfp8(x, M, K, ldx, codes_row, scales_row, codes_colT, scales_colT,
+                                                 ld_colT, group_offsets, group_offsets ? G : 1, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                     int64_t M, int64_t K, int64_t rows_per_scale, void *out, int out_dtype,
+                                     void *stream) {
+    if (!codes || !scales || !out) return BSP_ERR_INVALID_ARG;
+    if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
+    if (out_dtype != BSP_DTYPE_F32 && out_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
+    if (fmt == BSP_FMT_NVFP4 && !outer) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0) return BSP_ERR_SHAPE;
+    if (fmt == BSP_FMT_NVFP4 && (K % 16 || rows_per_scale <= 0 || M % rows_per_scale)) return BSP_ERR_SHAPE;
+    if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(out) || !aligned16_or_null(outer))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_dequantize(fmt, codes, scales, outer, M, K, fmt == BSP_FMT_NVFP4 ? rows_per_scale : 1,
+                                             out, out_dtype, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                               int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT,
+                                               float *outerT, uint64_t seed, uint32_t flags, void *workspace,
+                                               size_t ws_bytes, void *stream) {
+    if (!codes || !scales || !outer || !codesT || !scalesT || !outerT) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_SR) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || M % 16 || K % 16) return BSP_ERR_SHAPE;
+    if (!workspace || ws_bytes < bsp_requant_workspace_size(M)) return BSP_ERR_WORKSPACE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(outer) || !aligned16(codesT) || !aligned16(scalesT) ||
+        !aligned16(outerT) || !aligned16(workspace))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_requant(codes, scales, outer, M, K, codesT, scalesT, outerT, seed,
+                                          (flags & BSP_SR) != 0, reinterpret_cast<float *>(workspace),
+                                          as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes,
+                                                       const uint8_t *a_scales, const float *a_outer,
+                                                       const int32_t *a_gather, int64_t a_rows,
+                                                       const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                       int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                                                       const float *b_outer, void *c, int c_dtype, int64_t ldc,
+                                                       void *workspace, size_t ws_bytes, void *stream) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
+    if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return BSP_ERR_INVALID_ARG;
+    if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
+    if (fmt == BSP_FMT_NVFP4 && (!a_outer || !b_outer)) return BSP_ERR_INVALID_ARG;
+    if (fmt == BSP_FMT_MXFP8 && (a_outer || b_outer)) return BSP_ERR_INVALID_ARG;
+    if (mode == BSP_GEMM_WGRAD) {
+        if (fmt != BSP_FMT_MXFP8) return BSP_ERR_UNSUPPORTED;
+        if (a_gather) return BSP_ERR_INVALID_ARG;
+    }
+    if (G < 1 || M <= 0 || N <= 0 || K <= 0 || ldc < N) return BSP_ERR_SHAPE;
+    if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
+    if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
+    if (fmt == BSP_FMT_NVFP4 && K % 16) return BSP_ERR_SHAPE;
+    if (mode != BSP_GEMM_WGRAD && !a_gather && a_rows != M) return BSP_ERR_SHAPE;
+    if (mode == BSP_GEMM_WGRAD && a_rows != M) return BSP_ERR_SHAPE;
+    if (a_rows <= 0) return BSP_ERR_SHAPE;
+    if (!workspace || ws_bytes < bsp_gemm_workspace_size(mode, M, G)) return BSP_ERR_WORKSPACE;
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) ||
+        !aligned16(group_offsets) || !aligned16(c) || !aligned16(workspace) || !aligned16_or_null(a_outer) ||
+        !aligned16_or_null(b_outer) || !aligned16_or_null(a_gather))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
+                                       b_codes, b_scales, b_outer, c, c_dtype, ldc, workspace, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_swiglu_quantize(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out,
+                                          int fmt, uint8_t *codes, uint8_t *scales, float *outer, uint32_t flags,
+                                          void *stream) {
+    if (!h13) return BSP_ERR_INVALID_ARG;
+    if (in_dtype != BSP_DTYPE_F32 && in_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
+    if (fmt != -1 && fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
+    if (fmt == -1 && !h_out) return BSP_ERR_INVALID_ARG;
+    if (fmt >= 0 && (!codes || !scales)) return BSP_ERR_INVALID_ARG;
+    if (fmt == BSP_FMT_NVFP4 && !outer) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_NVFP4_46) return BSP_ERR_INVALID_ARG;
+    if ((flags & BSP_NVFP4_46) && fmt != BSP_FMT_NVFP4) return BSP_ERR_INVALID_ARG;
+    if (R <= 0 || I <= 0 || I % 32 || I > 8192) return BSP_ERR_SHAPE;
+    if (!aligned16(h13) || !aligned16_or_null(h_out) || !aligned16_or_null(codes) || !aligned16_or_null(scales) ||
+        !aligned16_or_null(outer))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_swiglu(h13, in_dtype, R, I, h_out, fmt, (flags & BSP_NVFP4_46) != 0,
+                                         fmt >= 0 ? codes : nullptr, fmt >= 0 ? scales : nullptr,
+                                         fmt == BSP_FMT_NVFP4 ? outer : nullptr, as_stream(stream)));
+}

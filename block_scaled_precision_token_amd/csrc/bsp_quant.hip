@@ -1,0 +1,836 @@
+// bsp_quant.hip -- memory-bound kernels of the block-scaled path for gfx950:
+// NVFP4 quantize (per token / per scope, standard or 4/6), MXFP8 quantize
+// (rowwise + columnwise from one read, optionally grouped), dequantize,
+// dequantize -> transpose -> requantize with stochastic rounding, and
+// SwiGLU fused with the quantization of its output.
+//
+// Every kernel reads its input once with 16-byte loads, keeps block
+// reductions inside a lane (one lane owns whole 16/32-value blocks, so the
+// amax of a block needs no cross-lane traffic), and writes codes and scales
+// with coalesced stores.  All arithmetic is IEEE f32 (no contraction, correctly
+// rounded division), so codes and scales do not depend on launch geometry.
+#include "bsp_device.hpp"
+#include "bsp_internal.hpp"
+
+namespace bsp {
+
+// --------------------------------------------------------------------------
+// NVFP4
+// --------------------------------------------------------------------------
+
+struct Nvfp4Block {
+    uint32_t lo, hi;  // 16 nibbles, element 2j in the low nibble of byte j
+    uint32_t s;       // E4M3 code
+};
+
+__device__ __forceinline__ void unpack16(const uint4 (&v)[2], float (&xf)[16]) {
+    const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        xf[2 * i] = bf16_lo(w[i]);
+        xf[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+__device__ __forceinline__ float absmax16(const float (&xf)[16]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(xf[i]));
+    return a;
+}
+
+// One candidate block scale with divisor D (6: standard; 4: the "4" of 4/6).
+__device__ __forceinline__ Nvfp4Block nvfp4_candidate(const float (&xf)[16], float a, float g, float D,
+                                                      float &eff) {
+    Nvfp4Block b;
+    b.s = 0u;
+    eff = 0.0f;
+    if (g > 0.0f) {
+        float denom = D * g;
+        b.s = e4m3_encode(a / denom);
+        eff = e4m3_decode(b.s) * g;
+    }
+    b.lo = 0u;
+    b.hi = 0u;
+    if (!(g > 0.0f) || eff < kFlushBelow) {
+        b.s = 0u;
+        eff = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            b.lo |= ((__float_as_uint(xf[i]) >> 28) & 8u) << (4 * i);
+            b.hi |= ((__float_as_uint(xf[8 + i]) >> 28) & 8u) << (4 * i);
+        }
+        return b;
+    }
+    float r = 1.0f / eff;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        b.lo |= e2m1_encode(xf[i] * r) << (4 * i);
+        b.hi |= e2m1_encode(xf[8 + i] * r) << (4 * i);
+    }
+    return b;
+}
+
+__device__ __forceinline__ float nvfp4_sse(const float (&xf)[16], const Nvfp4Block &b, float eff) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        uint32_t c = ((i < 8 ? b.lo : b.hi) >> (4 * (i & 7))) & 15u;
+        float d = __builtin_fmaf(-e2m1_value(c), eff, xf[i]);
+        acc = __builtin_fmaf(d, d, acc);
+    }
+    return acc;
+}
+
+template <bool M46>
+__device__ __forceinline__ Nvfp4Block nvfp4_block(const float (&xf)[16], float g) {
+    float a = absmax16(xf);
+    float eff6;
+    Nvfp4Block b6 = nvfp4_candidate(xf, a, g, 6.0f, eff6);
+    if (!M46) return b6;
+    float eff4;
+    Nvfp4Block b4 = nvfp4_candidate(xf, a, g, 4.0f, eff4);
+    float e6 = nvfp4_sse(xf, b6, eff6);
+    float e4 = nvfp4_sse(xf, b4, eff4);
+    return (e4 < e6) ? b4 : b6;
+}
+
+// Outer scope = one row, whole row kept in registers: one wavefront per row,
+// lane l owns the 16-value blocks starting at k = 1024 j + 16 l.
+template <bool M46, int MAXIT>
+__global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                   int64_t ldx, uint8_t *__restrict__ codes,
+                                                   uint8_t *__restrict__ scales, float *__restrict__ outer) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const uint16_t *xr = x + row * ldx;
+    uint4 v[MAXIT][2];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAXIT; j++) {
+        const int64_t k0 = (int64_t)j * 1024 + lane * 16;
+        if (k0 < K) {
+            v[j][0] = *reinterpret_cast<const uint4 *>(xr + k0);
+            v[j][1] = *reinterpret_cast<const uint4 *>(xr + k0 + 8);
+            float xf[16];
+            unpack16(v[j], xf);
+            amax = fmaxf(amax, absmax16(xf));
+        }
+    }
+    amax = wave_max(amax);
+    const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
+    if (lane == 0) outer[row] = g;
+#pragma unroll
+    for (int j = 0; j < MAXIT; j++) {
+        const int64_t k0 = (int64_t)j * 1024 + lane * 16;
+        if (k0 < K) {
+            float xf[16];
+            unpack16(v[j], xf);
+            Nvfp4Block b = nvfp4_block<M46>(xf, g);
+            *reinterpret_cast<uint2 *>(codes + row * (K / 2) + k0 / 2) = make_uint2(b.lo, b.hi);
+            scales[row * (K / 16) + k0 / 16] = (uint8_t)b.s;
+        }
+    }
+}
+
+// Scope amax for scopes of several rows (or rows too long to keep in
+// registers).  Block (scope, slice) reduces one contiguous slice of a scope
+// and issues one atomic max of the non-negative f32 bit pattern (ordered like
+// an unsigned integer) into `outer`, which holds zero on entry.
+__global__ __launch_bounds__(256) void k_scope_amax(const uint16_t *__restrict__ x, int64_t K, int64_t ldx,
+                                                    int64_t rows_per_scale, float *outer) {
+    const int64_t scope = blockIdx.x;
+    const int64_t nblk_row = K / 16;
+    const int64_t nblk = rows_per_scale * nblk_row;
+    const int64_t chunk = (nblk + gridDim.y - 1) / gridDim.y;
+    const int64_t b0 = (int64_t)blockIdx.y * chunk;
+    const int64_t b1 = b0 + chunk < nblk ? b0 + chunk : nblk;
+    float a = 0.0f;
+    for (int64_t b = b0 + threadIdx.x; b < b1; b += blockDim.x) {
+        const int64_t r = scope * rows_per_scale + b / nblk_row, kb = b % nblk_row;
+        uint4 v[2];
+        v[0] = *reinterpret_cast<const uint4 *>(x + r * ldx + kb * 16);
+        v[1] = *reinterpret_cast<const uint4 *>(x + r * ldx + kb * 16 + 8);
+        float xf[16];
+        unpack16(v, xf);
+        a = fmaxf(a, absmax16(xf));
+    }
+    a = wave_max(a);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (a > 0.0f) atomicMax(reinterpret_cast<unsigned int *>(outer + scope), __float_as_uint(a));
+    }
+}
+
+__global__ void k_fill_f32(float *p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// outer[s] holds amax; turn it into the decode scale g = amax / 2688.
+__global__ void k_amax_to_g(float *outer, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const float a = outer[i];
+        outer[i] = (a == 0.0f) ? 0.0f : a / 2688.0f;
+    }
+}
+
+// Quantize with precomputed outer scales: one lane per 16-value block.
+template <bool M46>
+__global__ __launch_bounds__(256) void k_nvfp4_blocks(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                      int64_t ldx, int64_t rows_per_scale,
+                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                      const float *__restrict__ outer) {
+    const int64_t nblk_row = K / 16;
+    const int64_t total = M * nblk_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / nblk_row, kb = i - r * nblk_row;
+        uint4 v[2];
+        v[0] = *reinterpret_cast<const uint4 *>(x + r * ldx + kb * 16);
+        v[1] = *reinterpret_cast<const uint4 *>(x + r * ldx + kb * 16 + 8);
+        float xf[16];
+        unpack16(v, xf);
+        Nvfp4Block b = nvfp4_block<M46>(xf, outer[r / rows_per_scale]);
+        *reinterpret_cast<uint2 *>(codes + r * (K / 2) + kb * 8) = make_uint2(b.lo, b.hi);
+        scales[r * nblk_row + kb] = (uint8_t)b.s;
+    }
+}
+
+static int grid_for(int64_t work, int per_block = 256, int cap = 65536) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    return (int)(g > cap ? cap : g);
+}
+
+hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, uint8_t *codes,
+                                 uint8_t *scales, float *outer, bool m46, hipStream_t s) {
+    if (rps == 1 && K <= 8192) {
+        dim3 grid((unsigned)((M + 3) / 4)), block(256);
+        if (K <= 2048) {
+            if (m46) k_nvfp4_row<true, 2><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
+            else k_nvfp4_row<false, 2><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
+        } else {
+            if (m46) k_nvfp4_row<true, 8><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
+            else k_nvfp4_row<false, 8><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
+        }
+        return hipGetLastError();
+    }
+    const int64_t nscope = M / rps;
+    k_fill_f32<<<grid_for(nscope), 256, 0, s>>>(outer, nscope, 0.0f);
+    const int64_t nblk = M * (K / 16);
+    const int64_t per_scope = rps * (K / 16);
+    int64_t slices = (2048 + nscope - 1) / nscope;                     // about 2048 blocks in flight
+    const int64_t max_slices = (per_scope + 1023) / 1024;              // at least 1024 16-blocks each
+    slices = slices < max_slices ? slices : max_slices;
+    slices = slices < 1 ? 1 : (slices > 65535 ? 65535 : slices);
+    k_scope_amax<<<dim3((unsigned)nscope, (unsigned)slices), 256, 0, s>>>(x, K, ldx, rps, outer);
+    k_amax_to_g<<<grid_for(nscope), 256, 0, s>>>(outer, nscope);
+    if (m46) k_nvfp4_blocks<true><<<grid_for(nblk, 256, 16384), 256, 0, s>>>(x, M, K, ldx, rps, codes, scales, outer);
+    else k_nvfp4_blocks<false><<<grid_for(nblk, 256, 16384), 256, 0, s>>>(x, M, K, ldx, rps, codes, scales, outer);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// MXFP8
+// --------------------------------------------------------------------------
+
+// Quantize 32 values (f32) sharing one E8M0 scale; returns the scale code.
+__device__ __forceinline__ uint32_t mxfp8_block(const float (&xf)[32], uint32_t (&q)[8]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) a = fmaxf(a, fabsf(xf[i]));
+    const int k = mx_block_exponent(a);
+    // 2^-k is a normal f32 for k in [-127, 119]; the product is exact unless it
+    // falls below 2^-126, far under E4M3's rounding threshold.
+    const float inv = exp2i(-k);
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) word |= e4m3_encode(xf[4 * w + b] * inv) << (8 * b);
+        q[w] = word;
+    }
+    return (uint32_t)(k + 127);
+}
+
+constexpr int MX_TR = 128;  // tile rows (padded row space)
+constexpr int MX_TC = 64;   // tile columns
+constexpr int MX_MAXG = 2048;
+
+// One 128 x 64 tile: rowwise blocks (32 along K) straight from registers and
+// columnwise blocks (32 along rows) through LDS, from a single read of x.
+// Grouped: tile rows live in the padded row space; block b belongs to the
+// group g with P[g] <= 32 b < P[g + 1] and reads source row
+// off[g] + (p - P[g]) (zero past the group).
+template <bool ROW, bool COL, bool GROUPED>
+__global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                    int64_t ldx, uint8_t *__restrict__ codes_row,
+                                                    uint8_t *__restrict__ scales_row, uint8_t *__restrict__ codes_colT,
+                                                    uint8_t *__restrict__ scales_colT, int64_t ld_colT,
+                                                    const int64_t *__restrict__ group_offsets, int G) {
+    __shared__ uint16_t tile[MX_TR][MX_TC + 8];
+    __shared__ int64_t sP[GROUPED ? MX_MAXG + 1 : 1];
+    __shared__ int64_t sOff[GROUPED ? MX_MAXG + 1 : 1];
+    __shared__ int64_t blk_src0[MX_TR / 32], blk_end[MX_TR / 32];
+    const int t = threadIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * MX_TR;
+    const int64_t k0 = (int64_t)blockIdx.x * MX_TC;
+    int64_t ptotal = M;
+
+    if (GROUPED) {
+        // padded group starts P (running sum of roundup32(n_g)), scanned in LDS
+        for (int g = t; g <= G; g += 256) sOff[g] = group_offsets[g];
+        __syncthreads();
+        const int per = (G + 255) / 256;
+        const int g0 = t * per;
+        int64_t local = 0;
+        for (int g = g0; g < g0 + per && g < G; g++) local += (sOff[g + 1] - sOff[g] + 31) / 32 * 32;
+        __shared__ int64_t part[256];
+        part[t] = local;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            int64_t v = (t >= o) ? part[t - o] : 0;
+            __syncthreads();
+            part[t] += v;
+            __syncthreads();
+        }
+        int64_t run = part[t] - local;
+        for (int g = g0; g < g0 + per && g < G; g++) {
+            sP[g] = run;
+            run += (sOff[g + 1] - sOff[g] + 31) / 32 * 32;
+        }
+        if (t == 255) sP[G] = part[255];
+        __syncthreads();
+        ptotal = sP[G];
+        if (t < MX_TR / 32) {
+            const int64_t pb = p0 + 32 * t;
+            int64_t src0 = 0, end = 0;
+            if (pb < ptotal) {
+                int lo = 0, hi = G - 1;  // last g with P[g] <= pb
+                while (lo < hi) {
+                    int mid = (lo + hi + 1) / 2;
+                    if (sP[mid] <= pb) lo = mid;
+                    else hi = mid - 1;
+                }
+                // skip empty groups sharing the same start
+                while (lo + 1 < G && sP[lo + 1] <= pb) lo++;
+                src0 = sOff[lo] + (pb - sP[lo]);
+                end = sOff[lo + 1] < M ? sOff[lo + 1] : M;  // offsets past M are never read
+            }
+            blk_src0[t] = src0;
+            blk_end[t] = end;
+        }
+        __syncthreads();
+        if (p0 >= ptotal) return;
+    }
+
+    // ---- load: thread t owns tile row t/2, columns [32 (t%2), +32) ----
+    const int tr = t >> 1, half = t & 1;
+    const int64_t p = p0 + tr;
+    const int64_t kc = k0 + 32 * half;
+    int64_t src = -1;
+    if (GROUPED) {
+        const int b = tr >> 5;
+        const int64_t s_ = blk_src0[b] + (tr & 31);
+        if (p < ptotal && s_ >= 0 && s_ < blk_end[b]) src = s_;
+    } else {
+        if (p < M) src = p;
+    }
+    const bool col_ok = kc < K;
+    float xf[32];
+    uint4 raw[4] = {};
+    if (src >= 0 && col_ok) {
+        const uint16_t *xp = x + src * ldx + kc;
+#pragma unroll
+        for (int i = 0; i < 4; i++) raw[i] = reinterpret_cast<const uint4 *>(xp)[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            xf[8 * i + 2 * j] = bf16_lo(w[j]);
+            xf[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+        }
+    }
+    if (ROW && src >= 0 && col_ok) {
+        uint32_t q[8];
+        const uint32_t sc = mxfp8_block(xf, q);
+        uint4 *dst = reinterpret_cast<uint4 *>(codes_row + src * K + kc);
+        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+        scales_row[src * (K / 32) + kc / 32] = (uint8_t)sc;
+    }
+    if (!COL) return;
+#pragma unroll
+    for (int i = 0; i < 4; i++) *reinterpret_cast<uint4 *>(&tile[tr][32 * half + 8 * i]) = raw[i];
+    __syncthreads();
+
+    // ---- columns: thread t owns column t%64 of the 32-row block t/64 ----
+    const int c = t & 63, b = t >> 6;
+    const int64_t kcol = k0 + c;
+    const int64_t pb = p0 + 32 * b;
+    const int64_t plimit = GROUPED ? ptotal : M;
+    if (kcol >= K || pb >= plimit) return;
+    float cf[32];
+#pragma unroll
+    for (int i = 0; i < 32; i++) cf[i] = __uint_as_float((uint32_t)tile[32 * b + i][c] << 16);
+    uint32_t q[8];
+    const uint32_t sc = mxfp8_block(cf, q);
+    uint4 *dst = reinterpret_cast<uint4 *>(codes_colT + kcol * ld_colT + pb);
+    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+    scales_colT[kcol * (ld_colT / 32) + pb / 32] = (uint8_t)sc;
+}
+
+// Rowwise-only MXFP8: one lane per 32-value block.
+__global__ __launch_bounds__(256) void k_mxfp8_row(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const int64_t nb = K / 32, total = M * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / nb, kb = i - r * nb;
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + r * ldx + kb * 32);
+        float xf[32];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const uint4 raw = src[v];
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xf[8 * v + 2 * j] = bf16_lo(w[j]);
+                xf[8 * v + 2 * j + 1] = bf16_hi(w[j]);
+            }
+        }
+        uint32_t q[8];
+        const uint32_t sc = mxfp8_block(xf, q);
+        uint4 *dst = reinterpret_cast<uint4 *>(codes + r * K + kb * 32);
+        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+        scales[i] = (uint8_t)sc;
+    }
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
+                                 uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT, int64_t ld_colT,
+                                 const int64_t *group_offsets, int64_t G, hipStream_t s) {
+    const bool row = codes_row != nullptr, col = codes_colT != nullptr;
+    if (!col) {
+        k_mxfp8_row<<<grid_for(M * (K / 32), 256, 1 << 20), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row);
+        return hipGetLastError();
+    }
+    const unsigned gx = (unsigned)((K + MX_TC - 1) / MX_TC);
+    if (group_offsets) {
+        const unsigned gy = (unsigned)((ld_colT + MX_TR - 1) / MX_TR);
+        if (row)
+            k_mxfp8_tile<true, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                        codes_colT, scales_colT, ld_colT,
+                                                                        group_offsets, (int)G);
+        else
+            k_mxfp8_tile<false, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                         codes_colT, scales_colT, ld_colT,
+                                                                         group_offsets, (int)G);
+    } else {
+        const unsigned gy = (unsigned)((M + MX_TR - 1) / MX_TR);
+        if (row)
+            k_mxfp8_tile<true, true, false><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                         codes_colT, scales_colT, ld_colT, nullptr, 1);
+        else
+            k_mxfp8_tile<false, true, false><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                          codes_colT, scales_colT, ld_colT, nullptr,
+                                                                          1);
+    }
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Dequantize
+// --------------------------------------------------------------------------
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ scales,
+                                                       const float *__restrict__ outer, int64_t M, int64_t K,
+                                                       int64_t rps, void *__restrict__ out) {
+    const int64_t nb = K / 16, total = M * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / nb;
+        const float eff = e4m3_decode(scales[i]) * outer[r / rps];
+        const uint2 c = *reinterpret_cast<const uint2 *>(codes + i * 8);
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            y[j] = e2m1_value((c.x >> (4 * j)) & 15u) * eff;
+            y[8 + j] = e2m1_value((c.y >> (4 * j)) & 15u) * eff;
+        }
+        if (BF16) {
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) w[j] = f32_to_bf16(y[2 * j]) | (f32_to_bf16(y[2 * j + 1]) << 16);
+            uint4 *d = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + i * 16);
+            d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+            float4 *d = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + i * 16);
+#pragma unroll
+            for (int j = 0; j < 4; j++) d[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+        }
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequant_mxfp8(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ scales, int64_t M, int64_t K,
+                                                       void *__restrict__ out) {
+    const int64_t nb = K / 32, total = M * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int k = (int)scales[i] - 127;
+        const uint4 *cp = reinterpret_cast<const uint4 *>(codes + i * 32);
+        const uint4 c0 = cp[0], c1 = cp[1];
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        float y[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) y[j] = ldexpf(e4m3_decode((w[j >> 2] >> (8 * (j & 3))) & 0xFFu), k);
+        if (BF16) {
+            uint4 *d = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + i * 32);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t v[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    v[j] = f32_to_bf16(y[8 * q + 2 * j]) | (f32_to_bf16(y[8 * q + 2 * j + 1]) << 16);
+                d[q] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        } else {
+            float4 *d = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + i * 32);
+#pragma unroll
+            for (int j = 0; j < 8; j++) d[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+        }
+    }
+}
+
+hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M,
+                             int64_t K, int64_t rps, void *out, int out_dtype, hipStream_t s) {
+    const bool bf = out_dtype == 1;
+    if (fmt == 0) {
+        const int grid = grid_for(M * (K / 16), 256, 1 << 20);
+        if (bf) k_dequant_nvfp4<true><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, rps, out);
+        else k_dequant_nvfp4<false><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, rps, out);
+    } else {
+        const int grid = grid_for(M * (K / 32), 256, 1 << 20);
+        if (bf) k_dequant_mxfp8<true><<<grid, 256, 0, s>>>(codes, scales, M, K, out);
+        else k_dequant_mxfp8<false><<<grid, 256, 0, s>>>(codes, scales, M, K, out);
+    }
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Dequantize -> transpose -> requantize (stochastic rounding)
+// --------------------------------------------------------------------------
+
+constexpr int RQ_TM = 128;  // input rows (m) per tile
+constexpr int RQ_TK = 128;  // input columns (k) per tile
+constexpr int RQ_MAXPART = 64;
+
+// Partial maxima of the per-row outer scales (G = max over all partials).
+__global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restrict__ outer, int64_t M,
+                                                           float *__restrict__ part) {
+    const int64_t chunk = (M + gridDim.x - 1) / gridDim.x;
+    const int64_t a = (int64_t)blockIdx.x * chunk, b = a + chunk < M ? a + chunk : M;
+    float m = 0.0f;
+    for (int64_t i = a + threadIdx.x; i < b; i += blockDim.x) m = fmaxf(m, outer[i]);
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Stochastic rounding of v >= 0 onto the E2M1 grid with 16 random bits u.
+__device__ __forceinline__ uint32_t e2m1_sr_mag(float v, uint32_t u) {
+    if (v >= 6.0f) return 7u;
+    // lower neighbour: truncating encode (largest grid value <= v)
+    uint32_t lo;
+    float lov, gap;
+    if (v < 2.0f) {
+        lo = (uint32_t)(v * 2.0f);          // 0..3: grid step 0.5 below 2
+        lov = 0.5f * (float)lo;
+        gap = 0.5f;
+    } else if (v < 4.0f) {
+        lo = v < 3.0f ? 4u : 5u;
+        lov = v < 3.0f ? 2.0f : 3.0f;
+        gap = 1.0f;
+    } else {
+        lo = 6u;
+        lov = 4.0f;
+        gap = 2.0f;
+    }
+    const float frac = (v - lov) / gap;    // exact: Sterbenz, then a power of two
+    return ((float)u < frac * 65536.0f) ? lo + 1u : lo;
+}
+
+template <bool SR>
+__global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 const float *__restrict__ outer, int64_t M, int64_t K,
+                                                 uint8_t *__restrict__ codesT, uint8_t *__restrict__ scalesT,
+                                                 float *__restrict__ outerT, const float *__restrict__ part, int npart,
+                                                 uint32_t key0, uint32_t key1) {
+    __shared__ uint8_t sc[RQ_TM][RQ_TK / 2 + 4];
+    __shared__ float seff[RQ_TM][RQ_TK / 16 + 1];
+    const int t = threadIdx.x;
+    const int64_t m0 = (int64_t)blockIdx.y * RQ_TM, k0 = (int64_t)blockIdx.x * RQ_TK;
+
+    float G = 0.0f;
+    if (t < 64) {
+        G = (t < npart) ? part[t] : 0.0f;
+        G = wave_max(G);
+    }
+    __shared__ float sG;
+    if (t == 0) {
+        sG = G;
+        if (blockIdx.x == 0 && blockIdx.y == 0) *outerT = G;
+    }
+
+    // load: thread t -> input row m0 + t/2, 32 code bytes (64 k values), in
+    // 8-byte units of 16 k values (the row pitch K/2 is a multiple of 8)
+    {
+        const int r = t >> 1, h = t & 1;
+        const int64_t m = m0 + r, kb = k0 + 64 * h;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            uint2 c = make_uint2(0u, 0u);
+            if (m < M && kb + 16 * u < K) c = *reinterpret_cast<const uint2 *>(codes + m * (K / 2) + kb / 2 + 8 * u);
+            *reinterpret_cast<uint2 *>(&sc[r][32 * h + 8 * u]) = c;
+        }
+        if (h == 0 && m < M) {
+            const float g = outer[m];
+            for (int j = 0; j < RQ_TK / 16; j++) {
+                const int64_t kk = k0 + 16 * j;
+                seff[r][j] = (kk < K) ? e4m3_decode(scales[m * (K / 16) + kk / 16]) * g : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+    G = sG;
+
+    // outputs: item = (output row k, 16-row block j); 8 consecutive threads
+    // cover the 8 blocks of one output row (64 contiguous bytes)
+    for (int it = t; it < RQ_TK * (RQ_TM / 16); it += 256) {
+        const int kk = it >> 3, j = it & 7;
+        const int64_t k = k0 + kk, mb = m0 + 16 * j;
+        if (k >= K || mb >= M) continue;
+        float d[16];
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t byte = sc[16 * j + i][kk >> 1];
+            const uint32_t c = (kk & 1) ? (byte >> 4) : (byte & 15u);
+            d[i] = e2m1_value(c) * seff[16 * j + i][kk >> 4];
+            a = fmaxf(a, fabsf(d[i]));
+        }
+        uint32_t s = 0u;
+        float eff = 0.0f;
+        if (G > 0.0f) {
+            const float denom = 6.0f * G;
+            s = e4m3_encode(a / denom);
+            eff = e4m3_decode(s) * G;
+        }
+        uint32_t lo = 0u, hi = 0u;
+        if (!(G > 0.0f) || eff < kFlushBelow) {
+            s = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                lo |= ((__float_as_uint(d[i]) >> 28) & 8u) << (4 * i);
+                hi |= ((__float_as_uint(d[8 + i]) >> 28) & 8u) << (4 * i);
+            }
+        } else {
+            const float r = 1.0f / eff;
+            uint32_t rnd[8];
+            if (SR) {
+                // element index i = k*M + m; Philox block (i / 8) gives 8 x 16 bits
+                const uint64_t blk = ((uint64_t)k * (uint64_t)M + (uint64_t)mb) >> 3;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    uint32_t c[4] = {(uint32_t)(blk + h), (uint32_t)((blk + h) >> 32), 0u, 0u};
+                    philox4x32_10(c, key0, key1);
+#pragma unroll
+                    for (int w = 0; w < 4; w++) rnd[4 * h + w] = c[w];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const float v = fabsf(d[i]) * r;
+                uint32_t mag;
+                if (SR) {
+                    const uint32_t word = rnd[i >> 1];
+                    mag = e2m1_sr_mag(v, (i & 1) ? (word >> 16) : (word & 0xFFFFu));
+                } else {
+                    mag = e2m1_mag(v);
+                }
+                const uint32_t code = ((__float_as_uint(d[i]) >> 28) & 8u) | mag;
+                if (i < 8) lo |= code << (4 * i);
+                else hi |= code << (4 * (i - 8));
+            }
+        }
+        *reinterpret_cast<uint2 *>(codesT + k * (M / 2) + mb / 2) = make_uint2(lo, hi);
+        scalesT[k * (M / 16) + mb / 16] = (uint8_t)s;
+    }
+}
+
+int requant_partials(int64_t M) {
+    int64_t n = (M + 4095) / 4096;
+    return (int)(n < 1 ? 1 : (n > RQ_MAXPART ? RQ_MAXPART : n));
+}
+
+hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M, int64_t K,
+                          uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed, bool sr, float *part,
+                          hipStream_t s) {
+    const int np = requant_partials(M);
+    k_outer_partial_max<<<np, 256, 0, s>>>(outer, M, part);
+    dim3 grid((unsigned)((K + RQ_TK - 1) / RQ_TK), (unsigned)((M + RQ_TM - 1) / RQ_TM));
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    if (sr) k_requant<true><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1);
+    else k_requant<false><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// SwiGLU + quantization of its output
+// --------------------------------------------------------------------------
+
+// exp(x) in f32 by one fixed sequence: n = rint(x / ln 2), r = x - n ln 2 with
+// ln 2 split in a 16-bit head (n * head is exact) and a tail, e^r by its
+// degree-7 Taylor polynomial in Horner form, then the exact scaling by 2^n.
+__device__ __forceinline__ float exp_cw(float x) {
+    if (x >= 89.0f) return __builtin_huge_valf();
+    if (x <= -104.0f) return 0.0f;
+    const float n = rintf(x * 1.44269504088896341f);
+    const float r = (x - n * 0.693145751953125f) - n * 1.428606765330187e-06f;
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T *p);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+
+// One wavefront per row of h; lane l owns the 32-value chunks starting at
+// i = 2048 j + 32 l.  FMT: -1 = h only, 0 = NVFP4 per token, 1 = MXFP8 rowwise.
+template <typename T, int FMT, bool M46, int MAXIT>
+__global__ __launch_bounds__(256) void k_swiglu(const T *__restrict__ h13, int64_t R, int64_t I,
+                                                uint16_t *__restrict__ h_out, uint8_t *__restrict__ codes,
+                                                uint8_t *__restrict__ scales, float *__restrict__ outer) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= R) return;
+    const T *gp = h13 + row * 2 * I;
+    const T *up = gp + I;
+    float hv[MAXIT][32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAXIT; j++) {
+        const int64_t i0 = (int64_t)j * 2048 + lane * 32;
+        if (i0 < I) {
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                const float z = load_elem<T>(gp + i0 + i);
+                const float u = load_elem<T>(up + i0 + i);
+                const float silu = z / (1.0f + exp_cw(-z));
+                const uint32_t hb = f32_to_bf16(silu * u);
+                hv[j][i] = __uint_as_float(hb << 16);
+            }
+            if (h_out) {
+                uint4 *dst = reinterpret_cast<uint4 *>(h_out + row * I + i0);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        w[k] = (__float_as_uint(hv[j][8 * q + 2 * k]) >> 16) |
+                               (__float_as_uint(hv[j][8 * q + 2 * k + 1]) & 0xFFFF0000u);
+                    dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(hv[j][i]));
+        }
+    }
+    if (FMT < 0) return;
+    if (FMT == 0) {
+        amax = wave_max(amax);
+        const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
+        if (lane == 0) outer[row] = g;
+#pragma unroll
+        for (int j = 0; j < MAXIT; j++) {
+            const int64_t i0 = (int64_t)j * 2048 + lane * 32;
+            if (i0 < I) {
+#pragma unroll
+                for (int b = 0; b < 2; b++) {
+                    float xf[16];
+#pragma unroll
+                    for (int i = 0; i < 16; i++) xf[i] = hv[j][16 * b + i];
+                    Nvfp4Block nb = nvfp4_block<M46>(xf, g);
+                    *reinterpret_cast<uint2 *>(codes + row * (I / 2) + (i0 + 16 * b) / 2) = make_uint2(nb.lo, nb.hi);
+                    scales[row * (I / 16) + (i0 + 16 * b) / 16] = (uint8_t)nb.s;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < MAXIT; j++) {
+            const int64_t i0 = (int64_t)j * 2048 + lane * 32;
+            if (i0 < I) {
+                uint32_t q[8];
+                const uint32_t sc = mxfp8_block(hv[j], q);
+                uint4 *dst = reinterpret_cast<uint4 *>(codes + row * I + i0);
+                dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+                dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+                scales[row * (I / 32) + i0 / 32] = (uint8_t)sc;
+            }
+        }
+    }
+}
+
+template <typename T, int FMT, bool M46>
+static void swiglu_dispatch_it(const void *h13, int64_t R, int64_t I, uint16_t *h_out, uint8_t *codes,
+                               uint8_t *scales, float *outer, hipStream_t s) {
+    dim3 grid((unsigned)((R + 3) / 4)), block(256);
+    const T *in = reinterpret_cast<const T *>(h13);
+    if (I <= 2048) k_swiglu<T, FMT, M46, 1><<<grid, block, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else k_swiglu<T, FMT, M46, 4><<<grid, block, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+}
+
+template <typename T>
+static void swiglu_dispatch(const void *h13, int64_t R, int64_t I, uint16_t *h_out, int fmt, bool m46,
+                            uint8_t *codes, uint8_t *scales, float *outer, hipStream_t s) {
+    if (fmt < 0) swiglu_dispatch_it<T, -1, false>(h13, R, I, h_out, codes, scales, outer, s);
+    else if (fmt == 0 && m46) swiglu_dispatch_it<T, 0, true>(h13, R, I, h_out, codes, scales, outer, s);
+    else if (fmt == 0) swiglu_dispatch_it<T, 0, false>(h13, R, I, h_out, codes, scales, outer, s);
+    else swiglu_dispatch_it<T, 1, false>(h13, R, I, h_out, codes, scales, outer, s);
+}
+
+hipError_t launch_swiglu(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out, int fmt, bool m46,
+                         uint8_t *codes, uint8_t *scales, float *outer, hipStream_t s) {
+    if (in_dtype == 0) swiglu_dispatch<float>(h13, R, I, h_out, fmt, m46, codes, scales, outer, s);
+    else swiglu_dispatch<uint16_t>(h13, R, I, h_out, fmt, m46, codes, scales, outer, s);
+    return hipGetLastError();
+}
+
+}  // namespace bsp

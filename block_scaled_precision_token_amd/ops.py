@@ -1,0 +1,274 @@
+"""Python binding of the C ABI in ``include/bsp.h`` (argument marshalling only).
+
+Every function allocates its outputs as torch tensors on the input's device,
+passes raw device pointers and the current HIP stream to ``libbsp.so`` and
+returns the outputs; all computation happens in the library's kernels.  The
+library is loaded on first use and a missing library raises -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libbsp.so")
+
+FMT_NVFP4 = 0
+FMT_MXFP8 = 1
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+GEMM_FPROP = 0
+GEMM_DGRAD = 1
+GEMM_WGRAD = 2
+NVFP4_46 = 0x1
+SR = 0x2
+
+STATUS = {0: "BSP_OK", 1: "BSP_ERR_INVALID_ARG", 2: "BSP_ERR_SHAPE", 3: "BSP_ERR_ALIGNMENT",
+          4: "BSP_ERR_UNSUPPORTED", 5: "BSP_ERR_WORKSPACE", 6: "BSP_ERR_HIP"}
+
+EXPORTED = [
+    "bsp_version", "bsp_status_string", "bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize",
+    "bsp_requant_transpose_sr", "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes",
+    "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
+]
+
+
+class BspError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({_lib_raw().bsp_status_string(status).decode()})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+U32 = ctypes.c_uint32
+U64 = ctypes.c_uint64
+SZ = ctypes.c_size_t
+INT = ctypes.c_int
+
+
+def _declare(lib):
+    lib.bsp_version.restype = INT
+    lib.bsp_status_string.argtypes = [INT]
+    lib.bsp_status_string.restype = ctypes.c_char_p
+    lib.bsp_quantize_nvfp4_per_token.argtypes = [P, I64, I64, I64, I64, P, P, P, U32, P]
+    lib.bsp_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, U32, P]
+    lib.bsp_dequantize.argtypes = [INT, P, P, P, I64, I64, I64, P, INT, P]
+    lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
+    lib.bsp_moe_grouped_gemm_blockscaled.argtypes = [INT, INT, P, P, P, P, I64, P, I64, I64, I64, I64, P, P, P, P,
+                                                     INT, I64, P, SZ, P]
+    lib.bsp_swiglu_quantize.argtypes = [P, INT, I64, I64, P, INT, P, P, P, U32, P]
+    lib.bsp_nvfp4_sizes.argtypes = [I64, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    lib.bsp_mxfp8_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    lib.bsp_mxfp8_grouped_cols.argtypes = [I64, I64]
+    lib.bsp_mxfp8_grouped_cols.restype = I64
+    lib.bsp_requant_workspace_size.argtypes = [I64]
+    lib.bsp_requant_workspace_size.restype = SZ
+    lib.bsp_gemm_workspace_size.argtypes = [INT, I64, I64]
+    lib.bsp_gemm_workspace_size.restype = SZ
+    for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
+                 "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes"):
+        getattr(lib, name).restype = INT
+
+
+def _lib_raw():
+    """Load libbsp.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                                   "(run `python -c 'import __graft_entry__ as g; g.build()'`)")
+            lib = ctypes.CDLL(LIB_PATH)
+            _declare(lib)
+            _lib = lib
+    return _lib
+
+
+lib = _lib_raw
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise BspError(status, fn)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+
+
+# ---------------------------------------------------------------------------
+# ops
+# ---------------------------------------------------------------------------
+
+def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1, mode46: bool = False, out=None):
+    """bf16 [M, K] -> (codes u8 [M, K/2], scales u8 [M, K/16], outer f32 [M / rows_per_scale])."""
+    _need_cuda(x, "x")
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        outer = torch.empty((max(M // max(rows_per_scale, 1), 1),), dtype=torch.float32, device=dev)
+    else:
+        codes, scales, outer = out
+    flags = NVFP4_46 if mode46 else 0
+    st = _lib_raw().bsp_quantize_nvfp4_per_token(_ptr(x), M, K, x.stride(0), rows_per_scale, _ptr(codes),
+                                                 _ptr(scales), _ptr(outer), flags, _stream(dev))
+    _check(st, "bsp_quantize_nvfp4_per_token")
+    return codes, scales, outer
+
+
+def mxfp8_grouped_cols(M: int, G: int) -> int:
+    return int(_lib_raw().bsp_mxfp8_grouped_cols(M, G))
+
+
+def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False, group_offsets=None,
+                   ld_colT: int | None = None, out=None):
+    """bf16 [M, K] -> dict with 'codes_row' [M,K], 'scales_row' [M,K/32], 'codes_colT' [K,ld], 'scales_colT' [K,ld/32]."""
+    _need_cuda(x, "x")
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    M, K = x.shape
+    dev = x.device
+    res = {"codes_row": None, "scales_row": None, "codes_colT": None, "scales_colT": None}
+    if out is not None:
+        res.update(out)
+    else:
+        if rowwise:
+            res["codes_row"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            res["scales_row"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        if colwise:
+            if ld_colT is None:
+                ld_colT = M if group_offsets is None else mxfp8_grouped_cols(M, group_offsets.numel() - 1)
+            res["codes_colT"] = torch.empty((K, ld_colT), dtype=torch.uint8, device=dev)
+            res["scales_colT"] = torch.empty((K, ld_colT // 32), dtype=torch.uint8, device=dev)
+    if res["codes_colT"] is not None:
+        ld_colT = res["codes_colT"].shape[1]
+    G = 0 if group_offsets is None else group_offsets.numel() - 1
+    st = _lib_raw().bsp_quantize_mxfp8(_ptr(x), M, K, x.stride(0), _ptr(res["codes_row"]), _ptr(res["scales_row"]),
+                                       _ptr(res["codes_colT"]), _ptr(res["scales_colT"]), ld_colT or 0,
+                                       _ptr(group_offsets), G, 0, _stream(dev))
+    _check(st, "bsp_quantize_mxfp8")
+    return res
+
+
+def dequantize(fmt: int, codes, scales, outer=None, rows_per_scale: int = 1, out_dtype=torch.float32, out=None):
+    _need_cuda(codes, "codes")
+    M = codes.shape[0]
+    K = codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=codes.device)
+    dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    st = _lib_raw().bsp_dequantize(fmt, _ptr(codes), _ptr(scales), _ptr(outer), M, K, rows_per_scale, _ptr(out), dt,
+                                   _stream(codes.device))
+    _check(st, "bsp_dequantize")
+    return out
+
+
+def requant_workspace_size(M: int) -> int:
+    return int(_lib_raw().bsp_requant_workspace_size(M))
+
+
+def requant_transpose_sr(codes, scales, outer, seed: int = 0, sr: bool = True, workspace=None, out=None):
+    """Rowwise NVFP4 [M, K] -> (codesT [K, M/2], scalesT [K, M/16], outerT [1])."""
+    _need_cuda(codes, "codes")
+    M, K = codes.shape[0], codes.shape[1] * 2
+    dev = codes.device
+    if out is None:
+        codesT = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
+        scalesT = torch.empty((K, M // 16), dtype=torch.uint8, device=dev)
+        outerT = torch.empty((4,), dtype=torch.float32, device=dev)
+    else:
+        codesT, scalesT, outerT = out
+    if workspace is None:
+        workspace = torch.empty((requant_workspace_size(M),), dtype=torch.uint8, device=dev)
+    st = _lib_raw().bsp_requant_transpose_sr(_ptr(codes), _ptr(scales), _ptr(outer), M, K, _ptr(codesT),
+                                             _ptr(scalesT), _ptr(outerT), seed & (2 ** 64 - 1), SR if sr else 0,
+                                             _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "bsp_requant_transpose_sr")
+    return codesT, scalesT, outerT[:1]
+
+
+def gemm_workspace_size(mode: int, M: int, G: int) -> int:
+    return int(_lib_raw().bsp_gemm_workspace_size(mode, M, G))
+
+
+def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets, N: int,
+                                 K: int, M: int | None = None, a_outer=None, b_outer=None, a_gather=None,
+                                 out_dtype=torch.float32, out=None, workspace=None):
+    """Grouped block-scaled GEMM; see bsp_moe_grouped_gemm_blockscaled in include/bsp.h.
+
+    FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
+    with M = rows of A (the columnwise copies' K dimension is their ld).
+    """
+    _need_cuda(a_codes, "a_codes")
+    dev = a_codes.device
+    G = group_offsets.numel() - 1
+    a_rows = a_codes.shape[0]
+    if M is None:
+        M = a_gather.numel() if a_gather is not None else a_rows
+    if out is None:
+        shape = (G, M, N) if mode == GEMM_WGRAD else (M, N)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    ldc = out.shape[-1] if out.dim() >= 2 else N
+    dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    if workspace is None:
+        workspace = torch.empty((max(gemm_workspace_size(mode, M, G), 16),), dtype=torch.uint8, device=dev)
+    st = _lib_raw().bsp_moe_grouped_gemm_blockscaled(fmt, mode, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer),
+                                                     _ptr(a_gather), a_rows, _ptr(group_offsets), G, M, N, K,
+                                                     _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt,
+                                                     ldc, _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "bsp_moe_grouped_gemm_blockscaled")
+    return out
+
+
+def swiglu_quantize(h13: torch.Tensor, fmt: int = -1, mode46: bool = False, return_h: bool = True, out=None):
+    """h13 [R, 2I] (f32 or bf16) -> (h bf16 [R, I] or None, codes, scales, outer)."""
+    _need_cuda(h13, "h13")
+    R, I2 = h13.shape
+    I = I2 // 2
+    dev = h13.device
+    h = codes = scales = outer = None
+    if out is not None:
+        h, codes, scales, outer = out
+    else:
+        if return_h or fmt < 0:
+            h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        if fmt == FMT_NVFP4:
+            codes = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((R, I // 16), dtype=torch.uint8, device=dev)
+            outer = torch.empty((R,), dtype=torch.float32, device=dev)
+        elif fmt == FMT_MXFP8:
+            codes = torch.empty((R, I), dtype=torch.uint8, device=dev)
+            scales = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+    dt = DTYPE_BF16 if h13.dtype == torch.bfloat16 else DTYPE_F32
+    st = _lib_raw().bsp_swiglu_quantize(_ptr(h13), dt, R, I, _ptr(h), fmt, _ptr(codes), _ptr(scales), _ptr(outer),
+                                        NVFP4_46 if mode46 else 0, _stream(dev))
+    _check(st, "bsp_swiglu_quantize")
+    return h, codes, scales, outer

@@ -1,0 +1,54 @@
+"""Helpers shared by the GPU parity tests (host <-> device marshalling and the
+GEMM tolerance)."""
+import numpy as np
+import torch
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def assert_bytes_equal(got, ref, what=""):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.dtype == np.float32:
+        got = got.view(np.uint32)
+        ref = ref.view(np.uint32)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]}"
+
+
+def gemm_errors(c: np.ndarray, ref: np.ndarray, refabs: np.ndarray):
+    """(max |C-R| / sum|a b|, max |C-R| / max |R|) -- the parity bound of the GEMM."""
+    d = np.abs(c.astype(np.float64) - ref)
+    norm = d / np.maximum(refabs, 1e-300)
+    norm[refabs == 0] = d[refabs == 0]
+    return float(norm.max()), float(d.max() / max(np.abs(ref).max(), 1e-300))
+
+
+def assert_gemm_close(c, ref, refabs, bf16=False, tol=1e-3):
+    c = np.asarray(c, dtype=np.float64)
+    if bf16:
+        # bf16 output adds its own relative rounding of 2^-9
+        d = np.abs(c - ref)
+        allowed = tol * refabs + 2.0 ** -8 * np.abs(ref) + 1e-300
+        assert np.all(d <= allowed), float((d / allowed).max())
+        return
+    e_norm, e_wise = gemm_errors(c, ref, refabs)
+    assert e_norm <= tol, e_norm
+    assert e_wise <= tol, e_wise

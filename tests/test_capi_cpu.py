@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, computes its size helpers, and rejects invalid calls before
+any HIP call (so nothing is enqueued and no device is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_precision_token_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsp.h")
+
+if not os.path.exists(ops.LIB_PATH):
+    pytest.skip("libbsp.so not built", allow_module_level=True)
+
+L = ops.lib()
+A = ctypes.c_void_p(1 << 20)        # a 16-byte aligned, never dereferenced address
+MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ops.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert L.bsp_version() == 100
+    for s in range(7):
+        assert len(L.bsp_status_string(s)) > 0
+    assert L.bsp_status_string(99) == b"unknown status"
+
+
+def test_size_helpers():
+    c, s, o = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.bsp_nvfp4_sizes(8192, 2048, 1, ctypes.byref(c), ctypes.byref(s), ctypes.byref(o)) == 0
+    assert (c.value, s.value, o.value) == (8192 * 1024, 8192 * 128, 8192)
+    assert L.bsp_nvfp4_sizes(8192, 2040, 1, ctypes.byref(c), ctypes.byref(s), ctypes.byref(o)) == 2
+    assert L.bsp_mxfp8_sizes(4096, 7168, ctypes.byref(c), ctypes.byref(s)) == 0
+    assert (c.value, s.value) == (4096 * 7168, 4096 * 224)
+    assert L.bsp_mxfp8_grouped_cols(100, 4) == 224          # roundup32(100 + 31*4)
+    assert L.bsp_gemm_workspace_size(0, 65536, 128) == (512 + 128) * 8
+    assert L.bsp_gemm_workspace_size(2, 36864, 257) == 258 * 8
+    assert L.bsp_requant_workspace_size(16384) >= 4
+
+
+def test_nvfp4_rejects_bad_arguments():
+    q = L.bsp_quantize_nvfp4_per_token
+    assert q(None, 4, 32, 32, 1, A, A, A, 0, None) == 1
+    assert q(A, 4, 30, 32, 1, A, A, A, 0, None) == 2        # K % 16
+    assert q(A, 4, 32, 16, 1, A, A, A, 0, None) == 2        # ldx < K
+    assert q(A, 4, 32, 32, 3, A, A, A, 0, None) == 2        # rows_per_scale does not divide M
+    assert q(A, 0, 32, 32, 1, A, A, A, 0, None) == 2
+    assert q(MIS, 4, 32, 32, 1, A, A, A, 0, None) == 3
+    assert q(A, 4, 32, 36, 1, A, A, A, 0, None) == 3        # ldx % 8
+    assert q(A, 4, 32, 32, 1, A, A, A, 0x80, None) == 1     # unknown flag
+
+
+def test_mxfp8_rejects_bad_arguments():
+    q = L.bsp_quantize_mxfp8
+    assert q(A, 64, 64, 64, None, None, None, None, 0, None, 0, 0, None) == 1   # nothing requested
+    assert q(A, 64, 64, 64, A, None, None, None, 0, None, 0, 0, None) == 1      # codes without scales
+    assert q(A, 64, 48, 64, A, A, None, None, 0, None, 0, 0, None) == 2         # K % 32
+    assert q(A, 48, 64, 64, None, None, A, A, 48, None, 0, 0, None) == 2        # ungrouped M % 32
+    assert q(A, 100, 64, 64, None, None, A, A, 192, A, 4, 0, None) == 2         # ld_colT < bound 224
+    assert q(A, 64, 64, 64, A, A, None, None, 0, A, 2, 0, None) == 1            # groups need the column copy
+    assert q(A, 64, 64, 64, A, A, None, None, 0, None, 0, 1, None) == 1         # flags
+
+
+def test_dequantize_and_requant_reject_bad_arguments():
+    d = L.bsp_dequantize
+    assert d(2, A, A, A, 4, 32, 1, A, 0, None) == 1
+    assert d(0, A, A, None, 4, 32, 1, A, 0, None) == 1      # NVFP4 needs outer
+    assert d(1, A, A, None, 4, 48, 1, A, 0, None) == 2
+    assert d(1, A, A, None, 4, 64, 1, A, 5, None) == 1
+    r = L.bsp_requant_transpose_sr
+    assert r(A, A, A, 24, 32, A, A, A, 0, 2, A, 4096, None) == 2      # M % 16
+    assert r(A, A, A, 32, 32, A, A, A, 0, 2, None, 0, None) == 5      # workspace
+    assert r(A, A, A, 32, 32, A, A, A, 0, 4, A, 4096, None) == 1      # flags
+
+
+def test_gemm_rejects_bad_arguments():
+    g = L.bsp_moe_grouped_gemm_blockscaled
+    ws = 1 << 16
+    # NVFP4 needs both outer scales; MXFP8 takes none
+    assert g(0, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, A, ws, None) == 1
+    assert g(1, 0, A, A, A, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 1
+    # NVFP4 weight gradient is not on the path
+    assert g(0, 2, A, A, A, None, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, A, ws, None) == 4
+    assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 48, A, A, None, A, 0, 64, A, ws, None) == 2
+    assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 32, A, ws, None) == 2   # ldc < N
+    assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, 8, None) == 5
+    assert g(1, 0, A, A, None, None, 32, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 2   # a_rows != M
+
+
+def test_python_binding_fails_loudly_without_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ops.quantize_nvfp4_per_token(torch.zeros(4, 32, dtype=torch.bfloat16))
