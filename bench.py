@@ -1,0 +1,611 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled quantization + grouped expert GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input.  The
+default workload is the DeepSeek-V3-shaped MoE layer on one GPU (4096 tokens,
+hidden 7168, 256 routed + 1 shared expert, top-8, expert projections
+7168 x 2048, uniform-plus-Zipf router load), all MXFP8 with rowwise and
+columnwise copies: per step the expert weights and the activations are
+quantized (row + column copies), then the forward (gate/up, SwiGLU + quantize,
+down), data-gradient and weight-gradient grouped GEMMs run.  Other workloads
+(--workload) time the Qwen3-30B-A3B-shaped NVFP4 forward, the MXFP8
+quantization of 8192 x 2048 activations plus 128 expert weights, the
+16384 x 2048 requant with stochastic rounding, and the 256 x 2048 round trip.
+
+Prints one JSON line: value = whole-step throughput (GEMM TFLOP/s for the MoE
+workloads, GB/s for the quantization workloads), the roofline of the dominant
+kernel (its algorithmic bytes or flops per launch over its mean duration,
+timed with HIP events on the launch stream), the CPU oracle timed on a
+bounded sample of the same workload, and a per-op breakdown.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
+SEED = 20261201
+
+
+class Op:
+    """One library call of the step with its algorithmic bytes and flops per launch."""
+
+    def __init__(self, name, fn, nbytes, flops=0.0, mfma=None):
+        self.name = name
+        self.fn = fn
+        self.nbytes = float(nbytes)
+        self.flops = float(flops)
+        self.mfma = mfma          # MFMA input type of a GEMM ("fp8", "fp16"), None for memory-bound ops
+        self.times = []
+
+    def bound(self):
+        if not self.mfma:
+            return "hbm"
+        t_mem = self.nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = self.flops / (MFMA_PEAK_TFLOPS[self.mfma] * 1e12)
+        return "mfma" if t_mfma >= t_mem else "hbm"
+
+
+def timed_until(unit_fn, min_seconds=10.0, max_reps=10000):
+    """Run unit_fn() (returning the work it did) until min_seconds have elapsed."""
+    work, reps = 0.0, 0
+    t0 = time.perf_counter()
+    while reps < max_reps:
+        work += unit_fn()
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    return work, time.perf_counter() - t0, reps
+
+
+def bf16_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class Dsv3MoeMxfp8:
+    """DeepSeek-V3-shaped MoE layer, MXFP8 forward + dgrad + wgrad (configs[4])."""
+    name = "dsv3_moe_mxfp8"
+    unit = "TFLOP/s"
+    dtype = "fp8_e4m3"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        self.ops_mod = ops
+        T, H, I, E, k = 4096, 7168, 2048, 256, 8
+        G = E + 1
+        N13 = 2 * I
+        self.shape = dict(T=T, H=H, I=I, E=E, k=k, G=G)
+        bias = synth.zipf_bias(SEED + 5, E, 1.1, uniform_mix=0.5)
+        off, src = synth.route_topk(SEED + 6, T, E, k, bias, shared_expert=True)
+        R = int(off[-1])
+        self.R = R
+        self.counts = np.diff(off)
+        self.off_h, self.src_h = off, src
+        off_d = torch.from_numpy(off).to(dev)
+        src_d = torch.from_numpy(src).to(dev)
+        X = synth.device_activations(SEED + 7, T, H, dev)
+        W13 = synth.device_weights(SEED + 8, G, N13, H, dev)
+        W2 = synth.device_weights(SEED + 9, G, H, I, dev)
+        dY = synth.device_activations(SEED + 10, R, H, dev)
+        dH13 = synth.device_activations(SEED + 11, R, N13, dev)
+        self.X, self.W13, self.W2 = X, W13, W2
+        u8, bf = torch.uint8, torch.bfloat16
+        ld = ops.mxfp8_grouped_cols(R, G)
+        emp = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
+        w13q = {"codes_row": emp(G, N13, H), "scales_row": emp(G, N13, H // 32),
+                "codes_colT": emp(G, H, N13), "scales_colT": emp(G, H, N13 // 32)}
+        w2q = {"codes_row": emp(G, H, I), "scales_row": emp(G, H, I // 32),
+               "codes_colT": emp(G, I, H), "scales_colT": emp(G, I, H // 32)}
+        xq = {"codes_row": emp(T, H), "scales_row": emp(T, H // 32)}
+        xgq = {"codes_colT": emp(H, ld), "scales_colT": emp(H, ld // 32)}
+        h13 = emp(R, N13, dt=bf)
+        hq = (emp(R, I, dt=bf), emp(R, I), emp(R, I // 32), None)
+        hcq = {"codes_colT": emp(I, ld), "scales_colT": emp(I, ld // 32)}
+        y = emp(R, H, dt=bf)
+        dyq = {"codes_row": emp(R, H), "scales_row": emp(R, H // 32), "codes_colT": emp(H, ld),
+               "scales_colT": emp(H, ld // 32)}
+        dh = emp(R, I, dt=bf)
+        dh13q = {"codes_row": emp(R, N13), "scales_row": emp(R, N13 // 32), "codes_colT": emp(N13, ld),
+                 "scales_colT": emp(N13, ld // 32)}
+        dxg = emp(R, H, dt=bf)
+        dw2 = emp(G, H, I, dt=bf)
+        dw13 = emp(G, N13, H, dt=bf)
+        ws = emp(max(ops.gemm_workspace_size(0, R, G), ops.gemm_workspace_size(2, H, G)))
+        q, gm = ops.quantize_mxfp8, ops.moe_grouped_gemm_blockscaled
+        F, D, W, M8 = ops.GEMM_FPROP, ops.GEMM_DGRAD, ops.GEMM_WGRAD, ops.FMT_MXFP8
+        s8 = 1 + 1 / 32                                 # MXFP8 bytes per value (code + scale share)
+        self.ops = [
+            Op("quant_w13_row_col", lambda: q(W13.view(G, N13, H), True, True, out=w13q),
+               G * N13 * H * (2 + 2 * s8)),
+            Op("quant_w2_row_col", lambda: q(W2.view(G, H, I), True, True, out=w2q), G * H * I * (2 + 2 * s8)),
+            Op("quant_x_row", lambda: q(X, True, False, out=xq), T * H * (2 + s8)),
+            Op("quant_xg_col_grouped", lambda: q(X, False, True, group_offsets=off_d, row_gather=src_d, out=xgq),
+               T * H * 2 + R * H * s8),
+            Op("gemm_fprop_gate_up", lambda: gm(M8, F, xq["codes_row"], xq["scales_row"], w13q["codes_row"],
+                                                 w13q["scales_row"], off_d, N13, H, M=R, a_gather=src_d, out=h13,
+                                                 workspace=ws),
+               G * N13 * H * s8 + T * H * s8 + R * N13 * 2, 2.0 * R * N13 * H, "fp8"),
+            Op("swiglu_quant_h", lambda: ops.swiglu_quantize(h13, ops.FMT_MXFP8, out=hq), R * N13 * 2 + R * I * (2 + s8)),
+            Op("quant_h_col_grouped", lambda: q(hq[0], False, True, group_offsets=off_d, out=hcq), R * I * (2 + s8)),
+            Op("gemm_fprop_down", lambda: gm(M8, F, hq[1], hq[2], w2q["codes_row"], w2q["scales_row"], off_d, H, I,
+                                              M=R, out=y, workspace=ws),
+               G * H * I * s8 + R * I * s8 + R * H * 2, 2.0 * R * H * I, "fp8"),
+            Op("quant_dy_row_col", lambda: q(dY, True, True, group_offsets=off_d, out=dyq), R * H * (2 + 2 * s8)),
+            Op("gemm_dgrad_down", lambda: gm(M8, D, dyq["codes_row"], dyq["scales_row"], w2q["codes_colT"],
+                                              w2q["scales_colT"], off_d, I, H, M=R, out=dh, workspace=ws),
+               G * H * I * s8 + R * H * s8 + R * I * 2, 2.0 * R * I * H, "fp8"),
+            Op("quant_dh13_row_col", lambda: q(dH13, True, True, group_offsets=off_d, out=dh13q),
+               R * N13 * (2 + 2 * s8)),
+            Op("gemm_dgrad_gate_up", lambda: gm(M8, D, dh13q["codes_row"], dh13q["scales_row"], w13q["codes_colT"],
+                                                 w13q["scales_colT"], off_d, H, N13, M=R, out=dxg, workspace=ws),
+               G * N13 * H * s8 + R * N13 * s8 + R * H * 2, 2.0 * R * H * N13, "fp8"),
+            Op("gemm_wgrad_down", lambda: gm(M8, W, dyq["codes_colT"], dyq["scales_colT"], hcq["codes_colT"],
+                                              hcq["scales_colT"], off_d, I, ld, M=H, out=dw2, workspace=ws),
+               R * H * s8 + R * I * s8 + G * H * I * 2, 2.0 * R * H * I, "fp8"),
+            Op("gemm_wgrad_gate_up", lambda: gm(M8, W, dh13q["codes_colT"], dh13q["scales_colT"], xgq["codes_colT"],
+                                                 xgq["scales_colT"], off_d, H, ld, M=N13, out=dw13, workspace=ws),
+               R * N13 * s8 + R * H * s8 + G * N13 * H * 2, 2.0 * R * N13 * H, "fp8"),
+        ]
+        self.gemm_flops = sum(o.flops for o in self.ops)
+
+    def config(self):
+        c = self.counts[:-1]
+        return {"workload": "dsv3_moe_layer_mxfp8_fwd_dgrad_wgrad", "tokens": self.shape["T"],
+                "hidden": self.shape["H"], "expert_intermediate": self.shape["I"],
+                "experts": self.shape["E"], "shared_experts": 1, "topk": self.shape["k"], "routed_rows": self.R,
+                "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(__import__("numpy").median(c)),
+                               "min": int(c.min()), "empty": int((c == 0).sum()), "shared": int(self.counts[-1])},
+                "weights_quantized_per_step": True, "gemm_flops_per_step": self.gemm_flops}
+
+    def value(self, ms_per_step):
+        return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def cpu_baseline(self, budget_s=10.0):
+        """Oracle on a sample: for experts taken in order of load from the median up,
+        MXFP8 quantize of the expert's gate/up weights and up to 64 of its token rows,
+        then those rows' fp64 forward GEMM; repeated until about 10 s of CPU work."""
+        import numpy as np
+        import torch
+        import oracle
+        H, N13 = self.shape["H"], 2 * self.shape["I"]
+        order = np.argsort(self.counts[:-1])
+        order = np.concatenate([order[len(order) // 2:], order[:len(order) // 2]])
+        it = iter(order.tolist())
+        used = []
+
+        def unit():
+            e = next(it)
+            used.append(e)
+            w = self.W13[e * N13:(e + 1) * N13].view(torch.int16).cpu().numpy().view(np.uint16)
+            rows = self.src_h[self.off_h[e]:self.off_h[e + 1]][:64]
+            x = self.X[rows.tolist()].view(torch.int16).cpu().numpy().view(np.uint16)
+            off = np.array([0, len(rows)], np.int64)
+            bc, bs = oracle.quantize_mxfp8_rowwise(w)
+            ac, as_ = oracle.quantize_mxfp8_rowwise(x)
+            oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac, as_, None, None, off, N13, H, bc, bs, None)
+            return 2.0 * len(rows) * N13 * H
+
+        flops, dt, reps = timed_until(unit, budget_s, max_reps=len(order))
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{reps} experts from the median load up: MXFP8 quantize of each expert's 4096x7168 "
+                          f"gate/up weights and up to 64 of its token rows, then those rows' forward GEMM in fp64 "
+                          f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, weight quantization included in the time)"}
+
+
+class Qwen3MoeNvfp4:
+    """Qwen3-30B-A3B-shaped MoE layer forward in NVFP4 (configs[3])."""
+    name = "qwen3_moe_nvfp4"
+    unit = "TFLOP/s"
+    dtype = "fp16"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        T, H, I, E, k = 8192, 2048, 768, 128, 8
+        N13 = 2 * I
+        self.shape = dict(T=T, H=H, I=I, E=E, k=k)
+        bias = synth.zipf_bias(SEED + 4, E, 1.1)
+        off, src = synth.route_topk(SEED + 5, T, E, k, bias)
+        R = int(off[-1])
+        self.R, self.counts, self.off_h, self.src_h = R, np.diff(off), off, src
+        off_d = torch.from_numpy(off).to(dev)
+        src_d = torch.from_numpy(src).to(dev)
+        X = synth.device_activations(SEED + 6, T, H, dev)
+        W13 = synth.device_weights(SEED + 7, E, N13, H, dev)
+        W2 = synth.device_weights(SEED + 8, E, H, I, dev)
+        self.X, self.W13 = X, W13
+        # weights are quantized once (rollout weights), per expert: gate and up share one outer scale
+        w13 = ops.quantize_nvfp4_per_token(W13, rows_per_scale=N13)
+        w2 = ops.quantize_nvfp4_per_token(W2, rows_per_scale=H)
+        u8, bf, f32 = torch.uint8, torch.bfloat16, torch.float32
+        emp = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
+        xq = (emp(T, H // 2), emp(T, H // 16), emp(T, dt=f32))
+        h13 = emp(R, N13, dt=bf)
+        hq = (None, emp(R, I // 2), emp(R, I // 16), emp(R, dt=f32))
+        y = emp(R, H, dt=bf)
+        ws = emp(ops.gemm_workspace_size(0, R, E))
+        gm, F, NV = ops.moe_grouped_gemm_blockscaled, ops.GEMM_FPROP, ops.FMT_NVFP4
+        s4 = 0.5 + 1 / 16
+        self.ops = [
+            Op("quant_x_nvfp4_46", lambda: ops.quantize_nvfp4_per_token(X, mode46=True, out=xq), T * H * (2 + s4) + T * 4),
+            Op("gemm_fprop_gate_up", lambda: gm(NV, F, xq[0], xq[1], w13[0], w13[1], off_d, N13, H, M=R,
+                                                 a_outer=xq[2], b_outer=w13[2], a_gather=src_d, out=h13, workspace=ws),
+               E * N13 * H * s4 + T * H * s4 + R * N13 * 2, 2.0 * R * N13 * H, "fp16"),
+            Op("swiglu_quant_h_nvfp4_46", lambda: ops.swiglu_quantize(h13, ops.FMT_NVFP4, mode46=True, return_h=False,
+                                                                        out=hq),
+               R * N13 * 2 + R * I * s4 + R * 4),
+            Op("gemm_fprop_down", lambda: gm(NV, F, hq[1], hq[2], w2[0], w2[1], off_d, H, I, M=R, a_outer=hq[3],
+                                              b_outer=w2[2], out=y, workspace=ws),
+               E * H * I * s4 + R * I * s4 + R * H * 2, 2.0 * R * H * I, "fp16"),
+        ]
+        self.gemm_flops = sum(o.flops for o in self.ops)
+
+    def config(self):
+        import numpy as np
+        c = self.counts
+        return {"workload": "qwen3_30b_a3b_moe_layer_nvfp4_forward", "tokens": self.shape["T"],
+                "hidden": self.shape["H"], "expert_intermediate": self.shape["I"], "experts": self.shape["E"],
+                "topk": self.shape["k"], "routed_rows": self.R, "activation_46": True,
+                "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(np.median(c)),
+                               "min": int(c.min()), "empty": int((c == 0).sum())},
+                "gemm_flops_per_step": self.gemm_flops}
+
+    def value(self, ms_per_step):
+        return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def cpu_baseline(self, budget_s=10.0):
+        """Oracle on a sample: experts from the median load up, NVFP4 quantize of the expert's
+        gate/up weights and up to 128 token rows (4/6), then their fp64 forward GEMM."""
+        import numpy as np
+        import torch
+        import oracle
+        H, N13 = self.shape["H"], 2 * self.shape["I"]
+        order = np.argsort(self.counts)
+        order = np.concatenate([order[len(order) // 2:], order[:len(order) // 2]])
+        it = iter(order.tolist())
+
+        def unit():
+            e = next(it)
+            w = self.W13[e * N13:(e + 1) * N13].view(torch.int16).cpu().numpy().view(np.uint16)
+            rows = self.src_h[self.off_h[e]:self.off_h[e + 1]][:128]
+            x = self.X[rows.tolist()].view(torch.int16).cpu().numpy().view(np.uint16)
+            off = np.array([0, len(rows)], np.int64)
+            bc, bs, bg = oracle.quantize_nvfp4(w, rows_per_scale=N13)
+            ac, as_, ag = oracle.quantize_nvfp4(x, mode46=True)
+            oracle.gemm_rowgroup(oracle.FMT_NVFP4, ac, as_, ag, None, off, N13, H, bc, bs, bg)
+            return 2.0 * len(rows) * N13 * H
+
+        flops, dt, reps = timed_until(unit, budget_s, max_reps=len(order))
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{reps} experts from the median load up: NVFP4 quantize of each expert's 1536x2048 "
+                          f"gate/up weights and up to 128 of its token rows (4/6), then their forward GEMM in fp64 "
+                          f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+class Mxfp8Quant:
+    """MXFP8 rowwise + columnwise quantization of 8192 x 2048 activations and rowwise
+    quantization of 128 expert weights 2048 x 768 (configs[1])."""
+    name = "mxfp8_quant"
+    unit = "GB/s"
+    dtype = "f32"
+
+    def __init__(self, dev):
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        M, K, E, N, KW = 8192, 2048, 128, 2048, 768
+        self.copies = 16     # rotate activation buffers so they do not stay resident in the 256 MB MALL
+        xs = [synth.device_activations(SEED + 20 + i, M, K, dev, row_log10_range=(-3, 2)) for i in range(self.copies)]
+        W = synth.device_weights(SEED + 40, E, N, KW, dev)
+        u8 = torch.uint8
+        emp = lambda *s: torch.empty(s, dtype=u8, device=dev)
+        outs = [{"codes_row": emp(M, K), "scales_row": emp(M, K // 32), "codes_colT": emp(K, M),
+                 "scales_colT": emp(K, M // 32)} for _ in range(self.copies)]
+        wq = {"codes_row": emp(E * N, KW), "scales_row": emp(E * N, KW // 32)}
+        self.step_i = 0
+        s8 = 1 + 1 / 32
+
+        def quant_x():
+            i = self.step_i % self.copies
+            ops.quantize_mxfp8(xs[i], True, True, out=outs[i])
+
+        def quant_w():
+            ops.quantize_mxfp8(W, True, False, out=wq)
+            self.step_i += 1
+
+        self.ops = [Op("quant_x_row_col", quant_x, M * K * (2 + 2 * s8)),
+                    Op("quant_weights_row", quant_w, E * N * KW * (2 + s8))]
+        self.total_bytes = sum(o.nbytes for o in self.ops)
+        self.x_host = None
+        self.X0 = xs[0]
+
+    def config(self):
+        return {"workload": "mxfp8_quant_activations_8192x2048_row_col_plus_128_weights_2048x768",
+                "bytes_per_step": self.total_bytes, "activation_copies_rotated": self.copies}
+
+    def value(self, ms_per_step):
+        return self.total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def cpu_baseline(self, budget_s=10.0):
+        import numpy as np
+        import torch
+        import oracle
+        x = self.X0.view(torch.int16).cpu().numpy().view(np.uint16)
+
+        def unit():
+            oracle.quantize_mxfp8_rowwise(x)
+            oracle.quantize_mxfp8_colwise(x)
+            return x.size * (2 + 2 * (1 + 1 / 32))
+
+        b, dt, reps = timed_until(unit, budget_s)
+        return {"value": b / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"rowwise + columnwise MXFP8 of one 8192x2048 activation tensor, {reps} times "
+                          f"({dt:.1f} s)"}
+
+
+class RequantSr:
+    """Dequantize -> transpose -> requantize with SR of a 16384 x 2048 NVFP4 tensor (configs[2])."""
+    name = "requant_sr"
+    unit = "GB/s"
+    dtype = "f32"
+
+    def __init__(self, dev):
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        M, K = 16384, 2048
+        self.M, self.K = M, K
+        self.copies = 32     # 32 x 37.8 MB rotated: larger than the MALL
+        ins, outs = [], []
+        for i in range(self.copies):
+            x = synth.device_activations(SEED + 60 + i, M, K, dev)
+            ins.append(ops.quantize_nvfp4_per_token(x))
+            outs.append((torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((K, M // 16), dtype=torch.uint8, device=dev),
+                         torch.empty((4,), dtype=torch.float32, device=dev)))
+            if i == 0:
+                self.x0 = x
+            del x
+        ws = torch.empty((ops.requant_workspace_size(M),), dtype=torch.uint8, device=dev)
+        self.step_i = 0
+
+        def run():
+            i = self.step_i % self.copies
+            c, s, g = ins[i]
+            ops.requant_transpose_sr(c, s, g, seed=0x5EED + self.step_i, sr=True, workspace=ws, out=outs[i])
+            self.step_i += 1
+
+        nbytes = M * K * (0.5 + 1 / 16) * 2 + M * 4 + 4
+        self.ops = [Op("requant_transpose_sr", run, nbytes)]
+        self.total_bytes = nbytes
+
+    def config(self):
+        return {"workload": "nvfp4_requant_transpose_sr_16384x2048", "bytes_per_step": self.total_bytes,
+                "input_copies_rotated": self.copies, "rng": "philox4x32-10"}
+
+    def value(self, ms_per_step):
+        return self.total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def cpu_baseline(self, budget_s=10.0):
+        import numpy as np
+        import torch
+        import oracle
+        x = self.x0[:4096].view(torch.int16).cpu().numpy().view(np.uint16)
+        c, s, g = oracle.quantize_nvfp4(x)
+        seeds = iter(range(1, 1 << 30))
+
+        def unit():
+            oracle.requant_transpose_sr(c, s, g, seed=next(seeds), use_sr=True)
+            return x.size * (0.5 + 1 / 16) * 2 + x.shape[0] * 4
+
+        b, dt, reps = timed_until(unit, budget_s)
+        return {"value": b / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"requant + SR of the first 4096 of the 16384 rows, {reps} seeds ({dt:.1f} s)"}
+
+
+class RoundTrip:
+    """256 x 2048 activation round trip + small GEMM against a 2048 x 768 weight (configs[0])."""
+    name = "roundtrip"
+    unit = "us"
+    dtype = "f32"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        M, K, N = 256, 2048, 768
+        x = bf16_dev(synth.activations(SEED, M, K), dev)
+        w = bf16_dev(synth.weights(SEED + 1, 1, N, K), dev)
+        off = torch.tensor([0, M], dtype=torch.int64, device=dev)
+        st = {}
+
+        def nv():
+            st["xn"] = ops.quantize_nvfp4_per_token(x)
+            st["wn"] = ops.quantize_nvfp4_per_token(w, rows_per_scale=N)
+
+        def mx():
+            st["xm"] = ops.quantize_mxfp8(x)
+            st["wm"] = ops.quantize_mxfp8(w)
+
+        def dq():
+            ops.dequantize(ops.FMT_NVFP4, *st["xn"])
+            ops.dequantize(ops.FMT_MXFP8, st["xm"]["codes_row"], st["xm"]["scales_row"])
+
+        def gemm():
+            ops.moe_grouped_gemm_blockscaled(ops.FMT_NVFP4, ops.GEMM_FPROP, st["xn"][0], st["xn"][1], st["wn"][0],
+                                             st["wn"][1], off, N, K, a_outer=st["xn"][2], b_outer=st["wn"][2])
+            ops.moe_grouped_gemm_blockscaled(ops.FMT_MXFP8, ops.GEMM_FPROP, st["xm"]["codes_row"],
+                                             st["xm"]["scales_row"], st["wm"]["codes_row"], st["wm"]["scales_row"],
+                                             off, N, K)
+
+        self.ops = [Op("quant_nvfp4_x_w", nv, (M + N) * K * 2.56), Op("quant_mxfp8_x_w", mx, (M + N) * K * 3.03),
+                    Op("dequant_both", dq, M * K * (0.56 + 4 + 1.03 + 4)),
+                    Op("gemm_nvfp4_and_mxfp8", gemm, (M + N) * K * 1.6 + M * N * 8, 4.0 * M * N * K, "fp16")]
+
+    def config(self):
+        return {"workload": "roundtrip_256x2048_and_gemm_768", "launch_bound": True}
+
+    def value(self, ms_per_step):
+        return ms_per_step * 1e3
+
+    def cpu_baseline(self, budget_s=10.0):
+        import numpy as np
+        import oracle
+        from block_scaled_precision_token_amd import synth
+        x = synth.activations(SEED, 256, 2048)
+        w = synth.weights(SEED + 1, 1, 768, 2048)
+        t0 = time.perf_counter()
+        c, s, g = oracle.quantize_nvfp4(x)
+        wc, ws_, wg = oracle.quantize_nvfp4(w, rows_per_scale=768)
+        mc, ms = oracle.quantize_mxfp8_rowwise(x)
+        oracle.dequantize_nvfp4(c, s, g)
+        oracle.dequantize_mxfp8(mc, ms)
+        off = np.array([0, 256], np.int64)
+        oracle.gemm_rowgroup(oracle.FMT_NVFP4, c, s, g, None, off, 768, 2048, wc, ws_, wg)
+        dt = time.perf_counter() - t0
+        return {"value": dt * 1e6, "unit": "us", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "the whole round trip: NVFP4 quantize of x and w, MXFP8 quantize of x, both dequantizes "
+                          "and the 256x768x2048 NVFP4 GEMM in fp64"}
+
+
+class HbmCopy:
+    """A plain 1 GiB device-to-device copy: the achievable HBM rate, and the kernel of
+    known size that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    name = "hbm_copy"
+    unit = "GB/s"
+    dtype = "u8"
+
+    def __init__(self, dev):
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        self.ops = [Op("copy_1GiB", lambda: dst.copy_(src), 2.0 * n)]
+        self.total_bytes = 2.0 * n
+
+    def config(self):
+        return {"workload": "device_copy_1GiB", "bytes_per_step": self.total_bytes}
+
+    def value(self, ms_per_step):
+        return self.total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def cpu_baseline(self, budget_s=10.0):
+        return None
+
+
+WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Mxfp8Quant, RequantSr, RoundTrip, HbmCopy)}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    from block_scaled_precision_token_amd import ops
+    ops.lib()      # fails loudly when the HIP library is missing
+
+    wl = WORKLOADS[args.workload](dev)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {wl.name} ready; {len(wl.ops)} ops per step", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for op in wl.ops:
+            op.fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for _ in range(args.steps):
+        for op in wl.ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            op.fn()
+            b.record(stream)
+            events.append((op, a, b))
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for op, a, b in events:
+        op.times.append(a.elapsed_time(b))
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms_per_step:.3f})",
+          file=sys.stderr, flush=True)
+
+    comps = {}
+    for op in wl.ops:
+        ms = sum(op.times) / len(op.times)
+        d = {"ms": round(ms, 4), "GB_s": round(op.nbytes / (ms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(op.nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": op.bound()}
+        if op.flops:
+            tf = op.flops / (ms * 1e-3) / 1e12
+            d["TFLOP_s"] = round(tf, 1)
+            d["mfma_frac"] = round(tf / MFMA_PEAK_TFLOPS[op.mfma], 4)
+        comps[op.name] = d
+    dom = max(wl.ops, key=lambda o: sum(o.times))
+    dom_ms = sum(dom.times) / len(dom.times)
+    if dom.bound() == "mfma":
+        ach = dom.flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS[dom.mfma], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS[dom.mfma], 4), "traffic": None, "kernel": dom.name}
+    else:
+        ach = dom.nbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom.name}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        try:
+            cpu = wl.cpu_baseline()
+        except Exception as exc:  # the baseline is reported, never required
+            cpu = {"error": repr(exc)}
+
+    value = wl.value(ms_per_step)
+    line = {
+        "metric": "quantize/requant GB/s (% HBM peak); MoE block-scaled GEMM TFLOPS (% MFMA)",
+        "value": round(value, 3), "unit": wl.unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": wl.unit != "us", "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": wl.config(), "roofline": roof, "cpu_baseline": cpu, "components": comps,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

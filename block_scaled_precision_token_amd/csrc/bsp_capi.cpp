@@ -78,7 +78,8 @@ BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M,
                                                  (flags & BSP_NVFP4_46) != 0, as_stream(stream)));
 }
 
-BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
+BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx,
+                                         const int32_t *row_gather, int64_t M, int64_t batch, uint8_t *codes_row,
                                          uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT,
                                          int64_t ld_colT, const int64_t *group_offsets, int64_t G, uint32_t flags,
                                          void *stream) {
@@ -88,7 +89,10 @@ BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K
     if ((codes_colT == nullptr) != (scales_colT == nullptr)) return BSP_ERR_INVALID_ARG;
     if (!codes_row && !codes_colT) return BSP_ERR_INVALID_ARG;
     if (group_offsets && !codes_colT) return BSP_ERR_INVALID_ARG;
-    if (M <= 0 || K < 32 || K % 32 || ldx < K) return BSP_ERR_SHAPE;
+    if (M <= 0 || x_rows <= 0 || K < 32 || K % 32 || ldx < K) return BSP_ERR_SHAPE;
+    if (!row_gather && M != x_rows) return BSP_ERR_SHAPE;
+    if (batch < 1 || batch > 65535) return BSP_ERR_SHAPE;
+    if (batch > 1 && (row_gather || group_offsets)) return BSP_ERR_UNSUPPORTED;
     if (codes_colT) {
         if (ld_colT <= 0 || ld_colT % 32) return BSP_ERR_SHAPE;
         if (group_offsets) {
@@ -99,10 +103,12 @@ BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K
         }
     }
     if (!aligned16(x) || ldx % 8 || !aligned16_or_null(codes_row) || !aligned16_or_null(scales_row) ||
-        !aligned16_or_null(codes_colT) || !aligned16_or_null(scales_colT) || !aligned16_or_null(group_offsets))
+        !aligned16_or_null(codes_colT) || !aligned16_or_null(scales_colT) || !aligned16_or_null(group_offsets) ||
+        !aligned16_or_null(row_gather))
         return BSP_ERR_ALIGNMENT;
-    return hip_status(bsp::launch_quantize_mxfp8(x, M, K, ldx, codes_row, scales_row, codes_colT, scales_colT,
-                                                 ld_colT, group_offsets, group_offsets ? G : 1, as_stream(stream)));
+    return hip_status(bsp::launch_quantize_mxfp8(x, x_rows, K, ldx, row_gather, M, codes_row, scales_row, codes_colT,
+                                                 scales_colT, ld_colT, group_offsets, group_offsets ? G : 1, batch,
+                                                 as_stream(stream)));
 }
 
 BSP_EXPORT bsp_status bsp_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, const float *outer,

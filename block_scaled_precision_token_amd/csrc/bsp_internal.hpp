@@ -11,9 +11,10 @@ namespace bsp {
 
 hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, uint8_t *codes,
                                  uint8_t *scales, float *outer, bool m46, hipStream_t s);
-hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
-                                 uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT, int64_t ld_colT,
-                                 const int64_t *group_offsets, int64_t G, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx, const int32_t *gather,
+                                 int64_t M, uint8_t *codes_row, uint8_t *scales_row, uint8_t *codes_colT,
+                                 uint8_t *scales_colT, int64_t ld_colT, const int64_t *group_offsets, int64_t G,
+                                 int64_t batch, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M,
                              int64_t K, int64_t rps, void *out, int out_dtype, hipStream_t s);
 int requant_partials(int64_t M);

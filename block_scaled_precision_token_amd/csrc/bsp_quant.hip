@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
                                                     int64_t ldx, uint8_t *__restrict__ codes_row,
                                                     uint8_t *__restrict__ scales_row, uint8_t *__restrict__ codes_colT,
                                                     uint8_t *__restrict__ scales_colT, int64_t ld_colT,
-                                                    const int64_t *__restrict__ group_offsets, int G) {
+                                                    const int64_t *__restrict__ group_offsets, int G,
+                                                    const int32_t *__restrict__ gather, int64_t x_rows) {
     __shared__ uint16_t tile[MX_TR][MX_TC + 8];
     __shared__ int64_t sP[GROUPED ? MX_MAXG + 1 : 1];
     __shared__ int64_t sOff[GROUPED ? MX_MAXG + 1 : 1];
@@ -281,6 +282,16 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     const int64_t p0 = (int64_t)blockIdx.y * MX_TR;
     const int64_t k0 = (int64_t)blockIdx.x * MX_TC;
     int64_t ptotal = M;
+    if (!GROUPED && gridDim.z > 1) {  // stacked independent matrices (no gather, no groups)
+        const int64_t b = blockIdx.z;
+        x += b * x_rows * ldx;
+        if (codes_row) {
+            codes_row += b * M * K;
+            scales_row += b * M * (K / 32);
+        }
+        codes_colT += b * K * ld_colT;
+        scales_colT += b * K * (ld_colT / 32);
+    }
 
     if (GROUPED) {
         // padded group starts P (running sum of roundup32(n_g)), scanned in LDS
@@ -342,10 +353,16 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
         if (p < M) src = p;
     }
     const bool col_ok = kc < K;
+    // physical row of x: the gathered row (out-of-range indices read as zeros)
+    int64_t xrow = src;
+    if (src >= 0 && gather) {
+        xrow = gather[src];
+        if (xrow < 0 || xrow >= x_rows) xrow = -1;
+    }
     float xf[32];
     uint4 raw[4] = {};
-    if (src >= 0 && col_ok) {
-        const uint16_t *xp = x + src * ldx + kc;
+    if (xrow >= 0 && col_ok) {
+        const uint16_t *xp = x + xrow * ldx + kc;
 #pragma unroll
         for (int i = 0; i < 4; i++) raw[i] = reinterpret_cast<const uint4 *>(xp)[i];
     }
@@ -390,16 +407,28 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
 
 // Rowwise-only MXFP8: one lane per 32-value block.
 __global__ __launch_bounds__(256) void k_mxfp8_row(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                   const int32_t *__restrict__ gather, int64_t x_rows) {
     const int64_t nb = K / 32, total = M * nb;
+    if (gridDim.z > 1) {  // stacked independent matrices
+        const int64_t b = blockIdx.z;
+        x += b * x_rows * ldx;
+        codes += b * M * K;
+        scales += b * M * nb;
+    }
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / nb, kb = i - r * nb;
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + r * ldx + kb * 32);
+        int64_t xr = r;
+        if (gather) {
+            xr = gather[r];
+            if (xr < 0 || xr >= x_rows) xr = -1;
+        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + (xr < 0 ? 0 : xr) * ldx + kb * 32);
         float xf[32];
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const uint4 raw = src[v];
+            const uint4 raw = xr < 0 ? make_uint4(0u, 0u, 0u, 0u) : src[v];
             const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -416,12 +445,14 @@ __global__ __launch_bounds__(256) void k_mxfp8_row(const uint16_t *__restrict__ 
     }
 }
 
-hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
-                                 uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT, int64_t ld_colT,
-                                 const int64_t *group_offsets, int64_t G, hipStream_t s) {
+hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx, const int32_t *gather,
+                                 int64_t M, uint8_t *codes_row, uint8_t *scales_row, uint8_t *codes_colT,
+                                 uint8_t *scales_colT, int64_t ld_colT, const int64_t *group_offsets, int64_t G,
+                                 int64_t batch, hipStream_t s) {
     const bool row = codes_row != nullptr, col = codes_colT != nullptr;
     if (!col) {
-        k_mxfp8_row<<<grid_for(M * (K / 32), 256, 1 << 20), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row);
+        const int gx = grid_for(M * (K / 32), 256, batch > 1 ? 4096 : (1 << 20));
+        k_mxfp8_row<<<dim3(gx, 1, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row, gather, x_rows);
         return hipGetLastError();
     }
     const unsigned gx = (unsigned)((K + MX_TC - 1) / MX_TC);
@@ -430,20 +461,21 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_
         if (row)
             k_mxfp8_tile<true, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
                                                                         codes_colT, scales_colT, ld_colT,
-                                                                        group_offsets, (int)G);
+                                                                        group_offsets, (int)G, gather, x_rows);
         else
             k_mxfp8_tile<false, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
                                                                          codes_colT, scales_colT, ld_colT,
-                                                                         group_offsets, (int)G);
+                                                                         group_offsets, (int)G, gather, x_rows);
     } else {
         const unsigned gy = (unsigned)((M + MX_TR - 1) / MX_TR);
         if (row)
-            k_mxfp8_tile<true, true, false><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
-                                                                         codes_colT, scales_colT, ld_colT, nullptr, 1);
+            k_mxfp8_tile<true, true, false><<<dim3(gx, gy, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                         codes_colT, scales_colT, ld_colT, nullptr, 1,
+                                                                         gather, x_rows);
         else
-            k_mxfp8_tile<false, true, false><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+            k_mxfp8_tile<false, true, false><<<dim3(gx, gy, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
                                                                           codes_colT, scales_colT, ld_colT, nullptr,
-                                                                          1);
+                                                                          1, gather, x_rows);
     }
     return hipGetLastError();
 }

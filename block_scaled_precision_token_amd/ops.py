@@ -59,7 +59,7 @@ def _declare(lib):
     lib.bsp_status_string.argtypes = [INT]
     lib.bsp_status_string.restype = ctypes.c_char_p
     lib.bsp_quantize_nvfp4_per_token.argtypes = [P, I64, I64, I64, I64, P, P, P, U32, P]
-    lib.bsp_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, P, P, P, I64, P, I64, U32, P]
+    lib.bsp_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P, P, I64, P, I64, U32, P]
     lib.bsp_dequantize.argtypes = [INT, P, P, P, I64, I64, I64, P, INT, P]
     lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
     lib.bsp_moe_grouped_gemm_blockscaled.argtypes = [INT, INT, P, P, P, P, I64, P, I64, I64, I64, I64, P, P, P, P,
@@ -148,32 +148,48 @@ def mxfp8_grouped_cols(M: int, G: int) -> int:
 
 
 def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False, group_offsets=None,
-                   ld_colT: int | None = None, out=None):
-    """bf16 [M, K] -> dict with 'codes_row' [M,K], 'scales_row' [M,K/32], 'codes_colT' [K,ld], 'scales_colT' [K,ld/32]."""
+                   ld_colT: int | None = None, row_gather=None, out=None):
+    """bf16 [x_rows, K] (or a stack [batch, x_rows, K]) -> dict with 'codes_row' [M,K],
+    'scales_row' [M,K/32], 'codes_colT' [K,ld], 'scales_colT' [K,ld/32] (each with the
+    leading batch dimension for a stack).
+
+    M = x_rows, or the length of row_gather (row r is then x[row_gather[r]]).
+    """
     _need_cuda(x, "x")
-    _rowmajor(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bfloat16")
-    M, K = x.shape
+    batch = 1
+    if x.dim() == 3:
+        if not x.is_contiguous():
+            raise ValueError("a stacked x must be contiguous")
+        batch = x.shape[0]
+        x2 = x[0]
+    else:
+        _rowmajor(x, "x")
+        x2 = x
+    x_rows, K = x2.shape
+    M = x_rows if row_gather is None else row_gather.numel()
     dev = x.device
+    lead = (batch,) if x.dim() == 3 else ()
     res = {"codes_row": None, "scales_row": None, "codes_colT": None, "scales_colT": None}
     if out is not None:
         res.update(out)
     else:
         if rowwise:
-            res["codes_row"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            res["scales_row"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+            res["codes_row"] = torch.empty(lead + (M, K), dtype=torch.uint8, device=dev)
+            res["scales_row"] = torch.empty(lead + (M, K // 32), dtype=torch.uint8, device=dev)
         if colwise:
             if ld_colT is None:
                 ld_colT = M if group_offsets is None else mxfp8_grouped_cols(M, group_offsets.numel() - 1)
-            res["codes_colT"] = torch.empty((K, ld_colT), dtype=torch.uint8, device=dev)
-            res["scales_colT"] = torch.empty((K, ld_colT // 32), dtype=torch.uint8, device=dev)
+            res["codes_colT"] = torch.empty(lead + (K, ld_colT), dtype=torch.uint8, device=dev)
+            res["scales_colT"] = torch.empty(lead + (K, ld_colT // 32), dtype=torch.uint8, device=dev)
     if res["codes_colT"] is not None:
-        ld_colT = res["codes_colT"].shape[1]
+        ld_colT = res["codes_colT"].shape[-1]
     G = 0 if group_offsets is None else group_offsets.numel() - 1
-    st = _lib_raw().bsp_quantize_mxfp8(_ptr(x), M, K, x.stride(0), _ptr(res["codes_row"]), _ptr(res["scales_row"]),
-                                       _ptr(res["codes_colT"]), _ptr(res["scales_colT"]), ld_colT or 0,
-                                       _ptr(group_offsets), G, 0, _stream(dev))
+    st = _lib_raw().bsp_quantize_mxfp8(_ptr(x), x_rows, K, x2.stride(0), _ptr(row_gather), M, batch,
+                                       _ptr(res["codes_row"]),
+                                       _ptr(res["scales_row"]), _ptr(res["codes_colT"]), _ptr(res["scales_colT"]),
+                                       ld_colT or 0, _ptr(group_offsets), G, 0, _stream(dev))
     _check(st, "bsp_quantize_mxfp8")
     return res
 

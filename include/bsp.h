@@ -99,8 +99,18 @@ bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K,
  * [alphasignal.ai, Recipe 1: 32 consecutive E4M3 values share one E8M0 scale;
  * both row-wise and column-wise copies are made from the original input].
  *
- *   x            device bf16 [M, K], row stride ldx (ldx >= K, ldx % 8 == 0)
+ *   x            device bf16 [x_rows, K], row stride ldx (ldx >= K, ldx % 8 == 0)
  *   K            K % 32 == 0
+ *   row_gather   device int32 [M] or NULL: row r of the quantized tensor is
+ *                x[row_gather[r]] (an index outside [0, x_rows) reads as a
+ *                zero row); NULL means M == x_rows and row r is x[r]
+ *   M            rows of the quantized tensor
+ *   batch        number of stacked independent matrices (>= 1): x is
+ *                [batch, x_rows, K] (matrix stride x_rows * ldx) and every
+ *                output gains a leading batch dimension ([batch, M, K],
+ *                [batch, M, K/32], [batch, K, ld_colT], [batch, K, ld_colT/32]),
+ *                e.g. the per-expert columnwise copies of stacked expert
+ *                weights.  batch > 1 takes neither row_gather nor groups.
  *   codes_row    device u8 [M, K] or NULL      (blocks along K)
  *   scales_row   device u8 [M, K/32] E8M0 or NULL (both NULL or both set)
  *   codes_colT   device u8 [K, ld_colT] or NULL (blocks along M, stored transposed)
@@ -120,10 +130,10 @@ bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K,
  * [-127, 119]; codes = E4M3(x * 2^-k) (RNE, saturating).  At least one of the
  * two copies must be requested.
  */
-bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes_row,
-                              uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT,
-                              int64_t ld_colT, const int64_t *group_offsets, int64_t G, uint32_t flags,
-                              void *stream);
+bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx, const int32_t *row_gather,
+                              int64_t M, int64_t batch, uint8_t *codes_row, uint8_t *scales_row, uint8_t *codes_colT,
+                              uint8_t *scales_colT, int64_t ld_colT, const int64_t *group_offsets, int64_t G,
+                              uint32_t flags, void *stream);
 
 /*
  * Dequantize NVFP4 or MXFP8 to f32 or bf16 [remio.ai, section "Entrambe le

@@ -68,13 +68,19 @@ def test_nvfp4_rejects_bad_arguments():
 
 def test_mxfp8_rejects_bad_arguments():
     q = L.bsp_quantize_mxfp8
-    assert q(A, 64, 64, 64, None, None, None, None, 0, None, 0, 0, None) == 1   # nothing requested
-    assert q(A, 64, 64, 64, A, None, None, None, 0, None, 0, 0, None) == 1      # codes without scales
-    assert q(A, 64, 48, 64, A, A, None, None, 0, None, 0, 0, None) == 2         # K % 32
-    assert q(A, 48, 64, 64, None, None, A, A, 48, None, 0, 0, None) == 2        # ungrouped M % 32
-    assert q(A, 100, 64, 64, None, None, A, A, 192, A, 4, 0, None) == 2         # ld_colT < bound 224
-    assert q(A, 64, 64, 64, A, A, None, None, 0, A, 2, 0, None) == 1            # groups need the column copy
-    assert q(A, 64, 64, 64, A, A, None, None, 0, None, 0, 1, None) == 1         # flags
+    # (x, x_rows, K, ldx, gather, M, batch, codes_row, scales_row, codes_colT, scales_colT, ld_colT, offsets, G,
+    #  flags, stream)
+    assert q(A, 64, 64, 64, None, 64, 1, None, None, None, None, 0, None, 0, 0, None) == 1   # nothing requested
+    assert q(A, 64, 64, 64, None, 64, 1, A, None, None, None, 0, None, 0, 0, None) == 1      # codes without scales
+    assert q(A, 64, 48, 64, None, 64, 1, A, A, None, None, 0, None, 0, 0, None) == 2         # K % 32
+    assert q(A, 48, 64, 64, None, 48, 1, None, None, A, A, 48, None, 0, 0, None) == 2        # ungrouped M % 32
+    assert q(A, 100, 64, 64, None, 100, 1, None, None, A, A, 192, A, 4, 0, None) == 2        # ld_colT < bound 224
+    assert q(A, 64, 64, 64, None, 64, 1, A, A, None, None, 0, A, 2, 0, None) == 1            # groups need the column copy
+    assert q(A, 64, 64, 64, None, 64, 1, A, A, None, None, 0, None, 0, 1, None) == 1         # flags
+    assert q(A, 64, 64, 64, None, 32, 1, A, A, None, None, 0, None, 0, 0, None) == 2         # M != x_rows without gather
+    assert q(A, 64, 64, 64, MIS, 32, 1, A, A, None, None, 0, None, 0, 0, None) == 3          # misaligned gather
+    assert q(A, 64, 64, 64, None, 64, 0, A, A, None, None, 0, None, 0, 0, None) == 2         # batch < 1
+    assert q(A, 64, 64, 64, A, 64, 2, A, A, None, None, 0, None, 0, 0, None) == 4            # batch with gather
 
 
 def test_dequantize_and_requant_reject_bad_arguments():

@@ -157,6 +157,51 @@ def test_mxfp8_grouped_columnwise(counts):
     assert_bytes_equal(host(q["codes_row"]), rc, "row codes")
 
 
+@pytest.mark.parametrize("grouped", [False, True])
+def test_mxfp8_with_row_gather(grouped):
+    T, R = 50, 96
+    x = synth.activations(91, T, 64)
+    rng = np.random.default_rng(92)
+    src = rng.integers(0, T, R).astype(np.int32)
+    xg = x[src]
+    if grouped:
+        off = np.array([0, 10, 10, 70, 96], np.int64)
+        q = ops.quantize_mxfp8(to_dev_bf16(x), rowwise=True, colwise=True, group_offsets=to_dev(off),
+                               row_gather=to_dev(src))
+        ld = q["codes_colT"].shape[1]
+        tc, ts = oracle.quantize_mxfp8_colwise(xg, off, ldT=ld)
+        used = int(oracle.padded_offsets(off)[-1])
+        assert_bytes_equal(host(q["codes_colT"])[:, :used], tc[:, :used], "gathered grouped col codes")
+        assert_bytes_equal(host(q["scales_colT"])[:, :used // 32], ts[:, :used // 32], "gathered grouped col scales")
+    else:
+        q = ops.quantize_mxfp8(to_dev_bf16(x), rowwise=True, colwise=True, row_gather=to_dev(src))
+        tc, ts = oracle.quantize_mxfp8_colwise(xg)
+        assert_bytes_equal(host(q["codes_colT"]), tc, "gathered col codes")
+        assert_bytes_equal(host(q["scales_colT"]), ts, "gathered col scales")
+    rc, rs = oracle.quantize_mxfp8_rowwise(xg)
+    assert_bytes_equal(host(q["codes_row"]), rc, "gathered row codes")
+    assert_bytes_equal(host(q["scales_row"]), rs, "gathered row scales")
+    # rowwise-only kernel with a gather
+    q = ops.quantize_mxfp8(to_dev_bf16(x), rowwise=True, colwise=False, row_gather=to_dev(src))
+    assert_bytes_equal(host(q["codes_row"]), rc, "gathered row-only codes")
+
+
+@pytest.mark.parametrize("rowwise", [True, False])
+def test_mxfp8_batched_per_expert_columnwise(rowwise):
+    # stacked expert weights [E, N, K]: one launch, per-expert columnwise copies
+    E, N, K = 3, 96, 64
+    w = synth.weights(93, E, N, K)
+    q = ops.quantize_mxfp8(to_dev_bf16(w).reshape(E, N, K), rowwise=rowwise, colwise=True)
+    for e in range(E):
+        tc, ts = oracle.quantize_mxfp8_colwise(w[e * N:(e + 1) * N])
+        assert_bytes_equal(host(q["codes_colT"][e]), tc, f"expert {e} col codes")
+        assert_bytes_equal(host(q["scales_colT"][e]), ts, f"expert {e} col scales")
+        if rowwise:
+            rc, rs = oracle.quantize_mxfp8_rowwise(w[e * N:(e + 1) * N])
+            assert_bytes_equal(host(q["codes_row"][e]), rc, f"expert {e} row codes")
+            assert_bytes_equal(host(q["scales_row"][e]), rs, f"expert {e} row scales")
+
+
 # ---------------------------------------------------------------------------
 # dequantize
 # ---------------------------------------------------------------------------
