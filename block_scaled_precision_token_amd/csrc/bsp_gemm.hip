@@ -8,21 +8,29 @@
 // MXFP8: 32 E4M3 values per E8M0 scale is exactly the operand format of
 // gfx950's block-scaled MFMA (V_MFMA_SCALE_F32_32X32X64_F8F6F4): per 64-value
 // K step each row has two 32-value blocks, each with the E8M0 byte supplied by
-// one lane half, so codes and scales go to the matrix core unchanged (see
-// load_mx_frag for the byte placement the instruction expects).
+// one lane half, so codes and scales go to the matrix core unchanged.
 //
 // NVFP4: the E4M3 scale covers 16 values and the matrix core only scales by
 // powers of two per 32, so the operand value q * s (E2M1 times E4M3, at most
 // 6 significant bits, magnitude in [2^-10, 2688]) is rebuilt exactly in fp16
-// in registers and multiplied on the fp16 MFMA (V_MFMA_F32_32X32X16_F16); the
-// FP32 outer scales (per token for A, per expert for B) are applied in the
-// epilogue, so no separate scaling pass is needed.
+// while the tile is staged into LDS (once per workgroup) and multiplied on
+// the fp16 MFMA (V_MFMA_F32_32X32X16_F16); the FP32 outer scales (per token
+// for A, per expert for B) are applied in the epilogue.
 //
-// Tiling: 256 threads = 4 wavefronts in 2 x 2, each computing 64 x 64 of a
-// 128 x 128 output tile as 2 x 2 MFMA 32 x 32 tiles, f32 accumulation.
-// Row tiles never straddle two experts: a setup kernel lists the
-// (expert, first row) of every 128-row tile from the device-side group
-// offsets, so no host synchronization is needed.
+// Tiling: 256 threads = 4 wavefronts in 2 x 2.  Output tile BM x 128 with
+// BM = 128 (compute-bound calls) or 256 (weight-streaming calls: fewer row
+// tiles per expert, so each weight panel is fetched fewer times).  K moves in
+// 64-value stages through double-buffered LDS with register prefetch of the
+// next stage.  Row tiles never straddle two experts: a setup kernel lists the
+// (expert, first row) of every row tile from the device-side group offsets,
+// so no host synchronization is needed.
+//
+// Tile order: workgroup ids are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  A workgroup's id is mapped to an XCD-contiguous chunk of
+// the row-major tile sequence (row tile outer, column tile inner), so the
+// workgroups in flight on one XCD are consecutive column tiles of the same
+// row tiles: they share the activation tile, and successive row tiles of one
+// expert re-read the same weight panels while they are still in that L2.
 #include "bsp_device.hpp"
 #include "bsp_internal.hpp"
 
@@ -31,8 +39,11 @@ namespace bsp {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-constexpr int GBM = 128, GBN = 128;
+constexpr int GBN = 128;   // output columns per workgroup
+constexpr int GBK = 64;    // K values per LDS stage
+constexpr int NXCD = 8;
 
 struct GemmArgs {
     const uint8_t *a_codes, *a_scales;
@@ -42,20 +53,24 @@ struct GemmArgs {
     const uint8_t *b_codes, *b_scales;
     const float *b_outer;
     void *c;
-    const int64_t *tiles;     // FPROP/DGRAD: [ntile_max] packed (group << 40) | row0; WGRAD: padded starts [G+1]
+    const int64_t *tiles;     // row-grouped form: packed (group << 40) | first row; WGRAD: padded starts [G+1]
     int64_t G, M, N, K, ldc, a_rows;
+    int64_t ntm;              // row tiles (row-grouped form: tile-list length; WGRAD: G * ceil(M / BM))
+    int64_t ntn;              // column tiles
 };
 
-// Tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
-__global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t ntile_max, int64_t *__restrict__ tiles) {
+// Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
+__global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t M, int64_t bm, int64_t ntile_max,
+                            int64_t *__restrict__ tiles) {
     __shared__ int64_t base[1025];
-    // single workgroup: running tile counts (G <= 1024 per chunk loop)
     int64_t carry = 0;
     for (int64_t g0 = 0; g0 < G; g0 += 1024) {
         const int64_t n = (G - g0) < 1024 ? (G - g0) : 1024;
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int64_t rows = off[g0 + i + 1] - off[g0 + i];
-            base[i + 1] = (rows + GBM - 1) / GBM;
+            int64_t lo = off[g0 + i], hi = off[g0 + i + 1];
+            lo = lo < M ? lo : M;
+            hi = hi < M ? hi : M;
+            base[i + 1] = hi > lo ? (hi - lo + bm - 1) / bm : 0;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -67,7 +82,7 @@ __global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t 
             const int64_t g = g0 + i;
             const int64_t r0 = off[g];
             for (int64_t t = base[i]; t < base[i + 1] && t < ntile_max; t++)
-                tiles[t] = (g << 40) | (r0 + (t - base[i]) * GBM);
+                tiles[t] = (g << 40) | (r0 + (t - base[i]) * bm);
         }
         carry = base[n];
         __syncthreads();
@@ -85,28 +100,6 @@ __global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int6
         }
         P[G] = run;
     }
-}
-
-// ---------------------------------------------------------------------------
-// fragment loaders
-// ---------------------------------------------------------------------------
-
-// MXFP8 operand of V_MFMA_SCALE_F32_32X32X64_F8F6F4 for one row and the
-// 64-value K step starting at k0.  The instruction works as two 32-value
-// halves: bytes 0-15 of both lane halves form K block 0 (scaled by the E8M0
-// byte of lane half 0) and bytes 16-31 form K block 1 (scaled by lane half
-// 1's byte).  So lane half h holds K [k0 + 16h, +16) then [k0 + 32 + 16h, +16)
-// and the scale of block k0/32 + h.  Blocks past kend read as zeros.
-__device__ __forceinline__ void load_mx_frag(const uint8_t *codes, const uint8_t *scales, int64_t ld_codes,
-                                             int64_t row, bool valid, int64_t k0, int64_t kend, int h, v8i &frag,
-                                             int &scale) {
-    const uint8_t *rp = codes + row * ld_codes;
-    uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
-    if (valid && k0 < kend) u0 = *reinterpret_cast<const uint4 *>(rp + k0 + 16 * h);
-    if (valid && k0 + 32 < kend) u1 = *reinterpret_cast<const uint4 *>(rp + k0 + 32 + 16 * h);
-    frag[0] = (int)u0.x; frag[1] = (int)u0.y; frag[2] = (int)u0.z; frag[3] = (int)u0.w;
-    frag[4] = (int)u1.x; frag[5] = (int)u1.y; frag[6] = (int)u1.z; frag[7] = (int)u1.w;
-    scale = (valid && k0 + 32 * h < kend) ? (int)scales[row * (ld_codes / 32) + k0 / 32 + h] : 127;
 }
 
 // 8 E2M1 nibbles (one 32-bit word, element 2j in the low nibble of byte j)
@@ -127,42 +120,125 @@ __device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, uint32_t (&h)[4]) {
     h[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
 }
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ uint32_t hmul2(uint32_t a, h2 s) {
     h2 x = __builtin_bit_cast(h2, a);
     x = x * s;
     return __builtin_bit_cast(uint32_t, x);
 }
 
-// NVFP4: lane holds the 32 elements [kk, kk + 32) of one row (two 16-blocks)
-// dequantized to fp16 as four 8-element MFMA operands.
-__device__ __forceinline__ void load_nv_frag(const uint8_t *codes, const uint8_t *scales, int64_t K, int64_t row,
-                                             bool valid, int64_t kk, v8h (&frag)[4]) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    float s0 = 0.0f, s1 = 0.0f;
-    if (valid && kk < K) {
-        const uint8_t *cp = codes + row * (K / 2) + kk / 2;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(cp);
-        w[0] = lo.x; w[1] = lo.y;
-        s0 = e4m3_decode(scales[row * (K / 16) + kk / 16]);
-        if (kk + 16 < K) {
-            const uint2 hi = *reinterpret_cast<const uint2 *>(cp + 8);
-            w[2] = hi.x; w[3] = hi.y;
-            s1 = e4m3_decode(scales[row * (K / 16) + kk / 16 + 1]);
+// ---------------------------------------------------------------------------
+// Stage loaders: global -> registers (prefetch) and registers -> LDS.
+// ---------------------------------------------------------------------------
+
+// MXFP8 stage = 64 K bytes per row = two 32-value blocks.  For a 128-row
+// operand loader thread t takes row t/2, block t%2; for 256 rows, row t and
+// both blocks.
+template <int ROWS>
+struct MxStage {
+    static constexpr int NB = ROWS * 2 / 256;   // 32-byte blocks per thread (1 or 2)
+    uint4 v[NB][2];
+    uint32_t s[NB];
+};
+
+template <int ROWS>
+__device__ __forceinline__ void mx_load(MxStage<ROWS> &st, const uint8_t *codes, const uint8_t *scales,
+                                        int64_t ld, const int64_t *rowp, int64_t k0, int64_t kend) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int b = 0; b < MxStage<ROWS>::NB; b++) {
+        const int blk = (MxStage<ROWS>::NB == 1) ? (t & 1) : b;
+        const int64_t kk = k0 + 32 * blk;
+        const int64_t r = rowp[(MxStage<ROWS>::NB == 1) ? 0 : 0];
+        if (r >= 0 && kk < kend) {
+            const uint4 *q = reinterpret_cast<const uint4 *>(codes + r * ld + kk);
+            st.v[b][0] = q[0];
+            st.v[b][1] = q[1];
+            st.s[b] = scales[r * (ld / 32) + kk / 32];
+        } else {
+            st.v[b][0] = make_uint4(0u, 0u, 0u, 0u);
+            st.v[b][1] = st.v[b][0];
+            st.s[b] = 127u;
         }
     }
-    const h2 sv0 = {(_Float16)s0, (_Float16)s0};
-    const h2 sv1 = {(_Float16)s1, (_Float16)s1};
+}
+
+// LDS row layout (MXFP8): 64 code bytes + 16 pad; scales [rows][2].
+constexpr int MX_LDS_STRIDE = 80;
+
+template <int ROWS>
+__device__ __forceinline__ void mx_store(const MxStage<ROWS> &st, uint8_t *sc, uint8_t *ss) {
+    const int t = threadIdx.x;
+    const int row = (MxStage<ROWS>::NB == 1) ? (t >> 1) : t;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        uint32_t h[4];
-        e2m1x8_to_f16(w[q], h);
-        const h2 sv = (q < 2) ? sv0 : sv1;
-        uint32_t o[4];
+    for (int b = 0; b < MxStage<ROWS>::NB; b++) {
+        const int blk = (MxStage<ROWS>::NB == 1) ? (t & 1) : b;
+        uint4 *d = reinterpret_cast<uint4 *>(sc + row * MX_LDS_STRIDE + 32 * blk);
+        d[0] = st.v[b][0];
+        d[1] = st.v[b][1];
+        ss[row * 2 + blk] = (uint8_t)st.s[b];
+    }
+}
+
+// NVFP4 stage = 64 K values per row = 32 code bytes (four 16-blocks).  For a
+// 128-row operand thread t takes row t/2, blocks 2(t%2) and 2(t%2)+1; for 256
+// rows, row t and all four blocks.
+template <int ROWS>
+struct NvStage {
+    static constexpr int NP = ROWS * 2 / 256;   // pairs of 16-blocks per thread (1 or 2)
+    uint32_t w[NP][4];
+    uint32_t s[NP][2];
+};
+
+template <int ROWS>
+__device__ __forceinline__ void nv_load(NvStage<ROWS> &st, const uint8_t *codes, const uint8_t *scales, int64_t K,
+                                        int64_t r, int64_t k0) {
+    const int t = threadIdx.x;
 #pragma unroll
-        for (int j = 0; j < 4; j++) o[j] = hmul2(h[j], sv);
-        frag[q] = __builtin_bit_cast(v8h, make_uint4(o[0], o[1], o[2], o[3]));
+    for (int b = 0; b < NvStage<ROWS>::NP; b++) {
+        const int pair = (NvStage<ROWS>::NP == 1) ? (t & 1) : b;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int64_t kk = k0 + 32 * pair + 16 * h;
+            if (r >= 0 && kk < K) {
+                const uint2 c = *reinterpret_cast<const uint2 *>(codes + r * (K / 2) + kk / 2);
+                st.w[b][2 * h] = c.x;
+                st.w[b][2 * h + 1] = c.y;
+                st.s[b][h] = scales[r * (K / 16) + kk / 16];
+            } else {
+                st.w[b][2 * h] = 0u;
+                st.w[b][2 * h + 1] = 0u;
+                st.s[b][h] = 0u;
+            }
+        }
+    }
+}
+
+// LDS row layout (NVFP4): 64 fp16 + 8 pad.
+constexpr int NV_LDS_STRIDE = 72;   // in halves
+
+template <int ROWS>
+__device__ __forceinline__ void nv_store(const NvStage<ROWS> &st, _Float16 *sh) {
+    const int t = threadIdx.x;
+    const int row = (NvStage<ROWS>::NP == 1) ? (t >> 1) : t;
+#pragma unroll
+    for (int b = 0; b < NvStage<ROWS>::NP; b++) {
+        const int pair = (NvStage<ROWS>::NP == 1) ? (t & 1) : b;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const float sf = e4m3_decode(st.s[b][h]);
+            const h2 sv = {(_Float16)sf, (_Float16)sf};
+            uint32_t o[8];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                uint32_t hh[4];
+                e2m1x8_to_f16(st.w[b][2 * h + q], hh);
+#pragma unroll
+                for (int j = 0; j < 4; j++) o[4 * q + j] = hmul2(hh[j], sv);
+            }
+            uint4 *d = reinterpret_cast<uint4 *>(sh + row * NV_LDS_STRIDE + 32 * pair + 16 * h);
+            d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
     }
 }
 
@@ -170,20 +246,32 @@ __device__ __forceinline__ void load_nv_frag(const uint8_t *codes, const uint8_t
 // kernel
 // ---------------------------------------------------------------------------
 
-template <int FMT, int MODE, bool BF16OUT>
+template <int FMT, int MODE, bool BF16OUT, int BM>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr int WM = BM / 2;            // rows per wavefront
+    constexpr int TI = WM / 32;           // 32-row MFMA tiles per wavefront
+    constexpr int LDS_ROW = (FMT == BSP_FMT_MXFP8) ? MX_LDS_STRIDE : NV_LDS_STRIDE * 2;   // bytes
+    constexpr int STAGE_BYTES = (BM + GBN) * LDS_ROW + ((FMT == BSP_FMT_MXFP8) ? (BM + GBN) * 2 : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31, lh = lane >> 5;
 
+    // ---- XCD-aware tile order ----
+    const int64_t total = p.ntm * p.ntn;
+    const int64_t chunk = (total + NXCD - 1) / NXCD;
+    const int64_t lin = (int64_t)(blockIdx.x % NXCD) * chunk + blockIdx.x / NXCD;
+    if (lin >= total) return;
+    const int64_t ty = lin / p.ntn, tx = lin - ty * p.ntn;
+
     int64_t g, row0, row_end, kbeg, kend;
     const uint8_t *bc, *bs;
-    int64_t a_ld_rows;  // for WGRAD: row pitch of A and B in codes is ld_k
-    (void)a_ld_rows;
     if (MODE == BSP_GEMM_WGRAD) {
-        g = blockIdx.y;
-        row0 = (int64_t)(blockIdx.x / ((p.N + GBN - 1) / GBN)) * GBM;
+        const int64_t mt_per_g = (p.M + BM - 1) / BM;
+        g = ty / mt_per_g;
+        row0 = (ty - g * mt_per_g) * BM;
         row_end = p.M;
         kbeg = p.tiles[g];
         kend = kbeg + (p.group_offsets[g + 1] - p.group_offsets[g] + 31) / 32 * 32;
@@ -191,7 +279,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         bc = p.b_codes;
         bs = p.b_scales;
     } else {
-        const int64_t tile = p.tiles[blockIdx.y];
+        const int64_t tile = p.tiles[ty];
         if (tile < 0) return;
         g = tile >> 40;
         row0 = tile & ((1ll << 40) - 1);
@@ -204,129 +292,222 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         bc = p.b_codes + g * bcs;
         bs = p.b_scales + g * bss;
     }
-    const int64_t ntn = (p.N + GBN - 1) / GBN;
-    const int64_t col0 = (MODE == BSP_GEMM_WGRAD ? (int64_t)(blockIdx.x % ntn) : (int64_t)blockIdx.x) * GBN;
+    const int64_t col0 = tx * GBN;
 
-    // rows and columns this lane loads
-    int64_t arow[2], brow[2];
-    bool aval[2], bval[2];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t r = row0 + wm * 64 + i * 32 + lr;
-        aval[i] = r < row_end;
-        int64_t t = r;
-        if (aval[i] && MODE != BSP_GEMM_WGRAD && p.a_gather) {
-            t = (int64_t)p.a_gather[r];
-            aval[i] = t >= 0 && t < p.a_rows;  // an out-of-range gather index reads as a zero row
+    // ---- the operand rows this loader thread stages (fixed for the whole K loop) ----
+    int64_t arow;
+    {
+        const int lrow = (BM == 128) ? (t >> 1) : t;
+        const int64_t r = row0 + lrow;
+        arow = -1;
+        if (r < row_end) {
+            arow = r;
+            if (MODE != BSP_GEMM_WGRAD && p.a_gather) {
+                arow = (int64_t)p.a_gather[r];
+                if (arow < 0 || arow >= p.a_rows) arow = -1;  // an out-of-range gather index reads as a zero row
+            }
         }
-        arow[i] = aval[i] ? t : 0;
-        const int64_t cn = col0 + wn * 64 + i * 32 + lr;
-        bval[i] = cn < p.N;
-        brow[i] = bval[i] ? cn : 0;
+    }
+    int64_t brow;
+    {
+        const int64_t cn = col0 + (t >> 1);
+        brow = cn < p.N ? cn : -1;
     }
 
-    v16f acc[2][2];
+    v16f acc[TI][2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
+    const int64_t nk = (kend - kbeg + GBK - 1) / GBK;
     if (FMT == BSP_FMT_MXFP8) {
-        const int64_t ldk = p.K;  // codes row pitch (FPROP: K; WGRAD: ld_colT)
-        for (int64_t k0 = kbeg; k0 < kend; k0 += 64) {
-            v8i af[2], bf[2];
-            int as[2], bsc[2];
+        const int64_t ldk = p.K;
+        MxStage<BM> sa;
+        MxStage<GBN> sb;
+        uint8_t *const lA0 = smem, *const lB0 = smem + BM * MX_LDS_STRIDE;
+        uint8_t *const lAs0 = smem + (BM + GBN) * MX_LDS_STRIDE, *const lBs0 = lAs0 + BM * 2;
+        if (nk > 0) {
+            mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg, kend);
+            mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg, kend);
+            mx_store<BM>(sa, lA0, lAs0);
+            mx_store<GBN>(sb, lB0, lBs0);
+        }
+        if (nk > 1) {
+            mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg + GBK, kend);
+            mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg + GBK, kend);
+        }
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; kt++) {
+            const int buf = (int)(kt & 1);
+            const uint8_t *A = lA0 + buf * STAGE_BYTES, *B = lB0 + buf * STAGE_BYTES;
+            const uint8_t *AS = lAs0 + buf * STAGE_BYTES, *BS = lBs0 + buf * STAGE_BYTES;
+            // Row bytes [0, 32) hold K block 0 and [32, 64) block 1.  The
+            // instruction wants lane half h to supply bytes [16h, 16h + 16) of
+            // block 0 then of block 1 (offsets 16h and 32 + 16h), with the E8M0
+            // byte of block h.
+            v8i af[TI], bf[2];
+            int as[TI], bsc[2];
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                load_mx_frag(p.a_codes, p.a_scales, ldk, arow[i], aval[i], k0, kend, lh, af[i], as[i]);
-                load_mx_frag(bc, bs, ldk, brow[i], bval[i], k0, kend, lh, bf[i], bsc[i]);
+            for (int i = 0; i < TI; i++) {
+                const int r = wm * WM + 32 * i + lr;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 16 * lh);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 32 + 16 * lh);
+                af[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                as[i] = AS[r * 2 + lh];
             }
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int j = 0; j < 2; j++) {
+                const int r = wn * 64 + 32 * j + lr;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 16 * lh);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 32 + 16 * lh);
+                bf[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                bsc[j] = BS[r * 2 + lh];
+            }
+#pragma unroll
+            for (int i = 0; i < TI; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0,
                                                                                 as[i], 0, bsc[j]);
+            if (kt + 1 < nk) {
+                mx_store<BM>(sa, lA0 + (buf ^ 1) * STAGE_BYTES, lAs0 + (buf ^ 1) * STAGE_BYTES);
+                mx_store<GBN>(sb, lB0 + (buf ^ 1) * STAGE_BYTES, lBs0 + (buf ^ 1) * STAGE_BYTES);
+            }
+            if (kt + 2 < nk) {
+                mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg + (kt + 2) * GBK, kend);
+                mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg + (kt + 2) * GBK, kend);
+            }
+            __syncthreads();
         }
     } else {
-        for (int64_t k0 = 0; k0 < p.K; k0 += 64) {
-            const int64_t kk = k0 + 32 * lh;
-            v8h af[2][4], bf[2][4];
+        NvStage<BM> sa;
+        NvStage<GBN> sb;
+        _Float16 *const lA0 = reinterpret_cast<_Float16 *>(smem);
+        _Float16 *const lB0 = reinterpret_cast<_Float16 *>(smem + BM * NV_LDS_STRIDE * 2);
+        constexpr int STAGE_H = STAGE_BYTES / 2;
+        if (nk > 0) {
+            nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, 0);
+            nv_load<GBN>(sb, bc, bs, p.K, brow, 0);
+            nv_store<BM>(sa, lA0);
+            nv_store<GBN>(sb, lB0);
+        }
+        if (nk > 1) {
+            nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, GBK);
+            nv_load<GBN>(sb, bc, bs, p.K, brow, GBK);
+        }
+        __syncthreads();
+        for (int64_t kt = 0; kt < nk; kt++) {
+            const int buf = (int)(kt & 1);
+            const _Float16 *A = lA0 + buf * STAGE_H, *B = lB0 + buf * STAGE_H;
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                load_nv_frag(p.a_codes, p.a_scales, p.K, arow[i], aval[i], kk, af[i]);
-                load_nv_frag(bc, bs, p.K, brow[i], bval[i], kk, bf[i]);
-            }
+            for (int q = 0; q < 4; q++) {
+                v8h af[TI], bf[2];
 #pragma unroll
-            for (int q = 0; q < 4; q++)
+                for (int i = 0; i < TI; i++)
+                    af[i] = *reinterpret_cast<const v8h *>(A + (wm * WM + 32 * i + lr) * NV_LDS_STRIDE + 16 * q + 8 * lh);
 #pragma unroll
-                for (int i = 0; i < 2; i++)
+                for (int j = 0; j < 2; j++)
+                    bf[j] = *reinterpret_cast<const v8h *>(B + (wn * 64 + 32 * j + lr) * NV_LDS_STRIDE + 16 * q + 8 * lh);
+#pragma unroll
+                for (int i = 0; i < TI; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][q], bf[j][q], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < nk) {
+                nv_store<BM>(sa, lA0 + (buf ^ 1) * STAGE_H);
+                nv_store<GBN>(sb, lB0 + (buf ^ 1) * STAGE_H);
+            }
+            if (kt + 2 < nk) {
+                nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, (kt + 2) * GBK);
+                nv_load<GBN>(sb, bc, bs, p.K, brow, (kt + 2) * GBK);
+            }
+            __syncthreads();
         }
     }
 
-    // epilogue: lane holds column (lane % 32) and rows 8 (e / 4) + 4 (lane / 32) + e % 4
+    // ---- epilogue: lane holds column (lane % 32), rows 8 (e / 4) + 4 (lane / 32) + e % 4 ----
     const float gb = (FMT == BSP_FMT_NVFP4) ? p.b_outer[g] : 1.0f;
-    char *cbase = reinterpret_cast<char *>(p.c);
-    const int64_t esz = BF16OUT ? 2 : 4;
     const int64_t goff = (MODE == BSP_GEMM_WGRAD) ? g * p.M * p.ldc : 0;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TI; i++) {
+        float ga[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int64_t r = row0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+            float s = 1.0f;
+            if (FMT == BSP_FMT_NVFP4 && r < row_end) {
+                const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
+                s = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
+            }
+            ga[e] = s;
+        }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int64_t cn = col0 + wn * 64 + j * 32 + lr;
+            const int64_t cn = col0 + wn * 64 + 32 * j + lr;
             if (cn >= p.N) continue;
 #pragma unroll
             for (int e = 0; e < 16; e++) {
-                const int64_t r = row0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+                const int64_t r = row0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
                 if (r >= row_end) continue;
                 float v = acc[i][j][e];
-                if (FMT == BSP_FMT_NVFP4) {
-                    const int64_t t = p.a_gather ? (int64_t)p.a_gather[r] : r;
-                    v = (t >= 0 && t < p.a_rows) ? v * (p.a_outer[t] * gb) : 0.0f;
-                }
+                if (FMT == BSP_FMT_NVFP4) v = v * ga[e];
                 const int64_t off = goff + r * p.ldc + cn;
-                if (BF16OUT) reinterpret_cast<uint16_t *>(cbase)[off] = (uint16_t)f32_to_bf16(v);
-                else reinterpret_cast<float *>(cbase)[off] = v;
-                (void)esz;
+                if (BF16OUT) reinterpret_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16(v);
+                else reinterpret_cast<float *>(p.c)[off] = v;
             }
         }
+    }
 }
 
-int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + GBM - 1) / GBM + G; }
+// Rows per tile for a call: 256 when the call streams more weight bytes than
+// it does work on them (few rows per expert), 128 otherwise.
+static int pick_bm(int mode, int64_t M, int64_t G) {
+    if (mode == BSP_GEMM_WGRAD) return 128;
+    return (M / G) < 192 ? 256 : 128;
+}
+
+int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
+
+template <int FMT, int MODE, int BM>
+static void launch_k(const GemmArgs &p, bool bf, hipStream_t s) {
+    const int64_t total = p.ntm * p.ntn;
+    const int64_t chunk = (total + NXCD - 1) / NXCD;
+    dim3 grid((unsigned)(chunk * NXCD)), block(256);
+    if (bf) k_gemm<FMT, MODE, true, BM><<<grid, block, 0, s>>>(p);
+    else k_gemm<FMT, MODE, false, BM><<<grid, block, 0, s>>>(p);
+}
 
 hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
-                       const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
-                       int64_t K, const uint8_t *b_codes, const uint8_t *b_scales, const float *b_outer, void *c,
-                       int c_dtype, int64_t ldc, void *workspace, hipStream_t s) {
+                       const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G,
+                       int64_t M, int64_t N, int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                       const float *b_outer, void *c, int c_dtype, int64_t ldc, void *workspace, hipStream_t s) {
     GemmArgs p;
     p.a_codes = a_codes; p.a_scales = a_scales; p.a_outer = a_outer; p.a_gather = a_gather;
     p.group_offsets = group_offsets; p.b_codes = b_codes; p.b_scales = b_scales; p.b_outer = b_outer;
     p.c = c; p.G = G; p.M = M; p.N = N; p.K = K; p.ldc = ldc; p.a_rows = a_rows;
     int64_t *ws = reinterpret_cast<int64_t *>(workspace);
     p.tiles = ws;
+    p.ntn = (N + GBN - 1) / GBN;
     const bool bf = c_dtype == BSP_DTYPE_BF16;
-    dim3 block(256);
     if (mode == BSP_GEMM_WGRAD) {
         k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws);
-        dim3 grid((unsigned)(((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN)), (unsigned)G);
-        if (bf) k_gemm<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, true><<<grid, block, 0, s>>>(p);
-        else k_gemm<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, false><<<grid, block, 0, s>>>(p);
+        p.ntm = G * ((M + 127) / 128);
+        launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
         return hipGetLastError();
     }
-    const int64_t nt = gemm_tile_count(M, G);
-    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, nt, ws);
-    dim3 grid((unsigned)((N + GBN - 1) / GBN), (unsigned)nt);
+    const int bm = pick_bm(mode, M, G);
+    p.ntm = (M + bm - 1) / bm + G;   // upper bound of the row-tile count
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bm, p.ntm, ws);
     if (fmt == BSP_FMT_MXFP8) {
-        if (bf) k_gemm<BSP_FMT_MXFP8, BSP_GEMM_FPROP, true><<<grid, block, 0, s>>>(p);
-        else k_gemm<BSP_FMT_MXFP8, BSP_GEMM_FPROP, false><<<grid, block, 0, s>>>(p);
+        if (bm == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
+        else launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
     } else {
-        if (bf) k_gemm<BSP_FMT_NVFP4, BSP_GEMM_FPROP, true><<<grid, block, 0, s>>>(p);
-        else k_gemm<BSP_FMT_NVFP4, BSP_GEMM_FPROP, false><<<grid, block, 0, s>>>(p);
+        if (bm == 256) launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);
+        else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
     }
     return hipGetLastError();
 }
