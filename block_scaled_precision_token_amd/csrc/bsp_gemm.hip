@@ -17,9 +17,8 @@
 // the fp16 MFMA (V_MFMA_F32_32X32X16_F16); the FP32 outer scales (per token
 // for A, per expert for B) are applied in the epilogue.
 //
-// Tiling: 256 threads = 4 wavefronts in 2 x 2.  Output tile BM x 128 with
-// BM = 128 (compute-bound calls) or 256 (weight-streaming calls: fewer row
-// tiles per expert, so each weight panel is fetched fewer times).  K moves in
+// Tiling: 256 threads = 4 wavefronts in 2 x 2.  Output tile BM x 128 (BM =
+// 128; a 256-row variant exists behind a build switch).  K moves in
 // 64-value stages through double-buffered LDS with register prefetch of the
 // next stage.  Row tiles never straddle two experts: a setup kernel lists the
 // (expert, first row) of every row tile from the device-side group offsets,
@@ -40,6 +39,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GBN = 128;   // output columns per workgroup
 constexpr int GBK = 64;    // K values per LDS stage
@@ -148,7 +148,7 @@ __device__ __forceinline__ void mx_load(MxStage<ROWS> &st, const uint8_t *codes,
     for (int b = 0; b < MxStage<ROWS>::NB; b++) {
         const int blk = (MxStage<ROWS>::NB == 1) ? (t & 1) : b;
         const int64_t kk = k0 + 32 * blk;
-        const int64_t r = rowp[(MxStage<ROWS>::NB == 1) ? 0 : 0];
+        const int64_t r = rowp[0];
         if (r >= 0 && kk < kend) {
             const uint4 *q = reinterpret_cast<const uint4 *>(codes + r * ld + kk);
             st.v[b][0] = q[0];
@@ -429,45 +429,76 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         }
     }
 
-    // ---- epilogue: lane holds column (lane % 32), rows 8 (e / 4) + 4 (lane / 32) + e % 4 ----
+    // ---- epilogue ----
+    // The MFMA leaves lane l with column l % 32 of a 32 x 32 block and rows
+    // 8 (e / 4) + 4 (l / 32) + e % 4.  Each wavefront stages one 32 x 64 slice
+    // of its outputs in LDS (the stage buffers are free: the K loop ended with
+    // a barrier), then writes whole rows with 16-byte non-temporal stores, so
+    // the output streams past L2 instead of evicting reusable operand panels.
+    constexpr int ESZ = BF16OUT ? 2 : 4;
+    constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
+    constexpr int CHUNKS = 64 / VEC;               // 16-byte chunks per 64-column row
     const float gb = (FMT == BSP_FMT_NVFP4) ? p.b_outer[g] : 1.0f;
     const int64_t goff = (MODE == BSP_GEMM_WGRAD) ? g * p.M * p.ldc : 0;
+    uint8_t *ep = smem + wave * (32 * 64 * ESZ);
+    const bool vec_ok = (p.ldc % VEC) == 0;
 #pragma unroll
     for (int i = 0; i < TI; i++) {
-        float ga[16];
 #pragma unroll
         for (int e = 0; e < 16; e++) {
-            const int64_t r = row0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+            const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
             float s = 1.0f;
-            if (FMT == BSP_FMT_NVFP4 && r < row_end) {
-                const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
-                s = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
+            if (FMT == BSP_FMT_NVFP4) {
+                const int64_t r = row0 + wm * WM + 32 * i + rin;
+                s = 0.0f;
+                if (r < row_end) {
+                    const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
+                    s = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
+                }
             }
-            ga[e] = s;
-        }
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t cn = col0 + wn * 64 + 32 * j + lr;
-            if (cn >= p.N) continue;
-#pragma unroll
-            for (int e = 0; e < 16; e++) {
-                const int64_t r = row0 + wm * WM + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
-                if (r >= row_end) continue;
-                float v = acc[i][j][e];
-                if (FMT == BSP_FMT_NVFP4) v = v * ga[e];
-                const int64_t off = goff + r * p.ldc + cn;
-                if (BF16OUT) reinterpret_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16(v);
-                else reinterpret_cast<float *>(p.c)[off] = v;
+            for (int j = 0; j < 2; j++) {
+                const float v = acc[i][j][e] * s;
+                const int cin = 32 * j + lr;
+                if (BF16OUT) reinterpret_cast<uint16_t *>(ep)[rin * 64 + cin] = (uint16_t)f32_to_bf16(v);
+                else reinterpret_cast<float *>(ep)[rin * 64 + cin] = v;
             }
         }
+        __syncthreads();
+#pragma unroll
+        for (int pass = 0; pass < 32 * CHUNKS / 64; pass++) {
+            const int idx = pass * 64 + lane;
+            const int rin = idx / CHUNKS, ch = idx % CHUNKS;
+            const int64_t r = row0 + wm * WM + 32 * i + rin;
+            const int64_t cn = col0 + wn * 64 + ch * VEC;
+            if (r >= row_end || cn >= p.N) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(ep + (rin * 64 + ch * VEC) * ESZ);
+            char *dst = reinterpret_cast<char *>(p.c) + (goff + r * p.ldc + cn) * ESZ;
+            if (vec_ok && cn + VEC <= p.N) {
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (int q = 0; q < VEC && cn + q < p.N; q++) {
+                    if (BF16OUT) reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+                    else reinterpret_cast<uint32_t *>(dst)[q] = w[q];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
-// Rows per tile for a call: 256 when the call streams more weight bytes than
-// it does work on them (few rows per expert), 128 otherwise.
+// Rows per tile.  Measured on the DeepSeek-V3-shaped forward GEMM, 128-row
+// tiles (three wavefronts per SIMD) beat 256-row tiles (one wavefront per
+// SIMD, fewer weight re-reads) by 1.2x: the kernel is latency-bound, so
+// occupancy matters more than the extra panel fetches, which mostly hit L2.
+// The 256-row variant is kept behind a build switch for such measurements.
+#ifndef BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP
+#define BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP 0
+#endif
 static int pick_bm(int mode, int64_t M, int64_t G) {
     if (mode == BSP_GEMM_WGRAD) return 128;
-    return (M / G) < 192 ? 256 : 128;
+    return (M / G) < BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP ? 256 : 128;
 }
 
 int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
@@ -502,13 +533,16 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     const int bm = pick_bm(mode, M, G);
     p.ntm = (M + bm - 1) / bm + G;   // upper bound of the row-tile count
     k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bm, p.ntm, ws);
-    if (fmt == BSP_FMT_MXFP8) {
-        if (bm == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
-        else launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
-    } else {
-        if (bm == 256) launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);
-        else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
+#if BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP > 0
+    if (bm == 256) {
+        if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
+        else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);
+        return hipGetLastError();
     }
+#endif
+    (void)bm;
+    if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
+    else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
     return hipGetLastError();
 }
 
