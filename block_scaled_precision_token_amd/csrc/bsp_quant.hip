@@ -64,9 +64,9 @@ __device__ __forceinline__ Nvfp4Block nvfp4_candidate(const float (&xf)[16], flo
     }
     float r = 1.0f / eff;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        b.lo |= e2m1_encode(xf[i] * r) << (4 * i);
-        b.hi |= e2m1_encode(xf[8 + i] * r) << (4 * i);
+    for (int i = 0; i < 4; i++) {
+        b.lo |= e2m1x2_hw(xf[2 * i] * r, xf[2 * i + 1] * r) << (8 * i);
+        b.hi |= e2m1x2_hw(xf[8 + 2 * i] * r, xf[8 + 2 * i + 1] * r) << (8 * i);
     }
     return b;
 }
@@ -249,23 +249,30 @@ __device__ __forceinline__ uint32_t mxfp8_block(const float (&xf)[32], uint32_t 
     // falls below 2^-126, far under E4M3's rounding threshold.
     const float inv = exp2i(-k);
 #pragma unroll
-    for (int w = 0; w < 8; w++) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int b = 0; b < 4; b++) word |= e4m3_encode(xf[4 * w + b] * inv) << (8 * b);
-        q[w] = word;
-    }
+    for (int w = 0; w < 8; w++)
+        q[w] = e4m3x4_hw(xf[4 * w] * inv, xf[4 * w + 1] * inv, xf[4 * w + 2] * inv, xf[4 * w + 3] * inv);
     return (uint32_t)(k + 127);
 }
 
 constexpr int MX_TR = 128;  // tile rows (padded row space)
-constexpr int MX_TC = 64;   // tile columns
+constexpr int MX_TC = 128;  // tile columns
 constexpr int MX_MAXG = 2048;
 
-// One 128 x 64 tile: rowwise blocks (32 along K) straight from registers and
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// One 128 x 128 tile: rowwise blocks (32 along K) straight from registers and
 // columnwise blocks (32 along rows) through LDS, from a single read of x.
-// Grouped: tile rows live in the padded row space; block b belongs to the
-// group g with P[g] <= 32 b < P[g + 1] and reads source row
+// Each pair of threads writes a full 128-byte row of codes and each pair of
+// column threads a full 128-byte column run, so stores fill whole cache lines.
+// Grouped: tile rows live in the padded row space; 32-row block b belongs to
+// the group g with P[g] <= 32 b < P[g + 1] and reads source row
 // off[g] + (p - P[g]) (zero past the group).
 template <bool ROW, bool COL, bool GROUPED>
 __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__ x, int64_t M, int64_t K,
@@ -276,9 +283,9 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
                                                     const int32_t *__restrict__ gather, int64_t x_rows) {
     __shared__ uint16_t tile[MX_TR][MX_TC + 8];
     __shared__ int64_t sP[GROUPED ? MX_MAXG + 1 : 1];
-    __shared__ int64_t sOff[GROUPED ? MX_MAXG + 1 : 1];
     __shared__ int64_t blk_src0[MX_TR / 32], blk_end[MX_TR / 32];
-    const int t = threadIdx.x;
+    __shared__ int64_t wsum[4];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t p0 = (int64_t)blockIdx.y * MX_TR;
     const int64_t k0 = (int64_t)blockIdx.x * MX_TC;
     int64_t ptotal = M;
@@ -294,28 +301,21 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     }
 
     if (GROUPED) {
-        // padded group starts P (running sum of roundup32(n_g)), scanned in LDS
-        for (int g = t; g <= G; g += 256) sOff[g] = group_offsets[g];
-        __syncthreads();
+        // padded group starts P: thread t owns groups [t*per, t*per + per)
         const int per = (G + 255) / 256;
         const int g0 = t * per;
         int64_t local = 0;
-        for (int g = g0; g < g0 + per && g < G; g++) local += (sOff[g + 1] - sOff[g] + 31) / 32 * 32;
-        __shared__ int64_t part[256];
-        part[t] = local;
+        for (int g = g0; g < g0 + per && g < G; g++) local += (group_offsets[g + 1] - group_offsets[g] + 31) / 32 * 32;
+        const int64_t incl = wave_incl_scan(local, lane);
+        if (lane == 63) wsum[wv] = incl;
         __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            int64_t v = (t >= o) ? part[t - o] : 0;
-            __syncthreads();
-            part[t] += v;
-            __syncthreads();
-        }
-        int64_t run = part[t] - local;
+        int64_t run = incl - local;
+        for (int w = 0; w < wv; w++) run += wsum[w];
         for (int g = g0; g < g0 + per && g < G; g++) {
             sP[g] = run;
-            run += (sOff[g + 1] - sOff[g] + 31) / 32 * 32;
+            run += (group_offsets[g + 1] - group_offsets[g] + 31) / 32 * 32;
         }
-        if (t == 255) sP[G] = part[255];
+        if (t == 255) sP[G] = run;
         __syncthreads();
         ptotal = sP[G];
         if (t < MX_TR / 32) {
@@ -324,14 +324,12 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             if (pb < ptotal) {
                 int lo = 0, hi = G - 1;  // last g with P[g] <= pb
                 while (lo < hi) {
-                    int mid = (lo + hi + 1) / 2;
+                    const int mid = (lo + hi + 1) / 2;
                     if (sP[mid] <= pb) lo = mid;
                     else hi = mid - 1;
                 }
-                // skip empty groups sharing the same start
-                while (lo + 1 < G && sP[lo + 1] <= pb) lo++;
-                src0 = sOff[lo] + (pb - sP[lo]);
-                end = sOff[lo + 1] < M ? sOff[lo + 1] : M;  // offsets past M are never read
+                src0 = group_offsets[lo] + (pb - sP[lo]);
+                end = group_offsets[lo + 1] < M ? group_offsets[lo + 1] : M;  // offsets past M are never read
             }
             blk_src0[t] = src0;
             blk_end[t] = end;
@@ -340,10 +338,10 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
         if (p0 >= ptotal) return;
     }
 
-    // ---- load: thread t owns tile row t/2, columns [32 (t%2), +32) ----
+    // ---- load: thread t owns tile row t/2, columns [64 (t%2), +64): two 32-blocks ----
     const int tr = t >> 1, half = t & 1;
     const int64_t p = p0 + tr;
-    const int64_t kc = k0 + 32 * half;
+    const int64_t kc = k0 + 64 * half;
     int64_t src = -1;
     if (GROUPED) {
         const int b = tr >> 5;
@@ -352,57 +350,95 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     } else {
         if (p < M) src = p;
     }
-    const bool col_ok = kc < K;
     // physical row of x: the gathered row (out-of-range indices read as zeros)
     int64_t xrow = src;
     if (src >= 0 && gather) {
         xrow = gather[src];
         if (xrow < 0 || xrow >= x_rows) xrow = -1;
     }
-    float xf[32];
-    uint4 raw[4] = {};
-    if (xrow >= 0 && col_ok) {
-        const uint16_t *xp = x + xrow * ldx + kc;
+    uint4 raw[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) raw[i] = reinterpret_cast<const uint4 *>(xp)[i];
-    }
+    for (int i = 0; i < 8; i++) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    const bool blk0_ok = kc < K, blk1_ok = kc + 32 < K;
+    if (xrow >= 0) {
+        const uint4 *xp = reinterpret_cast<const uint4 *>(x + xrow * ldx + kc);
+        if (blk0_ok) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            for (int i = 0; i < 4; i++) raw[i] = xp[i];
+        }
+        if (blk1_ok) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            xf[8 * i + 2 * j] = bf16_lo(w[j]);
-            xf[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+            for (int i = 4; i < 8; i++) raw[i] = xp[i];
         }
     }
-    if (ROW && src >= 0 && col_ok) {
-        uint32_t q[8];
-        const uint32_t sc = mxfp8_block(xf, q);
-        uint4 *dst = reinterpret_cast<uint4 *>(codes_row + src * K + kc);
-        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-        scales_row[src * (K / 32) + kc / 32] = (uint8_t)sc;
+    if (ROW) {
+        uint32_t sc2 = 0;
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            float xf[32];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t w[4] = {raw[4 * b + i].x, raw[4 * b + i].y, raw[4 * b + i].z, raw[4 * b + i].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    xf[8 * i + 2 * j] = bf16_lo(w[j]);
+                    xf[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+                }
+            }
+            uint32_t q[8];
+            const uint32_t sc = mxfp8_block(xf, q);
+            sc2 |= sc << (8 * b);
+            if (src >= 0 && (b == 0 ? blk0_ok : blk1_ok)) {
+                uint4 *dst = reinterpret_cast<uint4 *>(codes_row + src * K + kc + 32 * b);
+                dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+                dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+            }
+        }
+        // the row's four scale bytes: this thread's two and its neighbour's two
+        const uint32_t other = __shfl_xor(sc2, 1, 64);
+        if (src >= 0) {
+            uint8_t *sp = scales_row + src * (K / 32) + k0 / 32;
+            if (k0 + MX_TC <= K && (K % 128) == 0) {
+                if (half == 0) *reinterpret_cast<uint32_t *>(sp) = sc2 | (other << 16);
+            } else {
+                if (blk0_ok) sp[2 * half] = (uint8_t)sc2;
+                if (blk1_ok) sp[2 * half + 1] = (uint8_t)(sc2 >> 8);
+            }
+        }
     }
     if (!COL) return;
 #pragma unroll
-    for (int i = 0; i < 4; i++) *reinterpret_cast<uint4 *>(&tile[tr][32 * half + 8 * i]) = raw[i];
+    for (int i = 0; i < 8; i++) *reinterpret_cast<uint4 *>(&tile[tr][64 * half + 8 * i]) = raw[i];
     __syncthreads();
 
-    // ---- columns: thread t owns column t%64 of the 32-row block t/64 ----
-    const int c = t & 63, b = t >> 6;
+    // ---- columns: thread t owns column t % 128, rows [64 (t / 128), +64): two 32-blocks ----
+    const int c = t & 127, rh = t >> 7;
     const int64_t kcol = k0 + c;
-    const int64_t pb = p0 + 32 * b;
     const int64_t plimit = GROUPED ? ptotal : M;
-    if (kcol >= K || pb >= plimit) return;
-    float cf[32];
+    if (kcol >= K) return;
+    uint32_t scs = 0;
+    int nvalid = 0;
 #pragma unroll
-    for (int i = 0; i < 32; i++) cf[i] = __uint_as_float((uint32_t)tile[32 * b + i][c] << 16);
-    uint32_t q[8];
-    const uint32_t sc = mxfp8_block(cf, q);
-    uint4 *dst = reinterpret_cast<uint4 *>(codes_colT + kcol * ld_colT + pb);
-    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-    scales_colT[kcol * (ld_colT / 32) + pb / 32] = (uint8_t)sc;
+    for (int b = 0; b < 2; b++) {
+        const int64_t pb = p0 + 64 * rh + 32 * b;
+        if (pb >= plimit) break;
+        float cf[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) cf[i] = __uint_as_float((uint32_t)tile[64 * rh + 32 * b + i][c] << 16);
+        uint32_t q[8];
+        const uint32_t sc = mxfp8_block(cf, q);
+        uint4 *dst = reinterpret_cast<uint4 *>(codes_colT + kcol * ld_colT + pb);
+        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+        scs |= sc << (8 * b);
+        nvalid = b + 1;
+    }
+    uint8_t *sp = scales_colT + kcol * (ld_colT / 32) + (p0 + 64 * rh) / 32;
+    if (nvalid == 2 && (reinterpret_cast<uintptr_t>(sp) & 1) == 0) {
+        *reinterpret_cast<uint16_t *>(sp) = (uint16_t)scs;
+    } else {
+        for (int b = 0; b < nvalid; b++) sp[b] = (uint8_t)(scs >> (8 * b));
+    }
 }
 
 // Rowwise-only MXFP8: one lane per 32-value block.
@@ -696,19 +732,23 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
                     for (int w = 0; w < 4; w++) rnd[4 * h + w] = c[w];
                 }
             }
+            if (SR) {
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const float v = fabsf(d[i]) * r;
-                uint32_t mag;
-                if (SR) {
+                for (int i = 0; i < 16; i++) {
+                    const float v = fabsf(d[i]) * r;
                     const uint32_t word = rnd[i >> 1];
-                    mag = e2m1_sr_mag(v, (i & 1) ? (word >> 16) : (word & 0xFFFFu));
-                } else {
-                    mag = e2m1_mag(v);
+                    const uint32_t mag = e2m1_sr_mag(v, (i & 1) ? (word >> 16) : (word & 0xFFFFu));
+                    const uint32_t code = ((__float_as_uint(d[i]) >> 28) & 8u) | mag;
+                    if (i < 8) lo |= code << (4 * i);
+                    else hi |= code << (4 * (i - 8));
                 }
-                const uint32_t code = ((__float_as_uint(d[i]) >> 28) & 8u) | mag;
-                if (i < 8) lo |= code << (4 * i);
-                else hi |= code << (4 * (i - 8));
+            } else {
+                // |d| * r carries the sign of d into the hardware conversion
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    lo |= e2m1x2_hw(d[2 * i] * r, d[2 * i + 1] * r) << (8 * i);
+                    hi |= e2m1x2_hw(d[8 + 2 * i] * r, d[8 + 2 * i + 1] * r) << (8 * i);
+                }
             }
         }
         *reinterpret_cast<uint2 *>(codesT + k * (M / 2) + mb / 2) = make_uint2(lo, hi);
