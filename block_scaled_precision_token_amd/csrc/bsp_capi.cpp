@@ -62,8 +62,9 @@ BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
 
 BSP_EXPORT size_t bsp_gemm_workspace_size(int mode, int64_t M, int64_t G) {
     if (M < 0 || G < 1) return 0;
-    if (mode == BSP_GEMM_WGRAD) return (size_t)(G + 1) * sizeof(int64_t);
-    return (size_t)bsp::gemm_tile_count(M, G) * sizeof(int64_t);
+    // Tile list (or padded group starts), then the work-queue counters.
+    if (mode == BSP_GEMM_WGRAD) return (size_t)(G + 1 + bsp::kGemmSchedSlots) * sizeof(int64_t);
+    return (size_t)(bsp::gemm_tile_count(M, G) + bsp::kGemmSchedSlots) * sizeof(int64_t);
 }
 
 BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,

@@ -44,6 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int GBN = 128;   // output columns per workgroup
 constexpr int GBK = 64;    // K values per LDS stage
 constexpr int NXCD = 8;
+constexpr int kMaxDevices = 64;
 
 struct GemmArgs {
     const uint8_t *a_codes, *a_scales;
@@ -54,6 +55,7 @@ struct GemmArgs {
     const float *b_outer;
     void *c;
     const int64_t *tiles;     // row-grouped form: packed (group << 40) | first row; WGRAD: padded starts [G+1]
+    int64_t *sched;           // NXCD work-queue counters, then (row-grouped form) the listed row-tile count
     int64_t G, M, N, K, ldc, a_rows;
     int64_t ntm;              // row tiles (row-grouped form: tile-list length; WGRAD: G * ceil(M / BM))
     int64_t ntn;              // column tiles
@@ -61,7 +63,7 @@ struct GemmArgs {
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
 __global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t M, int64_t bm, int64_t ntile_max,
-                            int64_t *__restrict__ tiles) {
+                            int64_t *__restrict__ tiles, int64_t *__restrict__ sched) {
     __shared__ int64_t base[1025];
     int64_t carry = 0;
     for (int64_t g0 = 0; g0 < G; g0 += 1024) {
@@ -88,10 +90,14 @@ __global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t 
         __syncthreads();
     }
     for (int64_t t = carry + threadIdx.x; t < ntile_max; t += blockDim.x) tiles[t] = -1;
+    if (threadIdx.x < NXCD) sched[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sched[NXCD] = carry < ntile_max ? carry : ntile_max;
 }
 
 // Padded group starts P (running sum of roundup32(n_g)) for the weight-gradient form.
-__global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int64_t *__restrict__ P) {
+__global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int64_t *__restrict__ P,
+                                int64_t *__restrict__ sched) {
+    if (threadIdx.x < NXCD) sched[threadIdx.x] = 0;
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         int64_t run = 0;
         for (int64_t g = 0; g < G; g++) {
@@ -246,6 +252,62 @@ __device__ __forceinline__ void nv_store(const NvStage<ROWS> &st, _Float16 *sh) 
 // kernel
 // ---------------------------------------------------------------------------
 
+// One output tile: its expert, rows, K range and the operand rows this
+// thread stages (fixed for the whole K loop).
+struct TileCtx {
+    int64_t g, row0, row_end, kbeg, kend, col0, arow, brow, nk;
+    const uint8_t *bc, *bs;
+};
+
+template <int FMT, int MODE, int BM>
+__device__ __forceinline__ void tile_setup(const GemmArgs &p, int64_t lin, TileCtx &c) {
+    const int t = threadIdx.x;
+    const int64_t ty = lin / p.ntn, tx = lin - ty * p.ntn;
+    if (MODE == BSP_GEMM_WGRAD) {
+        const int64_t mt_per_g = (p.M + BM - 1) / BM;
+        c.g = ty / mt_per_g;
+        c.row0 = (ty - c.g * mt_per_g) * BM;
+        c.row_end = p.M;
+        c.kbeg = p.tiles[c.g];
+        c.kend = c.kbeg + (p.group_offsets[c.g + 1] - p.group_offsets[c.g] + 31) / 32 * 32;
+        c.kend = c.kend < p.K ? c.kend : p.K;  // offsets are trusted only up to the copies' width
+        c.bc = p.b_codes;
+        c.bs = p.b_scales;
+    } else {
+        const int64_t tile = p.tiles[ty];       // valid: ty < the tile count the setup kernel wrote
+        c.g = tile >> 40;
+        c.row0 = tile & ((1ll << 40) - 1);
+        c.row_end = p.group_offsets[c.g + 1];
+        c.row_end = c.row_end < p.M ? c.row_end : p.M;  // never past the rows of C
+        c.kbeg = 0;
+        c.kend = p.K;
+        const int64_t bcs = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 2 : p.N * p.K;
+        const int64_t bss = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 16 : p.N * p.K / 32;
+        c.bc = p.b_codes + c.g * bcs;
+        c.bs = p.b_scales + c.g * bss;
+    }
+    c.col0 = tx * GBN;
+    c.nk = c.kend > c.kbeg ? (c.kend - c.kbeg + GBK - 1) / GBK : 0;
+    const int lrow = (BM == 128) ? (t >> 1) : t;
+    const int64_t r = c.row0 + lrow;
+    c.arow = -1;
+    if (r < c.row_end) {
+        c.arow = r;
+        if (MODE != BSP_GEMM_WGRAD && p.a_gather) {
+            c.arow = (int64_t)p.a_gather[r];
+            if (c.arow < 0 || c.arow >= p.a_rows) c.arow = -1;  // an out-of-range gather index reads as a zero row
+        }
+    }
+    const int64_t cn = c.col0 + (t >> 1);
+    c.brow = cn < p.N ? cn : -1;
+}
+
+// Persistent workgroups.  Each XCD owns a work queue over a contiguous chunk
+// of the row-major tile sequence (so concurrent tiles on one L2 share the
+// activation tile and neighbouring weight panels) and, once it is empty,
+// steals from the other XCDs' queues, which balances experts of very
+// different sizes.  While a tile's epilogue runs, the first K stage of the
+// next tile is already being fetched.
 template <int FMT, int MODE, bool BF16OUT, int BM>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     constexpr int WM = BM / 2;            // rows per wavefront
@@ -253,238 +315,218 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     constexpr int LDS_ROW = (FMT == BSP_FMT_MXFP8) ? MX_LDS_STRIDE : NV_LDS_STRIDE * 2;   // bytes
     constexpr int STAGE_BYTES = (BM + GBN) * LDS_ROW + ((FMT == BSP_FMT_MXFP8) ? (BM + GBN) * 2 : 0);
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+    __shared__ int64_t s_lin;
 
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 31, lh = lane >> 5;
 
-    // ---- XCD-aware tile order ----
-    const int64_t total = p.ntm * p.ntn;
+    const int64_t ntm = (MODE == BSP_GEMM_WGRAD) ? p.ntm : p.sched[NXCD];   // row tiles actually listed
+    const int64_t total = ntm * p.ntn;
     const int64_t chunk = (total + NXCD - 1) / NXCD;
-    const int64_t lin = (int64_t)(blockIdx.x % NXCD) * chunk + blockIdx.x / NXCD;
-    if (lin >= total) return;
-    const int64_t ty = lin / p.ntn, tx = lin - ty * p.ntn;
-
-    int64_t g, row0, row_end, kbeg, kend;
-    const uint8_t *bc, *bs;
-    if (MODE == BSP_GEMM_WGRAD) {
-        const int64_t mt_per_g = (p.M + BM - 1) / BM;
-        g = ty / mt_per_g;
-        row0 = (ty - g * mt_per_g) * BM;
-        row_end = p.M;
-        kbeg = p.tiles[g];
-        kend = kbeg + (p.group_offsets[g + 1] - p.group_offsets[g] + 31) / 32 * 32;
-        kend = kend < p.K ? kend : p.K;  // offsets are trusted only up to the copies' width
-        bc = p.b_codes;
-        bs = p.b_scales;
-    } else {
-        const int64_t tile = p.tiles[ty];
-        if (tile < 0) return;
-        g = tile >> 40;
-        row0 = tile & ((1ll << 40) - 1);
-        row_end = p.group_offsets[g + 1];
-        row_end = row_end < p.M ? row_end : p.M;  // never past the rows of C
-        kbeg = 0;
-        kend = p.K;
-        const int64_t bcs = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 2 : p.N * p.K;
-        const int64_t bss = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 16 : p.N * p.K / 32;
-        bc = p.b_codes + g * bcs;
-        bs = p.b_scales + g * bss;
-    }
-    const int64_t col0 = tx * GBN;
-
-    // ---- the operand rows this loader thread stages (fixed for the whole K loop) ----
-    int64_t arow;
-    {
-        const int lrow = (BM == 128) ? (t >> 1) : t;
-        const int64_t r = row0 + lrow;
-        arow = -1;
-        if (r < row_end) {
-            arow = r;
-            if (MODE != BSP_GEMM_WGRAD && p.a_gather) {
-                arow = (int64_t)p.a_gather[r];
-                if (arow < 0 || arow >= p.a_rows) arow = -1;  // an out-of-range gather index reads as a zero row
+    const int xcd = blockIdx.x % NXCD;
+    auto grab = [&]() -> int64_t {
+        if (t == 0) {
+            int64_t got = -1;
+            for (int d = 0; d < NXCD && got < 0; d++) {
+                const int q = (xcd + d) % NXCD;
+                const int64_t qbeg = q * chunk;
+                const int64_t qlen = (total - qbeg) < chunk ? (total - qbeg) : chunk;
+                if (qlen <= 0) continue;
+                const int64_t i = (int64_t)atomicAdd(reinterpret_cast<unsigned long long *>(p.sched + q), 1ull);
+                if (i < qlen) got = qbeg + i;
             }
+            s_lin = got;
         }
-    }
-    int64_t brow;
-    {
-        const int64_t cn = col0 + (t >> 1);
-        brow = cn < p.N ? cn : -1;
-    }
+        __syncthreads();
+        // Uniform across the workgroup: move it to scalar registers so the
+        // whole tile context is computed once per wavefront, not per lane.
+        const uint64_t u = (uint64_t)s_lin;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+        __syncthreads();
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+
+    const int64_t ldk = p.K;
+    MxStage<BM> ma;
+    MxStage<GBN> mb;
+    NvStage<BM> na;
+    NvStage<GBN> nb;
+    auto load = [&](const TileCtx &c, int64_t stage) {
+        if (FMT == BSP_FMT_MXFP8) {
+            mx_load<BM>(ma, p.a_codes, p.a_scales, ldk, &c.arow, c.kbeg + stage * GBK, c.kend);
+            mx_load<GBN>(mb, c.bc, c.bs, ldk, &c.brow, c.kbeg + stage * GBK, c.kend);
+        } else {
+            nv_load<BM>(na, p.a_codes, p.a_scales, p.K, c.arow, stage * GBK);
+            nv_load<GBN>(nb, c.bc, c.bs, p.K, c.brow, stage * GBK);
+        }
+    };
+    uint8_t *const lA0 = smem, *const lB0 = smem + BM * LDS_ROW;
+    uint8_t *const lAs0 = smem + (BM + GBN) * LDS_ROW, *const lBs0 = lAs0 + BM * 2;   // MXFP8 scales
+    auto store = [&](int buf) {
+        if (FMT == BSP_FMT_MXFP8) {
+            mx_store<BM>(ma, lA0 + buf * STAGE_BYTES, lAs0 + buf * STAGE_BYTES);
+            mx_store<GBN>(mb, lB0 + buf * STAGE_BYTES, lBs0 + buf * STAGE_BYTES);
+        } else {
+            nv_store<BM>(na, reinterpret_cast<_Float16 *>(lA0 + buf * STAGE_BYTES));
+            nv_store<GBN>(nb, reinterpret_cast<_Float16 *>(lB0 + buf * STAGE_BYTES));
+        }
+    };
 
     v16f acc[TI][2];
+    TileCtx cur, nxt;
+    int64_t lin = grab();
+    bool have = lin >= 0;
+    if (have) {
+        tile_setup<FMT, MODE, BM>(p, lin, cur);
+        if (cur.nk > 0) load(cur, 0);
+    }
+    while (have) {
+        // Per-lane LDS offsets are rederived for every tile from an opaque
+        // copy of the thread index; hoisted out of the tile loop they would
+        // stay live through the epilogue and cost occupancy.
+        int tq = threadIdx.x;
+        asm volatile("" : "+v"(tq));
+        const int lane = tq & 63, wave = tq >> 6;
+        const int wm = wave >> 1, wn = wave & 1;
+        const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < TI; i++)
+        for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+                for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-    const int64_t nk = (kend - kbeg + GBK - 1) / GBK;
-    if (FMT == BSP_FMT_MXFP8) {
-        const int64_t ldk = p.K;
-        MxStage<BM> sa;
-        MxStage<GBN> sb;
-        uint8_t *const lA0 = smem, *const lB0 = smem + BM * MX_LDS_STRIDE;
-        uint8_t *const lAs0 = smem + (BM + GBN) * MX_LDS_STRIDE, *const lBs0 = lAs0 + BM * 2;
-        if (nk > 0) {
-            mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg, kend);
-            mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg, kend);
-            mx_store<BM>(sa, lA0, lAs0);
-            mx_store<GBN>(sb, lB0, lBs0);
-        }
-        if (nk > 1) {
-            mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg + GBK, kend);
-            mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg + GBK, kend);
-        }
+        // ---- K loop: double-buffered LDS, next stage prefetched in registers ----
+        const int64_t nk = cur.nk;
+        if (nk > 0) store(0);
+        if (nk > 1) load(cur, 1);
         __syncthreads();
         for (int64_t kt = 0; kt < nk; kt++) {
             const int buf = (int)(kt & 1);
-            const uint8_t *A = lA0 + buf * STAGE_BYTES, *B = lB0 + buf * STAGE_BYTES;
-            const uint8_t *AS = lAs0 + buf * STAGE_BYTES, *BS = lBs0 + buf * STAGE_BYTES;
-            // Row bytes [0, 32) hold K block 0 and [32, 64) block 1.  The
-            // instruction wants lane half h to supply bytes [16h, 16h + 16) of
-            // block 0 then of block 1 (offsets 16h and 32 + 16h), with the E8M0
-            // byte of block h.
-            v8i af[TI], bf[2];
-            int as[TI], bsc[2];
+            if (FMT == BSP_FMT_MXFP8) {
+                const uint8_t *A = lA0 + buf * STAGE_BYTES, *B = lB0 + buf * STAGE_BYTES;
+                const uint8_t *AS = lAs0 + buf * STAGE_BYTES, *BS = lBs0 + buf * STAGE_BYTES;
+                // Row bytes [0, 32) hold K block 0 and [32, 64) block 1.  The
+                // instruction wants lane half h to supply bytes [16h, 16h + 16) of
+                // block 0 then of block 1 (offsets 16h and 32 + 16h), with the
+                // E8M0 byte of block h.
+                v8i af[TI], bf[2];
+                int as[TI], bsc[2];
 #pragma unroll
-            for (int i = 0; i < TI; i++) {
-                const int r = wm * WM + 32 * i + lr;
-                const uint4 u0 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 16 * lh);
-                const uint4 u1 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 32 + 16 * lh);
-                af[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                as[i] = AS[r * 2 + lh];
-            }
+                for (int i = 0; i < TI; i++) {
+                    const int r = wm * WM + 32 * i + lr;
+                    const uint4 u0 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 16 * lh);
+                    const uint4 u1 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 32 + 16 * lh);
+                    af[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                    as[i] = AS[r * 2 + lh];
+                }
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int r = wn * 64 + 32 * j + lr;
-                const uint4 u0 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 16 * lh);
-                const uint4 u1 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 32 + 16 * lh);
-                bf[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                bsc[j] = BS[r * 2 + lh];
-            }
-#pragma unroll
-            for (int i = 0; i < TI; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0,
-                                                                                as[i], 0, bsc[j]);
-            if (kt + 1 < nk) {
-                mx_store<BM>(sa, lA0 + (buf ^ 1) * STAGE_BYTES, lAs0 + (buf ^ 1) * STAGE_BYTES);
-                mx_store<GBN>(sb, lB0 + (buf ^ 1) * STAGE_BYTES, lBs0 + (buf ^ 1) * STAGE_BYTES);
-            }
-            if (kt + 2 < nk) {
-                mx_load<BM>(sa, p.a_codes, p.a_scales, ldk, &arow, kbeg + (kt + 2) * GBK, kend);
-                mx_load<GBN>(sb, bc, bs, ldk, &brow, kbeg + (kt + 2) * GBK, kend);
-            }
-            __syncthreads();
-        }
-    } else {
-        NvStage<BM> sa;
-        NvStage<GBN> sb;
-        _Float16 *const lA0 = reinterpret_cast<_Float16 *>(smem);
-        _Float16 *const lB0 = reinterpret_cast<_Float16 *>(smem + BM * NV_LDS_STRIDE * 2);
-        constexpr int STAGE_H = STAGE_BYTES / 2;
-        if (nk > 0) {
-            nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, 0);
-            nv_load<GBN>(sb, bc, bs, p.K, brow, 0);
-            nv_store<BM>(sa, lA0);
-            nv_store<GBN>(sb, lB0);
-        }
-        if (nk > 1) {
-            nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, GBK);
-            nv_load<GBN>(sb, bc, bs, p.K, brow, GBK);
-        }
-        __syncthreads();
-        for (int64_t kt = 0; kt < nk; kt++) {
-            const int buf = (int)(kt & 1);
-            const _Float16 *A = lA0 + buf * STAGE_H, *B = lB0 + buf * STAGE_H;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                v8h af[TI], bf[2];
-#pragma unroll
-                for (int i = 0; i < TI; i++)
-                    af[i] = *reinterpret_cast<const v8h *>(A + (wm * WM + 32 * i + lr) * NV_LDS_STRIDE + 16 * q + 8 * lh);
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    bf[j] = *reinterpret_cast<const v8h *>(B + (wn * 64 + 32 * j + lr) * NV_LDS_STRIDE + 16 * q + 8 * lh);
+                for (int j = 0; j < 2; j++) {
+                    const int r = wn * 64 + 32 * j + lr;
+                    const uint4 u0 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 16 * lh);
+                    const uint4 u1 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 32 + 16 * lh);
+                    bf[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                    bsc[j] = BS[r * 2 + lh];
+                }
 #pragma unroll
                 for (int i = 0; i < TI; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
+                                                                                    0, as[i], 0, bsc[j]);
+            } else {
+                const _Float16 *A = reinterpret_cast<const _Float16 *>(lA0 + buf * STAGE_BYTES);
+                const _Float16 *B = reinterpret_cast<const _Float16 *>(lB0 + buf * STAGE_BYTES);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    v8h af[TI], bf[2];
+#pragma unroll
+                    for (int i = 0; i < TI; i++)
+                        af[i] = *reinterpret_cast<const v8h *>(A + (wm * WM + 32 * i + lr) * NV_LDS_STRIDE + 16 * q +
+                                                               8 * lh);
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        bf[j] = *reinterpret_cast<const v8h *>(B + (wn * 64 + 32 * j + lr) * NV_LDS_STRIDE + 16 * q +
+                                                               8 * lh);
+#pragma unroll
+                    for (int i = 0; i < TI; i++)
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                }
             }
-            if (kt + 1 < nk) {
-                nv_store<BM>(sa, lA0 + (buf ^ 1) * STAGE_H);
-                nv_store<GBN>(sb, lB0 + (buf ^ 1) * STAGE_H);
+            if (kt + 1 < nk) store(buf ^ 1);
+            if (kt + 2 < nk) load(cur, kt + 2);
+            __syncthreads();
+        }
+
+        // ---- next tile: its first stage is fetched while this epilogue runs ----
+        lin = grab();
+        const bool have_next = lin >= 0;
+        if (have_next) {
+            tile_setup<FMT, MODE, BM>(p, lin, nxt);
+            if (nxt.nk > 0) load(nxt, 0);
+        }
+        // ---- epilogue ----
+        // The MFMA leaves lane l with column l % 32 of a 32 x 32 block and rows
+        // 8 (e / 4) + 4 (l / 32) + e % 4.  Each wavefront stages one 32 x 64
+        // slice of its outputs in LDS (the stage buffers are free: the K loop
+        // ended with a barrier), then writes whole rows with 16-byte
+        // non-temporal stores, so the output streams past L2 instead of
+        // evicting reusable operand panels.
+        constexpr int ESZ = BF16OUT ? 2 : 4;
+        constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
+        constexpr int CHUNKS = 64 / VEC;               // 16-byte chunks per 64-column row
+        const float gb = (FMT == BSP_FMT_NVFP4) ? p.b_outer[cur.g] : 1.0f;
+        const int64_t goff = (MODE == BSP_GEMM_WGRAD) ? cur.g * p.M * p.ldc : 0;
+        uint8_t *ep = smem + wave * (32 * 64 * ESZ);
+        const bool vec_ok = (p.ldc % VEC) == 0;
+#pragma unroll
+        for (int i = 0; i < TI; i++) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
+                float sc = 1.0f;
+                if (FMT == BSP_FMT_NVFP4) {
+                    const int64_t r = cur.row0 + wm * WM + 32 * i + rin;
+                    sc = 0.0f;
+                    if (r < cur.row_end) {
+                        const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
+                        sc = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const float v = acc[i][j][e] * sc;
+                    const int cin = 32 * j + lr;
+                    if (BF16OUT) reinterpret_cast<uint16_t *>(ep)[rin * 64 + cin] = (uint16_t)f32_to_bf16(v);
+                    else reinterpret_cast<float *>(ep)[rin * 64 + cin] = v;
+                }
             }
-            if (kt + 2 < nk) {
-                nv_load<BM>(sa, p.a_codes, p.a_scales, p.K, arow, (kt + 2) * GBK);
-                nv_load<GBN>(sb, bc, bs, p.K, brow, (kt + 2) * GBK);
+            __syncthreads();
+#pragma unroll
+            for (int pass = 0; pass < 32 * CHUNKS / 64; pass++) {
+                const int idx = pass * 64 + lane;
+                const int rin = idx / CHUNKS, ch = idx % CHUNKS;
+                const int64_t r = cur.row0 + wm * WM + 32 * i + rin;
+                const int64_t cn = cur.col0 + wn * 64 + ch * VEC;
+                if (r >= cur.row_end || cn >= p.N) continue;
+                const uint4 v = *reinterpret_cast<const uint4 *>(ep + (rin * 64 + ch * VEC) * ESZ);
+                char *dst = reinterpret_cast<char *>(p.c) + (goff + r * p.ldc + cn) * ESZ;
+                if (vec_ok && cn + VEC <= p.N) {
+                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    for (int q = 0; q < VEC && cn + q < p.N; q++) {
+                        if (BF16OUT) reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+                        else reinterpret_cast<uint32_t *>(dst)[q] = w[q];
+                    }
+                }
             }
             __syncthreads();
         }
-    }
-
-    // ---- epilogue ----
-    // The MFMA leaves lane l with column l % 32 of a 32 x 32 block and rows
-    // 8 (e / 4) + 4 (l / 32) + e % 4.  Each wavefront stages one 32 x 64 slice
-    // of its outputs in LDS (the stage buffers are free: the K loop ended with
-    // a barrier), then writes whole rows with 16-byte non-temporal stores, so
-    // the output streams past L2 instead of evicting reusable operand panels.
-    constexpr int ESZ = BF16OUT ? 2 : 4;
-    constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
-    constexpr int CHUNKS = 64 / VEC;               // 16-byte chunks per 64-column row
-    const float gb = (FMT == BSP_FMT_NVFP4) ? p.b_outer[g] : 1.0f;
-    const int64_t goff = (MODE == BSP_GEMM_WGRAD) ? g * p.M * p.ldc : 0;
-    uint8_t *ep = smem + wave * (32 * 64 * ESZ);
-    const bool vec_ok = (p.ldc % VEC) == 0;
-#pragma unroll
-    for (int i = 0; i < TI; i++) {
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-            float s = 1.0f;
-            if (FMT == BSP_FMT_NVFP4) {
-                const int64_t r = row0 + wm * WM + 32 * i + rin;
-                s = 0.0f;
-                if (r < row_end) {
-                    const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
-                    s = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const float v = acc[i][j][e] * s;
-                const int cin = 32 * j + lr;
-                if (BF16OUT) reinterpret_cast<uint16_t *>(ep)[rin * 64 + cin] = (uint16_t)f32_to_bf16(v);
-                else reinterpret_cast<float *>(ep)[rin * 64 + cin] = v;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int pass = 0; pass < 32 * CHUNKS / 64; pass++) {
-            const int idx = pass * 64 + lane;
-            const int rin = idx / CHUNKS, ch = idx % CHUNKS;
-            const int64_t r = row0 + wm * WM + 32 * i + rin;
-            const int64_t cn = col0 + wn * 64 + ch * VEC;
-            if (r >= row_end || cn >= p.N) continue;
-            const uint4 v = *reinterpret_cast<const uint4 *>(ep + (rin * 64 + ch * VEC) * ESZ);
-            char *dst = reinterpret_cast<char *>(p.c) + (goff + r * p.ldc + cn) * ESZ;
-            if (vec_ok && cn + VEC <= p.N) {
-                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
-            } else {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                for (int q = 0; q < VEC && cn + q < p.N; q++) {
-                    if (BF16OUT) reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-                    else reinterpret_cast<uint32_t *>(dst)[q] = w[q];
-                }
-            }
-        }
-        __syncthreads();
+        cur = nxt;
+        have = have_next;
     }
 }
 
@@ -503,13 +545,37 @@ static int pick_bm(int mode, int64_t M, int64_t G) {
 
 int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
 
+// Workgroups resident per XCD for one instantiation on the current device
+// (compute units per XCD times workgroups per compute unit), cached per device.
+template <typename Kern>
+static int64_t resident_per_xcd(Kern kern, int *cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    if (cache[dev] == 0) {
+        int cus = 0, occ = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess || occ <= 0) occ = 1;
+        cache[dev] = (cus + NXCD - 1) / NXCD * occ;
+    }
+    return cache[dev];
+}
+
+template <int FMT, int MODE, bool BF, int BM>
+static void launch_one(const GemmArgs &p, hipStream_t s) {
+    static int cache[kMaxDevices] = {};
+    const int64_t per_xcd_max = resident_per_xcd(k_gemm<FMT, MODE, BF, BM>, cache);
+    const int64_t total = p.ntm * p.ntn;            // upper bound of the tile count
+    const int64_t per_xcd_need = (total + NXCD - 1) / NXCD;
+    const int64_t per_xcd = per_xcd_need < per_xcd_max ? per_xcd_need : per_xcd_max;
+    dim3 grid((unsigned)(per_xcd * NXCD)), block(256);
+    k_gemm<FMT, MODE, BF, BM><<<grid, block, 0, s>>>(p);
+}
+
 template <int FMT, int MODE, int BM>
 static void launch_k(const GemmArgs &p, bool bf, hipStream_t s) {
-    const int64_t total = p.ntm * p.ntn;
-    const int64_t chunk = (total + NXCD - 1) / NXCD;
-    dim3 grid((unsigned)(chunk * NXCD)), block(256);
-    if (bf) k_gemm<FMT, MODE, true, BM><<<grid, block, 0, s>>>(p);
-    else k_gemm<FMT, MODE, false, BM><<<grid, block, 0, s>>>(p);
+    if (bf) launch_one<FMT, MODE, true, BM>(p, s);
+    else launch_one<FMT, MODE, false, BM>(p, s);
 }
 
 hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
@@ -522,17 +588,19 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     p.c = c; p.G = G; p.M = M; p.N = N; p.K = K; p.ldc = ldc; p.a_rows = a_rows;
     int64_t *ws = reinterpret_cast<int64_t *>(workspace);
     p.tiles = ws;
+    // Work-queue counters follow the tile list (or the padded starts).
+    p.sched = ws + (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G));
     p.ntn = (N + GBN - 1) / GBN;
     const bool bf = c_dtype == BSP_DTYPE_BF16;
     if (mode == BSP_GEMM_WGRAD) {
-        k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws);
+        k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
         p.ntm = G * ((M + 127) / 128);
         launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
         return hipGetLastError();
     }
     const int bm = pick_bm(mode, M, G);
     p.ntm = (M + bm - 1) / bm + G;   // upper bound of the row-tile count
-    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bm, p.ntm, ws);
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bm, p.ntm, ws, p.sched);
 #if BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP > 0
     if (bm == 256) {
         if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);

@@ -204,7 +204,9 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
  *   a_gather, a_outer, b_outer must be NULL and a_rows == M.
  * Accumulation is f32 on the MFMA units; the epilogue applies gA * gB and
  * rounds to c_dtype (RNE for bf16).
- *   workspace  device, >= bsp_gemm_workspace_size(mode, M, G) bytes
+ *   workspace  device, >= bsp_gemm_workspace_size(mode, M, G) bytes; holds
+ *              the tile list and the work-queue counters, rewritten by every
+ *              call, so calls sharing one workspace must be stream-ordered
  */
 bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales,
                                             const float *a_outer, const int32_t *a_gather, int64_t a_rows,

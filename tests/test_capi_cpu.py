@@ -49,8 +49,8 @@ def test_size_helpers():
     assert L.bsp_mxfp8_sizes(4096, 7168, ctypes.byref(c), ctypes.byref(s)) == 0
     assert (c.value, s.value) == (4096 * 7168, 4096 * 224)
     assert L.bsp_mxfp8_grouped_cols(100, 4) == 224          # roundup32(100 + 31*4)
-    assert L.bsp_gemm_workspace_size(0, 65536, 128) == (512 + 128) * 8
-    assert L.bsp_gemm_workspace_size(2, 36864, 257) == 258 * 8
+    assert L.bsp_gemm_workspace_size(0, 65536, 128) == (512 + 128 + 16) * 8
+    assert L.bsp_gemm_workspace_size(2, 36864, 257) == (258 + 16) * 8
     assert L.bsp_requant_workspace_size(16384) >= 4
 
 
