@@ -164,7 +164,7 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
     if (G < 1 || M <= 0 || N <= 0 || K <= 0 || ldc < N) return BSP_ERR_SHAPE;
     if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
-    if (fmt == BSP_FMT_NVFP4 && K % 16) return BSP_ERR_SHAPE;
+    if (fmt == BSP_FMT_NVFP4 && K % 32) return BSP_ERR_SHAPE;   // rows of codes 16-byte aligned
     if (mode != BSP_GEMM_WGRAD && !a_gather && a_rows != M) return BSP_ERR_SHAPE;
     if (mode == BSP_GEMM_WGRAD && a_rows != M) return BSP_ERR_SHAPE;
     if (a_rows <= 0) return BSP_ERR_SHAPE;

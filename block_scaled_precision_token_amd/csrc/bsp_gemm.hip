@@ -11,25 +11,39 @@
 // one lane half, so codes and scales go to the matrix core unchanged.
 //
 // NVFP4: the E4M3 scale covers 16 values and the matrix core only scales by
-// powers of two per 32, so the operand value q * s (E2M1 times E4M3, at most
-// 6 significant bits, magnitude in [2^-10, 2688]) is rebuilt exactly in fp16
-// while the tile is staged into LDS (once per workgroup) and multiplied on
-// the fp16 MFMA (V_MFMA_F32_32X32X16_F16); the FP32 outer scales (per token
-// for A, per expert for B) are applied in the epilogue.
+// powers of two per 32, so each wavefront rebuilds its operand fragments
+// q * s exactly in fp16 (E2M1 times E4M3 has at most 6 significant bits and a
+// magnitude in [2^-10, 2688]) and multiplies on the fp16 MFMA
+// (V_MFMA_F32_32X32X16_F16); the FP32 outer scales (per token for A, per
+// expert for B) are applied in the epilogue.
 //
-// Tiling: 256 threads = 4 wavefronts in 2 x 2.  Output tile BM x 128 (BM =
-// 128; a 256-row variant exists behind a build switch).  K moves in
-// 64-value stages through double-buffered LDS with register prefetch of the
-// next stage.  Row tiles never straddle two experts: a setup kernel lists the
-// (expert, first row) of every row tile from the device-side group offsets,
-// so no host synchronization is needed.
+// Data movement.  Operand tiles stream from global memory straight into LDS
+// with the gfx950 LDS-DMA loads (GLOBAL_LOAD_LDS_DWORDX4 for codes, _DWORD
+// for scales): no registers are spent on staging, so a ring of four LDS
+// stages keeps three K steps (48 KB per workgroup for MXFP8) in flight while
+// the fourth is multiplied.  The ring runs across tile boundaries: the first
+// stages of a workgroup's next tile are fetched while the current tile is
+// finished and written back.  Completion is tracked with explicit vmcnt waits
+// (loads retire in order, so "at most 2 stages outstanding" means the oldest
+// stage has landed) followed by a workgroup barrier; the epilogue's stores are
+// issued so that the compiler's own counter model stays exact.
 //
-// Tile order: workgroup ids are dispatched round-robin over the 8 XCDs, each
-// with its own L2.  A workgroup's id is mapped to an XCD-contiguous chunk of
-// the row-major tile sequence (row tile outer, column tile inner), so the
-// workgroups in flight on one XCD are consecutive column tiles of the same
-// row tiles: they share the activation tile, and successive row tiles of one
-// expert re-read the same weight panels while they are still in that L2.
+// LDS layout of a stage: per operand 128 rows of 64 (MXFP8) or 32 (NVFP4)
+// code bytes, the 16-byte chunks of row r stored at position chunk ^ swz(r)
+// so that the 32 rows read by one fragment load hit distinct banks; then per
+// row the two aligned dwords that contain the stage's scale bytes.
+//
+// Tiling: 256 threads = 4 wavefronts in 2 x 2, output tile 128 x 128, 64 K
+// values per stage.  Row tiles never straddle two experts: a setup kernel lists
+// the (expert, first row) of every row tile from the device-side group
+// offsets, so no host synchronization is needed.  Persistent workgroups walk a
+// static tile sequence: for the row-grouped forms an XCD-contiguous chunk of
+// the row-major tile order (workgroups resident on one XCD share activation
+// rows and weight panels in that XCD's L2), for the weight-gradient form a
+// grid-strided order (every workgroup sees every expert, which balances
+// experts of very different token counts).
+#include <stdlib.h>
+
 #include "bsp_device.hpp"
 #include "bsp_internal.hpp"
 
@@ -41,8 +55,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GBN = 128;   // output columns per workgroup
-constexpr int GBK = 64;    // K values per LDS stage
+constexpr int GBK = 64;    // K values per stage
 constexpr int NXCD = 8;
 constexpr int kMaxDevices = 64;
 
@@ -55,10 +68,12 @@ struct GemmArgs {
     const float *b_outer;
     void *c;
     const int64_t *tiles;     // row-grouped form: packed (group << 40) | first row; WGRAD: padded starts [G+1]
-    int64_t *sched;           // NXCD work-queue counters, then (row-grouped form) the listed row-tile count
-    int64_t G, M, N, K, ldc, a_rows;
-    int64_t ntm;              // row tiles (row-grouped form: tile-list length; WGRAD: G * ceil(M / BM))
-    int64_t ntn;              // column tiles
+    int64_t *sched;           // [NXCD] spare counters, then (row-grouped form) the listed row-tile count
+    // Sizes fit 32 bits (checked at the C ABI), as do all tile and stage
+    // counts; byte offsets are formed in 64 bits where they can exceed that.
+    int32_t G, M, N, K, ldc, a_rows;
+    int32_t ntm;              // row tiles (row-grouped form: upper bound; WGRAD: G * ceil(M / BT))
+    int32_t ntn;              // column tiles
 };
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
@@ -108,474 +123,664 @@ __global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int6
     }
 }
 
-// 8 E2M1 nibbles (one 32-bit word, element 2j in the low nibble of byte j)
-// -> 8 fp16 values as 4 words: the fp16 of every E2M1 value has a zero low
-// byte, so the high byte comes from a byte-permute lookup of the magnitude
-// plus the sign bit.
-__device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, uint32_t (&h)[4]) {
-    const uint32_t lut_lo = 0x3E3C3800u;   // 0, 0.5, 1, 1.5 -> fp16 high bytes 00 38 3C 3E
-    const uint32_t lut_hi = 0x46444240u;   // 2, 3, 4, 6     -> 40 42 44 46
-    const uint32_t sel_e = w & 0x07070707u;
-    const uint32_t sel_o = (w >> 4) & 0x07070707u;
-    const uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_e) | ((w << 4) & 0x80808080u);
-    const uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, sel_o) | (w & 0x80808080u);
-    // word j = (element 2j, element 2j+1) = (he.byte j << 8) | (ho.byte j << 24)
-    h[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-    h[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-    h[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-    h[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
-}
-
-__device__ __forceinline__ uint32_t hmul2(uint32_t a, h2 s) {
-    h2 x = __builtin_bit_cast(h2, a);
-    x = x * s;
-    return __builtin_bit_cast(uint32_t, x);
-}
-
 // ---------------------------------------------------------------------------
-// Stage loaders: global -> registers (prefetch) and registers -> LDS.
+// Stage geometry, LDS-DMA and synchronization helpers.
 // ---------------------------------------------------------------------------
-
-// MXFP8 stage = 64 K bytes per row = two 32-value blocks.  For a 128-row
-// operand loader thread t takes row t/2, block t%2; for 256 rows, row t and
-// both blocks.
-template <int ROWS>
-struct MxStage {
-    static constexpr int NB = ROWS * 2 / 256;   // 32-byte blocks per thread (1 or 2)
-    uint4 v[NB][2];
-    uint32_t s[NB];
+// Square output tiles of BT x BT (BT = 128 or 256) on BT / 32 wavefronts in
+// 2 x (BT / 64): each wavefront owns (BT / 2) x 64 outputs, i.e. TI x 2
+// MFMA blocks of 32 x 32.
+template <int FMT, int BT>
+struct Geo {
+    static constexpr bool MX = FMT == BSP_FMT_MXFP8;
+    static constexpr int NW = BT / 32;                 // wavefronts
+    static constexpr int TI = BT / 64;                 // 32-row MFMA blocks per wavefront
+    static constexpr int ROWB = MX ? 64 : 32;          // code bytes per row per stage
+    static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
+    static constexpr int CODE = BT * ROWB;             // one operand's codes per stage
+    static constexpr int CIW = CODE / 1024 / NW;       // 1 KB DMA loads per wavefront per operand
+    static constexpr int A_SCL = 2 * CODE;             // per row: 2 dwords holding the stage's scale bytes
+    static constexpr int B_SCL = 2 * CODE + 8 * BT;
+    static constexpr int OPS = 2 * CIW + 2;            // DMA loads per wavefront per stage
+    static constexpr int SBLK = MX ? 32 : 16;          // values per scale
+    static constexpr int SPS = GBK / SBLK;             // scales per row per stage
+    // a ring stage also serves as the epilogue's transpose patch (32 x 144 bytes per wavefront)
+    static constexpr int SLOT = (2 * CODE + 16 * BT) > NW * 4608 ? (2 * CODE + 16 * BT) : NW * 4608;
+    static_assert(CIW >= 1 && 2 * BT == 64 * NW, "one scale DMA per wavefront and operand");
 };
 
-template <int ROWS>
-__device__ __forceinline__ void mx_load(MxStage<ROWS> &st, const uint8_t *codes, const uint8_t *scales,
-                                        int64_t ld, const int64_t *rowp, int64_t k0, int64_t kend) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int b = 0; b < MxStage<ROWS>::NB; b++) {
-        const int blk = (MxStage<ROWS>::NB == 1) ? (t & 1) : b;
-        const int64_t kk = k0 + 32 * blk;
-        const int64_t r = rowp[0];
-        if (r >= 0 && kk < kend) {
-            const uint4 *q = reinterpret_cast<const uint4 *>(codes + r * ld + kk);
-            st.v[b][0] = q[0];
-            st.v[b][1] = q[1];
-            st.s[b] = scales[r * (ld / 32) + kk / 32];
-        } else {
-            st.v[b][0] = make_uint4(0u, 0u, 0u, 0u);
-            st.v[b][1] = st.v[b][0];
-            st.s[b] = 127u;
-        }
-    }
+// Chunk position of chunk c of row r is c ^ swz(r): a fragment load reads one
+// chunk from each of 32 consecutive rows, and with this swizzle every group
+// of 8 (or 16) rows served together lands on distinct LDS banks.
+template <int FMT>
+__device__ __forceinline__ int swz(int r) {
+    return FMT == BSP_FMT_MXFP8 ? (((r >> 1) ^ (r >> 3)) & 3) : (((r >> 2) ^ (r >> 3)) & 1);
 }
 
-// LDS row layout (MXFP8): 64 code bytes + 16 pad; scales [rows][2].
-constexpr int MX_LDS_STRIDE = 80;
-
-template <int ROWS>
-__device__ __forceinline__ void mx_store(const MxStage<ROWS> &st, uint8_t *sc, uint8_t *ss) {
-    const int t = threadIdx.x;
-    const int row = (MxStage<ROWS>::NB == 1) ? (t >> 1) : t;
-#pragma unroll
-    for (int b = 0; b < MxStage<ROWS>::NB; b++) {
-        const int blk = (MxStage<ROWS>::NB == 1) ? (t & 1) : b;
-        uint4 *d = reinterpret_cast<uint4 *>(sc + row * MX_LDS_STRIDE + 32 * blk);
-        d[0] = st.v[b][0];
-        d[1] = st.v[b][1];
-        ss[row * 2 + blk] = (uint8_t)st.s[b];
-    }
+// LDS-DMA: every lane fetches `size` bytes from its own global address; the
+// wavefront's data lands contiguously at M0 + lane * size.  Issued as inline assembly: the
+// compiler would otherwise track these writes to LDS itself and, unable to
+// follow the ring across loop iterations, wait for all of them before every
+// LDS read.  Completion is covered by the explicit waits of the pipeline.
+// Nothing else in the kernel uses M0; the s_nop covers the M0-write to
+// LDS-DMA hazard.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+// base: wave-uniform 64-bit global address (SGPRs); voff: this lane's 32-bit
+// byte offset from it; m0: the wave's LDS destination.
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t *base, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+                 : "memory");
 }
 
-// NVFP4 stage = 64 K values per row = 32 code bytes (four 16-blocks).  For a
-// 128-row operand thread t takes row t/2, blocks 2(t%2) and 2(t%2)+1; for 256
-// rows, row t and all four blocks.
-template <int ROWS>
-struct NvStage {
-    static constexpr int NP = ROWS * 2 / 256;   // pairs of 16-blocks per thread (1 or 2)
-    uint32_t w[NP][4];
-    uint32_t s[NP][2];
+// s_waitcnt vmcnt(VM) lgkmcnt(LGKM) (expcnt untouched), gfx9 encoding.
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+// Workgroup barrier with no implied memory wait (a fence would wait for every
+// outstanding LDS-DMA load); callers wait explicitly first.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until the oldest outstanding stage has landed: `ahead` younger stages
+// (0..2) may stay in flight.
+template <int OPS>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    if (ahead >= 2) waitcnt<2 * OPS, 0>();
+    else if (ahead == 1) waitcnt<OPS, 0>();
+    else waitcnt<0, 0>();
+}
+
+// Output stores.  Issued as inline assembly so that the compiler's vmcnt
+// bookkeeping, which would treat pending stores and loads as completing out
+// of order and then wait for everything, only ever sees loads.  Store data
+// registers are read at issue, so no wait is needed before reusing them.
+__device__ __forceinline__ void st_nt16(void *p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off nt" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_b32(void *p, uint32_t v) {
+    asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_b16(void *p, uint32_t v) {
+    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+// Byte i (0..7) of a 64-bit word.
+__device__ __forceinline__ uint32_t byte_of(uint64_t w, int i) { return (uint32_t)(w >> (8 * i)) & 0xFFu; }
+
+// 8 E2M1 values (one dword, element 2j in the low nibble of byte j) times
+// the fp16 scale s, exactly: V_CVT_SCALEF32_PK_F16_FP4 at scale 1 decodes two
+// values, the packed fp16 multiply applies s (every product is representable).
+__device__ __forceinline__ v8h nv_frag(uint32_t w, h2 s) {
+    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+    return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// One output tile: expert, rows [row0, row_end), columns from col0, K range.
+struct Tile {
+    int g, row0, row_end, col0, kbeg, kend;
+    int nk;   // stages
 };
 
-template <int ROWS>
-__device__ __forceinline__ void nv_load(NvStage<ROWS> &st, const uint8_t *codes, const uint8_t *scales, int64_t K,
-                                        int64_t r, int64_t k0) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int b = 0; b < NvStage<ROWS>::NP; b++) {
-        const int pair = (NvStage<ROWS>::NP == 1) ? (t & 1) : b;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int64_t kk = k0 + 32 * pair + 16 * h;
-            if (r >= 0 && kk < K) {
-                const uint2 c = *reinterpret_cast<const uint2 *>(codes + r * (K / 2) + kk / 2);
-                st.w[b][2 * h] = c.x;
-                st.w[b][2 * h + 1] = c.y;
-                st.s[b][h] = scales[r * (K / 16) + kk / 16];
-            } else {
-                st.w[b][2 * h] = 0u;
-                st.w[b][2 * h + 1] = 0u;
-                st.s[b][h] = 0u;
-            }
-        }
-    }
-}
-
-// LDS row layout (NVFP4): 64 fp16 + 8 pad.
-constexpr int NV_LDS_STRIDE = 72;   // in halves
-
-template <int ROWS>
-__device__ __forceinline__ void nv_store(const NvStage<ROWS> &st, _Float16 *sh) {
-    const int t = threadIdx.x;
-    const int row = (NvStage<ROWS>::NP == 1) ? (t >> 1) : t;
-#pragma unroll
-    for (int b = 0; b < NvStage<ROWS>::NP; b++) {
-        const int pair = (NvStage<ROWS>::NP == 1) ? (t & 1) : b;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const float sf = e4m3_decode(st.s[b][h]);
-            const h2 sv = {(_Float16)sf, (_Float16)sf};
-            uint32_t o[8];
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                uint32_t hh[4];
-                e2m1x8_to_f16(st.w[b][2 * h + q], hh);
-#pragma unroll
-                for (int j = 0; j < 4; j++) o[4 * q + j] = hmul2(hh[j], sv);
-            }
-            uint4 *d = reinterpret_cast<uint4 *>(sh + row * NV_LDS_STRIDE + 32 * pair + 16 * h);
-            d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// kernel
-// ---------------------------------------------------------------------------
-
-// One output tile: its expert, rows, K range and the operand rows this
-// thread stages (fixed for the whole K loop).
-struct TileCtx {
-    int64_t g, row0, row_end, kbeg, kend, col0, arow, brow, nk;
-    const uint8_t *bc, *bs;
-};
-
-template <int FMT, int MODE, int BM>
-__device__ __forceinline__ void tile_setup(const GemmArgs &p, int64_t lin, TileCtx &c) {
-    const int t = threadIdx.x;
-    const int64_t ty = lin / p.ntn, tx = lin - ty * p.ntn;
+template <int MODE, int BT>
+__device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
+    Tile T;
+    const int ty = lin / p.ntn, tx = lin - ty * p.ntn;
     if (MODE == BSP_GEMM_WGRAD) {
-        const int64_t mt_per_g = (p.M + BM - 1) / BM;
-        c.g = ty / mt_per_g;
-        c.row0 = (ty - c.g * mt_per_g) * BM;
-        c.row_end = p.M;
-        c.kbeg = p.tiles[c.g];
-        c.kend = c.kbeg + (p.group_offsets[c.g + 1] - p.group_offsets[c.g] + 31) / 32 * 32;
-        c.kend = c.kend < p.K ? c.kend : p.K;  // offsets are trusted only up to the copies' width
-        c.bc = p.b_codes;
-        c.bs = p.b_scales;
+        const int mt_per_g = (p.M + BT - 1) / BT;
+        T.g = ty / mt_per_g;
+        T.row0 = (ty - T.g * mt_per_g) * BT;
+        T.row_end = p.M;
+        const int64_t kb = p.tiles[T.g];
+        const int64_t ke = kb + (p.group_offsets[T.g + 1] - p.group_offsets[T.g] + 31) / 32 * 32;
+        // offsets are trusted only up to the copies' width
+        T.kbeg = (int)(kb < p.K ? kb : p.K);
+        T.kend = (int)(ke < p.K ? ke : p.K);
     } else {
-        const int64_t tile = p.tiles[ty];       // valid: ty < the tile count the setup kernel wrote
-        c.g = tile >> 40;
-        c.row0 = tile & ((1ll << 40) - 1);
-        c.row_end = p.group_offsets[c.g + 1];
-        c.row_end = c.row_end < p.M ? c.row_end : p.M;  // never past the rows of C
-        c.kbeg = 0;
-        c.kend = p.K;
-        const int64_t bcs = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 2 : p.N * p.K;
-        const int64_t bss = (FMT == BSP_FMT_NVFP4) ? p.N * p.K / 16 : p.N * p.K / 32;
-        c.bc = p.b_codes + c.g * bcs;
-        c.bs = p.b_scales + c.g * bss;
+        const int64_t tile = p.tiles[ty];   // valid: ty < the listed tile count
+        T.g = (int)(tile >> 40);
+        T.row0 = (int)(tile & ((1ll << 40) - 1));
+        const int64_t re = p.group_offsets[T.g + 1];
+        T.row_end = (int)(re < p.M ? re : p.M);   // never past the rows of C
+        T.kbeg = 0;
+        T.kend = p.K;
     }
-    c.col0 = tx * GBN;
-    c.nk = c.kend > c.kbeg ? (c.kend - c.kbeg + GBK - 1) / GBK : 0;
-    const int lrow = (BM == 128) ? (t >> 1) : t;
-    const int64_t r = c.row0 + lrow;
-    c.arow = -1;
-    if (r < c.row_end) {
-        c.arow = r;
-        if (MODE != BSP_GEMM_WGRAD && p.a_gather) {
-            c.arow = (int64_t)p.a_gather[r];
-            if (c.arow < 0 || c.arow >= p.a_rows) c.arow = -1;  // an out-of-range gather index reads as a zero row
-        }
-    }
-    const int64_t cn = c.col0 + (t >> 1);
-    c.brow = cn < p.N ? cn : -1;
+    T.col0 = tx * BT;
+    T.nk = T.kend > T.kbeg ? (T.kend - T.kbeg + GBK - 1) / GBK : 0;
+    return T;
 }
 
-// Persistent workgroups.  Each XCD owns a work queue over a contiguous chunk
-// of the row-major tile sequence (so concurrent tiles on one L2 share the
-// activation tile and neighbouring weight panels) and, once it is empty,
-// steals from the other XCDs' queues, which balances experts of very
-// different sizes.  While a tile's epilogue runs, the first K stage of the
-// next tile is already being fetched.
-template <int FMT, int MODE, bool BF16OUT, int BM>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-    constexpr int WM = BM / 2;            // rows per wavefront
-    constexpr int TI = WM / 32;           // 32-row MFMA tiles per wavefront
-    constexpr int LDS_ROW = (FMT == BSP_FMT_MXFP8) ? MX_LDS_STRIDE : NV_LDS_STRIDE * 2;   // bytes
-    constexpr int STAGE_BYTES = (BM + GBN) * LDS_ROW + ((FMT == BSP_FMT_MXFP8) ? (BM + GBN) * 2 : 0);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
-    __shared__ int64_t s_lin;
+// ---------------------------------------------------------------------------
+// The kernel.
+// ---------------------------------------------------------------------------
+template <int N>
+struct IC {
+    static constexpr int v = N;
+};
 
-    const int t = threadIdx.x;
+template <int FMT, int MODE, bool BF16OUT, int BT>
+__global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
+    using GG = Geo<FMT, BT>;
+    constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
+    constexpr bool MX = GG::MX;
+    constexpr bool WG = MODE == BSP_GEMM_WGRAD;
+    constexpr int SEEK = 1, FIN = 2;
+    // Ring of four K stages.
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * SLOT_BYTES];
+    // Per tile (ordinal mod 8) and tile row: the A row read (-1: the row
+    // reads as zero) and, for NVFP4, the row's outer scale times the expert's.
+    // The producer runs at most 3 stages, hence at most 4 tiles, ahead.
+    __shared__ int32_t rowtok[8][BT];
+    __shared__ float rowmul[MX ? 1 : 8][BT];
 
-    const int64_t ntm = (MODE == BSP_GEMM_WGRAD) ? p.ntm : p.sched[NXCD];   // row tiles actually listed
-    const int64_t total = ntm * p.ntn;
-    const int64_t chunk = (total + NXCD - 1) / NXCD;
-    const int xcd = blockIdx.x % NXCD;
-    auto grab = [&]() -> int64_t {
-        if (t == 0) {
-            int64_t got = -1;
-            for (int d = 0; d < NXCD && got < 0; d++) {
-                const int q = (xcd + d) % NXCD;
-                const int64_t qbeg = q * chunk;
-                const int64_t qlen = (total - qbeg) < chunk ? (total - qbeg) : chunk;
-                if (qlen <= 0) continue;
-                const int64_t i = (int64_t)atomicAdd(reinterpret_cast<unsigned long long *>(p.sched + q), 1ull);
-                if (i < qlen) got = qbeg + i;
-            }
-            s_lin = got;
-        }
-        __syncthreads();
-        // Uniform across the workgroup: move it to scalar registers so the
-        // whole tile context is computed once per wavefront, not per lane.
-        const uint64_t u = (uint64_t)s_lin;
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-        __syncthreads();
-        return (int64_t)(((uint64_t)hi << 32) | lo);
-    };
+    const int t = threadIdx.x, l = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w / (GG::NW / 2), wn = w % (GG::NW / 2);   // 2 x (NW / 2) wavefronts
+    const int lr = l & 31, lh = l >> 5;
+    const uint32_t ring_lds = lds_addr(ring);
 
-    const int64_t ldk = p.K;
-    MxStage<BM> ma;
-    MxStage<GBN> mb;
-    NvStage<BM> na;
-    NvStage<GBN> nb;
-    auto load = [&](const TileCtx &c, int64_t stage) {
-        if (FMT == BSP_FMT_MXFP8) {
-            mx_load<BM>(ma, p.a_codes, p.a_scales, ldk, &c.arow, c.kbeg + stage * GBK, c.kend);
-            mx_load<GBN>(mb, c.bc, c.bs, ldk, &c.brow, c.kbeg + stage * GBK, c.kend);
-        } else {
-            nv_load<BM>(na, p.a_codes, p.a_scales, p.K, c.arow, stage * GBK);
-            nv_load<GBN>(nb, c.bc, c.bs, p.K, c.brow, stage * GBK);
-        }
-    };
-    uint8_t *const lA0 = smem, *const lB0 = smem + BM * LDS_ROW;
-    uint8_t *const lAs0 = smem + (BM + GBN) * LDS_ROW, *const lBs0 = lAs0 + BM * 2;   // MXFP8 scales
-    auto store = [&](int buf) {
-        if (FMT == BSP_FMT_MXFP8) {
-            mx_store<BM>(ma, lA0 + buf * STAGE_BYTES, lAs0 + buf * STAGE_BYTES);
-            mx_store<GBN>(mb, lB0 + buf * STAGE_BYTES, lBs0 + buf * STAGE_BYTES);
-        } else {
-            nv_store<BM>(na, reinterpret_cast<_Float16 *>(lA0 + buf * STAGE_BYTES));
-            nv_store<GBN>(nb, reinterpret_cast<_Float16 *>(lB0 + buf * STAGE_BYTES));
-        }
-    };
+    const uint32_t ldA = MX ? p.K : p.K / 2;           // code bytes per row (A and B)
+    const uint32_t SR = p.K / GG::SBLK;                // scale bytes per row (A and B)
 
-    v16f acc[TI][2];
-    TileCtx cur, nxt;
-    int64_t lin = grab();
-    bool have = lin >= 0;
-    if (have) {
-        tile_setup<FMT, MODE, BM>(p, lin, cur);
-        if (cur.nk > 0) load(cur, 0);
+    // ---- static tile sequence of this workgroup ----
+    int first, stride, last;
+    if (WG) {
+        first = blockIdx.x;
+        stride = gridDim.x;
+        last = p.ntm * p.ntn;
+    } else {
+        const int total = (int)p.sched[NXCD] * p.ntn;   // listed row tiles x column tiles
+        const int chunk = (total + NXCD - 1) / NXCD;
+        const int x = blockIdx.x % NXCD;
+        first = x * chunk + blockIdx.x / NXCD;
+        stride = gridDim.x / NXCD;
+        const int e = (x + 1) * chunk;
+        last = e < total ? e : total;
     }
-    while (have) {
-        // Per-lane LDS offsets are rederived for every tile from an opaque
-        // copy of the thread index; hoisted out of the tile loop they would
-        // stay live through the epilogue and cost occupancy.
-        int tq = threadIdx.x;
-        asm volatile("" : "+v"(tq));
-        const int lane = tq & 63, wave = tq >> 6;
-        const int wm = wave >> 1, wn = wave & 1;
-        const int lr = lane & 31, lh = lane >> 5;
+
+    // Fragment geometry (fixed per lane): LDS offsets inside a stage of the
+    // code chunks and scale dwords this lane feeds to the MFMA.
+    // Rows 32 apart share the swizzle, so one offset per operand serves all
+    // of the wavefront's blocks (plus 32 * ROWB bytes per block).
+    uint32_t fa0, fa1, fb0, fb1, fsa, fsb;
+    {
+        const int ra = wm * (BT / 2) + lr, rb = wn * 64 + lr;
+        if (MX) {
+            fa0 = ra * 64 + 16 * (lh ^ swz<FMT>(ra));
+            fa1 = ra * 64 + 16 * ((2 + lh) ^ swz<FMT>(ra));
+            fb0 = GG::CODE + rb * 64 + 16 * (lh ^ swz<FMT>(rb));
+            fb1 = GG::CODE + rb * 64 + 16 * ((2 + lh) ^ swz<FMT>(rb));
+        } else {
+            fa0 = fa1 = ra * 32 + 16 * (lh ^ swz<FMT>(ra));
+            fb0 = fb1 = GG::CODE + rb * 32 + 16 * (lh ^ swz<FMT>(rb));
+        }
+        fsa = GG::A_SCL + ra * 8;
+        fsb = GG::B_SCL + rb * 8;
+    }
+
+    // ---- producer state: next stage to fetch ----
+    int p_lin = first;
+    int p_ord = 0, p_kt = 0, p_nk = 0;
+    bool p_done = false;
+    Tile PT;
+    const uint8_t *pca = nullptr, *pcb = nullptr;     // code bases of the tile (uniform)
+    uint32_t poa[GG::CIW], pob[GG::CIW];              // this lane's code chunk offsets
+    uint32_t psa = 0, psb = 0;                         // this lane's scale offsets (+ 3 or 1 on odd lanes)
+
+    // A row of tile row r for the row-grouped form: its source row (or -1).
+    auto a_src = [&](const Tile &T, int r) __attribute__((always_inline)) -> int {
+        const int gr = T.row0 + r;
+        if (gr >= T.row_end) return -1;
+        if (!p.a_gather) return gr;
+        const int tok = p.a_gather[gr];
+        return (tok >= 0 && tok < p.a_rows) ? tok : -1;
+    };
+
+    // Move the producer to the next tile with K work and set up this lane's
+    // sources.  Tiles without K work (empty experts in the weight-gradient
+    // form) are only written by the consumer.
+    auto prod_seek = [&]() __attribute__((always_inline)) {
+        while (p_lin < last) {
+            PT = decode_tile<MODE, BT>(p, p_lin);
+            if (PT.nk > 0) break;
+            p_lin += stride;
+            p_ord++;
+        }
+        if (p_lin >= last) {
+            p_done = true;
+            return;
+        }
+        p_kt = 0;
+        p_nk = PT.nk;
+        const int ord = p_ord & 7;
+        pca = p.a_codes + (WG ? PT.kbeg : 0);
+        pcb = p.b_codes + (WG ? (size_t)PT.kbeg : (size_t)PT.g * p.N * ldA);
+        // codes: unit u = 64 (w CIW + j) + l covers row u / CH, chunk position u % CH
+#pragma unroll
+        for (int j = 0; j < GG::CIW; j++) {
+            const int u = 64 * (w * GG::CIW + j) + l;
+            const int r = u / GG::CH, cp = u % GG::CH;
+            const int c = cp ^ swz<FMT>(r);
+            int ar;
+            if (WG) {
+                ar = PT.row0 + r < p.M ? PT.row0 + r : PT.row0;
+            } else {
+                const int s = a_src(PT, r);
+                if (cp == 0) {
+                    rowtok[ord][r] = s;
+                    if (!MX) rowmul[MX ? 0 : ord][r] = s >= 0 ? p.a_outer[s] * p.b_outer[PT.g] : 0.0f;
+                }
+                ar = s >= 0 ? s : 0;   // rows outside the tile or with a bad index read row 0, result discarded
+            }
+            const int n = PT.col0 + r < p.N ? PT.col0 + r : p.N - 1;
+            poa[j] = (uint32_t)ar * ldA + 16 * c;
+            pob[j] = (uint32_t)n * ldA + 16 * c;
+        }
+        // scales: dword unit u = 64 w + l covers row u / 2; even lanes fetch
+        // the dword holding the stage's first scale byte, odd lanes the one
+        // holding its last (the same dword when they coincide)
+        {
+            const int r = 32 * w + (l >> 1);
+            int ar;
+            if (WG) {
+                ar = PT.row0 + r < p.M ? PT.row0 + r : PT.row0;
+            } else {
+                const int s = a_src(PT, r);
+                ar = s >= 0 ? s : 0;
+            }
+            const int n = PT.col0 + r < p.N ? PT.col0 + r : p.N - 1;
+            const uint32_t b0 = WG ? PT.kbeg / GG::SBLK : 0;
+            const uint32_t odd = (l & 1) ? GG::SPS - 1 : 0;
+            psa = (uint32_t)ar * SR + b0 + odd;
+            psb = (uint32_t)(WG ? n : PT.g * p.N + n) * SR + b0 + odd;
+        }
+    };
+
+    // Fetch the producer's next stage into ring stage `slot`.
+    auto issue = [&](int slot) __attribute__((always_inline)) {
+        // Opaque per call: hoisted out of the loop, the LDS addresses of every
+        // ring stage and DMA would each hold a scalar register.
+        uint32_t m0 = ring_lds + slot * SLOT_BYTES;
+        asm volatile("" : "+s"(m0));
+        const int k0 = PT.kbeg + p_kt * GBK;
+        const uint32_t kb = p_kt * GG::ROWB, so = p_kt * GG::SPS;
+        if (k0 + GBK / 2 < PT.kend) {
+#pragma unroll
+            for (int j = 0; j < GG::CIW; j++) dma16(pca + kb, poa[j], m0 + (w * GG::CIW + j) * 1024);
+#pragma unroll
+            for (int j = 0; j < GG::CIW; j++) dma16(pcb + kb, pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
+            dma4(p.a_scales, (psa + so) & ~3u, m0 + GG::A_SCL + 256 * w);
+            dma4(p.b_scales, (psb + so) & ~3u, m0 + GG::B_SCL + 256 * w);
+        } else {
+            // The stage's second half lies past the K end: its chunks re-read
+            // the first half (zeroed by the consumer) and odd lanes fetch the
+            // dword of the last valid scale byte.
+#pragma unroll
+            for (int j = 0; j < GG::CIW; j++) {
+                const int u = 64 * (w * GG::CIW + j) + l;
+                const int c = (u % GG::CH) ^ swz<FMT>(u / GG::CH);
+                const uint32_t back = c >= GG::CH / 2 ? 16 * (GG::CH / 2) : 0;
+                dma16(pca + kb, poa[j] - back, m0 + (w * GG::CIW + j) * 1024);
+                dma16(pcb + kb, pob[j] - back, m0 + GG::CODE + (w * GG::CIW + j) * 1024);
+            }
+            const uint32_t fix = (l & 1) ? GG::SPS / 2 : 0;   // SPS - 1 -> SPS / 2 - 1
+            dma4(p.a_scales, (psa + so - fix) & ~3u, m0 + GG::A_SCL + 256 * w);
+            dma4(p.b_scales, (psb + so - fix) & ~3u, m0 + GG::B_SCL + 256 * w);
+        }
+    };
+
+    // ---- consumer state ----
+    int c_lin = first;
+    int c_ord = 0, c_kt = 0;
+    bool c_done = first >= last;
+    Tile CT;
+    // 8 x (scale row offset mod 4) per fragment: the stage's first scale byte
+    // sits at byte (cs + SPS kt) mod 4 of the fetched dword pair, i.e. at cs
+    // for NVFP4 and at cs ^ 2 (kt & 1) for MXFP8.
+    uint32_t csa[TI], csb[2];
+    const uint32_t lh8 = 8 * (MX ? lh : 2 * lh);
+    v16f acc[TI][2];
+
+    auto cons_begin = [&]() __attribute__((always_inline)) {   // CT is set
+        const int ord = c_ord & 7;
+        const uint32_t b0 = WG ? CT.kbeg / GG::SBLK : 0;
+#pragma unroll
+        for (int i = 0; i < TI; i++) {
+            const int r = wm * (BT / 2) + 32 * i + lr;
+            int ar;
+            if (WG) {
+                ar = CT.row0 + r < p.M ? CT.row0 + r : CT.row0;
+            } else {
+                const int s = rowtok[ord][r];
+                ar = s >= 0 ? s : 0;
+            }
+            csa[i] = 8 * (((uint32_t)ar * SR + b0) & 3);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int r = wn * 64 + 32 * j + lr;
+            const int n = CT.col0 + r < p.N ? CT.col0 + r : p.N - 1;
+            csb[j] = 8 * (((uint32_t)(WG ? n : CT.g * p.N + n) * SR + b0) & 3);
+        }
 #pragma unroll
         for (int i = 0; i < TI; i++)
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+    };
 
-        // ---- K loop: double-buffered LDS, next stage prefetched in registers ----
-        const int64_t nk = cur.nk;
-        if (nk > 0) store(0);
-        if (nk > 1) load(cur, 1);
-        __syncthreads();
-        for (int64_t kt = 0; kt < nk; kt++) {
-            const int buf = (int)(kt & 1);
-            if (FMT == BSP_FMT_MXFP8) {
-                const uint8_t *A = lA0 + buf * STAGE_BYTES, *B = lB0 + buf * STAGE_BYTES;
-                const uint8_t *AS = lAs0 + buf * STAGE_BYTES, *BS = lBs0 + buf * STAGE_BYTES;
-                // Row bytes [0, 32) hold K block 0 and [32, 64) block 1.  The
-                // instruction wants lane half h to supply bytes [16h, 16h + 16) of
-                // block 0 then of block 1 (offsets 16h and 32 + 16h), with the
-                // E8M0 byte of block h.
-                v8i af[TI], bf[2];
-                int as[TI], bsc[2];
+    // Multiply the consumer's current stage, held in ring stage U.
+    auto compute = [&](auto U) __attribute__((always_inline)) {
+        // Opaque per call for the same reason (LDS offsets of stages 2 and 3
+        // do not fit the instruction's immediate field).
+        uint32_t soff = decltype(U)::v * SLOT_BYTES;
+        asm volatile("" : "+s"(soff));
+        const uint8_t *slot = ring + soff;
+        const int k0 = CT.kbeg + c_kt * GBK;
+        const bool h1 = k0 + GBK / 2 < CT.kend;
+        const int par = c_kt & 1;
+        if (MX) {
+            // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
+            // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
+            // low byte of the scale operand is read).
+            const uint32_t flip = par ? 16u : 0u;
+            uint4 b0[2], b1[2];
+            uint32_t bs[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 64 * j);
+                b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1 + 32 * 64 * j);
+                const uint64_t pb = *reinterpret_cast<const uint64_t *>(slot + fsb + 32 * 8 * j);
+                bs[j] = (uint32_t)(pb >> ((csb[j] ^ flip) + lh8));
+                if (!h1) {   // block 1 lies past the K end: zero codes, unit scale
+                    b1[j] = make_uint4(0u, 0u, 0u, 0u);
+                    bs[j] = lh ? 127u : bs[j];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TI; i++) {
+                const uint4 a0 = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * i);
+                uint4 a1 = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * i);
+                const uint64_t pa = *reinterpret_cast<const uint64_t *>(slot + fsa + 32 * 8 * i);
+                uint32_t as = (uint32_t)(pa >> ((csa[i] ^ flip) + lh8));
+                if (!h1) {
+                    a1 = make_uint4(0u, 0u, 0u, 0u);
+                    as = lh ? 127u : as;
+                }
+                const v8i fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const v8i fb = {(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w,
+                                    (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[i][j], 0, 0, 0, (int)as,
+                                                                                0, (int)bs[j]);
+                }
+            }
+        } else {
+            // K order inside a stage: lane half h, MFMA step q and element e
+            // take K = 32 h + 8 q + e, the same on both operands, so each lane
+            // reads one 16-byte chunk (32 values, scale blocks 2h and 2h + 1).
+            uint4 ua[TI], ub[2];
+            h2 sa[TI][2], sb[2][2];
+#pragma unroll
+            for (int i = 0; i < TI; i++) {
+                ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 32 * i);
+                const uint32_t xa =
+                    (uint32_t)(*reinterpret_cast<const uint64_t *>(slot + fsa + 32 * 8 * i) >> (csa[i] + lh8));
+                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xa, 0);
+                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xa, 1);
+                sa[i][0] = h2{s0, s0};
+                sa[i][1] = h2{s1, s1};
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 32 * j);
+                const uint32_t xb =
+                    (uint32_t)(*reinterpret_cast<const uint64_t *>(slot + fsb + 32 * 8 * j) >> (csb[j] + lh8));
+                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xb, 0);
+                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xb, 1);
+                sb[j][0] = h2{t0, t0};
+                sb[j][1] = h2{t1, t1};
+            }
+            if (!h1) {   // the upper 32 values lie past the K end
+                const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+                if (lh) {
+#pragma unroll
+                    for (int i = 0; i < TI; i++) {
+                        ua[i] = make_uint4(0u, 0u, 0u, 0u);
+                        sa[i][0] = sa[i][1] = one;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        ub[j] = make_uint4(0u, 0u, 0u, 0u);
+                        sb[j][0] = sb[j][1] = one;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                v8h fa[TI], fb[2];
 #pragma unroll
                 for (int i = 0; i < TI; i++) {
-                    const int r = wm * WM + 32 * i + lr;
-                    const uint4 u0 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 16 * lh);
-                    const uint4 u1 = *reinterpret_cast<const uint4 *>(A + r * MX_LDS_STRIDE + 32 + 16 * lh);
-                    af[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                    as[i] = AS[r * 2 + lh];
+                    const uint32_t wa = q == 0 ? ua[i].x : q == 1 ? ua[i].y : q == 2 ? ua[i].z : ua[i].w;
+                    fa[i] = nv_frag(wa, sa[i][q >> 1]);
                 }
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
-                    const int r = wn * 64 + 32 * j + lr;
-                    const uint4 u0 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 16 * lh);
-                    const uint4 u1 = *reinterpret_cast<const uint4 *>(B + r * MX_LDS_STRIDE + 32 + 16 * lh);
-                    bf[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                    bsc[j] = BS[r * 2 + lh];
+                    const uint32_t wb = q == 0 ? ub[j].x : q == 1 ? ub[j].y : q == 2 ? ub[j].z : ub[j].w;
+                    fb[j] = nv_frag(wb, sb[j][q >> 1]);
                 }
 #pragma unroll
                 for (int i = 0; i < TI; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
-                                                                                    0, as[i], 0, bsc[j]);
-            } else {
-                const _Float16 *A = reinterpret_cast<const _Float16 *>(lA0 + buf * STAGE_BYTES);
-                const _Float16 *B = reinterpret_cast<const _Float16 *>(lB0 + buf * STAGE_BYTES);
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    v8h af[TI], bf[2];
-#pragma unroll
-                    for (int i = 0; i < TI; i++)
-                        af[i] = *reinterpret_cast<const v8h *>(A + (wm * WM + 32 * i + lr) * NV_LDS_STRIDE + 16 * q +
-                                                               8 * lh);
-#pragma unroll
-                    for (int j = 0; j < 2; j++)
-                        bf[j] = *reinterpret_cast<const v8h *>(B + (wn * 64 + 32 * j + lr) * NV_LDS_STRIDE + 16 * q +
-                                                               8 * lh);
-#pragma unroll
-                    for (int i = 0; i < TI; i++)
-#pragma unroll
-                        for (int j = 0; j < 2; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-                }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
-            if (kt + 1 < nk) store(buf ^ 1);
-            if (kt + 2 < nk) load(cur, kt + 2);
-            __syncthreads();
         }
+    };
 
-        // ---- next tile: its first stage is fetched while this epilogue runs ----
-        lin = grab();
-        const bool have_next = lin >= 0;
-        if (have_next) {
-            tile_setup<FMT, MODE, BM>(p, lin, nxt);
-            if (nxt.nk > 0) load(nxt, 0);
-        }
-        // ---- epilogue ----
-        // The MFMA leaves lane l with column l % 32 of a 32 x 32 block and rows
-        // 8 (e / 4) + 4 (l / 32) + e % 4.  Each wavefront stages one 32 x 64
-        // slice of its outputs in LDS (the stage buffers are free: the K loop
-        // ended with a barrier), then writes whole rows with 16-byte
-        // non-temporal stores, so the output streams past L2 instead of
-        // evicting reusable operand panels.
+    // Write the consumer's tile.  The MFMA leaves lane l with column l % 32
+    // of each 32 x 32 block and rows 8 (e / 4) + 4 (l / 32) + e % 4; each
+    // wavefront transposes a block through its own LDS patch in a ring stage
+    // no load targets, then writes whole 16-byte row pieces.
+    auto epilogue = [&](uint8_t *slot) __attribute__((always_inline)) {
         constexpr int ESZ = BF16OUT ? 2 : 4;
         constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
-        constexpr int CHUNKS = 64 / VEC;               // 16-byte chunks per 64-column row
-        const float gb = (FMT == BSP_FMT_NVFP4) ? p.b_outer[cur.g] : 1.0f;
-        const int64_t goff = (MODE == BSP_GEMM_WGRAD) ? cur.g * p.M * p.ldc : 0;
-        uint8_t *ep = smem + wave * (32 * 64 * ESZ);
+        constexpr int RB = 32 * ESZ;                   // bytes of a 32-column row piece
+        constexpr int STR = RB + 16;                   // padded LDS row stride
+        constexpr int CPR = RB / 16;                   // 16-byte chunks per row piece
+        uint8_t *ep = slot + w * (32 * STR);
+        const int ord = c_ord & 7;
         const bool vec_ok = (p.ldc % VEC) == 0;
+        const int64_t goff = WG ? (int64_t)CT.g * p.M * p.ldc : 0;
 #pragma unroll
         for (int i = 0; i < TI; i++) {
+            float mul[16];
 #pragma unroll
             for (int e = 0; e < 16; e++) {
-                const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-                float sc = 1.0f;
-                if (FMT == BSP_FMT_NVFP4) {
-                    const int64_t r = cur.row0 + wm * WM + 32 * i + rin;
-                    sc = 0.0f;
-                    if (r < cur.row_end) {
-                        const int64_t tt = p.a_gather ? (int64_t)p.a_gather[r] : r;
-                        sc = (tt >= 0 && tt < p.a_rows) ? p.a_outer[tt] * gb : 0.0f;
+                const int rt = wm * (BT / 2) + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+                if (WG) mul[e] = 1.0f;
+                else if (MX) mul[e] = rowtok[ord][rt] >= 0 ? 1.0f : 0.0f;
+                else mul[e] = rowmul[MX ? 0 : ord][rt];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
+                    const float v = mul[e] == 0.0f ? 0.0f : acc[i][j][e] * mul[e];
+                    if (BF16OUT) *reinterpret_cast<uint16_t *>(ep + rin * STR + lr * 2) = (uint16_t)f32_to_bf16(v);
+                    else *reinterpret_cast<float *>(ep + rin * STR + lr * 4) = v;
+                }
+                __builtin_amdgcn_wave_barrier();   // the patch is private to this wavefront
+#pragma unroll
+                for (int pass = 0; pass < 32 * CPR / 64; pass++) {
+                    const int idx = pass * 64 + l;
+                    const int rin = idx / CPR, ch = idx % CPR;
+                    const int r = CT.row0 + wm * (BT / 2) + 32 * i + rin;
+                    const int cn = CT.col0 + wn * 64 + 32 * j + ch * VEC;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ep + rin * STR + ch * 16);
+                    if (r < CT.row_end && cn < p.N) {
+                        char *dst = reinterpret_cast<char *>(p.c) + (goff + (int64_t)r * p.ldc + cn) * ESZ;
+                        if (vec_ok && cn + VEC <= p.N) {
+                            st_nt16(dst, u32x4{v.x, v.y, v.z, v.w});
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < VEC; q++) {
+                                const int d = BF16OUT ? q >> 1 : q;
+                                const uint32_t wq = d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+                                if (cn + q < p.N) {
+                                    if (BF16OUT) st_b16(dst + 2 * q, wq >> (16 * (q & 1)));
+                                    else st_b32(dst + 4 * q, wq);
+                                }
+                            }
+                        }
                     }
                 }
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const float v = acc[i][j][e] * sc;
-                    const int cin = 32 * j + lr;
-                    if (BF16OUT) reinterpret_cast<uint16_t *>(ep)[rin * 64 + cin] = (uint16_t)f32_to_bf16(v);
-                    else reinterpret_cast<float *>(ep)[rin * 64 + cin] = v;
-                }
+                __builtin_amdgcn_wave_barrier();
             }
-            __syncthreads();
-#pragma unroll
-            for (int pass = 0; pass < 32 * CHUNKS / 64; pass++) {
-                const int idx = pass * 64 + lane;
-                const int rin = idx / CHUNKS, ch = idx % CHUNKS;
-                const int64_t r = cur.row0 + wm * WM + 32 * i + rin;
-                const int64_t cn = cur.col0 + wn * 64 + ch * VEC;
-                if (r >= cur.row_end || cn >= p.N) continue;
-                const uint4 v = *reinterpret_cast<const uint4 *>(ep + (rin * 64 + ch * VEC) * ESZ);
-                char *dst = reinterpret_cast<char *>(p.c) + (goff + r * p.ldc + cn) * ESZ;
-                if (vec_ok && cn + VEC <= p.N) {
-                    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(dst));
-                } else {
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                    for (int q = 0; q < VEC && cn + q < p.N; q++) {
-                        if (BF16OUT) reinterpret_cast<uint16_t *>(dst)[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-                        else reinterpret_cast<uint32_t *>(dst)[q] = w[q];
-                    }
-                }
-            }
-            __syncthreads();
         }
-        cur = nxt;
-        have = have_next;
+    };
+
+    // Advance the consumer to its next tile.
+    auto cons_next = [&]() __attribute__((always_inline)) {
+        c_lin += stride;
+        c_ord++;
+        if (c_lin >= last) {
+            c_done = true;
+            return;
+        }
+        CT = decode_tile<MODE, BT>(p, c_lin);
+        c_kt = 0;
+        cons_begin();
+    };
+
+    // ---- prologue: first tiles, first three stages ----
+    int p_q = 0, c_q = 0;   // stages issued / consumed
+    prod_seek();
+    waitcnt<63, 0>();
+    barrier();   // row table of the first tile is visible
+    if (!c_done) {
+        CT = decode_tile<MODE, BT>(p, c_lin);
+        cons_begin();
+    }
+    for (int s = 0; s < 3 && !p_done; s++) {
+        issue(s);
+        p_q++;
+        if (++p_kt == p_nk) {
+            p_lin += stride;
+            p_ord++;
+            prod_seek();
+        }
+    }
+
+    // One pipeline step: the consumer's stage q sits in ring stage U = q % 4
+    // and the producer refills ring stage (U + 3) % 4, which held stage q - 1,
+    // so three stages stay in flight.
+    auto step = [&](auto U) __attribute__((always_inline)) -> int {
+        wait_stage<GG::OPS>(p_q - c_q - 1);
+        barrier();   // stage q landed for every wavefront; the ring stage of q - 1 is free
+        int fl = 0;
+        if (!p_done) {
+            issue((decltype(U)::v + 3) & 3);
+            p_q++;
+            if (++p_kt == p_nk) fl |= SEEK;
+        }
+        compute(U);
+        c_q++;
+        if (++c_kt == CT.nk) fl |= FIN;
+        return fl;
+    };
+
+    // ---- main loop ----
+    // Ring stages are compile-time constants inside the unrolled steps; the
+    // walk leaves the unrolled sequence when the producer needs its next tile
+    // or the consumer finished one, and re-enters at the stage it stopped.
+    // A finished tile is written through the LDS of the stage just consumed;
+    // tiles without K work (weight-gradient form only) use the ring stage that
+    // precedes the next stage to consume, which no load targets at that point.
+    while (!c_done) {
+        int fl = 0;
+        if (WG && CT.nk == 0) {
+            fl = FIN;
+        } else {
+            const int u0 = c_q & 3;
+            if (u0 == 0) fl = step(IC<0>{});
+            if (!fl && u0 <= 1) fl = step(IC<1>{});
+            if (!fl && u0 <= 2) fl = step(IC<2>{});
+            if (!fl) fl = step(IC<3>{});
+        }
+        if (fl & SEEK) {
+            p_lin += stride;
+            p_ord++;
+            prod_seek();
+        }
+        if (fl & FIN) {
+            waitcnt<63, 0>();
+            barrier();   // every wavefront is done reading the stage
+            epilogue(ring + ((c_q + 3) & 3) * SLOT_BYTES);
+            cons_next();
+        }
     }
 }
 
-// Rows per tile.  Measured on the DeepSeek-V3-shaped forward GEMM, 128-row
-// tiles (three wavefronts per SIMD) beat 256-row tiles (one wavefront per
-// SIMD, fewer weight re-reads) by 1.2x: the kernel is latency-bound, so
-// occupancy matters more than the extra panel fetches, which mostly hit L2.
-// The 256-row variant is kept behind a build switch for such measurements.
-#ifndef BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP
-#define BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP 0
-#endif
-static int pick_bm(int mode, int64_t M, int64_t G) {
-    if (mode == BSP_GEMM_WGRAD) return 128;
-    return (M / G) < BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP ? 256 : 128;
-}
-
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
 int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
 
 // Workgroups resident per XCD for one instantiation on the current device
 // (compute units per XCD times workgroups per compute unit), cached per device.
 template <typename Kern>
-static int64_t resident_per_xcd(Kern kern, int *cache) {
+static int64_t resident_per_xcd(Kern kern, int threads, int *cache) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
     if (cache[dev] == 0) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess || occ <= 0) occ = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess || occ <= 0) occ = 1;
         cache[dev] = (cus + NXCD - 1) / NXCD * occ;
     }
     return cache[dev];
 }
 
-template <int FMT, int MODE, bool BF, int BM>
+template <int FMT, int MODE, bool BF, int BT>
 static void launch_one(const GemmArgs &p, hipStream_t s) {
     static int cache[kMaxDevices] = {};
-    const int64_t per_xcd_max = resident_per_xcd(k_gemm<FMT, MODE, BF, BM>, cache);
-    const int64_t total = p.ntm * p.ntn;            // upper bound of the tile count
+    const int64_t per_xcd_max = resident_per_xcd(k_gemm<FMT, MODE, BF, BT>, 2 * BT, cache);
+    const int64_t total = (int64_t)p.ntm * p.ntn;   // upper bound of the tile count
     const int64_t per_xcd_need = (total + NXCD - 1) / NXCD;
     const int64_t per_xcd = per_xcd_need < per_xcd_max ? per_xcd_need : per_xcd_max;
-    dim3 grid((unsigned)(per_xcd * NXCD)), block(256);
-    k_gemm<FMT, MODE, BF, BM><<<grid, block, 0, s>>>(p);
+    dim3 grid((unsigned)(per_xcd * NXCD)), block(2 * BT);
+    k_gemm<FMT, MODE, BF, BT><<<grid, block, 0, s>>>(p);
 }
 
-template <int FMT, int MODE, int BM>
+template <int FMT, int MODE, int BT>
 static void launch_k(const GemmArgs &p, bool bf, hipStream_t s) {
-    if (bf) launch_one<FMT, MODE, true, BM>(p, s);
-    else launch_one<FMT, MODE, false, BM>(p, s);
+    if (bf) launch_one<FMT, MODE, true, BT>(p, s);
+    else launch_one<FMT, MODE, false, BT>(p, s);
+}
+
+// Tile edge: 256 (eight wavefronts, half the operand traffic per output of a
+// 128 tile) once there are enough tiles to occupy every compute unit twice
+// over, else 128.
+// BSP_GEMM_TILE=128 or 256 in the environment pins the choice (tests use it
+// to run both tile shapes on small problems).
+static int pick_tile(int64_t tiles256) {
+    const char *e = getenv("BSP_GEMM_TILE");
+    const int forced = e ? atoi(e) : 0;
+    if (forced == 128 || forced == 256) return forced;
+    return tiles256 >= 512 ? 256 : 128;
 }
 
 hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
@@ -585,32 +790,33 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     GemmArgs p;
     p.a_codes = a_codes; p.a_scales = a_scales; p.a_outer = a_outer; p.a_gather = a_gather;
     p.group_offsets = group_offsets; p.b_codes = b_codes; p.b_scales = b_scales; p.b_outer = b_outer;
-    p.c = c; p.G = G; p.M = M; p.N = N; p.K = K; p.ldc = ldc; p.a_rows = a_rows;
+    p.c = c; p.G = (int32_t)G; p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K; p.ldc = (int32_t)ldc;
+    p.a_rows = (int32_t)a_rows;
     int64_t *ws = reinterpret_cast<int64_t *>(workspace);
     p.tiles = ws;
-    // Work-queue counters follow the tile list (or the padded starts).
+    // The listed tile count follows the tile list (or the padded starts).
     p.sched = ws + (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G));
-    p.ntn = (N + GBN - 1) / GBN;
     const bool bf = c_dtype == BSP_DTYPE_BF16;
     if (mode == BSP_GEMM_WGRAD) {
+        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
+        p.ntn = (int32_t)((N + bt - 1) / bt);
+        p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
         k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
-        p.ntm = G * ((M + 127) / 128);
-        launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
+        if (bt == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>(p, bf, s);
+        else launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
         return hipGetLastError();
     }
-    const int bm = pick_bm(mode, M, G);
-    p.ntm = (M + bm - 1) / bm + G;   // upper bound of the row-tile count
-    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bm, p.ntm, ws, p.sched);
-#if BSP_GEMM_BM256_BELOW_ROWS_PER_GROUP > 0
-    if (bm == 256) {
+    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256));
+    p.ntn = (int32_t)((N + bt - 1) / bt);
+    p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
+    if (bt == 256) {
         if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
         else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);
-        return hipGetLastError();
+    } else {
+        if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
+        else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
     }
-#endif
-    (void)bm;
-    if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
-    else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
     return hipGetLastError();
 }
 

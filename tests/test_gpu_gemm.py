@@ -15,6 +15,17 @@ import oracle
 from block_scaled_precision_token_amd import ops, synth
 from tests.gpu_util import DEV, assert_gemm_close, host, to_dev
 
+
+@pytest.fixture(params=["auto", "128", "256"], autouse=True)
+def gemm_tile(request, monkeypatch):
+    """Run every GEMM case with the library's tile choice and with each tile
+    edge pinned (the C library reads BSP_GEMM_TILE on every call)."""
+    if request.param == "auto":
+        monkeypatch.delenv("BSP_GEMM_TILE", raising=False)
+    else:
+        monkeypatch.setenv("BSP_GEMM_TILE", request.param)
+    return request.param
+
 pytestmark = pytest.mark.gpu
 
 
@@ -28,7 +39,8 @@ CASES = [
     # (tokens, K, N, group sizes of the gathered rows)
     (40, 64, 96, [10, 0, 1, 29, 40]),
     (200, 160, 130, [129, 0, 128, 1, 142]),
-    (64, 80, 64, [64, 64]),
+    (64, 96, 64, [64, 64]),
+    (40, 32, 96, [3, 37]),
     (300, 2048, 256, [300, 37, 5, 258]),
 ]
 
