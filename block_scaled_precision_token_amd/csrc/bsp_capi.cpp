@@ -165,6 +165,16 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
     if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_NVFP4 && K % 32) return BSP_ERR_SHAPE;   // rows of codes 16-byte aligned
+    // The kernel keeps sizes, tile counts and per-lane byte offsets in 32 bits.
+    {
+        const int64_t lim31 = (1ll << 31) - 1, lim32 = 1ll << 32;
+        if (M > lim31 || N > lim31 || K > lim31 || ldc > lim31 || a_rows > lim31) return BSP_ERR_SHAPE;
+        const int64_t rowb = fmt == BSP_FMT_MXFP8 ? K : K / 2;     // code bytes per row
+        const int64_t sr = fmt == BSP_FMT_MXFP8 ? K / 32 : K / 16;  // scale bytes per row
+        if (a_rows * rowb >= lim32 || N * rowb >= lim32) return BSP_ERR_SHAPE;
+        if (mode != BSP_GEMM_WGRAD && G * N * sr >= lim32) return BSP_ERR_SHAPE;
+        if (((M + 127) / 128 + G) * ((N + 127) / 128) > lim31) return BSP_ERR_SHAPE;
+    }
     if (mode != BSP_GEMM_WGRAD && !a_gather && a_rows != M) return BSP_ERR_SHAPE;
     if (mode == BSP_GEMM_WGRAD && a_rows != M) return BSP_ERR_SHAPE;
     if (a_rows <= 0) return BSP_ERR_SHAPE;

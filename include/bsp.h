@@ -192,7 +192,9 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
  *     a_gather  device int32 [M] or NULL (then a_rows == M)
  *     group_offsets  device int64 [G+1]: rows of C per group, off[G] == M
  *     M, N, K   rows of C, columns of C, reduction length (K % 32 == 0 for
- *               both formats: operand rows are fetched in 16-byte pieces)
+ *               both formats: operand rows are fetched in 16-byte pieces);
+ *               sizes below 2^31, and each operand's codes (A, one expert
+ *               of B) and B's scales below 4 GiB, else BSP_ERR_SHAPE
  *     b_codes/b_scales  device B [G, N, K] quantized along K
  *     b_outer   device f32 [G] (NVFP4 per-expert scales; NULL for MXFP8)
  *     c         device [M, ldc] of c_dtype (BSP_DTYPE_F32 or BSP_DTYPE_BF16)

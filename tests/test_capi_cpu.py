@@ -106,6 +106,8 @@ def test_gemm_rejects_bad_arguments():
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 48, A, A, None, A, 0, 64, A, ws, None) == 2
     # both formats fetch operand rows in 16-byte pieces: K % 32 == 0
     assert g(0, 0, A, A, A, None, 64, A, 2, 64, 64, 48, A, A, A, A, 0, 64, A, ws, None) == 2
+    # 32-bit limits: A codes of 2^32 bytes or more
+    assert g(1, 0, A, A, None, A, 1 << 22, A, 2, 64, 64, 1024, A, A, None, A, 0, 64, A, ws, None) == 2
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 32, A, ws, None) == 2   # ldc < N
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, 8, None) == 5
     assert g(1, 0, A, A, None, None, 32, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 2   # a_rows != M
