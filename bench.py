@@ -126,7 +126,9 @@ class Dsv3MoeMxfp8:
         dxg = emp(R, H, dt=bf)
         dw2 = emp(G, H, I, dt=bf)
         dw13 = emp(G, N13, H, dt=bf)
-        ws = emp(max(ops.gemm_workspace_size(0, R, G), ops.gemm_workspace_size(2, H, G)))
+        # (mode, M, N, K) of the six GEMMs below; one workspace serves them in turn
+        shapes = [(0, R, N13, H), (0, R, H, I), (1, R, I, H), (1, R, H, N13), (2, H, I, ld), (2, N13, H, ld)]
+        ws = emp(max(ops.gemm_workspace_size(ops.FMT_MXFP8, m, a, b, c, G) for m, a, b, c in shapes))
         q, gm = ops.quantize_mxfp8, ops.moe_grouped_gemm_blockscaled
         F, D, W, M8 = ops.GEMM_FPROP, ops.GEMM_DGRAD, ops.GEMM_WGRAD, ops.FMT_MXFP8
         s8 = 1 + 1 / 32                                 # MXFP8 bytes per value (code + scale share)
@@ -240,7 +242,7 @@ class Qwen3MoeNvfp4:
         h13 = emp(R, N13, dt=bf)
         hq = (None, emp(R, I // 2), emp(R, I // 16), emp(R, dt=f32))
         y = emp(R, H, dt=bf)
-        ws = emp(ops.gemm_workspace_size(0, R, E))
+        ws = emp(max(ops.gemm_workspace_size(ops.FMT_NVFP4, 0, R, n, k, E) for n, k in ((N13, H), (H, I))))
         gm, F, NV = ops.moe_grouped_gemm_blockscaled, ops.GEMM_FPROP, ops.FMT_NVFP4
         s4 = 0.5 + 1 / 16
         self.ops = [

@@ -60,11 +60,10 @@ BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
     return 64 * sizeof(float);
 }
 
-BSP_EXPORT size_t bsp_gemm_workspace_size(int mode, int64_t M, int64_t G) {
-    if (M < 0 || G < 1) return 0;
-    // Tile list (or padded group starts), then the work-queue counters.
-    if (mode == BSP_GEMM_WGRAD) return (size_t)(G + 1 + bsp::kGemmSchedSlots) * sizeof(int64_t);
-    return (size_t)(bsp::gemm_tile_count(M, G) + bsp::kGemmSchedSlots) * sizeof(int64_t);
+BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
+    if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
+    if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return 0;
+    return (size_t)bsp::gemm_workspace_bytes(fmt, mode, M, N, K, G);
 }
 
 BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
@@ -178,7 +177,7 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
     if (mode != BSP_GEMM_WGRAD && !a_gather && a_rows != M) return BSP_ERR_SHAPE;
     if (mode == BSP_GEMM_WGRAD && a_rows != M) return BSP_ERR_SHAPE;
     if (a_rows <= 0) return BSP_ERR_SHAPE;
-    if (!workspace || ws_bytes < bsp_gemm_workspace_size(mode, M, G)) return BSP_ERR_WORKSPACE;
+    if (!workspace || ws_bytes < bsp_gemm_workspace_size(fmt, mode, M, N, K, G)) return BSP_ERR_WORKSPACE;
     if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) ||
         !aligned16(group_offsets) || !aligned16(c) || !aligned16(workspace) || !aligned16_or_null(a_outer) ||
         !aligned16_or_null(b_outer) || !aligned16_or_null(a_gather))

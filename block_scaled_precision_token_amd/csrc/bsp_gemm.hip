@@ -74,6 +74,10 @@ struct GemmArgs {
     int32_t G, M, N, K, ldc, a_rows;
     int32_t ntm;              // row tiles (row-grouped form: upper bound; WGRAD: G * ceil(M / BT))
     int32_t ntn;              // column tiles
+    // Scale planes in the workspace: plane[(z * nbp + block) * rp + row],
+    // one byte per (block, row), rows of the A plane in tile-list order.
+    const uint8_t *a_plane, *b_plane;
+    int32_t a_rp, b_rp, nbp;
 };
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
@@ -123,6 +127,78 @@ __global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int6
     }
 }
 
+// Scale planes.  The operands' scales arrive row-major ([rows][K / SBLK]);
+// a K step needs SBLK-th bytes from every row of a tile, which as loads are
+// one cache line per row.  Transposed to block-major planes, the bytes of a
+// K step for the tile's rows are contiguous: a few lines per operand.
+// plane[(z * nbp + b) * rp + r] = scale b of the source row of (z, r), or 0
+// where (z, r) has no source row or b is past the row's blocks.
+struct PlaneArgs {
+    const uint8_t *src;
+    int64_t src_rows;          // rows of src
+    int32_t sr;                // scale bytes per source row (= blocks per row)
+    uint8_t *plane;
+    int32_t nbp, rp;           // padded blocks, row pitch of the plane
+    int32_t rows_z;            // direct map: source row of (z, r) = z * rows_z + r for r < rows_z
+    // tile-list map (row-grouped A): plane row r = slot * bt + i
+    const int64_t *tiles, *sched, *off;
+    const int32_t *gather;
+    int32_t bt, M, a_rows;
+};
+
+template <bool TILE_MAP>
+__global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
+    __shared__ uint8_t tr[64][65];
+    const int t = threadIdx.x;
+    const int r0 = blockIdx.x * 64, b0 = blockIdx.y * 64, z = blockIdx.z;
+    {
+        const int rr = t >> 2, part = t & 3;
+        const int r = r0 + rr;
+        int64_t srow = -1;
+        if (TILE_MAP) {
+            const int slot = r / a.bt, i = r - slot * a.bt;
+            if (slot < *a.sched) {
+                const int64_t tile = a.tiles[slot];
+                const int64_t g = tile >> 40, gr = (tile & ((1ll << 40) - 1)) + i;
+                const int64_t re = a.off[g + 1] < a.M ? a.off[g + 1] : a.M;
+                if (gr < re) {
+                    const int64_t tok = a.gather ? (int64_t)a.gather[gr] : gr;
+                    if (tok >= 0 && tok < a.a_rows) srow = tok;
+                }
+            }
+        } else if (r < a.rows_z) {
+            srow = (int64_t)z * a.rows_z + r;
+        }
+        const int bb = b0 + 16 * part;
+        const uint8_t *src = a.src + srow * a.sr + bb;
+        if (srow >= 0 && bb + 16 <= a.sr && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 16; k++) tr[rr][16 * part + k] = (uint8_t)(w4[k >> 2] >> (8 * (k & 3)));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; k++) tr[rr][16 * part + k] = (srow >= 0 && bb + k < a.sr) ? src[k] : 0;
+        }
+    }
+    __syncthreads();
+    {
+        const int bl = t >> 2, part = t & 3;
+        const int b = b0 + bl;
+        if (b < a.nbp) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int i = 16 * part + 4 * q;
+                w4[q] = (uint32_t)tr[i][bl] | ((uint32_t)tr[i + 1][bl] << 8) | ((uint32_t)tr[i + 2][bl] << 16) |
+                        ((uint32_t)tr[i + 3][bl] << 24);
+            }
+            uint8_t *dst = a.plane + ((int64_t)z * a.nbp + b) * a.rp + r0 + 16 * part;
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Stage geometry, LDS-DMA and synchronization helpers.
 // ---------------------------------------------------------------------------
@@ -138,14 +214,16 @@ struct Geo {
     static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
     static constexpr int CODE = BT * ROWB;             // one operand's codes per stage
     static constexpr int CIW = CODE / 1024 / NW;       // 1 KB DMA loads per wavefront per operand
-    static constexpr int A_SCL = 2 * CODE;             // per row: 2 dwords holding the stage's scale bytes
-    static constexpr int B_SCL = 2 * CODE + 8 * BT;
-    static constexpr int OPS = 2 * CIW + 2;            // DMA loads per wavefront per stage
     static constexpr int SBLK = MX ? 32 : 16;          // values per scale
     static constexpr int SPS = GBK / SBLK;             // scales per row per stage
+    static constexpr int SCLB = SPS * BT;              // scale bytes per operand per stage: [SPS][BT]
+    static constexpr int A_SCL = 2 * CODE;
+    static constexpr int B_SCL = 2 * CODE + SCLB;
+    static constexpr int SCI = 2 * SCLB / 256;         // 256-byte scale DMA loads per stage (both operands)
+    static constexpr int OPS = 2 * CIW;                // code DMA loads per wavefront per stage (+1 for w < SCI)
     // a ring stage also serves as the epilogue's transpose patch (32 x 144 bytes per wavefront)
-    static constexpr int SLOT = (2 * CODE + 16 * BT) > NW * 4608 ? (2 * CODE + 16 * BT) : NW * 4608;
-    static_assert(CIW >= 1 && 2 * BT == 64 * NW, "one scale DMA per wavefront and operand");
+    static constexpr int SLOT = (2 * CODE + 2 * SCLB) > NW * 4608 ? (2 * CODE + 2 * SCLB) : NW * 4608;
+    static_assert(CIW >= 1 && SCI <= NW && SCI % 2 == 0, "DMA split over the wavefronts");
 };
 
 // Chunk position of chunk c of row r is c ^ swz(r): a fragment load reads one
@@ -168,6 +246,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 // base: wave-uniform 64-bit global address (SGPRs); voff: this lane's 32-bit
 // byte offset from it; m0: the wave's LDS destination.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
                  : "memory");
@@ -194,6 +277,12 @@ __device__ __forceinline__ void wait_stage(int ahead) {
     if (ahead >= 2) waitcnt<2 * OPS, 0>();
     else if (ahead == 1) waitcnt<OPS, 0>();
     else waitcnt<0, 0>();
+}
+// Wavefronts below `sci` issue one scale load per stage on top of OPS.
+template <int OPS>
+__device__ __forceinline__ void wait_stage_w(int ahead, bool scl) {
+    if (scl) wait_stage<OPS + 1>(ahead);
+    else wait_stage<OPS>(ahead);
 }
 
 // Output stores.  Issued as inline assembly so that the compiler's vmcnt
@@ -227,7 +316,8 @@ __device__ __forceinline__ v8h nv_frag(uint32_t w, h2 s) {
 // One output tile: expert, rows [row0, row_end), columns from col0, K range.
 struct Tile {
     int g, row0, row_end, col0, kbeg, kend;
-    int nk;   // stages
+    int nk;     // stages
+    int slot;   // row-tile index (row-grouped form: position in the tile list)
 };
 
 template <int MODE, int BT>
@@ -254,6 +344,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
         T.kend = p.K;
     }
     T.col0 = tx * BT;
+    T.slot = ty;
     T.nk = T.kend > T.kbeg ? (T.kend - T.kbeg + GBK - 1) / GBK : 0;
     return T;
 }
@@ -288,7 +379,6 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     const uint32_t ring_lds = lds_addr(ring);
 
     const uint32_t ldA = MX ? p.K : p.K / 2;           // code bytes per row (A and B)
-    const uint32_t SR = p.K / GG::SBLK;                // scale bytes per row (A and B)
 
     // ---- static tile sequence of this workgroup ----
     int first, stride, last;
@@ -322,8 +412,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             fa0 = fa1 = ra * 32 + 16 * (lh ^ swz<FMT>(ra));
             fb0 = fb1 = GG::CODE + rb * 32 + 16 * (lh ^ swz<FMT>(rb));
         }
-        fsa = GG::A_SCL + ra * 8;
-        fsb = GG::B_SCL + rb * 8;
+        // MXFP8 lane half h reads block h's byte; NVFP4 blocks 2h and 2h + 1
+        fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
+        fsb = GG::B_SCL + (MX ? lh : 2 * lh) * BT + rb;
     }
 
     // ---- producer state: next stage to fetch ----
@@ -333,7 +424,14 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     Tile PT;
     const uint8_t *pca = nullptr, *pcb = nullptr;     // code bases of the tile (uniform)
     uint32_t poa[GG::CIW], pob[GG::CIW];              // this lane's code chunk offsets
-    uint32_t psa = 0, psb = 0;                         // this lane's scale offsets (+ 3 or 1 on odd lanes)
+    // Scale DMA (wavefronts w < SCI): operand and 256-byte piece of its
+    // [SPS][BT] stage region; this lane covers block sbl, rows sr0..sr0+3.
+    const bool scl_w = w < GG::SCI;
+    const bool scl_b = w >= GG::SCI / 2;
+    const int scl_o = 256 * (w % (GG::SCI / 2)) + 4 * l;
+    const int sbl = scl_o / BT, sr0 = scl_o % BT;
+    const uint32_t psv = (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;   // lane offset in the plane
+    const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
 
     // A row of tile row r for the row-grouped form: its source row (or -1).
     auto a_src = [&](const Tile &T, int r) __attribute__((always_inline)) -> int {
@@ -384,23 +482,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             poa[j] = (uint32_t)ar * ldA + 16 * c;
             pob[j] = (uint32_t)n * ldA + 16 * c;
         }
-        // scales: dword unit u = 64 w + l covers row u / 2; even lanes fetch
-        // the dword holding the stage's first scale byte, odd lanes the one
-        // holding its last (the same dword when they coincide)
         {
-            const int r = 32 * w + (l >> 1);
-            int ar;
-            if (WG) {
-                ar = PT.row0 + r < p.M ? PT.row0 + r : PT.row0;
-            } else {
-                const int s = a_src(PT, r);
-                ar = s >= 0 ? s : 0;
-            }
-            const int n = PT.col0 + r < p.N ? PT.col0 + r : p.N - 1;
-            const uint32_t b0 = WG ? PT.kbeg / GG::SBLK : 0;
-            const uint32_t odd = (l & 1) ? GG::SPS - 1 : 0;
-            psa = (uint32_t)ar * SR + b0 + odd;
-            psb = (uint32_t)(WG ? n : PT.g * p.N + n) * SR + b0 + odd;
+            const int b0 = WG ? PT.kbeg / GG::SBLK : 0;
+            if (scl_b) psbase = p.b_plane + ((size_t)(WG ? 0 : PT.g) * p.nbp + b0) * p.b_rp + PT.col0;
+            else psbase = p.a_plane + (size_t)b0 * p.a_rp + (WG ? PT.row0 : PT.slot * BT);
         }
     };
 
@@ -417,12 +502,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             for (int j = 0; j < GG::CIW; j++) dma16(pca + kb, poa[j], m0 + (w * GG::CIW + j) * 1024);
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) dma16(pcb + kb, pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
-            dma4(p.a_scales, (psa + so) & ~3u, m0 + GG::A_SCL + 256 * w);
-            dma4(p.b_scales, (psb + so) & ~3u, m0 + GG::B_SCL + 256 * w);
         } else {
             // The stage's second half lies past the K end: its chunks re-read
-            // the first half (zeroed by the consumer) and odd lanes fetch the
-            // dword of the last valid scale byte.
+            // the first half (zeroed by the consumer).
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) {
                 const int u = 64 * (w * GG::CIW + j) + l;
@@ -431,10 +513,11 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 dma16(pca + kb, poa[j] - back, m0 + (w * GG::CIW + j) * 1024);
                 dma16(pcb + kb, pob[j] - back, m0 + GG::CODE + (w * GG::CIW + j) * 1024);
             }
-            const uint32_t fix = (l & 1) ? GG::SPS / 2 : 0;   // SPS - 1 -> SPS / 2 - 1
-            dma4(p.a_scales, (psa + so - fix) & ~3u, m0 + GG::A_SCL + 256 * w);
-            dma4(p.b_scales, (psb + so - fix) & ~3u, m0 + GG::B_SCL + 256 * w);
         }
+        // scale bytes of the stage: SPS plane rows (padded past the K end)
+        if (scl_w)
+            dma4(uniform_ptr(psbase + (size_t)so * (scl_b ? p.b_rp : p.a_rp)), psv,
+                 m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 256 * (w % (GG::SCI / 2)));
     };
 
     // ---- consumer state ----
@@ -442,34 +525,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     int c_ord = 0, c_kt = 0;
     bool c_done = first >= last;
     Tile CT;
-    // 8 x (scale row offset mod 4) per fragment: the stage's first scale byte
-    // sits at byte (cs + SPS kt) mod 4 of the fetched dword pair, i.e. at cs
-    // for NVFP4 and at cs ^ 2 (kt & 1) for MXFP8.
-    uint32_t csa[TI], csb[2];
-    const uint32_t lh8 = 8 * (MX ? lh : 2 * lh);
     v16f acc[TI][2];
 
     auto cons_begin = [&]() __attribute__((always_inline)) {   // CT is set
-        const int ord = c_ord & 7;
-        const uint32_t b0 = WG ? CT.kbeg / GG::SBLK : 0;
-#pragma unroll
-        for (int i = 0; i < TI; i++) {
-            const int r = wm * (BT / 2) + 32 * i + lr;
-            int ar;
-            if (WG) {
-                ar = CT.row0 + r < p.M ? CT.row0 + r : CT.row0;
-            } else {
-                const int s = rowtok[ord][r];
-                ar = s >= 0 ? s : 0;
-            }
-            csa[i] = 8 * (((uint32_t)ar * SR + b0) & 3);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int r = wn * 64 + 32 * j + lr;
-            const int n = CT.col0 + r < p.N ? CT.col0 + r : p.N - 1;
-            csb[j] = 8 * (((uint32_t)(WG ? n : CT.g * p.N + n) * SR + b0) & 3);
-        }
 #pragma unroll
         for (int i = 0; i < TI; i++)
 #pragma unroll
@@ -487,20 +545,17 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const uint8_t *slot = ring + soff;
         const int k0 = CT.kbeg + c_kt * GBK;
         const bool h1 = k0 + GBK / 2 < CT.kend;
-        const int par = c_kt & 1;
         if (MX) {
             // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
             // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
             // low byte of the scale operand is read).
-            const uint32_t flip = par ? 16u : 0u;
             uint4 b0[2], b1[2];
             uint32_t bs[2];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 64 * j);
                 b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1 + 32 * 64 * j);
-                const uint64_t pb = *reinterpret_cast<const uint64_t *>(slot + fsb + 32 * 8 * j);
-                bs[j] = (uint32_t)(pb >> ((csb[j] ^ flip) + lh8));
+                bs[j] = slot[fsb + 32 * j];
                 if (!h1) {   // block 1 lies past the K end: zero codes, unit scale
                     b1[j] = make_uint4(0u, 0u, 0u, 0u);
                     bs[j] = lh ? 127u : bs[j];
@@ -510,8 +565,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             for (int i = 0; i < TI; i++) {
                 const uint4 a0 = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * i);
                 uint4 a1 = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * i);
-                const uint64_t pa = *reinterpret_cast<const uint64_t *>(slot + fsa + 32 * 8 * i);
-                uint32_t as = (uint32_t)(pa >> ((csa[i] ^ flip) + lh8));
+                uint32_t as = slot[fsa + 32 * i];
                 if (!h1) {
                     a1 = make_uint4(0u, 0u, 0u, 0u);
                     as = lh ? 127u : as;
@@ -534,20 +588,16 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < TI; i++) {
                 ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 32 * i);
-                const uint32_t xa =
-                    (uint32_t)(*reinterpret_cast<const uint64_t *>(slot + fsa + 32 * 8 * i) >> (csa[i] + lh8));
-                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xa, 0);
-                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xa, 1);
+                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + 32 * i], 0);
+                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + BT + 32 * i], 0);
                 sa[i][0] = h2{s0, s0};
                 sa[i][1] = h2{s1, s1};
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 32 * j);
-                const uint32_t xb =
-                    (uint32_t)(*reinterpret_cast<const uint64_t *>(slot + fsb + 32 * 8 * j) >> (csb[j] + lh8));
-                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xb, 0);
-                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)xb, 1);
+                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + 32 * j], 0);
+                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + BT + 32 * j], 0);
                 sb[j][0] = h2{t0, t0};
                 sb[j][1] = h2{t1, t1};
             }
@@ -687,7 +737,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     // and the producer refills ring stage (U + 3) % 4, which held stage q - 1,
     // so three stages stay in flight.
     auto step = [&](auto U) __attribute__((always_inline)) -> int {
-        wait_stage<GG::OPS>(p_q - c_q - 1);
+        wait_stage_w<GG::OPS>(p_q - c_q - 1, scl_w);
         barrier();   // stage q landed for every wavefront; the ring stage of q - 1 is free
         int fl = 0;
         if (!p_done) {
@@ -738,6 +788,31 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 // ---------------------------------------------------------------------------
 int64_t gemm_tile_count(int64_t M, int64_t G) { return (M + 127) / 128 + G; }
 
+// Workspace: tile list (or padded group starts) and counters, then the A
+// and B scale planes, each 256-byte aligned.
+struct WsLayout {
+    int64_t head, a_off, b_off, total;
+    int32_t nbp, a_rp, b_rp;
+};
+static int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+static WsLayout ws_layout(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
+    WsLayout L;
+    const int64_t sblk = fmt == BSP_FMT_MXFP8 ? 32 : 16, sps = 64 / sblk;
+    const int64_t nblk = K / sblk;
+    L.nbp = (int32_t)(up(nblk, sps) + sps);   // K-tail stages read one padded step past the end
+    const int64_t entries = (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G)) + kGemmSchedSlots;
+    L.head = up(entries * 8, 256);
+    L.a_rp = (int32_t)(mode == BSP_GEMM_WGRAD ? up(M, 256) : ((M + 255) / 256 + G) * 256);
+    L.b_rp = (int32_t)up(N, 256);
+    L.a_off = L.head;
+    L.b_off = L.a_off + up((int64_t)L.nbp * L.a_rp, 256);
+    L.total = L.b_off + up((mode == BSP_GEMM_WGRAD ? 1 : G) * (int64_t)L.nbp * L.b_rp, 256);
+    return L;
+}
+int64_t gemm_workspace_bytes(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
+    return ws_layout(fmt, mode, M, N, K, G).total;
+}
+
 // Workgroups resident per XCD for one instantiation on the current device
 // (compute units per XCD times workgroups per compute unit), cached per device.
 template <typename Kern>
@@ -787,21 +862,36 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
                        const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G,
                        int64_t M, int64_t N, int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
                        const float *b_outer, void *c, int c_dtype, int64_t ldc, void *workspace, hipStream_t s) {
+    const WsLayout L = ws_layout(fmt, mode, M, N, K, G);
     GemmArgs p;
     p.a_codes = a_codes; p.a_scales = a_scales; p.a_outer = a_outer; p.a_gather = a_gather;
     p.group_offsets = group_offsets; p.b_codes = b_codes; p.b_scales = b_scales; p.b_outer = b_outer;
     p.c = c; p.G = (int32_t)G; p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K; p.ldc = (int32_t)ldc;
     p.a_rows = (int32_t)a_rows;
+    uint8_t *wsb = reinterpret_cast<uint8_t *>(workspace);
     int64_t *ws = reinterpret_cast<int64_t *>(workspace);
     p.tiles = ws;
     // The listed tile count follows the tile list (or the padded starts).
     p.sched = ws + (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G));
+    p.a_plane = wsb + L.a_off;
+    p.b_plane = wsb + L.b_off;
+    p.a_rp = L.a_rp; p.b_rp = L.b_rp; p.nbp = L.nbp;
     const bool bf = c_dtype == BSP_DTYPE_BF16;
+    const int32_t sr = (int32_t)(K / (fmt == BSP_FMT_MXFP8 ? 32 : 16));
+    const unsigned gy = (unsigned)((L.nbp + 63) / 64);
+
+    PlaneArgs pb = {};
+    pb.src = b_scales; pb.sr = sr; pb.plane = wsb + L.b_off; pb.nbp = L.nbp; pb.rp = L.b_rp; pb.rows_z = (int32_t)N;
     if (mode == BSP_GEMM_WGRAD) {
         const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
         k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
+        PlaneArgs pa = {};
+        pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
+        pa.rows_z = (int32_t)M;
+        k_scale_plane<false><<<dim3((unsigned)(L.a_rp / 64), gy, 1), 256, 0, s>>>(pa);
+        k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, 1), 256, 0, s>>>(pb);
         if (bt == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>(p, bf, s);
         else launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
         return hipGetLastError();
@@ -810,6 +900,12 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     p.ntn = (int32_t)((N + bt - 1) / bt);
     p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
     k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
+    PlaneArgs pa = {};
+    pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
+    pa.tiles = ws; pa.sched = p.sched + NXCD; pa.off = group_offsets; pa.gather = a_gather;
+    pa.bt = bt; pa.M = (int32_t)M; pa.a_rows = (int32_t)a_rows;
+    k_scale_plane<true><<<dim3((unsigned)((int64_t)p.ntm * bt / 64), gy, 1), 256, 0, s>>>(pa);
+    k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, (unsigned)G), 256, 0, s>>>(pb);
     if (bt == 256) {
         if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
         else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);

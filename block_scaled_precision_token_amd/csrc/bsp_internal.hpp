@@ -24,7 +24,8 @@ hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const flo
 hipError_t launch_swiglu(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out, int fmt, bool m46,
                          uint8_t *codes, uint8_t *scales, float *outer, hipStream_t s);
 int64_t gemm_tile_count(int64_t M, int64_t G);
-constexpr int64_t kGemmSchedSlots = 16;   // per-XCD work-queue counters and the listed tile count
+constexpr int64_t kGemmSchedSlots = 16;   // spare counters and the listed tile count
+int64_t gemm_workspace_bytes(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
                        const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G,
                        int64_t M, int64_t N,

@@ -71,7 +71,7 @@ def _declare(lib):
     lib.bsp_mxfp8_grouped_cols.restype = I64
     lib.bsp_requant_workspace_size.argtypes = [I64]
     lib.bsp_requant_workspace_size.restype = SZ
-    lib.bsp_gemm_workspace_size.argtypes = [INT, I64, I64]
+    lib.bsp_gemm_workspace_size.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.bsp_gemm_workspace_size.restype = SZ
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes"):
@@ -231,8 +231,9 @@ def requant_transpose_sr(codes, scales, outer, seed: int = 0, sr: bool = True, w
     return codesT, scalesT, outerT[:1]
 
 
-def gemm_workspace_size(mode: int, M: int, G: int) -> int:
-    return int(_lib_raw().bsp_gemm_workspace_size(mode, M, G))
+def gemm_workspace_size(fmt: int, mode: int, M: int, N: int, K: int, G: int) -> int:
+    """Bytes of device workspace for one grouped GEMM call of these sizes."""
+    return int(_lib_raw().bsp_gemm_workspace_size(fmt, mode, M, N, K, G))
 
 
 def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets, N: int,
@@ -255,7 +256,8 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
     ldc = out.shape[-1] if out.dim() >= 2 else N
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
     if workspace is None:
-        workspace = torch.empty((max(gemm_workspace_size(mode, M, G), 16),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((max(gemm_workspace_size(fmt, mode, M, N, K, G), 16),), dtype=torch.uint8,
+                                device=dev)
     st = _lib_raw().bsp_moe_grouped_gemm_blockscaled(fmt, mode, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer),
                                                      _ptr(a_gather), a_rows, _ptr(group_offsets), G, M, N, K,
                                                      _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt,

@@ -206,9 +206,10 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
  *   a_gather, a_outer, b_outer must be NULL and a_rows == M.
  * Accumulation is f32 on the MFMA units; the epilogue applies gA * gB and
  * rounds to c_dtype (RNE for bf16).
- *   workspace  device, >= bsp_gemm_workspace_size(mode, M, G) bytes; holds
- *              the tile list and the work-queue counters, rewritten by every
- *              call, so calls sharing one workspace must be stream-ordered
+ *   workspace  device, >= bsp_gemm_workspace_size(fmt, mode, M, N, K, G)
+ *              bytes, 16-byte aligned; holds the tile list and block-major
+ *              copies of both operands' scales, rewritten by every call, so
+ *              calls sharing one workspace must be stream-ordered
  */
 bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales,
                                             const float *a_outer, const int32_t *a_gather, int64_t a_rows,
@@ -243,7 +244,7 @@ bsp_status bsp_mxfp8_sizes(int64_t M, int64_t K, size_t *codes_bytes, size_t *sc
  * sum over groups of roundup32(n_g) <= roundup32(M + 31 * G). */
 int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
 size_t bsp_requant_workspace_size(int64_t M);
-size_t bsp_gemm_workspace_size(int mode, int64_t M, int64_t G);
+size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 
 #ifdef __cplusplus
 }

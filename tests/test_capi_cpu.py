@@ -49,8 +49,19 @@ def test_size_helpers():
     assert L.bsp_mxfp8_sizes(4096, 7168, ctypes.byref(c), ctypes.byref(s)) == 0
     assert (c.value, s.value) == (4096 * 7168, 4096 * 224)
     assert L.bsp_mxfp8_grouped_cols(100, 4) == 224          # roundup32(100 + 31*4)
-    assert L.bsp_gemm_workspace_size(0, 65536, 128) == (512 + 128 + 16) * 8
-    assert L.bsp_gemm_workspace_size(2, 36864, 257) == (258 + 16) * 8
+    # tile list + counters (256-byte aligned), then block-major scale planes:
+    # blocks padded to whole K steps plus one, rows padded to 256
+    def up(x, a):
+        return (x + a - 1) // a * a
+    head = up((512 + 128 + 16) * 8, 256)
+    nbp = 2048 // 16 + 4
+    a_plane = nbp * ((65536 + 255) // 256 + 128) * 256
+    b_plane = 128 * nbp * up(1536, 256)
+    assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) == head + up(a_plane, 256) + up(b_plane, 256)
+    head = up((258 + 16) * 8, 256)
+    nbp = 37120 // 32 + 2
+    assert L.bsp_gemm_workspace_size(1, 2, 4096, 7168, 37120, 257) == head + nbp * 4096 + nbp * 7168
+    assert L.bsp_gemm_workspace_size(7, 0, 64, 64, 64, 1) == 0
     assert L.bsp_requant_workspace_size(16384) >= 4
 
 
