@@ -14,6 +14,8 @@
 
 namespace bsp {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // --------------------------------------------------------------------------
 // NVFP4
 // --------------------------------------------------------------------------
@@ -281,8 +283,9 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
                                                     uint8_t *__restrict__ scales_colT, int64_t ld_colT,
                                                     const int64_t *__restrict__ group_offsets, int G,
                                                     const int32_t *__restrict__ gather, int64_t x_rows) {
-    __shared__ uint16_t tile[MX_TR][MX_TC + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[MX_TR][MX_TC + 8];
     __shared__ int64_t sP[GROUPED ? MX_MAXG + 1 : 1];
+    __shared__ int64_t rsrc[ROW ? MX_TR : 1];   // destination row of each tile row in codes_row (-1: none)
     __shared__ int64_t blk_src0[MX_TR / 32], blk_end[MX_TR / 32];
     __shared__ int64_t wsum[4];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -350,6 +353,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     } else {
         if (p < M) src = p;
     }
+    if (ROW && half == 0) rsrc[tr] = src;
     // physical row of x: the gathered row (out-of-range indices read as zeros)
     int64_t xrow = src;
     if (src >= 0 && gather) {
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             for (int i = 4; i < 8; i++) raw[i] = xp[i];
         }
     }
+    uint32_t qrow[16];
     if (ROW) {
         uint32_t sc2 = 0;
 #pragma unroll
@@ -387,12 +392,9 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             }
             uint32_t q[8];
             const uint32_t sc = mxfp8_block(xf, q);
+#pragma unroll
+            for (int i = 0; i < 8; i++) qrow[8 * b + i] = q[i];
             sc2 |= sc << (8 * b);
-            if (src >= 0 && (b == 0 ? blk0_ok : blk1_ok)) {
-                uint4 *dst = reinterpret_cast<uint4 *>(codes_row + src * K + kc + 32 * b);
-                dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-                dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-            }
         }
         // the row's four scale bytes: this thread's two and its neighbour's two
         const uint32_t other = __shfl_xor(sc2, 1, 64);
@@ -406,7 +408,6 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             }
         }
     }
-    if (!COL) return;
 #pragma unroll
     for (int i = 0; i < 8; i++) *reinterpret_cast<uint4 *>(&tile[tr][64 * half + 8 * i]) = raw[i];
     __syncthreads();
@@ -415,29 +416,66 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     const int c = t & 127, rh = t >> 7;
     const int64_t kcol = k0 + c;
     const int64_t plimit = GROUPED ? ptotal : M;
-    if (kcol >= K) return;
-    uint32_t scs = 0;
-    int nvalid = 0;
+    uint32_t qcol[16];
+    {
+        uint32_t scs = 0;
+        int nvalid = 0;
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-        const int64_t pb = p0 + 64 * rh + 32 * b;
-        if (pb >= plimit) break;
-        float cf[32];
+        for (int b = 0; b < 2; b++) {
+            const int64_t pb = p0 + 64 * rh + 32 * b;
+            float cf[32];
 #pragma unroll
-        for (int i = 0; i < 32; i++) cf[i] = __uint_as_float((uint32_t)tile[64 * rh + 32 * b + i][c] << 16);
-        uint32_t q[8];
-        const uint32_t sc = mxfp8_block(cf, q);
-        uint4 *dst = reinterpret_cast<uint4 *>(codes_colT + kcol * ld_colT + pb);
-        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-        scs |= sc << (8 * b);
-        nvalid = b + 1;
+            for (int i = 0; i < 32; i++) cf[i] = __uint_as_float((uint32_t)tile[64 * rh + 32 * b + i][c] << 16);
+            uint32_t q[8];
+            const uint32_t sc = mxfp8_block(cf, q);
+#pragma unroll
+            for (int i = 0; i < 8; i++) qcol[8 * b + i] = q[i];
+            if (pb < plimit) {
+                scs |= sc << (8 * b);
+                nvalid = b + 1;
+            }
+        }
+        if (kcol < K && nvalid > 0) {
+            uint8_t *sp = scales_colT + kcol * (ld_colT / 32) + (p0 + 64 * rh) / 32;
+            if (nvalid == 2 && (reinterpret_cast<uintptr_t>(sp) & 1) == 0) {
+                *reinterpret_cast<uint16_t *>(sp) = (uint16_t)scs;
+            } else {
+                for (int b = 0; b < nvalid; b++) sp[b] = (uint8_t)(scs >> (8 * b));
+            }
+        }
     }
-    uint8_t *sp = scales_colT + kcol * (ld_colT / 32) + (p0 + 64 * rh) / 32;
-    if (nvalid == 2 && (reinterpret_cast<uintptr_t>(sp) & 1) == 0) {
-        *reinterpret_cast<uint16_t *>(sp) = (uint16_t)scs;
-    } else {
-        for (int b = 0; b < nvalid; b++) sp[b] = (uint8_t)(scs >> (8 * b));
+    __syncthreads();   // the input tile is no longer read
+
+    // ---- stage both code tiles in LDS, then write them back with every
+    // store instruction covering whole 128-byte rows (8 lanes per row):
+    // lane-scattered 16-byte stores would cost one L2 request each ----
+    uint8_t *stage = reinterpret_cast<uint8_t *>(&tile[0][0]);
+    constexpr int COLB = ROW ? 128 * 128 : 0;   // column codes follow the row codes
+    if (ROW) {
+        uint4 *d = reinterpret_cast<uint4 *>(stage + tr * 128 + 64 * half);
+#pragma unroll
+        for (int i = 0; i < 4; i++) d[i] = make_uint4(qrow[4 * i], qrow[4 * i + 1], qrow[4 * i + 2], qrow[4 * i + 3]);
+    }
+    {
+        uint4 *d = reinterpret_cast<uint4 *>(stage + COLB + c * 128 + 64 * rh);
+#pragma unroll
+        for (int i = 0; i < 4; i++) d[i] = make_uint4(qcol[4 * i], qcol[4 * i + 1], qcol[4 * i + 2], qcol[4 * i + 3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int id = 256 * i + t, r = id >> 3, piece = id & 7;
+        if (ROW) {
+            const int64_t dr = rsrc[r];
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * piece);
+            if (dr >= 0 && k0 + 16 * piece < K)
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                            reinterpret_cast<u32x4 *>(codes_row + dr * K + k0 + 16 * piece));
+        }
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + COLB + r * 128 + 16 * piece);
+        if (k0 + r < K && p0 + 16 * piece < plimit)
+            __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<u32x4 *>(codes_colT + (k0 + r) * ld_colT + p0 + 16 * piece));
     }
 }
 
