@@ -639,13 +639,16 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     };
 
     // Write the consumer's tile.  The MFMA leaves lane l with column l % 32
-    // of each 32 x 32 block and rows 8 (e / 4) + 4 (l / 32) + e % 4; each
-    // wavefront transposes a block through its own LDS patch in a ring stage
-    // no load targets, then writes whole 16-byte row pieces.
+    // of each 32 x 32 block and rows 8 (e / 4) + 4 (l / 32) + e % 4; the
+    // transpose goes through an LDS patch in a ring stage no load targets.
     auto epilogue = [&](uint8_t *slot) __attribute__((always_inline)) {
+        // Each wavefront stages a 32-row slice of its outputs in its own LDS
+        // patch and writes it back in whole 128-byte row pieces: 32 x 64
+        // columns for bf16 (both column blocks at once), 32 x 32 for f32.
         constexpr int ESZ = BF16OUT ? 2 : 4;
         constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
-        constexpr int RB = 32 * ESZ;                   // bytes of a 32-column row piece
+        constexpr int NJ = BF16OUT ? 2 : 1;            // column blocks per staged slice
+        constexpr int RB = 32 * NJ * ESZ;              // bytes of a staged row piece (128)
         constexpr int STR = RB + 16;                   // padded LDS row stride
         constexpr int CPR = RB / 16;                   // 16-byte chunks per row piece
         uint8_t *ep = slot + w * (32 * STR);
@@ -663,13 +666,28 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 else mul[e] = rowmul[MX ? 0 : ord][rt];
             }
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
+            for (int j0 = 0; j0 < 2; j0 += NJ) {
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);
-                    const float v = mul[e] == 0.0f ? 0.0f : acc[i][j][e] * mul[e];
-                    if (BF16OUT) *reinterpret_cast<uint16_t *>(ep + rin * STR + lr * 2) = (uint16_t)f32_to_bf16(v);
-                    else *reinterpret_cast<float *>(ep + rin * STR + lr * 4) = v;
+                for (int jj = 0; jj < NJ; jj++) {
+                    const int j = j0 + jj;
+#pragma unroll
+                    for (int e = 0; e < 16; e += 2) {
+                        const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);   // rows rin, rin + 1
+                        const float v0 = mul[e] == 0.0f ? 0.0f : acc[i][j][e] * mul[e];
+                        const float v1 = mul[e + 1] == 0.0f ? 0.0f : acc[i][j][e + 1] * mul[e + 1];
+                        if (BF16OUT) {
+                            // V_CVT_PK_BF16_F32: round to nearest even, like f32_to_bf16
+                            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                            typedef float f2 __attribute__((ext_vector_type(2)));
+                            const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v0, v1}, bf2));
+                            *reinterpret_cast<uint16_t *>(ep + rin * STR + (32 * jj + lr) * 2) = (uint16_t)pk;
+                            *reinterpret_cast<uint16_t *>(ep + (rin + 1) * STR + (32 * jj + lr) * 2) =
+                                (uint16_t)(pk >> 16);
+                        } else {
+                            *reinterpret_cast<float *>(ep + rin * STR + lr * 4) = v0;
+                            *reinterpret_cast<float *>(ep + (rin + 1) * STR + lr * 4) = v1;
+                        }
+                    }
                 }
                 __builtin_amdgcn_wave_barrier();   // the patch is private to this wavefront
 #pragma unroll
@@ -677,7 +695,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     const int idx = pass * 64 + l;
                     const int rin = idx / CPR, ch = idx % CPR;
                     const int r = CT.row0 + wm * (BT / 2) + 32 * i + rin;
-                    const int cn = CT.col0 + wn * 64 + 32 * j + ch * VEC;
+                    const int cn = CT.col0 + wn * 64 + 32 * j0 + ch * VEC;
                     const uint4 v = *reinterpret_cast<const uint4 *>(ep + rin * STR + ch * 16);
                     if (r < CT.row_end && cn < p.N) {
                         char *dst = reinterpret_cast<char *>(p.c) + (goff + (int64_t)r * p.ldc + cn) * ESZ;
