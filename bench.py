@@ -515,6 +515,35 @@ WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Mxfp8Quant, Requan
 
 # ---------------------------------------------------------------------------
 
+def kernel_source_digest():
+    """sha256 over the HIP sources the library is built from (file names and bytes)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_precision_token_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, op):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = table.get("ops", {}).get(f"{workload}/{op}")
+    if not ent or ent.get("source_sha256") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -522,6 +551,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="time just this op of the workload (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -537,6 +567,12 @@ def main():
     ops.lib()      # fails loudly when the HIP library is missing
 
     wl = WORKLOADS[args.workload](dev)
+    if args.only:
+        sel = [op for op in wl.ops if op.name == args.only]
+        if not sel:
+            print(f"bench.py: no op {args.only!r} in {wl.name}; ops: {[op.name for op in wl.ops]}", file=sys.stderr)
+            sys.exit(2)
+        wl.ops = sel
     torch.cuda.synchronize()
     print(f"[bench] workload {wl.name} ready; {len(wl.ops)} ops per step", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -581,14 +617,15 @@ def main():
         comps[op.name] = d
     dom = max(wl.ops, key=lambda o: sum(o.times))
     dom_ms = sum(dom.times) / len(dom.times)
+    traffic = measured_traffic(wl.name, dom.name)
     if dom.bound() == "mfma":
         ach = dom.flops / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS[dom.mfma], "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS[dom.mfma], 4), "traffic": None, "kernel": dom.name}
+                "frac": round(ach / MFMA_PEAK_TFLOPS[dom.mfma], 4), "traffic": traffic, "kernel": dom.name}
     else:
         ach = dom.nbytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom.name}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom.name}
 
     cpu = None
     if not args.no_cpu_baseline:
