@@ -641,7 +641,8 @@ def main():
         "value": round(value, 3), "unit": wl.unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": wl.unit != "us", "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": wl.config(), "roofline": roof, "cpu_baseline": cpu, "components": comps,
+        "config": dict(wl.config(), **({"only_op": args.only} if args.only else {})), "roofline": roof,
+        "cpu_baseline": cpu, "components": comps,
     }
     print(json.dumps(line), flush=True)
 

@@ -841,79 +841,148 @@ __device__ __forceinline__ float load_elem<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
 
-// One wavefront per row of h; lane l owns the 32-value chunks starting at
-// i = 2048 j + 32 l.  FMT: -1 = h only, 0 = NVFP4 per token, 1 = MXFP8 rowwise.
-template <typename T, int FMT, bool M46, int MAXIT>
+// 32 consecutive inputs starting at p (16-byte aligned) as f32, in 16-byte loads.
+template <typename T>
+__device__ __forceinline__ void load32(const T *p, float (&v)[32]);
+template <>
+__device__ __forceinline__ void load32<float>(const float *p, float (&v)[32]) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float4 f = q[i];
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+}
+template <>
+__device__ __forceinline__ void load32<uint16_t>(const uint16_t *p, float (&v)[32]) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint4 u = q[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v[8 * i + 2 * k] = bf16_lo(w[k]);
+            v[8 * i + 2 * k + 1] = bf16_hi(w[k]);
+        }
+    }
+}
+
+// LPR lanes per row of h (64, or 32 / 16 for short rows so that lanes are
+// not left idle); lane l of a row owns the 32-value chunks starting at
+// i = 32 LPR j + 32 l (whole quantization blocks per lane).  Outputs whose
+// per-lane pieces are not contiguous across lanes (h, MXFP8 codes) go through
+// a per-wavefront LDS patch so that every store instruction writes a
+// contiguous run.  FMT: -1 = h only, 0 = NVFP4 per token, 1 = MXFP8 rowwise.
+template <typename T, int FMT, bool M46, int MAXIT, int LPR>
 __global__ __launch_bounds__(256) void k_swiglu(const T *__restrict__ h13, int64_t R, int64_t I,
                                                 uint16_t *__restrict__ h_out, uint8_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales, float *__restrict__ outer) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= R) return;
+    // per wavefront: 64 lanes x (64 + 16) bytes (padding keeps the 64-byte
+    // lane pieces on distinct banks)
+    __shared__ __attribute__((aligned(16))) uint8_t stg[4][64 * 80];
+    constexpr int RPW = 64 / LPR;               // rows per wavefront
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & (LPR - 1), sub = (threadIdx.x & 63) / LPR;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + wv) * RPW + sub;
+    if (row >= R) return;                       // whole row groups leave together
+    uint8_t *sw = stg[wv] + sub * (LPR * 80);
     const T *gp = h13 + row * 2 * I;
     const T *up = gp + I;
     float hv[MAXIT][32];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < MAXIT; j++) {
-        const int64_t i0 = (int64_t)j * 2048 + lane * 32;
+        const int64_t c0 = (int64_t)j * 32 * LPR;   // this chunk's first element
+        const int64_t i0 = c0 + lane * 32;
+        if (c0 >= I) break;                     // wave-uniform
         if (i0 < I) {
+            float z[32], u[32];
+            load32<T>(gp + i0, z);
+            load32<T>(up + i0, u);
 #pragma unroll
             for (int i = 0; i < 32; i++) {
-                const float z = load_elem<T>(gp + i0 + i);
-                const float u = load_elem<T>(up + i0 + i);
-                const float silu = z / (1.0f + exp_cw(-z));
-                const uint32_t hb = f32_to_bf16(silu * u);
-                hv[j][i] = __uint_as_float(hb << 16);
+                const float silu = z[i] / (1.0f + exp_cw(-z[i]));
+                hv[j][i] = __uint_as_float(f32_to_bf16(silu * u[i]) << 16);
+                amax = fmaxf(amax, fabsf(hv[j][i]));
             }
-            if (h_out) {
-                uint4 *dst = reinterpret_cast<uint4 *>(h_out + row * I + i0);
+        } else {
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    uint32_t w[4];
+            for (int i = 0; i < 32; i++) hv[j][i] = 0.0f;
+        }
+        if (h_out) {
+            uint4 *d = reinterpret_cast<uint4 *>(sw + lane * 80);
 #pragma unroll
-                    for (int k = 0; k < 4; k++)
-                        w[k] = (__float_as_uint(hv[j][8 * q + 2 * k]) >> 16) |
-                               (__float_as_uint(hv[j][8 * q + 2 * k + 1]) & 0xFFFF0000u);
-                    dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int q = 0; q < 4; q++) {
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    w[k] = (__float_as_uint(hv[j][8 * q + 2 * k]) >> 16) |
+                           (__float_as_uint(hv[j][8 * q + 2 * k + 1]) & 0xFFFF0000u);
+                d[q] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int m = LPR * k + lane;             // 16-byte piece of the chunk
+                if (c0 + 8 * m < I) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(sw + 80 * (m >> 2) + 16 * (m & 3));
+                    *reinterpret_cast<uint4 *>(h_out + row * I + c0 + 8 * m) = v;
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(hv[j][i]));
+            __builtin_amdgcn_wave_barrier();
         }
     }
     if (FMT < 0) return;
     if (FMT == 0) {
-        amax = wave_max(amax);
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
         const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
         if (lane == 0) outer[row] = g;
 #pragma unroll
         for (int j = 0; j < MAXIT; j++) {
-            const int64_t i0 = (int64_t)j * 2048 + lane * 32;
+            const int64_t i0 = (int64_t)j * 32 * LPR + lane * 32;
             if (i0 < I) {
+                uint32_t w4[4], sc = 0;
 #pragma unroll
                 for (int b = 0; b < 2; b++) {
                     float xf[16];
 #pragma unroll
                     for (int i = 0; i < 16; i++) xf[i] = hv[j][16 * b + i];
                     Nvfp4Block nb = nvfp4_block<M46>(xf, g);
-                    *reinterpret_cast<uint2 *>(codes + row * (I / 2) + (i0 + 16 * b) / 2) = make_uint2(nb.lo, nb.hi);
-                    scales[row * (I / 16) + (i0 + 16 * b) / 16] = (uint8_t)nb.s;
+                    w4[2 * b] = nb.lo;
+                    w4[2 * b + 1] = nb.hi;
+                    sc |= nb.s << (8 * b);
                 }
+                // lane pieces are contiguous across lanes: one 16-byte and one 2-byte store
+                *reinterpret_cast<uint4 *>(codes + row * (I / 2) + i0 / 2) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                *reinterpret_cast<uint16_t *>(scales + row * (I / 16) + i0 / 16) = (uint16_t)sc;
             }
         }
     } else {
 #pragma unroll
         for (int j = 0; j < MAXIT; j++) {
-            const int64_t i0 = (int64_t)j * 2048 + lane * 32;
-            if (i0 < I) {
-                uint32_t q[8];
-                const uint32_t sc = mxfp8_block(hv[j], q);
-                uint4 *dst = reinterpret_cast<uint4 *>(codes + row * I + i0);
-                dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-                dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-                scales[row * (I / 32) + i0 / 32] = (uint8_t)sc;
+            const int64_t c0 = (int64_t)j * 32 * LPR;
+            const int64_t i0 = c0 + lane * 32;
+            if (c0 >= I) break;
+            uint32_t q[8];
+            const uint32_t sc = mxfp8_block(hv[j], q);
+            if (i0 < I) scales[row * (I / 32) + i0 / 32] = (uint8_t)sc;
+            uint4 *d = reinterpret_cast<uint4 *>(sw + lane * 48);
+            d[0] = make_uint4(q[0], q[1], q[2], q[3]);
+            d[1] = make_uint4(q[4], q[5], q[6], q[7]);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const int m = LPR * k + lane;             // 16-byte piece of the code chunk
+                if (c0 + 16 * m < I) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(sw + 48 * (m >> 1) + 16 * (m & 1));
+                    *reinterpret_cast<uint4 *>(codes + row * I + c0 + 16 * m) = v;
+                }
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -921,10 +990,12 @@ __global__ __launch_bounds__(256) void k_swiglu(const T *__restrict__ h13, int64
 template <typename T, int FMT, bool M46>
 static void swiglu_dispatch_it(const void *h13, int64_t R, int64_t I, uint16_t *h_out, uint8_t *codes,
                                uint8_t *scales, float *outer, hipStream_t s) {
-    dim3 grid((unsigned)((R + 3) / 4)), block(256);
     const T *in = reinterpret_cast<const T *>(h13);
-    if (I <= 2048) k_swiglu<T, FMT, M46, 1><<<grid, block, 0, s>>>(in, R, I, h_out, codes, scales, outer);
-    else k_swiglu<T, FMT, M46, 4><<<grid, block, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    auto grid = [&](int lpr) { return dim3((unsigned)((R + 4 * (64 / lpr) - 1) / (4 * (64 / lpr)))); };
+    if (I <= 512) k_swiglu<T, FMT, M46, 1, 16><<<grid(16), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (I <= 1024) k_swiglu<T, FMT, M46, 1, 32><<<grid(32), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (I <= 2048) k_swiglu<T, FMT, M46, 1, 64><<<grid(64), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else k_swiglu<T, FMT, M46, 4, 64><<<grid(64), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
 }
 
 template <typename T>

@@ -270,7 +270,7 @@ def test_requant_worked_example_on_device():
 # SwiGLU + quantize
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,I", [(5, 32), (130, 768), (17, 2048), (9, 4096)])
+@pytest.mark.parametrize("R,I", [(5, 32), (37, 480), (130, 768), (21, 992), (17, 2048), (9, 4096)])
 @pytest.mark.parametrize("fmt,m46", [(-1, False), (0, True), (0, False), (1, False)])
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
 def test_swiglu_quantize_parity(R, I, fmt, m46, in_dtype):
