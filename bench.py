@@ -32,26 +32,31 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}
+# VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, in lane-operations per
+# second (a quarter-rate instruction counts 4)
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 SEED = 20261201
 
 
 class Op:
     """One library call of the step with its algorithmic bytes and flops per launch."""
 
-    def __init__(self, name, fn, nbytes, flops=0.0, mfma=None):
+    def __init__(self, name, fn, nbytes, flops=0.0, mfma=None, valu=0.0):
         self.name = name
         self.fn = fn
         self.nbytes = float(nbytes)
         self.flops = float(flops)
         self.mfma = mfma          # MFMA input type of a GEMM ("fp8", "fp16"), None for memory-bound ops
+        self.valu = float(valu)   # algorithmic VALU lane-operations per launch (0: not counted)
         self.times = []
 
     def bound(self):
-        if not self.mfma:
-            return "hbm"
         t_mem = self.nbytes / (HBM_PEAK_GBS * 1e9)
-        t_mfma = self.flops / (MFMA_PEAK_TFLOPS[self.mfma] * 1e12)
-        return "mfma" if t_mfma >= t_mem else "hbm"
+        t_valu = self.valu / (VALU_PEAK_TOPS * 1e12)
+        if self.mfma:
+            t_mfma = self.flops / (MFMA_PEAK_TFLOPS[self.mfma] * 1e12)
+            return "mfma" if t_mfma >= t_mem else "hbm"
+        return "alu" if t_valu > t_mem else "hbm"
 
 
 def timed_until(unit_fn, min_seconds=10.0, max_reps=10000):
@@ -307,6 +312,7 @@ class Mxfp8Quant:
     name = "mxfp8_quant"
     unit = "GB/s"
     dtype = "f32"
+    graph = True
 
     def __init__(self, dev):
         import torch
@@ -326,10 +332,10 @@ class Mxfp8Quant:
         def quant_x():
             i = self.step_i % self.copies
             ops.quantize_mxfp8(xs[i], True, True, out=outs[i])
+            self.step_i += 1
 
         def quant_w():
             ops.quantize_mxfp8(W, True, False, out=wq)
-            self.step_i += 1
 
         self.ops = [Op("quant_x_row_col", quant_x, M * K * (2 + 2 * s8)),
                     Op("quant_weights_row", quant_w, E * N * KW * (2 + s8))]
@@ -366,6 +372,7 @@ class RequantSr:
     name = "requant_sr"
     unit = "GB/s"
     dtype = "f32"
+    graph = True
 
     def __init__(self, dev):
         import torch
@@ -393,7 +400,13 @@ class RequantSr:
             self.step_i += 1
 
         nbytes = M * K * (0.5 + 1 / 16) * 2 + M * 4 + 4
-        self.ops = [Op("requant_transpose_sr", run, nbytes)]
+        # The generator alone fixes the VALU floor: Philox4x32-10 gives 8 elements
+        # their 16 bits with 19 32x32->64 products (V_MAD_U64_U32, quarter rate: 4
+        # each; round 1 has one, two counter words being zero) and 20 three-input
+        # xors (1 each), 96 lane-operations; plus the dequantizing and the rescaling
+        # multiply of every element: 14 per element.
+        valu = M * K * (96 / 8 + 2)
+        self.ops = [Op("requant_transpose_sr", run, nbytes, valu=valu)]
         self.total_bytes = nbytes
 
     def config(self):
@@ -544,6 +557,76 @@ def measured_traffic(workload, op):
     return ent.get("bytes_per_launch")
 
 
+def time_eager(wl, steps, dev):
+    """Launch `steps` steps from Python, with HIP events around every op on the
+    launch stream; returns (wall ms per step, event ms per step)."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for _ in range(steps):
+        for op in wl.ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            op.fn()
+            b.record(stream)
+            events.append((op, a, b))
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for op, a, b in events:
+        op.times.append(a.elapsed_time(b))
+    return wall * 1e3 / steps, e_start.elapsed_time(e_end) / steps
+
+
+def time_graphed(wl, steps, dev):
+    """Short steps are bound by the Python launch rate, not by the GPU: capture the
+    launches in HIP graphs and time their replay.  Each op is timed alone (a graph
+    of `steps` launches of it), then the whole step (a graph of `steps` steps);
+    every graph is replayed once untimed first.  Returns (wall ms per step of the
+    step graph's timed replay, event ms per step of it)."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+
+    def capture(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                for fn in fns:
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    for op in wl.ops:
+        g = capture([op.fn])
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        op.times.append(a.elapsed_time(b) / steps)
+        del g
+    g = capture([op.fn for op in wl.ops])
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    g.replay()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, e_start.elapsed_time(e_end) / steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,6 +635,8 @@ def main():
     ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="time just this op of the workload (for profiler runs)")
+    ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
+                    help="time HIP-graph replays instead of Python launches (auto: for the short-step workloads)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -580,30 +665,13 @@ def main():
             op.fn()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    events = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
-    e_start.record(stream)
-    for _ in range(args.steps):
-        for op in wl.ops:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            op.fn()
-            b.record(stream)
-            events.append((op, a, b))
-    e_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for op, a, b in events:
-        op.times.append(a.elapsed_time(b))
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms_per_step = e_start.elapsed_time(e_end) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms_per_step:.3f})",
-          file=sys.stderr, flush=True)
+    use_graph = {"auto": getattr(wl, "graph", False), "on": True, "off": False}[args.graph]
+    if use_graph:
+        ms_per_step, ev_ms_per_step = time_graphed(wl, args.steps, dev)
+    else:
+        ms_per_step, ev_ms_per_step = time_eager(wl, args.steps, dev)
+    print(f"[bench] timed {args.steps} steps{' (HIP graph replay)' if use_graph else ''}: "
+          f"{ms_per_step:.3f} ms/step (events {ev_ms_per_step:.3f})", file=sys.stderr, flush=True)
 
     comps = {}
     for op in wl.ops:
@@ -614,6 +682,10 @@ def main():
             tf = op.flops / (ms * 1e-3) / 1e12
             d["TFLOP_s"] = round(tf, 1)
             d["mfma_frac"] = round(tf / MFMA_PEAK_TFLOPS[op.mfma], 4)
+        if op.valu:
+            to = op.valu / (ms * 1e-3) / 1e12
+            d["TOP_s"] = round(to, 2)
+            d["alu_frac"] = round(to / VALU_PEAK_TOPS, 4)
         comps[op.name] = d
     dom = max(wl.ops, key=lambda o: sum(o.times))
     dom_ms = sum(dom.times) / len(dom.times)
@@ -622,6 +694,11 @@ def main():
         ach = dom.flops / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS[dom.mfma], "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS[dom.mfma], 4), "traffic": traffic, "kernel": dom.name}
+    elif dom.bound() == "alu":
+        ach = dom.valu / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": traffic, "kernel": dom.name,
+                "hbm_GB_s": round(dom.nbytes / (dom_ms * 1e-3) / 1e9, 1)}
     else:
         ach = dom.nbytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -641,7 +718,8 @@ def main():
         "value": round(value, 3), "unit": wl.unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": wl.unit != "us", "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": dict(wl.config(), **({"only_op": args.only} if args.only else {})), "roofline": roof,
+        "config": dict(wl.config(), **({"only_op": args.only} if args.only else {}),
+                       **({"timing": "hip_graph_replay"} if use_graph else {})), "roofline": roof,
         "cpu_baseline": cpu, "components": comps,
     }
     print(json.dumps(line), flush=True)

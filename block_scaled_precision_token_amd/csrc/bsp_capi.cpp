@@ -56,8 +56,8 @@ BSP_EXPORT int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G) {
 }
 
 BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
-    (void)M;
-    return 64 * sizeof(float);
+    if (M <= 0) return 0;
+    return (size_t)bsp::requant_partials(M) * sizeof(float);
 }
 
 BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {

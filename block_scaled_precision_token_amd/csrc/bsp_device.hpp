@@ -143,14 +143,16 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; r++) {
-        uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-        uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-        uint32_t n0 = hi1 ^ c[1] ^ k0;
-        uint32_t n2 = hi0 ^ c[3] ^ k1;
+        // one V_MAD_U64_U32 per product gives both halves
+        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+        // three-input xor in one V_BITOP3_B32 (truth table 0x96)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
         c[0] = n0;
-        c[1] = lo1;
+        c[1] = (uint32_t)p1;
         c[2] = n2;
-        c[3] = lo0;
+        c[3] = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }

@@ -641,17 +641,28 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
 // Dequantize -> transpose -> requantize (stochastic rounding)
 // --------------------------------------------------------------------------
 
-constexpr int RQ_TM = 128;  // input rows (m) per tile
-constexpr int RQ_TK = 128;  // input columns (k) per tile
-constexpr int RQ_MAXPART = 64;
+constexpr int RQ_TM = 256;            // input rows (m) per tile: 16 output blocks of 16
+constexpr int RQ_TK = 128;            // input columns (k) per tile: 16 groups of 8
+constexpr int RQ_CS = RQ_TM + 4;      // word stride of the transposed code tile in LDS
+constexpr int RQ_MAXPART = 1024;      // partial maxima of the outer scales
+constexpr int RQ_PCHUNK = 2048;       // outer scales per partial-max block
 
-// Partial maxima of the per-row outer scales (G = max over all partials).
+// Partial maxima of the per-row outer scales (G = max over all partials,
+// starting from 0).  Chunks are multiples of 4 floats, so every chunk starts
+// 16-byte aligned.
 __global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restrict__ outer, int64_t M,
                                                            float *__restrict__ part) {
-    const int64_t chunk = (M + gridDim.x - 1) / gridDim.x;
+    const int64_t chunk = ((M + gridDim.x - 1) / gridDim.x + 3) & ~(int64_t)3;
     const int64_t a = (int64_t)blockIdx.x * chunk, b = a + chunk < M ? a + chunk : M;
     float m = 0.0f;
-    for (int64_t i = a + threadIdx.x; i < b; i += blockDim.x) m = fmaxf(m, outer[i]);
+    for (int64_t i = a + 4 * (int64_t)threadIdx.x; i < b; i += 4 * (int64_t)blockDim.x) {
+        if (i + 4 <= b) {
+            const float4 v = *reinterpret_cast<const float4 *>(outer + i);
+            m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        } else {
+            for (int64_t j = i; j < b; j++) m = fmaxf(m, outer[j]);
+        }
+    }
     m = wave_max(m);
     __shared__ float red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -659,143 +670,280 @@ __global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restri
     if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Stochastic rounding of v >= 0 onto the E2M1 grid with 16 random bits u.
-__device__ __forceinline__ uint32_t e2m1_sr_mag(float v, uint32_t u) {
-    if (v >= 6.0f) return 7u;
-    // lower neighbour: truncating encode (largest grid value <= v)
-    uint32_t lo;
-    float lov, gap;
-    if (v < 2.0f) {
-        lo = (uint32_t)(v * 2.0f);          // 0..3: grid step 0.5 below 2
-        lov = 0.5f * (float)lo;
-        gap = 0.5f;
-    } else if (v < 4.0f) {
-        lo = v < 3.0f ? 4u : 5u;
-        lov = v < 3.0f ? 2.0f : 3.0f;
-        gap = 1.0f;
-    } else {
-        lo = 6u;
-        lov = 4.0f;
-        gap = 2.0f;
-    }
-    const float frac = (v - lov) / gap;    // exact: Sterbenz, then a power of two
-    return ((float)u < frac * 65536.0f) ? lo + 1u : lo;
+// a[15:0] * b[15:0] + c (low half of a) and a[31:16] * b[15:0] + c (high
+// half): one V_MAD_U32_U16 each.
+__device__ __forceinline__ uint32_t mad_u16_lo(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ uint32_t mad_u16_hi(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+    return d;
 }
 
+// floor(-y) as an int: V_CVT_FLR_I32_F32 with a negated operand, so that
+// -result = ceil(y) in one instruction.
+__device__ __forceinline__ int32_t neg_ceil_i32(float y) {
+    int32_t f;
+    asm("v_cvt_flr_i32_f32 %0, -%1" : "=v"(f) : "v"(y));
+    return f;
+}
+
+// Stochastic rounding of x = d * r (r >= 0) onto the E2M1 grid with 16
+// random bits u, passed as nw = ~word with u in its low (HI = false) or high
+// half.  v = |x| is rounded up to the next grid value iff u < frac * 2^16,
+// frac being v's exact position between its grid neighbours; v >= 6 gives 6.
+// Returns the signed 4-bit code in bits 28-31 (lower bits are junk).
+// Branch-free and exact:
+//  - v in [1, 6]: the E2M1 value is v's exponent and top mantissa bit; frac *
+//    2^22 is the 22 mantissa bits m below them.  Adding 2^22 - 1 - 64 u to
+//    the bit pattern carries into bit 22 iff m > 64 u, i.e. iff u < frac *
+//    2^16.  Bits 22 and up then read 252 + code.
+//  - v < 1: the grid step is 0.5; with c = ceil(v * 2^17) (exact), floor(2 v)
+//    plus the decision is (c + 65535 - u) >> 16, laid out as 252 + code from
+//    bit 22 up as well.
+// Adding 4 << 22 turns 252 + code into 256 + code, so bits 22-25 are the code
+// with bit 25 clear.  Everything is computed shifted left by 6 (mod 2^32),
+// which puts bits 22-25 at 28-31 with bit 31 clear for the sign of x; the
+// random term 64 (65535 - u) << 6 is (~u & 0xFFFF) * 4096.
+template <bool HI>
+__device__ __forceinline__ uint32_t e2m1_sr_code_hi(float d, float r, uint32_t nw) {
+    // |d * r| == |d| * r for r >= 0, and d * r keeps the sign of d (r = 0 too)
+    const float x = d * r;
+    const float v = fminf(fabsf(x), 6.0f);
+    // (bits(v) + 0x0100003F) << 6 and (64 c + 0x3F000000 - 63 + 0x0100003F) << 6
+    // = c << 12, with c = ceil(v * 2^17) <= 2^17
+    const uint32_t pa = (__float_as_uint(v) << 6) + 0x40000FC0u;
+    const uint32_t pb = (uint32_t)__mul24(neg_ceil_i32(v * 131072.0f), -4096);
+    // select by mask: a plain ?: is turned into a divergent branch
+    const uint32_t below = 0u - (uint32_t)(v < 1.0f);
+    const uint32_t p = (pb & below) | (pa & ~below);
+    const uint32_t t = HI ? mad_u16_hi(nw, 4096u, p) : mad_u16_lo(nw, 4096u, p);
+    return t | (__float_as_uint(x) & 0x80000000u);
+}
+
+// Quantize one output block (16 values d of one output row k, m = mb ..
+// mb + 15) and store its 8 code bytes at cp and its scale at sp.  blk is the
+// Philox block of the block's first element, (k * M + mb) / 8.  rlut[s] is
+// 1 / (E4M3(s) * G), or 0 where that product is below 2^-126 (the block is
+// flushed: scale 0, every code keeps only its sign).
+template <bool SR>
+__device__ __forceinline__ void requant_block(const float (&d)[16], float G, const float *rlut, uint64_t blk,
+                                              uint8_t *cp, uint8_t *sp, uint32_t key0, uint32_t key1) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) a = fmaxf(a, fabsf(d[i]));
+    uint32_t s = 0u;
+    float r = 0.0f;
+    if (G > 0.0f) {
+        s = e4m3x2_hw(a / (6.0f * G), 0.0f) & 0xFFu;  // a >= 0: s <= 0x7E
+        r = rlut[s];
+        s = r == 0.0f ? 0u : s;
+    }
+    uint32_t lo = 0u, hi = 0u;
+    if (SR) {
+        // k * M and mb are multiples of 16, so blk is even and the block's
+        // two Philox blocks are blk and blk | 1: 8 x 16 bits each
+        uint32_t rnd[8];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t c[4] = {(uint32_t)blk | (uint32_t)h, (uint32_t)(blk >> 32), 0u, 0u};
+            philox4x32_10(c, key0, key1);
+#pragma unroll
+            for (int w = 0; w < 4; w++) rnd[4 * h + w] = c[w];
+        }
+        // pack by funnel shifts, last element first: each step moves the
+        // word up one nibble and brings the next code in at the bottom
+        lo = e2m1_sr_code_hi<true>(d[7], r, ~rnd[3]) >> 28;
+        hi = e2m1_sr_code_hi<true>(d[15], r, ~rnd[7]) >> 28;
+#pragma unroll
+        for (int q = 3; q >= 0; q--) {
+            const uint32_t nw = ~rnd[q];
+            if (q < 3) lo = __builtin_amdgcn_alignbit(lo, e2m1_sr_code_hi<true>(d[2 * q + 1], r, nw), 28);
+            lo = __builtin_amdgcn_alignbit(lo, e2m1_sr_code_hi<false>(d[2 * q], r, nw), 28);
+        }
+#pragma unroll
+        for (int q = 3; q >= 0; q--) {
+            const uint32_t nw = ~rnd[4 + q];
+            if (q < 3) hi = __builtin_amdgcn_alignbit(hi, e2m1_sr_code_hi<true>(d[8 + 2 * q + 1], r, nw), 28);
+            hi = __builtin_amdgcn_alignbit(hi, e2m1_sr_code_hi<false>(d[8 + 2 * q], r, nw), 28);
+        }
+    } else {
+        // d * r keeps the sign of d for the hardware conversion
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            lo |= e2m1x2_hw(d[2 * i] * r, d[2 * i + 1] * r) << (8 * i);
+            hi |= e2m1x2_hw(d[8 + 2 * i] * r, d[8 + 2 * i + 1] * r) << (8 * i);
+        }
+    }
+    *reinterpret_cast<uint2 *>(cp) = make_uint2(lo, hi);
+    *sp = (uint8_t)s;
+}
+
+// Byte E of each of the 16 row words holds columns kbase + 2E (low nibble)
+// and kbase + 2E + 1: decode both (exact at scale 1), scale, requantize.
+// Output row kbase + e starts at block blk0 + e * bstep, code byte cp0 + e *
+// cstep and scale byte sp0 + e * sstep.
+template <bool SR, int E>
+__device__ __forceinline__ void requant_pair(const uint32_t (&cw)[16], const float (&sf)[16], float G,
+                                             const float *rlut, uint64_t blk0, uint64_t bstep, uint8_t *cp0,
+                                             int64_t cstep, uint8_t *sp0, int64_t sstep, uint32_t key0,
+                                             uint32_t key1) {
+    float d0[16], d1[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], 1.0f, E);
+        d0[i] = v[0] * sf[i];
+        d1[i] = v[1] * sf[i];
+    }
+    requant_block<SR>(d0, G, rlut, blk0 + (2 * E) * bstep, cp0 + (2 * E) * cstep, sp0 + (2 * E) * sstep, key0,
+                      key1);
+    requant_block<SR>(d1, G, rlut, blk0 + (2 * E + 1) * bstep, cp0 + (2 * E + 1) * cstep,
+                      sp0 + (2 * E + 1) * sstep, key0, key1);
+}
+
+// One 256 (m) x 128 (k) input tile per workgroup.  The code tile is stored
+// transposed in LDS as words tc[kq][m] (the 8 nibbles of k = 8 kq .. 8 kq + 7
+// of row m) and the effective scales s * g as tf[kb][m].  Thread (j, kq)
+// then holds rows 16 j .. 16 j + 15 of its 8 columns and produces the 8
+// output blocks (k, 16-row block j): for each k, the 16 lanes of one k write
+// 128 contiguous bytes of output row k.
 template <bool SR>
 __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                  const float *__restrict__ outer, int64_t M, int64_t K,
                                                  uint8_t *__restrict__ codesT, uint8_t *__restrict__ scalesT,
                                                  float *__restrict__ outerT, const float *__restrict__ part, int npart,
-                                                 uint32_t key0, uint32_t key1) {
-    __shared__ uint8_t sc[RQ_TM][RQ_TK / 2 + 4];
-    __shared__ float seff[RQ_TM][RQ_TK / 16 + 1];
+                                                 uint32_t key0, uint32_t key1, int ntk, int ntiles) {
+    __shared__ uint32_t tc[RQ_TK / 8][RQ_CS];
+    __shared__ float tf[RQ_TK / 16][RQ_TM];
+    __shared__ float red[4];
+    __shared__ float rlut[128];
     const int t = threadIdx.x;
-    const int64_t m0 = (int64_t)blockIdx.y * RQ_TM, k0 = (int64_t)blockIdx.x * RQ_TK;
+    // consecutive tiles (which share input cache lines) on one XCD
+    int tile = (int)blockIdx.x;
+    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+    const int64_t m0 = (int64_t)(tile / ntk) * RQ_TM, k0 = (int64_t)(tile % ntk) * RQ_TK;
 
-    float G = 0.0f;
-    if (t < 64) {
-        G = (t < npart) ? part[t] : 0.0f;
-        G = wave_max(G);
-    }
-    __shared__ float sG;
-    if (t == 0) {
-        sG = G;
-        if (blockIdx.x == 0 && blockIdx.y == 0) *outerT = G;
-    }
-
-    // load: thread t -> input row m0 + t/2, 32 code bytes (64 k values), in
-    // 8-byte units of 16 k values (the row pitch K/2 is a multiple of 8)
     {
-        const int r = t >> 1, h = t & 1;
-        const int64_t m = m0 + r, kb = k0 + 64 * h;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            uint2 c = make_uint2(0u, 0u);
-            if (m < M && kb + 16 * u < K) c = *reinterpret_cast<const uint2 *>(codes + m * (K / 2) + kb / 2 + 8 * u);
-            *reinterpret_cast<uint2 *>(&sc[r][32 * h + 8 * u]) = c;
-        }
-        if (h == 0 && m < M) {
-            const float g = outer[m];
-            for (int j = 0; j < RQ_TK / 16; j++) {
-                const int64_t kk = k0 + 16 * j;
-                seff[r][j] = (kk < K) ? e4m3_decode(scales[m * (K / 16) + kk / 16]) * g : 0.0f;
-            }
-        }
+        float g = 0.0f;
+        for (int i = t; i < npart; i += 256) g = fmaxf(g, part[i]);
+        g = wave_max(g);
+        if ((t & 63) == 0) red[t >> 6] = g;
     }
-    __syncthreads();
-    G = sG;
 
-    // outputs: item = (output row k, 16-row block j); 8 consecutive threads
-    // cover the 8 blocks of one output row (64 contiguous bytes)
-    for (int it = t; it < RQ_TK * (RQ_TM / 16); it += 256) {
-        const int kk = it >> 3, j = it & 7;
-        const int64_t k = k0 + kk, mb = m0 + 16 * j;
-        if (k >= K || mb >= M) continue;
-        float d[16];
-        float a = 0.0f;
+    // codes: thread t loads 16-byte pieces p = t & 3 (k0 + 32 p .. + 31) of
+    // rows t / 4 + 64 it; K is a multiple of 16, so a piece is whole, half
+    // or empty at the right edge
+    const int64_t rowb = K / 2;
+    if (m0 + RQ_TM <= M && k0 + RQ_TK <= K && (rowb & 15) == 0) {
+        // interior tile: all four loads in flight before the LDS writes
+        const int p = t & 3;
+        const uint8_t *src = codes + (m0 + (t >> 2)) * rowb + k0 / 2 + 16 * p;
+        uint4 v[4];
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint32_t byte = sc[16 * j + i][kk >> 1];
-            const uint32_t c = (kk & 1) ? (byte >> 4) : (byte & 15u);
-            d[i] = e2m1_value(c) * seff[16 * j + i][kk >> 4];
-            a = fmaxf(a, fabsf(d[i]));
+        for (int it = 0; it < 4; it++) v[it] = *reinterpret_cast<const uint4 *>(src + 64 * it * rowb);
+#pragma unroll
+        for (int it = 0; it < 4; it++) {
+            const int r = (t >> 2) + 64 * it;
+            tc[4 * p + 0][r] = v[it].x;
+            tc[4 * p + 1][r] = v[it].y;
+            tc[4 * p + 2][r] = v[it].z;
+            tc[4 * p + 3][r] = v[it].w;
         }
-        uint32_t s = 0u;
-        float eff = 0.0f;
-        if (G > 0.0f) {
-            const float denom = 6.0f * G;
-            s = e4m3_encode(a / denom);
-            eff = e4m3_decode(s) * G;
-        }
-        uint32_t lo = 0u, hi = 0u;
-        if (!(G > 0.0f) || eff < kFlushBelow) {
-            s = 0u;
+    } else {
+        const int p = t & 3;
+        const int64_t kb = k0 + 32 * p;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                lo |= ((__float_as_uint(d[i]) >> 28) & 8u) << (4 * i);
-                hi |= ((__float_as_uint(d[8 + i]) >> 28) & 8u) << (4 * i);
-            }
-        } else {
-            const float r = 1.0f / eff;
-            uint32_t rnd[8];
-            if (SR) {
-                // element index i = k*M + m; Philox block (i / 8) gives 8 x 16 bits
-                const uint64_t blk = ((uint64_t)k * (uint64_t)M + (uint64_t)mb) >> 3;
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    uint32_t c[4] = {(uint32_t)(blk + h), (uint32_t)((blk + h) >> 32), 0u, 0u};
-                    philox4x32_10(c, key0, key1);
-#pragma unroll
-                    for (int w = 0; w < 4; w++) rnd[4 * h + w] = c[w];
+        for (int it = 0; it < 4; it++) {
+            const int r = (t >> 2) + 64 * it;
+            const int64_t m = m0 + r;
+            uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
+            if (m < M) {
+                const uint8_t *src = codes + m * rowb + kb / 2;
+                if (kb + 32 <= K) {
+                    if ((rowb & 15) == 0) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                        w0 = v.x; w1 = v.y; w2 = v.z; w3 = v.w;
+                    } else {
+                        const uint2 a = reinterpret_cast<const uint2 *>(src)[0];
+                        const uint2 b = reinterpret_cast<const uint2 *>(src)[1];
+                        w0 = a.x; w1 = a.y; w2 = b.x; w3 = b.y;
+                    }
+                } else if (kb + 16 <= K) {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(src);
+                    w0 = a.x; w1 = a.y;
                 }
             }
-            if (SR) {
+            tc[4 * p + 0][r] = w0;
+            tc[4 * p + 1][r] = w1;
+            tc[4 * p + 2][r] = w2;
+            tc[4 * p + 3][r] = w3;
+        }
+    }
+    // effective scales of row m0 + t for the tile's 8 k blocks
+    {
+        const int64_t m = m0 + t;
+        uint32_t sb[RQ_TK / 16];
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const float v = fabsf(d[i]) * r;
-                    const uint32_t word = rnd[i >> 1];
-                    const uint32_t mag = e2m1_sr_mag(v, (i & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    const uint32_t code = ((__float_as_uint(d[i]) >> 28) & 8u) | mag;
-                    if (i < 8) lo |= code << (4 * i);
-                    else hi |= code << (4 * (i - 8));
+        for (int b = 0; b < RQ_TK / 16; b++) sb[b] = 0u;
+        float g = 0.0f;
+        if (m < M) {
+            g = outer[m];
+            const int64_t sp = K / 16;
+            const uint8_t *src = scales + m * sp + k0 / 16;
+            const int64_t left = sp - k0 / 16;
+            if (left >= RQ_TK / 16 && (sp & 7) == 0) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src);
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    sb[b] = (v.x >> (8 * b)) & 0xFFu;
+                    sb[4 + b] = (v.y >> (8 * b)) & 0xFFu;
                 }
             } else {
-                // |d| * r carries the sign of d into the hardware conversion
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    lo |= e2m1x2_hw(d[2 * i] * r, d[2 * i + 1] * r) << (8 * i);
-                    hi |= e2m1x2_hw(d[8 + 2 * i] * r, d[8 + 2 * i + 1] * r) << (8 * i);
-                }
+                for (int b = 0; b < RQ_TK / 16; b++)
+                    if (b < left) sb[b] = src[b];
             }
         }
-        *reinterpret_cast<uint2 *>(codesT + k * (M / 2) + mb / 2) = make_uint2(lo, hi);
-        scalesT[k * (M / 16) + mb / 16] = (uint8_t)s;
+#pragma unroll
+        for (int b = 0; b < RQ_TK / 16; b++) tf[b][t] = e4m3_decode(sb[b]) * g;
     }
+    __syncthreads();
+
+    const float G = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (tile == 0 && t == 0) *outerT = G;
+    if (t < 128) {
+        // 1 / (E4M3(s) * G) per scale code s, 0 where the block is flushed
+        const float eff = __builtin_amdgcn_cvt_f32_fp8(t, 0) * G;  // exact for s <= 0x7E
+        rlut[t] = (t == 127 || !(eff >= kFlushBelow)) ? 0.0f : 1.0f / eff;
+    }
+    __syncthreads();
+    const int lane = t & 63;
+    const int j = lane & 15, kq = 4 * (t >> 6) + (lane >> 4);
+    const int64_t mb = m0 + 16 * j, kbase = k0 + 8 * kq;
+    if (mb >= M || kbase >= K) return;
+    uint32_t cw[16];
+    float sf[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&tc[kq][16 * j + 4 * q]);
+        const float4 f = *reinterpret_cast<const float4 *>(&tf[kq >> 1][16 * j + 4 * q]);
+        cw[4 * q + 0] = c.x; cw[4 * q + 1] = c.y; cw[4 * q + 2] = c.z; cw[4 * q + 3] = c.w;
+        sf[4 * q + 0] = f.x; sf[4 * q + 1] = f.y; sf[4 * q + 2] = f.z; sf[4 * q + 3] = f.w;
+    }
+    const uint64_t blk0 = ((uint64_t)kbase * (uint64_t)M + (uint64_t)mb) >> 3, bstep = (uint64_t)M >> 3;
+    uint8_t *cp0 = codesT + kbase * (M / 2) + mb / 2;
+    uint8_t *sp0 = scalesT + kbase * (M / 16) + mb / 16;
+    requant_pair<SR, 0>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
+    requant_pair<SR, 1>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
+    requant_pair<SR, 2>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
+    requant_pair<SR, 3>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
 }
 
 int requant_partials(int64_t M) {
-    int64_t n = (M + 4095) / 4096;
+    int64_t n = (M + RQ_PCHUNK - 1) / RQ_PCHUNK;
     return (int)(n < 1 ? 1 : (n > RQ_MAXPART ? RQ_MAXPART : n));
 }
 
@@ -804,10 +952,16 @@ hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const flo
                           hipStream_t s) {
     const int np = requant_partials(M);
     k_outer_partial_max<<<np, 256, 0, s>>>(outer, M, part);
-    dim3 grid((unsigned)((K + RQ_TK - 1) / RQ_TK), (unsigned)((M + RQ_TM - 1) / RQ_TM));
+    const int64_t ntk = (K + RQ_TK - 1) / RQ_TK, ntm = (M + RQ_TM - 1) / RQ_TM;
+    if (ntk * ntm > INT32_MAX) return hipErrorInvalidValue;
+    const int nt = (int)(ntk * ntm);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    if (sr) k_requant<true><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1);
-    else k_requant<false><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1);
+    if (sr)
+        k_requant<true><<<nt, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1,
+                                           (int)ntk, nt);
+    else
+        k_requant<false><<<nt, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1,
+                                            (int)ntk, nt);
     return hipGetLastError();
 }
 

@@ -243,6 +243,8 @@ bsp_status bsp_mxfp8_sizes(int64_t M, int64_t K, size_t *codes_bytes, size_t *sc
 /* Upper bound of the padded column count of a grouped columnwise copy:
  * sum over groups of roundup32(n_g) <= roundup32(M + 31 * G). */
 int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
+/* Bytes of requant workspace for M rows: one f32 partial maximum of the outer
+ * scales per 2048 rows (at most 1024 partials); 0 for M <= 0. */
 size_t bsp_requant_workspace_size(int64_t M);
 size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 

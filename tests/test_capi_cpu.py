@@ -62,7 +62,10 @@ def test_size_helpers():
     nbp = 37120 // 32 + 2
     assert L.bsp_gemm_workspace_size(1, 2, 4096, 7168, 37120, 257) == head + nbp * 4096 + nbp * 7168
     assert L.bsp_gemm_workspace_size(7, 0, 64, 64, 64, 1) == 0
-    assert L.bsp_requant_workspace_size(16384) >= 4
+    assert L.bsp_requant_workspace_size(16384) == 8 * 4
+    assert L.bsp_requant_workspace_size(16) == 4
+    assert L.bsp_requant_workspace_size(1 << 30) == 1024 * 4
+    assert L.bsp_requant_workspace_size(0) == 0
 
 
 def test_nvfp4_rejects_bad_arguments():

@@ -231,12 +231,35 @@ def test_dequantize_per_expert_scope():
 # requant + SR
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(16, 16), (48, 80), (272, 144), (16384, 2048)])
+@pytest.mark.parametrize("M,K", [(16, 16), (48, 80), (272, 144), (528, 272), (768, 384), (2048, 512),
+                                 (16384, 2048)])
 @pytest.mark.parametrize("sr", [True, False])
 def test_requant_parity(M, K, sr):
     x = synth.activations(20261203 + M, M, K)
     rc, rs, rg = oracle.quantize_nvfp4(x)
     seed = 0x5EED + M
+    ct, st, gt = ops.requant_transpose_sr(to_dev(rc), to_dev(rs), to_dev(rg), seed=seed, sr=sr)
+    rct, rst, rgt = oracle.requant_transpose_sr(rc, rs, rg, seed=seed, use_sr=sr)
+    assert_bytes_equal(host(gt), rgt, "outerT")
+    assert_bytes_equal(host(st), rst, "scalesT")
+    assert_bytes_equal(host(ct), rct, "codesT")
+
+
+@pytest.mark.parametrize("M,K", [(272, 144), (512, 256)])
+@pytest.mark.parametrize("sr", [True, False])
+def test_requant_arbitrary_operands(M, K, sr):
+    """Codes, scales and outer scales drawn directly rather than produced by
+    the quantizer: every code, negative and subnormal E4M3 scales, zero and
+    tiny outer scales (flushed blocks), and values v up to 9 after the
+    rescale, so that every rounding branch is taken."""
+    rng = np.random.default_rng(20261210 + M)
+    rc = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    rs = rng.integers(0, 256, size=(M, K // 16), dtype=np.uint8)
+    rs[(rs & 0x7F) == 0x7F] = 0x3F          # E4M3FN has no 0x7F / 0xFF value
+    rg = (10.0 ** rng.uniform(-3, 3, size=M)).astype(np.float32)
+    rg[::37] = 0.0
+    rg[5] = 1e-37
+    seed = 0xC0FFEE + M
     ct, st, gt = ops.requant_transpose_sr(to_dev(rc), to_dev(rs), to_dev(rg), seed=seed, sr=sr)
     rct, rst, rgt = oracle.requant_transpose_sr(rc, rs, rg, seed=seed, use_sr=sr)
     assert_bytes_equal(host(gt), rgt, "outerT")
