@@ -259,6 +259,12 @@ __device__ __forceinline__ void dma4(const uint8_t *base, uint32_t voff, uint32_
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
                  : "memory");
 }
+// The same with a full 64-bit address per lane.
+__device__ __forceinline__ void dma16v(const uint8_t *addr, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(m0) : "memory");
+}
+// Source of the chunks of a K stage that lie past the end of K.
+__device__ __attribute__((aligned(16))) uint8_t kZeroChunk[16];
 
 // s_waitcnt vmcnt(VM) lgkmcnt(LGKM) (expcnt untouched), gfx9 encoding.
 template <int VM, int LGKM>
@@ -503,15 +509,17 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) dma16(pcb + kb, pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
         } else {
-            // The stage's second half lies past the K end: its chunks re-read
-            // the first half (zeroed by the consumer).
+            // The stage's second half lies past the K end: its chunks load
+            // zeros, and their scales (plane padding, or the next group's
+            // columns in the weight-gradient form) are finite, so they add
+            // nothing and the consumer needs no special case.
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) {
                 const int u = 64 * (w * GG::CIW + j) + l;
                 const int c = (u % GG::CH) ^ swz<FMT>(u / GG::CH);
-                const uint32_t back = c >= GG::CH / 2 ? 16 * (GG::CH / 2) : 0;
-                dma16(pca + kb, poa[j] - back, m0 + (w * GG::CIW + j) * 1024);
-                dma16(pcb + kb, pob[j] - back, m0 + GG::CODE + (w * GG::CIW + j) * 1024);
+                const bool past = c >= GG::CH / 2;
+                dma16v(past ? kZeroChunk : pca + kb + poa[j], m0 + (w * GG::CIW + j) * 1024);
+                dma16v(past ? kZeroChunk : pcb + kb + pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
             }
         }
         // scale bytes of the stage: SPS plane rows (padded past the K end)
@@ -536,6 +544,16 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
     };
 
+    // 32-row blocks of this wavefront's half of the consumer's tile that hold
+    // rows of the group (uniform).  Small experts leave most of a row tile
+    // empty: those blocks skip their MFMAs, fragment reads and epilogue.
+    auto live_blocks = [&]() __attribute__((always_inline)) -> int {
+        if (WG) return TI;
+        const int rem = CT.row_end - CT.row0 - wm * (BT / 2);
+        const int nb = (rem + 31) >> 5;
+        return rem <= 0 ? 0 : (nb < TI ? nb : TI);
+    };
+
     // Multiply the consumer's current stage, held in ring stage U.
     auto compute = [&](auto U) __attribute__((always_inline)) {
         // Opaque per call for the same reason (LDS offsets of stages 2 and 3
@@ -543,8 +561,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         uint32_t soff = decltype(U)::v * SLOT_BYTES;
         asm volatile("" : "+s"(soff));
         const uint8_t *slot = ring + soff;
-        const int k0 = CT.kbeg + c_kt * GBK;
-        const bool h1 = k0 + GBK / 2 < CT.kend;
+        const int nv = live_blocks();
+        if (nv == 0) return;
         if (MX) {
             // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
             // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
@@ -556,20 +574,13 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 64 * j);
                 b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1 + 32 * 64 * j);
                 bs[j] = slot[fsb + 32 * j];
-                if (!h1) {   // block 1 lies past the K end: zero codes, unit scale
-                    b1[j] = make_uint4(0u, 0u, 0u, 0u);
-                    bs[j] = lh ? 127u : bs[j];
-                }
             }
 #pragma unroll
             for (int i = 0; i < TI; i++) {
+                if (i >= nv) break;
                 const uint4 a0 = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * i);
-                uint4 a1 = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * i);
-                uint32_t as = slot[fsa + 32 * i];
-                if (!h1) {
-                    a1 = make_uint4(0u, 0u, 0u, 0u);
-                    as = lh ? 127u : as;
-                }
+                const uint4 a1 = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * i);
+                const uint32_t as = slot[fsa + 32 * i];
                 const v8i fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
@@ -587,6 +598,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             h2 sa[TI][2], sb[2][2];
 #pragma unroll
             for (int i = 0; i < TI; i++) {
+                if (i >= nv) break;
                 ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 32 * i);
                 const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + 32 * i], 0);
                 const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + BT + 32 * i], 0);
@@ -601,26 +613,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 sb[j][0] = h2{t0, t0};
                 sb[j][1] = h2{t1, t1};
             }
-            if (!h1) {   // the upper 32 values lie past the K end
-                const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-                if (lh) {
-#pragma unroll
-                    for (int i = 0; i < TI; i++) {
-                        ua[i] = make_uint4(0u, 0u, 0u, 0u);
-                        sa[i][0] = sa[i][1] = one;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        ub[j] = make_uint4(0u, 0u, 0u, 0u);
-                        sb[j][0] = sb[j][1] = one;
-                    }
-                }
-            }
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 v8h fa[TI], fb[2];
 #pragma unroll
                 for (int i = 0; i < TI; i++) {
+                    if (i >= nv) break;
                     const uint32_t wa = q == 0 ? ua[i].x : q == 1 ? ua[i].y : q == 2 ? ua[i].z : ua[i].w;
                     fa[i] = nv_frag(wa, sa[i][q >> 1]);
                 }
@@ -630,10 +628,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     fb[j] = nv_frag(wb, sb[j][q >> 1]);
                 }
 #pragma unroll
-                for (int i = 0; i < TI; i++)
+                for (int i = 0; i < TI; i++) {
+                    if (i >= nv) break;
 #pragma unroll
                     for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                }
             }
         }
     };
@@ -655,8 +655,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const int ord = c_ord & 7;
         const bool vec_ok = (p.ldc % VEC) == 0;
         const int64_t goff = WG ? (int64_t)CT.g * p.M * p.ldc : 0;
+        const int nv = live_blocks();
 #pragma unroll
         for (int i = 0; i < TI; i++) {
+            if (i >= nv) break;
             float mul[16];
 #pragma unroll
             for (int e = 0; e < 16; e++) {
