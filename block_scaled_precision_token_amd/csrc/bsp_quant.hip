@@ -15,6 +15,7 @@
 namespace bsp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // --------------------------------------------------------------------------
 // NVFP4
@@ -271,8 +272,9 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 
 // One 128 x 128 tile: rowwise blocks (32 along K) straight from registers and
 // columnwise blocks (32 along rows) through LDS, from a single read of x.
-// Each pair of threads writes a full 128-byte row of codes and each pair of
-// column threads a full 128-byte column run, so stores fill whole cache lines.
+// Loads and rowwise stores cover whole rows per instruction (16 lanes per
+// 256-byte input row, 8 bytes of codes each); column codes are staged in LDS
+// and written back in whole 128-byte rows.
 // Grouped: tile rows live in the padded row space; 32-row block b belongs to
 // the group g with P[g] <= 32 b < P[g + 1] and reads source row
 // off[g] + (p - P[g]) (zero past the group).
@@ -341,75 +343,73 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
         if (p0 >= ptotal) return;
     }
 
-    // ---- load: thread t owns tile row t/2, columns [64 (t%2), +64): two 32-blocks ----
-    const int tr = t >> 1, half = t & 1;
-    const int64_t p = p0 + tr;
-    const int64_t kc = k0 + 64 * half;
-    int64_t src = -1;
-    if (GROUPED) {
-        const int b = tr >> 5;
-        const int64_t s_ = blk_src0[b] + (tr & 31);
-        if (p < ptotal && s_ >= 0 && s_ < blk_end[b]) src = s_;
-    } else {
-        if (p < M) src = p;
+    // ---- per-row sources: destination row of codes_row and row of x ----
+    __shared__ int64_t xsrc[MX_TR];
+    if (t < MX_TR) {
+        const int64_t p = p0 + t;
+        int64_t src = -1;
+        if (GROUPED) {
+            const int b = t >> 5;
+            const int64_t s_ = blk_src0[b] + (t & 31);
+            if (p < ptotal && s_ >= 0 && s_ < blk_end[b]) src = s_;
+        } else {
+            if (p < M) src = p;
+        }
+        if (ROW) rsrc[t] = src;
+        // physical row of x: the gathered row (out-of-range indices read as zeros)
+        int64_t xrow = src;
+        if (src >= 0 && gather) {
+            xrow = gather[src];
+            if (xrow < 0 || xrow >= x_rows) xrow = -1;
+        }
+        xsrc[t] = xrow;
     }
-    if (ROW && half == 0) rsrc[tr] = src;
-    // physical row of x: the gathered row (out-of-range indices read as zeros)
-    int64_t xrow = src;
-    if (src >= 0 && gather) {
-        xrow = gather[src];
-        if (xrow < 0 || xrow >= x_rows) xrow = -1;
-    }
+    __syncthreads();
+
+    // ---- load: lane l of wavefront w reads 16-byte chunk l % 16 of tile row
+    // 32 w + 4 i + l / 16 (i = 0..7), so each load covers four whole 256-byte
+    // rows.  A 32-value block is the chunks of four neighbouring lanes. ----
+    const int ch = lane & 15, rq = lane >> 4;
+    const int64_t kc = k0 + 8 * ch;
+    const bool col_ok = kc < K;   // K % 32 == 0: a block's four lanes agree
     uint4 raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    const bool blk0_ok = kc < K, blk1_ok = kc + 32 < K;
-    if (xrow >= 0) {
-        const uint4 *xp = reinterpret_cast<const uint4 *>(x + xrow * ldx + kc);
-        if (blk0_ok) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) raw[i] = xp[i];
-        }
-        if (blk1_ok) {
-#pragma unroll
-            for (int i = 4; i < 8; i++) raw[i] = xp[i];
+    for (int i = 0; i < 8; i++) {
+        const int64_t xr = xsrc[32 * wv + 4 * i + rq];
+        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (xr >= 0 && col_ok) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + xr * ldx + kc));
+            raw[i] = make_uint4(v.x, v.y, v.z, v.w);
         }
     }
-    uint32_t qrow[16];
     if (ROW) {
-        uint32_t sc2 = 0;
 #pragma unroll
-        for (int b = 0; b < 2; b++) {
-            float xf[32];
+        for (int i = 0; i < 8; i++) {
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            float xf[8];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const uint32_t w[4] = {raw[4 * b + i].x, raw[4 * b + i].y, raw[4 * b + i].z, raw[4 * b + i].w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    xf[8 * i + 2 * j] = bf16_lo(w[j]);
-                    xf[8 * i + 2 * j + 1] = bf16_hi(w[j]);
-                }
+            for (int j = 0; j < 4; j++) {
+                xf[2 * j] = bf16_lo(w[j]);
+                xf[2 * j + 1] = bf16_hi(w[j]);
             }
-            uint32_t q[8];
-            const uint32_t sc = mxfp8_block(xf, q);
+            float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) qrow[8 * b + i] = q[i];
-            sc2 |= sc << (8 * b);
-        }
-        // the row's four scale bytes: this thread's two and its neighbour's two
-        const uint32_t other = __shfl_xor(sc2, 1, 64);
-        if (src >= 0) {
-            uint8_t *sp = scales_row + src * (K / 32) + k0 / 32;
-            if (k0 + MX_TC <= K && (K % 128) == 0) {
-                if (half == 0) *reinterpret_cast<uint32_t *>(sp) = sc2 | (other << 16);
-            } else {
-                if (blk0_ok) sp[2 * half] = (uint8_t)sc2;
-                if (blk1_ok) sp[2 * half + 1] = (uint8_t)(sc2 >> 8);
+            for (int j = 0; j < 8; j++) a = fmaxf(a, fabsf(xf[j]));
+            a = fmaxf(a, __shfl_xor(a, 1, 64));
+            a = fmaxf(a, __shfl_xor(a, 2, 64));
+            const int k = mx_block_exponent(a);
+            const float inv = exp2i(-k);   // see mxfp8_block
+            const uint32_t q0 = e4m3x4_hw(xf[0] * inv, xf[1] * inv, xf[2] * inv, xf[3] * inv);
+            const uint32_t q1 = e4m3x4_hw(xf[4] * inv, xf[5] * inv, xf[6] * inv, xf[7] * inv);
+            const int64_t dr = rsrc[32 * wv + 4 * i + rq];
+            if (dr >= 0 && col_ok) {
+                __builtin_nontemporal_store(u32x2{q0, q1}, reinterpret_cast<u32x2 *>(codes_row + dr * K + kc));
+                if ((ch & 3) == 0) scales_row[dr * (K / 32) + kc / 32] = (uint8_t)(k + 127);
             }
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) *reinterpret_cast<uint4 *>(&tile[tr][64 * half + 8 * i]) = raw[i];
+    for (int i = 0; i < 8; i++) *reinterpret_cast<uint4 *>(&tile[32 * wv + 4 * i + rq][8 * ch]) = raw[i];
     __syncthreads();
 
     // ---- columns: thread t owns column t % 128, rows [64 (t / 128), +64): two 32-blocks ----
@@ -446,18 +446,12 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     }
     __syncthreads();   // the input tile is no longer read
 
-    // ---- stage both code tiles in LDS, then write them back with every
+    // ---- stage the column codes in LDS, then write them back with every
     // store instruction covering whole 128-byte rows (8 lanes per row):
     // lane-scattered 16-byte stores would cost one L2 request each ----
     uint8_t *stage = reinterpret_cast<uint8_t *>(&tile[0][0]);
-    constexpr int COLB = ROW ? 128 * 128 : 0;   // column codes follow the row codes
-    if (ROW) {
-        uint4 *d = reinterpret_cast<uint4 *>(stage + tr * 128 + 64 * half);
-#pragma unroll
-        for (int i = 0; i < 4; i++) d[i] = make_uint4(qrow[4 * i], qrow[4 * i + 1], qrow[4 * i + 2], qrow[4 * i + 3]);
-    }
     {
-        uint4 *d = reinterpret_cast<uint4 *>(stage + COLB + c * 128 + 64 * rh);
+        uint4 *d = reinterpret_cast<uint4 *>(stage + c * 128 + 64 * rh);
 #pragma unroll
         for (int i = 0; i < 4; i++) d[i] = make_uint4(qcol[4 * i], qcol[4 * i + 1], qcol[4 * i + 2], qcol[4 * i + 3]);
     }
@@ -465,14 +459,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int id = 256 * i + t, r = id >> 3, piece = id & 7;
-        if (ROW) {
-            const int64_t dr = rsrc[r];
-            const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * piece);
-            if (dr >= 0 && k0 + 16 * piece < K)
-                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
-                                            reinterpret_cast<u32x4 *>(codes_row + dr * K + k0 + 16 * piece));
-        }
-        const uint4 v = *reinterpret_cast<const uint4 *>(stage + COLB + r * 128 + 16 * piece);
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * piece);
         if (k0 + r < K && p0 + 16 * piece < plimit)
             __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                         reinterpret_cast<u32x4 *>(codes_colT + (k0 + r) * ld_colT + p0 + 16 * piece));
