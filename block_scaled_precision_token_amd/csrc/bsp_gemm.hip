@@ -239,7 +239,9 @@ __device__ __forceinline__ int swz(int r) {
 // compiler would otherwise track these writes to LDS itself and, unable to
 // follow the ring across loop iterations, wait for all of them before every
 // LDS read.  Completion is covered by the explicit waits of the pipeline.
-// M0 is declared clobbered; the s_nop covers the M0-write to LDS-DMA hazard.
+// M0 is a reserved register: the compiler sets it right before each of its
+// own uses and keeps nothing in it, so the asm may overwrite it freely; the
+// s_nop covers the M0-write to LDS-DMA hazard.
 // The pipeline's vector-memory waits count these loads only, so the kernel
 // must not spill to scratch (checked by a CPU test on the compiled code).
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -254,15 +256,15 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 }
 __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
-                 : "memory", "m0");
+                 : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t *base, uint32_t voff, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
-                 : "memory", "m0");
+                 : "memory");
 }
 // The same with a full 64-bit address per lane.
 __device__ __forceinline__ void dma16v(const uint8_t *addr, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(m0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(m0) : "memory");
 }
 // Source of the chunks of a K stage that lie past the end of K.
 __device__ __attribute__((aligned(16))) uint8_t kZeroChunk[16];
