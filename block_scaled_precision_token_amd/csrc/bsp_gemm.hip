@@ -569,28 +569,39 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         if (MX) {
             // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
             // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
-            // low byte of the scale operand is read).
-            uint4 b0[2], b1[2];
-            uint32_t bs[2];
+            // low byte of the scale operand is read).  Block i + 1's A
+            // fragment is read before block i's MFMAs are issued (the empty
+            // asm keeps the order), so the LDS reads run under the matrix
+            // work; blocks past the group's rows skip their MFMAs.
+            uint4 b0[2], b1[2], a0[TI], a1[TI];
+            uint32_t bs[2], as[TI];
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 64 * j);
                 b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1 + 32 * 64 * j);
                 bs[j] = slot[fsb + 32 * j];
             }
+            a0[0] = *reinterpret_cast<const uint4 *>(slot + fa0);
+            a1[0] = *reinterpret_cast<const uint4 *>(slot + fa1);
+            as[0] = slot[fsa];
 #pragma unroll
             for (int i = 0; i < TI; i++) {
-                if (i >= nv) break;
-                const uint4 a0 = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * i);
-                const uint4 a1 = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * i);
-                const uint32_t as = slot[fsa + 32 * i];
-                const v8i fa = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                if (i + 1 < TI) {
+                    a0[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * (i + 1));
+                    a1[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * (i + 1));
+                    as[i + 1] = slot[fsa + 32 * (i + 1)];
+                }
+                asm volatile("" ::: "memory");
+                if (i < nv) {
+                    const v8i fa = {(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
+                                    (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const v8i fb = {(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w,
-                                    (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[i][j], 0, 0, 0, (int)as,
-                                                                                0, (int)bs[j]);
+                    for (int j = 0; j < 2; j++) {
+                        const v8i fb = {(int)b0[j].x, (int)b0[j].y, (int)b0[j].z, (int)b0[j].w,
+                                        (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[i][j], 0, 0, 0,
+                                                                                    (int)as[i], 0, (int)bs[j]);
+                    }
                 }
             }
         } else {
