@@ -529,15 +529,22 @@ WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Mxfp8Quant, Requan
 # ---------------------------------------------------------------------------
 
 def kernel_source_digest():
-    """sha256 over the HIP sources the library is built from (file names and bytes)."""
+    """sha256 over the HIP sources the library is built from (file names and
+    code with comments and whitespace runs removed, so that documentation edits
+    keep the measurements valid)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_precision_token_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
             h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+            h.update(text.encode())
     return h.hexdigest()
 
 

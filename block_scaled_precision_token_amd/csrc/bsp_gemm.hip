@@ -28,13 +28,16 @@
 // stage has landed) followed by a workgroup barrier; the epilogue's stores are
 // issued so that the compiler's own counter model stays exact.
 //
-// LDS layout of a stage: per operand 128 rows of 64 (MXFP8) or 32 (NVFP4)
+// LDS layout of a stage: per operand BT rows of 64 (MXFP8) or 32 (NVFP4)
 // code bytes, the 16-byte chunks of row r stored at position chunk ^ swz(r)
-// so that the 32 rows read by one fragment load hit distinct banks; then per
-// row the two aligned dwords that contain the stage's scale bytes.
+// so that the 32 rows read by one fragment load hit distinct banks; then the
+// stage's scale bytes, block-major ([scale block][row]) as copied from the
+// scale planes a setup kernel builds in the workspace.
 //
-// Tiling: 256 threads = 4 wavefronts in 2 x 2, output tile 128 x 128, 64 K
-// values per stage.  Row tiles never straddle two experts: a setup kernel lists
+// Tiling: output tiles of BT x BT (256 on eight wavefronts, or 128 on four),
+// each wavefront (BT / 2) x 64 outputs, 64 K values per stage; wavefronts skip
+// the 32-row blocks of a tile past its expert's rows.  Row tiles never
+// straddle two experts: a setup kernel lists
 // the (expert, first row) of every row tile from the device-side group
 // offsets, so no host synchronization is needed.  Persistent workgroups walk a
 // static tile sequence: for the row-grouped forms an XCD-contiguous chunk of
