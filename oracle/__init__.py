@@ -86,6 +86,8 @@ def _declare(lib):
     lib.orc_requant_transpose_sr.argtypes = [P, P, P, I64, I64, U64, ctypes.c_int, P, P, P]
     lib.orc_gemm_rowgroup.argtypes = [ctypes.c_int, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, I64, P, P]
     lib.orc_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
+    lib.orc_gemm_bf16_rowgroup.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, P, I64, I64, I64, P, I64, P, P]
+    lib.orc_gemm_bf16_wgrad.argtypes = [P, I64, P, I64, P, I64, P, I64, P, I64, P, P]
     lib.orc_exp_f32.argtypes = [ctypes.c_float]
     lib.orc_exp_f32.restype = ctypes.c_float
     lib.orc_silu_f32.argtypes = [ctypes.c_float]
@@ -333,6 +335,46 @@ def gemm_wgrad(a_codesT, a_scalesT, b_codesT, b_scalesT, group_offsets, sel):
     cabs = np.empty((sel.shape[0], NB), np.float64)
     _load().orc_gemm_wgrad(_ptr(a_codesT), _ptr(a_scalesT), _ptr(b_codesT), _ptr(b_scalesT), _ptr(off), G, NA,
                            NB, ldk, _ptr(sel), sel.shape[0], _ptr(c), _ptr(cabs))
+    return c, cabs
+
+
+GEMM_FPROP = 0
+GEMM_DGRAD = 1
+
+
+def gemm_bf16_rowgroup(mode, a, b, gather, group_offsets, N, K, rows=None):
+    """BF16 forward (mode 0, B [G, N, K]) or data-gradient (mode 1, B [G, K, N])
+    form in binary64 on bf16 bit arrays; the backward GEMMs of the NVFP4 MoE
+    layer in either mode [remio.ai, section "Entrambe le ricette supportano";
+    alphasignal.ai, Recipe 2].  Returns (C [len(rows), N], sum|AB|)."""
+    a = _c(a, np.uint16)
+    b = _c(b, np.uint16)
+    off = _c(group_offsets, np.int64)
+    G = off.size - 1
+    M = int(off[-1])
+    gather = None if gather is None else _c(gather, np.int32)
+    rows_arr = None if rows is None else _c(rows, np.int64)
+    n = M if rows is None else rows_arr.size
+    c = np.empty((n, N), np.float64)
+    cabs = np.empty((n, N), np.float64)
+    _load().orc_gemm_bf16_rowgroup(int(mode), _ptr(a), a.shape[1], a.shape[0], _ptr(b), b.shape[-1],
+                                   _ptr(gather), _ptr(off), G, N, K, _ptr(rows_arr), n, _ptr(c), _ptr(cabs))
+    return c, cabs
+
+
+def gemm_bf16_wgrad(a, b, gather, group_offsets, sel):
+    """BF16 weight-gradient form in binary64: C_g[m, n] = sum over the rows r of
+    group g of A[r, m] * B[gather[r], n], for the (g, m) pairs in sel."""
+    a = _c(a, np.uint16)
+    b = _c(b, np.uint16)
+    off = _c(group_offsets, np.int64)
+    gather = None if gather is None else _c(gather, np.int32)
+    sel = _c(sel, np.int64).reshape(-1, 2)
+    N = b.shape[1]
+    c = np.empty((sel.shape[0], N), np.float64)
+    cabs = np.empty((sel.shape[0], N), np.float64)
+    _load().orc_gemm_bf16_wgrad(_ptr(a), a.shape[1], _ptr(b), b.shape[1], _ptr(gather), b.shape[0], _ptr(off), N,
+                                _ptr(sel), sel.shape[0], _ptr(c), _ptr(cabs))
     return c, cabs
 
 

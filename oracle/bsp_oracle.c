@@ -555,6 +555,77 @@ ORC_API void orc_gemm_wgrad(const uint8_t *a_codes, const uint8_t *a_scales, con
 }
 
 /* ------------------------------------------------------------------------ */
+/* BF16 grouped GEMM reference for the backward GEMMs of the NVFP4 MoE layer */
+/* (binary64 on the exact bf16 operand values).  The pages run the NVFP4     */
+/* recipe's backward in BF16, either on the original high-precision operands  */
+/* or on dequantized copies of the forward's NVFP4 operands [remio, section   */
+/* "Entrambe le ricette supportano ..."; lmsys, Recipe 2]; both modes reduce  */
+/* to the same BF16 GEMMs, only the operands differ.  A gathered row whose    */
+/* index is outside [0, src_rows) reads as zeros.                             */
+/* ------------------------------------------------------------------------ */
+
+static double bf16_at(const uint16_t *m, int64_t ld, int64_t r, int64_t k) {
+    return (double)orc_bf16_to_f32(m[r * ld + k]);
+}
+
+/* Row-grouped forms, C[r, n] for the rows listed in `rows` (all M rows when
+ * rows == NULL), t = gather[r] (or r) and e the group holding row r:
+ *   mode 0 (forward):       C[r, n] = sum_k A[t, k] * B_e[n, k], B [G, N, ldb]
+ *   mode 1 (data gradient): C[r, n] = sum_k A[t, k] * B_e[k, n], B [G, K, ldb]
+ * A is [src_rows, lda]; c and c_abs (sum_k |A B|) are [nrows, N]. */
+ORC_API void orc_gemm_bf16_rowgroup(int mode, const uint16_t *a, int64_t lda, int64_t src_rows, const uint16_t *b,
+                                    int64_t ldb, const int32_t *gather, const int64_t *group_offsets, int64_t G,
+                                    int64_t N, int64_t K, const int64_t *rows, int64_t nrows, double *c,
+                                    double *c_abs) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t r = rows ? rows[i] : i;
+        int64_t e = 0;
+        while (e < G && group_offsets[e + 1] <= r) e++;
+        int64_t t = gather ? (int64_t)gather[r] : r;
+        int valid = t >= 0 && t < src_rows;
+        const uint16_t *be = b + e * (mode == 0 ? N : K) * ldb;
+        for (int64_t n = 0; n < N; n++) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; valid && k < K; k++) {
+                double bv = mode == 0 ? bf16_at(be, ldb, n, k) : bf16_at(be, ldb, k, n);
+                double p = bf16_at(a, lda, t, k) * bv;
+                s += p;
+                sa += fabs(p);
+            }
+            c[i * N + n] = s;
+            if (c_abs) c_abs[i * N + n] = sa;
+        }
+    }
+}
+
+/* Weight-gradient form: for group g, reducing over the group's rows,
+ *   C_g[m, n] = sum_{r in [off[g], off[g+1])} A[r, m] * B[t, n],
+ * t = gather[r] (or r), A [off[G], lda], B [src_rows, ldb].  The (g, m)
+ * output rows to compute are listed in sel (pairs); c and c_abs are
+ * [nsel, N]. */
+ORC_API void orc_gemm_bf16_wgrad(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                                 const int32_t *gather, int64_t src_rows, const int64_t *group_offsets, int64_t N,
+                                 const int64_t *sel, int64_t nsel, double *c, double *c_abs) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nsel; i++) {
+        int64_t g = sel[2 * i], m = sel[2 * i + 1];
+        for (int64_t n = 0; n < N; n++) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t r = group_offsets[g]; r < group_offsets[g + 1]; r++) {
+                int64_t t = gather ? (int64_t)gather[r] : r;
+                if (t < 0 || t >= src_rows) continue;
+                double p = bf16_at(a, lda, r, m) * bf16_at(b, ldb, t, n);
+                s += p;
+                sa += fabs(p);
+            }
+            c[i * N + n] = s;
+            if (c_abs) c_abs[i * N + n] = sa;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* SwiGLU between the gate/up and down projections.                          */
 /* The pages give no arithmetic for it; the reading is h = silu(gate) * up    */
 /* with silu(z) = z / (1 + exp(-z)), gate = columns [0, I) and up = columns  */

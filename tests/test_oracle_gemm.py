@@ -1,8 +1,8 @@
 """Pins of the oracle's grouped GEMM reference and SwiGLU.
 
 GEMM: numpy float64 matmul (a library routine) on operands decoded
-independently (the pages' E2M1 value set and torch's float8 decode), and
-identity-weight cases whose result is known in closed form.
+independently (the pages' E2M1 value set, torch's float8 and bfloat16
+decodes), and identity-weight cases whose result is known in closed form.
 SwiGLU: the explicit f32 exp against numpy's exp (within 2 ulp), the silu
 formula in float64, and exact special values.
 """
@@ -113,6 +113,66 @@ def test_wgrad_matches_float64_matmul_per_group():
         n_g = off[g + 1] - off[g]
         ref2 = B[:, P[g]:P[g] + n_g] @ A[n, P[g]:P[g] + n_g]
         np.testing.assert_allclose(c[i], ref2, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def bf16_vals(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).double().numpy()
+
+
+def test_bf16_fprop_and_dgrad_match_float64_matmul():
+    T, E, k, N, K = 40, 3, 2, 24, 56
+    off, src = routing(T, E, k, 13)
+    x = synth.activations(14, T, K)
+    w_fp = synth.weights(15, E, N, K)                        # forward-form B [E, N, K]
+    w_dg = synth.weights(16, E, K, N)                        # data-gradient form B [E, K, N]
+    A = bf16_vals(x)
+    src = src.copy()
+    src[3] = -1                                              # out-of-range gathers read as zero rows
+    src[7] = T
+    c0, cabs0 = oracle.gemm_bf16_rowgroup(oracle.GEMM_FPROP, x, w_fp.reshape(E * N, K), src, off, N, K)
+    c1, _ = oracle.gemm_bf16_rowgroup(oracle.GEMM_DGRAD, x, w_dg.reshape(E * K, N), src, off, N, K)
+    B0 = bf16_vals(w_fp.reshape(E, N, K))
+    B1 = bf16_vals(w_dg.reshape(E, K, N))
+    for r in range(int(off[-1])):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        t = src[r]
+        a = A[t] if 0 <= t < T else np.zeros(K)
+        ref0 = B0[e] @ a
+        ref1 = a @ B1[e]
+        np.testing.assert_allclose(c0[r], ref0, rtol=1e-12, atol=1e-12 * max(np.abs(ref0).max(), 1e-300))
+        np.testing.assert_allclose(c1[r], ref1, rtol=1e-12, atol=1e-12 * max(np.abs(ref1).max(), 1e-300))
+        np.testing.assert_allclose(cabs0[r], np.abs(B0[e]) @ np.abs(a), rtol=1e-12)
+    assert not c0[3].any() and not c1[7].any()
+    # the two forms agree when B_e of one is the transpose of the other's
+    wt = np.ascontiguousarray(w_fp.reshape(E, N, K).transpose(0, 2, 1)).reshape(E * K, N)
+    c2, _ = oracle.gemm_bf16_rowgroup(oracle.GEMM_DGRAD, x, wt, src, off, N, K, rows=np.array([0, 9, 20]))
+    np.testing.assert_array_equal(c2, c0[[0, 9, 20]])
+
+
+def test_bf16_wgrad_matches_float64_matmul_per_group():
+    T, E, k, M, N = 30, 4, 2, 40, 24
+    off, src = routing(T, E, k, 17)
+    R = int(off[-1])
+    dy = synth.activations(18, R, M)                         # A: group rows in routed order
+    x = synth.activations(19, T, N)                          # B: gathered by the routing map
+    src = src.copy()
+    src[2] = -5
+    sel = np.array([[g, m] for g in range(E) for m in (0, 11, M - 1)], np.int64)
+    c, cabs = oracle.gemm_bf16_wgrad(dy, x, src, off, sel)
+    A = bf16_vals(dy)
+    X = bf16_vals(x)
+    Xg = np.where((src >= 0)[:, None], X[np.clip(src, 0, T - 1)], 0.0)
+    for i, (g, m) in enumerate(sel):
+        rows = slice(off[g], off[g + 1])
+        ref = A[rows, m] @ Xg[rows]
+        np.testing.assert_allclose(c[i], ref, rtol=1e-12, atol=1e-12 * max(np.abs(ref).max(), 1e-300))
+        np.testing.assert_allclose(cabs[i], np.abs(A[rows, m]) @ np.abs(Xg[rows]), rtol=1e-12)
+    # without a gather, B's rows are the group rows themselves
+    xr = synth.activations(20, R, N)
+    c3, _ = oracle.gemm_bf16_wgrad(dy, xr, None, off, sel[:3])
+    ref3 = A[off[0]:off[1]].T @ bf16_vals(xr)[off[0]:off[1]]
+    np.testing.assert_allclose(c3, ref3[[0, 11, M - 1]], rtol=1e-12, atol=1e-12 * np.abs(ref3).max())
 
 
 def test_exp_f32_within_two_ulp_of_numpy():
