@@ -66,6 +66,12 @@ BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t 
     return (size_t)bsp::gemm_workspace_bytes(fmt, mode, M, N, K, G);
 }
 
+BSP_EXPORT size_t bsp_gemm_bf16_workspace_size(int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
+    if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return 0;
+    return (size_t)bsp::gemm_bf16_workspace_bytes(mode, M, G);
+}
+
 BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                                                    int64_t rows_per_scale, uint8_t *codes, uint8_t *scales,
                                                    float *outer, uint32_t flags, void *stream) {
@@ -184,6 +190,48 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
         return BSP_ERR_ALIGNMENT;
     return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
                                        b_codes, b_scales, b_outer, c, c_dtype, ldc, workspace, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b,
+                                                int64_t ldb, const int32_t *gather, int64_t src_rows,
+                                                const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                int64_t K, void *c, int c_dtype, int64_t ldc, void *workspace,
+                                                size_t ws_bytes, void *stream) {
+    if (!a || !b || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return BSP_ERR_INVALID_ARG;
+    if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
+    if (G < 1 || M <= 0 || N <= 0 || K <= 0 || src_rows <= 0 || ldc < N) return BSP_ERR_SHAPE;
+    if (G >= (1ll << 23)) return BSP_ERR_SHAPE;
+    const bool wg = mode == BSP_GEMM_WGRAD;
+    // Operand rows are fetched in 16-byte pieces (8 elements) along their
+    // contiguous dimension: K for K-major operands, M or N for MN-major ones.
+    if (wg) {
+        if (M % 8 || N % 8 || lda < M || ldb < N) return BSP_ERR_SHAPE;
+        if (!gather && src_rows != K) return BSP_ERR_SHAPE;
+    } else {
+        if (K % 8 || lda < K) return BSP_ERR_SHAPE;
+        if (mode == BSP_GEMM_FPROP && ldb < K) return BSP_ERR_SHAPE;
+        if (mode == BSP_GEMM_DGRAD && (N % 8 || ldb < N)) return BSP_ERR_SHAPE;
+        if (!gather && src_rows != M) return BSP_ERR_SHAPE;
+    }
+    // The kernel keeps sizes, tile counts and per-lane byte offsets in 32 bits.
+    {
+        const int64_t lim31 = (1ll << 31) - 1, lim32 = 1ll << 32;
+        if (M > lim31 || N > lim31 || K > lim31 || ldc > lim31 || src_rows > lim31) return BSP_ERR_SHAPE;
+        if (lda >= (1ll << 26) || ldb >= (1ll << 26)) return BSP_ERR_SHAPE;
+        if (!wg && (src_rows * lda * 2 >= lim32 || (mode == BSP_GEMM_FPROP && N * ldb * 2 >= lim32)))
+            return BSP_ERR_SHAPE;
+        const int64_t tiles = wg ? G * ((M + 127) / 128) * ((N + 127) / 128) : ((M + 127) / 128 + G) * ((N + 127) / 128);
+        if (tiles > lim31) return BSP_ERR_SHAPE;
+    }
+    const size_t need = bsp_gemm_bf16_workspace_size(mode, M, N, K, G);
+    if (need > 0 && (!workspace || ws_bytes < need)) return BSP_ERR_WORKSPACE;
+    if (lda % 8 || ldb % 8) return BSP_ERR_ALIGNMENT;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(group_offsets) || !aligned16(c) ||
+        !aligned16_or_null(workspace) || !aligned16_or_null(gather))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_gemm_bf16(mode, a, lda, b, ldb, gather, src_rows, group_offsets, G, M, N, K, c,
+                                            c_dtype, ldc, workspace, as_stream(stream)));
 }
 
 BSP_EXPORT bsp_status bsp_swiglu_quantize(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out,

@@ -57,8 +57,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int GBK = 64;    // K values per stage
+constexpr int GBK = 64;    // K values per stage (block-scaled formats)
+constexpr int FMT_BF16 = 2;   // plain bf16 operands (internal format tag of the BF16 GEMM)
 constexpr int NXCD = 8;
 constexpr int kMaxDevices = 64;
 
@@ -81,6 +85,11 @@ struct GemmArgs {
     // one byte per (block, row), rows of the A plane in tile-list order.
     const uint8_t *a_plane, *b_plane;
     int32_t a_rp, b_rp, nbp;
+    // BF16 GEMM: bytes per operand row, and (weight-gradient form) the gather
+    // of B's rows with B's row count.
+    int32_t lda_b, ldb_b;
+    const int32_t *b_gather;
+    int32_t b_rows;
 };
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
@@ -208,17 +217,24 @@ __global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
 // Square output tiles of BT x BT (BT = 128 or 256) on BT / 32 wavefronts in
 // 2 x (BT / 64): each wavefront owns (BT / 2) x 64 outputs, i.e. TI x 2
 // MFMA blocks of 32 x 32.
+// BF16 stages hold 32 K values in the MXFP8 geometry (64 bytes per K-major
+// row); an operand stored with its M or N dimension contiguous (MN-major,
+// BF16 only) occupies the same bytes as 32 K rows of BT elements.
 template <int FMT, int BT>
 struct Geo {
     static constexpr bool MX = FMT == BSP_FMT_MXFP8;
+    static constexpr bool BF = FMT == FMT_BF16;
+    static constexpr int BK = BF ? 32 : GBK;           // K values per stage
     static constexpr int NW = BT / 32;                 // wavefronts
     static constexpr int TI = BT / 64;                 // 32-row MFMA blocks per wavefront
-    static constexpr int ROWB = MX ? 64 : 32;          // code bytes per row per stage
+    static constexpr int ROWB = (MX || BF) ? 64 : 32;  // code bytes per row per stage
     static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
     static constexpr int CODE = BT * ROWB;             // one operand's codes per stage
     static constexpr int CIW = CODE / 1024 / NW;       // 1 KB DMA loads per wavefront per operand
+    static constexpr int RPI = 64 / (BT / 8);          // MN-major K rows per wavefront DMA load
+    static constexpr int KPW = CIW * RPI;              // MN-major K rows per wavefront per stage
     static constexpr int SBLK = MX ? 32 : 16;          // values per scale
-    static constexpr int SPS = GBK / SBLK;             // scales per row per stage
+    static constexpr int SPS = BF ? 0 : GBK / SBLK;    // scales per row per stage
     static constexpr int SCLB = SPS * BT;              // scale bytes per operand per stage: [SPS][BT]
     static constexpr int A_SCL = 2 * CODE;
     static constexpr int B_SCL = 2 * CODE + SCLB;
@@ -234,8 +250,13 @@ struct Geo {
 // of 8 (or 16) rows served together lands on distinct LDS banks.
 template <int FMT>
 __device__ __forceinline__ int swz(int r) {
-    return FMT == BSP_FMT_MXFP8 ? (((r >> 1) ^ (r >> 3)) & 3) : (((r >> 2) ^ (r >> 3)) & 1);
+    return FMT == BSP_FMT_NVFP4 ? (((r >> 2) ^ (r >> 3)) & 1) : (((r >> 1) ^ (r >> 3)) & 3);
 }
+// MN-major stages: K row k holds BT / 8 chunks of 8 elements, chunk c stored
+// at position c ^ swz_mn(k).  A transposed fragment read (below) touches 8 K
+// rows, four consecutive ones twice, 64 bytes each; the XOR moves the four
+// consecutive rows to distinct 64-byte bank windows.
+__device__ __forceinline__ int swz_mn(int k) { return 4 * (k & 3); }
 
 // LDS-DMA: every lane fetches `size` bytes from its own global address; the
 // wavefront's data lands contiguously at M0 + lane * size.  Issued as inline assembly: the
@@ -332,8 +353,9 @@ struct Tile {
     int slot;   // row-tile index (row-grouped form: position in the tile list)
 };
 
-template <int MODE, int BT>
+template <int FMT, int MODE, int BT>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
+    constexpr int BK = Geo<FMT, BT>::BK;
     Tile T;
     const int ty = lin / p.ntn, tx = lin - ty * p.ntn;
     if (MODE == BSP_GEMM_WGRAD) {
@@ -341,11 +363,13 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
         T.g = ty / mt_per_g;
         T.row0 = (ty - T.g * mt_per_g) * BT;
         T.row_end = p.M;
-        const int64_t kb = p.tiles[T.g];
-        const int64_t ke = kb + (p.group_offsets[T.g + 1] - p.group_offsets[T.g] + 31) / 32 * 32;
+        // MXFP8: the group's padded token columns; BF16: the group's rows
+        const int64_t kb = FMT == FMT_BF16 ? p.group_offsets[T.g] : p.tiles[T.g];
+        const int64_t ke = FMT == FMT_BF16 ? p.group_offsets[T.g + 1]
+                                           : kb + (p.group_offsets[T.g + 1] - p.group_offsets[T.g] + 31) / 32 * 32;
         // offsets are trusted only up to the copies' width
-        T.kbeg = (int)(kb < p.K ? kb : p.K);
-        T.kend = (int)(ke < p.K ? ke : p.K);
+        T.kbeg = (int)(kb < 0 ? 0 : kb < p.K ? kb : p.K);
+        T.kend = (int)(ke < 0 ? 0 : ke < p.K ? ke : p.K);
     } else {
         const int64_t tile = p.tiles[ty];   // valid: ty < the listed tile count
         T.g = (int)(tile >> 40);
@@ -357,7 +381,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
     }
     T.col0 = tx * BT;
     T.slot = ty;
-    T.nk = T.kend > T.kbeg ? (T.kend - T.kbeg + GBK - 1) / GBK : 0;
+    T.nk = T.kend > T.kbeg ? (T.kend - T.kbeg + BK - 1) / BK : 0;
     return T;
 }
 
@@ -373,8 +397,14 @@ template <int FMT, int MODE, bool BF16OUT, int BT>
 __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     using GG = Geo<FMT, BT>;
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
-    constexpr bool MX = GG::MX;
+    constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
+    // BF16 operand layouts: the forward form takes both operands K-major; the
+    // data-gradient form takes B as the forward weight is stored ([K, N] per
+    // expert, N contiguous); the weight-gradient form reduces over rows, so
+    // both operands arrive with M or N contiguous.
+    constexpr bool A_MN = BF && WG, B_MN = BF && MODE != BSP_GEMM_FPROP;
+    constexpr int RP = BT * 2;                         // bytes of an MN-major K row in LDS
     constexpr int SEEK = 1, FIN = 2;
     // Ring of four K stages.
     __shared__ __attribute__((aligned(16))) uint8_t ring[4 * SLOT_BYTES];
@@ -382,7 +412,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     // reads as zero) and, for NVFP4, the row's outer scale times the expert's.
     // The producer runs at most 3 stages, hence at most 4 tiles, ahead.
     __shared__ int32_t rowtok[8][BT];
-    __shared__ float rowmul[MX ? 1 : 8][BT];
+    __shared__ float rowmul[NV ? 8 : 1][BT];
 
     const int t = threadIdx.x, l = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -390,7 +420,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     const int lr = l & 31, lh = l >> 5;
     const uint32_t ring_lds = lds_addr(ring);
 
-    const uint32_t ldA = MX ? p.K : p.K / 2;           // code bytes per row (A and B)
+    // bytes per operand row
+    const uint32_t ldA = BF ? (uint32_t)p.lda_b : MX ? p.K : p.K / 2;
+    const uint32_t ldB = BF ? (uint32_t)p.ldb_b : ldA;
 
     // ---- static tile sequence of this workgroup ----
     int first, stride, last;
@@ -413,9 +445,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     // Rows 32 apart share the swizzle, so one offset per operand serves all
     // of the wavefront's blocks (plus 32 * ROWB bytes per block).
     uint32_t fa0, fa1, fb0, fb1, fsa, fsb;
+    // MN-major operands: base offset of this lane's transposed reads for each
+    // 32-wide block (see mn_frag).
+    uint32_t tra[A_MN ? TI : 1], trb[B_MN ? 2 : 1];
     {
         const int ra = wm * (BT / 2) + lr, rb = wn * 64 + lr;
-        if (MX) {
+        if (MX || BF) {
             fa0 = ra * 64 + 16 * (lh ^ swz<FMT>(ra));
             fa1 = ra * 64 + 16 * ((2 + lh) ^ swz<FMT>(ra));
             fb0 = GG::CODE + rb * 64 + 16 * (lh ^ swz<FMT>(rb));
@@ -427,6 +462,22 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         // MXFP8 lane half h reads block h's byte; NVFP4 blocks 2h and 2h + 1
         fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
         fsb = GG::B_SCL + (MX ? lh : 2 * lh) * BT + rb;
+        // A transposed read (DS_READ_B64_TR_B16) works on groups of 16 lanes:
+        // in-group lane 4 e + c gives the address of 4 consecutive elements
+        // (piece c) of K row e, and in-group lane j receives element j of the
+        // 16 columns from each of the 4 rows.  Lane group q = l / 16 serves
+        // K rows 8 (q / 2) + 0..3 (lane half = K half) and columns
+        // 16 (q % 2) + 0..15 of the block.
+        const int q4 = l >> 4, e4 = (l >> 2) & 3, c4 = l & 3;
+        auto tr_base = [&](int col) __attribute__((always_inline)) -> uint32_t {
+            const int krow = 8 * (q4 >> 1) + e4;    // krow & 3 == e4
+            const int chunk = (col >> 3) + 2 * (q4 & 1) + (c4 >> 1);
+            return (uint32_t)(krow * RP + ((chunk ^ swz_mn(krow)) << 4) + 8 * (c4 & 1));
+        };
+#pragma unroll
+        for (int i = 0; i < (A_MN ? TI : 1); i++) tra[i] = tr_base(wm * (BT / 2) + 32 * i);
+#pragma unroll
+        for (int j = 0; j < (B_MN ? 2 : 1); j++) trb[j] = GG::CODE + tr_base(wn * 64 + 32 * j);
     }
 
     // ---- producer state: next stage to fetch ----
@@ -438,9 +489,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     uint32_t poa[GG::CIW], pob[GG::CIW];              // this lane's code chunk offsets
     // Scale DMA (wavefronts w < SCI): operand and 256-byte piece of its
     // [SPS][BT] stage region; this lane covers block sbl, rows sr0..sr0+3.
-    const bool scl_w = w < GG::SCI;
+    constexpr int SCH = GG::SCI > 0 ? GG::SCI / 2 : 1;
+    const bool scl_w = GG::SCI > 0 && w < GG::SCI;
     const bool scl_b = w >= GG::SCI / 2;
-    const int scl_o = 256 * (w % (GG::SCI / 2)) + 4 * l;
+    const int scl_o = 256 * (w % SCH) + 4 * l;
     const int sbl = scl_o / BT, sr0 = scl_o % BT;
     const uint32_t psv = (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;   // lane offset in the plane
     const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
@@ -454,12 +506,46 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         return (tok >= 0 && tok < p.a_rows) ? tok : -1;
     };
 
+    // BF16 producer set-up for tile PT.  K-major operands as for MXFP8 (unit u
+    // = 64 (w CIW + j) + l covers row u / 4, chunk position u % 4; per-stage
+    // offset 64 bytes); MN-major units cover K row u / (BT / 8), chunk
+    // position u % (BT / 8).  Columns past the operand's width read its last
+    // chunk (their outputs are discarded).
+    auto bf_seek = [&](int ord) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < GG::CIW; j++) {
+            const int u = 64 * (w * GG::CIW + j) + l;
+            const int r = u / GG::CH, cp = u % GG::CH, c = cp ^ swz<FMT>(r);
+            const int kr = u / (BT / 8), cm = (u % (BT / 8)) ^ swz_mn(kr);
+            if constexpr (A_MN) {
+                const int col = PT.row0 + 8 * cm < p.M - 8 ? PT.row0 + 8 * cm : p.M - 8;
+                poa[j] = (uint32_t)kr * ldA + 2 * col;
+            } else {
+                const int s = a_src(PT, r);
+                if (cp == 0) rowtok[ord][r] = s;
+                poa[j] = (uint32_t)(s >= 0 ? s : 0) * ldA + 16 * c;
+            }
+            if constexpr (B_MN) {
+                const int col = PT.col0 + 8 * cm < p.N - 8 ? PT.col0 + 8 * cm : p.N - 8;
+                pob[j] = (WG ? 0u : (uint32_t)kr * ldB) + 2 * col;
+            } else {
+                const int n = PT.col0 + r < p.N ? PT.col0 + r : p.N - 1;
+                pob[j] = (uint32_t)n * ldB + 16 * c;
+            }
+        }
+        // A: weight-gradient form from the group's first row; B: the expert's
+        // matrix ([N, K] forward form, [K, N] data-gradient form) or, in the
+        // weight-gradient form, rows addressed one by one through the gather
+        pca = p.a_codes + (WG ? (size_t)PT.kbeg * ldA : 0);
+        pcb = p.b_codes + (WG ? 0 : (size_t)PT.g * (B_MN ? p.K : p.N) * ldB);
+    };
+
     // Move the producer to the next tile with K work and set up this lane's
     // sources.  Tiles without K work (empty experts in the weight-gradient
     // form) are only written by the consumer.
     auto prod_seek = [&]() __attribute__((always_inline)) {
         while (p_lin < last) {
-            PT = decode_tile<MODE, BT>(p, p_lin);
+            PT = decode_tile<FMT, MODE, BT>(p, p_lin);
             if (PT.nk > 0) break;
             p_lin += stride;
             p_ord++;
@@ -471,6 +557,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         p_kt = 0;
         p_nk = PT.nk;
         const int ord = p_ord & 7;
+        if constexpr (BF) {
+            bf_seek(ord);
+            return;
+        }
         pca = p.a_codes + (WG ? PT.kbeg : 0);
         pcb = p.b_codes + (WG ? (size_t)PT.kbeg : (size_t)PT.g * p.N * ldA);
         // codes: unit u = 64 (w CIW + j) + l covers row u / CH, chunk position u % CH
@@ -486,7 +576,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 const int s = a_src(PT, r);
                 if (cp == 0) {
                     rowtok[ord][r] = s;
-                    if (!MX) rowmul[MX ? 0 : ord][r] = s >= 0 ? p.a_outer[s] * p.b_outer[PT.g] : 0.0f;
+                    if (NV) rowmul[NV ? ord : 0][r] = s >= 0 ? p.a_outer[s] * p.b_outer[PT.g] : 0.0f;
                 }
                 ar = s >= 0 ? s : 0;   // rows outside the tile or with a bad index read row 0, result discarded
             }
@@ -501,12 +591,86 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         }
     };
 
+    // BF16 stage fetch: 32 K values from k0.  K values past the tile's K end
+    // (chunks of K-major rows, whole K rows of MN-major operands) load zeros.
+    auto bf_issue = [&](uint32_t m0) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(PT.kbeg + p_kt * GG::BK);
+        const int kend = __builtin_amdgcn_readfirstlane(PT.kend);
+        const bool full = k0 + GG::BK <= kend;
+        const uint32_t kb = p_kt * GG::ROWB;
+        // K-major operand: chunk c of the row holds K values k0 + 8 c.
+        auto kmajor = [&](const uint8_t *base, const uint32_t *off, uint32_t dst) __attribute__((always_inline)) {
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < GG::CIW; j++) dma16(base + kb, off[j], dst + (w * GG::CIW + j) * 1024);
+            } else {
+#pragma unroll
+                for (int j = 0; j < GG::CIW; j++) {
+                    const int u = 64 * (w * GG::CIW + j) + l;
+                    const int c = (u % GG::CH) ^ swz<FMT>(u / GG::CH);
+                    dma16v(k0 + 8 * c >= kend ? kZeroChunk : base + kb + off[j], dst + (w * GG::CIW + j) * 1024);
+                }
+            }
+        };
+        // MN-major operand with consecutive K rows: K row kr of the stage is
+        // row (first + kr) of the matrix at `base`.
+        auto mnmajor = [&](const uint8_t *base, const uint32_t *off, uint32_t dst) __attribute__((always_inline)) {
+            if (full) {
+#pragma unroll
+                for (int j = 0; j < GG::CIW; j++) dma16(base, off[j], dst + (w * GG::CIW + j) * 1024);
+            } else {
+#pragma unroll
+                for (int j = 0; j < GG::CIW; j++) {
+                    const int kr = (64 * (w * GG::CIW + j) + l) / (BT / 8);
+                    dma16v(k0 + kr >= kend ? kZeroChunk : base + off[j], dst + (w * GG::CIW + j) * 1024);
+                }
+            }
+        };
+        if constexpr (A_MN) mnmajor(uniform_ptr(pca + (size_t)p_kt * GG::BK * ldA), poa, m0);
+        else kmajor(pca, poa, m0);
+        if constexpr (!B_MN) {
+            kmajor(pcb, pob, m0 + GG::CODE);
+        } else if constexpr (!WG) {
+            mnmajor(uniform_ptr(pcb + (size_t)k0 * ldB), pob, m0 + GG::CODE);
+        } else {
+            // Weight-gradient form: K row kr is row gather[k0 + kr] of B (or
+            // row k0 + kr).  The wavefront's KPW indices come through scalar
+            // loads (the pipeline's vector-memory waits count DMA loads only);
+            // indices past the K end are clamped to the last row and their
+            // chunks load zeros, as do rows with an index outside B.
+            typedef const __attribute__((address_space(4))) int32_t cint32;
+            const cint32 *gq = (const cint32 *)p.b_gather;
+            int32_t tq[GG::KPW];
+#pragma unroll
+            for (int q = 0; q < GG::KPW; q++) {
+                const int kr = k0 + GG::KPW * w + q;
+                const int idx = kr < kend ? kr : kend - 1;
+                tq[q] = p.b_gather ? gq[idx] : idx;
+            }
+#pragma unroll
+            for (int j = 0; j < GG::CIW; j++) {
+                const int sub = l / (BT / 8);
+                int32_t tr = tq[j * GG::RPI];
+#pragma unroll
+                for (int q = 1; q < GG::RPI; q++) tr = sub == q ? tq[j * GG::RPI + q] : tr;
+                const int kr = GG::KPW * w + j * GG::RPI + sub;
+                const bool ok = k0 + kr < kend && tr >= 0 && tr < p.b_rows;
+                dma16v(ok ? pcb + (size_t)tr * ldB + pob[j] : kZeroChunk,
+                       m0 + GG::CODE + (w * GG::CIW + j) * 1024);
+            }
+        }
+    };
+
     // Fetch the producer's next stage into ring stage `slot`.
     auto issue = [&](int slot) __attribute__((always_inline)) {
         // Opaque per call: hoisted out of the loop, the LDS addresses of every
         // ring stage and DMA would each hold a scalar register.
         uint32_t m0 = ring_lds + slot * SLOT_BYTES;
         asm volatile("" : "+s"(m0));
+        if constexpr (BF) {
+            bf_issue(m0);
+            return;
+        }
         const int k0 = PT.kbeg + p_kt * GBK;
         const uint32_t kb = p_kt * GG::ROWB, so = p_kt * GG::SPS;
         if (k0 + GBK / 2 < PT.kend) {
@@ -531,7 +695,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         // scale bytes of the stage: SPS plane rows (padded past the K end)
         if (scl_w)
             dma4(uniform_ptr(psbase + (size_t)so * (scl_b ? p.b_rp : p.a_rp)), psv,
-                 m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 256 * (w % (GG::SCI / 2)));
+                 m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 256 * (w % SCH));
     };
 
     // ---- consumer state ----
@@ -569,7 +733,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const uint8_t *slot = ring + soff;
         const int nv = live_blocks();
         if (nv == 0) return;
-        if (MX) {
+        if constexpr (MX) {
             // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
             // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
             // low byte of the scale operand is read).  Block i + 1's A
@@ -604,6 +768,40 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                                         (int)b1[j].x, (int)b1[j].y, (int)b1[j].z, (int)b1[j].w};
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[i][j], 0, 0, 0,
                                                                                     (int)as[i], 0, (int)bs[j]);
+                    }
+                }
+            }
+        } else if constexpr (BF) {
+            // MFMA s covers K values 16 s + 0..15 of the stage, lane half h
+            // supplying 16 s + 8 h + 0..7 of its row (A) or column (B):
+            // K-major operands read chunk 2 s + h of the row (fa0 / fa1 as
+            // for MXFP8), MN-major ones two transposed reads of 4 K rows.
+            auto kfrag = [&](uint32_t off) __attribute__((always_inline)) -> v8bf {
+                return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4 *>(slot + off));
+            };
+            auto mfrag = [&](uint32_t off) __attribute__((always_inline)) -> v8bf {
+                typedef __attribute__((address_space(3))) v4s lds_v4s;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(slot + off));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(slot + off + 4 * RP));
+                return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++) {
+                v8bf fa[TI], fb[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    fb[j] = B_MN ? mfrag(trb[B_MN ? j : 0] + 16 * s2 * RP) : kfrag((s2 ? fb1 : fb0) + 32 * 64 * j);
+                fa[0] = A_MN ? mfrag(tra[0] + 16 * s2 * RP) : kfrag(s2 ? fa1 : fa0);
+#pragma unroll
+                for (int i = 0; i < TI; i++) {
+                    if (i + 1 < TI)
+                        fa[i + 1] = A_MN ? mfrag(tra[A_MN ? i + 1 : 0] + 16 * s2 * RP)
+                                         : kfrag((s2 ? fa1 : fa0) + 32 * 64 * (i + 1));
+                    asm volatile("" ::: "memory");
+                    if (i < nv) {
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
                     }
                 }
             }
@@ -681,8 +879,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             for (int e = 0; e < 16; e++) {
                 const int rt = wm * (BT / 2) + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
                 if (WG) mul[e] = 1.0f;
-                else if (MX) mul[e] = rowtok[ord][rt] >= 0 ? 1.0f : 0.0f;
-                else mul[e] = rowmul[MX ? 0 : ord][rt];
+                else if (!NV) mul[e] = rowtok[ord][rt] >= 0 ? 1.0f : 0.0f;
+                else mul[e] = rowmul[NV ? ord : 0][rt];
             }
 #pragma unroll
             for (int j0 = 0; j0 < 2; j0 += NJ) {
@@ -746,7 +944,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             c_done = true;
             return;
         }
-        CT = decode_tile<MODE, BT>(p, c_lin);
+        CT = decode_tile<FMT, MODE, BT>(p, c_lin);
         c_kt = 0;
         cons_begin();
     };
@@ -757,7 +955,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     waitcnt<63, 0>();
     barrier();   // row table of the first tile is visible
     if (!c_done) {
-        CT = decode_tile<MODE, BT>(p, c_lin);
+        CT = decode_tile<FMT, MODE, BT>(p, c_lin);
         cons_begin();
     }
     for (int s = 0; s < 3 && !p_done; s++) {
@@ -900,7 +1098,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
                        int64_t M, int64_t N, int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
                        const float *b_outer, void *c, int c_dtype, int64_t ldc, void *workspace, hipStream_t s) {
     const WsLayout L = ws_layout(fmt, mode, M, N, K, G);
-    GemmArgs p;
+    GemmArgs p = {};
     p.a_codes = a_codes; p.a_scales = a_scales; p.a_outer = a_outer; p.a_gather = a_gather;
     p.group_offsets = group_offsets; p.b_codes = b_codes; p.b_scales = b_scales; p.b_outer = b_outer;
     p.c = c; p.G = (int32_t)G; p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K; p.ldc = (int32_t)ldc;
@@ -949,6 +1147,55 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     } else {
         if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 128>(p, bf, s);
         else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 128>(p, bf, s);
+    }
+    return hipGetLastError();
+}
+
+// BF16 grouped GEMM.  Workspace: the row-tile list and counters of the
+// row-grouped forms; the weight-gradient form needs none.
+int64_t gemm_bf16_workspace_bytes(int mode, int64_t M, int64_t G) {
+    if (mode == BSP_GEMM_WGRAD) return 0;
+    return up((gemm_tile_count(M, G) + kGemmSchedSlots) * 8, 256);
+}
+
+hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                            const int32_t *gather, int64_t src_rows, const int64_t *group_offsets, int64_t G,
+                            int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *workspace,
+                            hipStream_t s) {
+    GemmArgs p = {};
+    const bool wg = mode == BSP_GEMM_WGRAD;
+    p.a_codes = reinterpret_cast<const uint8_t *>(a);
+    p.b_codes = reinterpret_cast<const uint8_t *>(b);
+    p.group_offsets = group_offsets;
+    p.a_gather = wg ? nullptr : gather;
+    p.b_gather = wg ? gather : nullptr;
+    p.a_rows = (int32_t)(wg ? K : src_rows);
+    p.b_rows = (int32_t)(wg ? src_rows : 0);
+    p.lda_b = (int32_t)(2 * lda);
+    p.ldb_b = (int32_t)(2 * ldb);
+    p.c = c; p.G = (int32_t)G; p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K; p.ldc = (int32_t)ldc;
+    const bool bf = c_dtype == BSP_DTYPE_BF16;
+    if (wg) {
+        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
+        p.ntn = (int32_t)((N + bt - 1) / bt);
+        p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
+        if (bt == 256) launch_k<FMT_BF16, BSP_GEMM_WGRAD, 256>(p, bf, s);
+        else launch_k<FMT_BF16, BSP_GEMM_WGRAD, 128>(p, bf, s);
+        return hipGetLastError();
+    }
+    int64_t *ws = reinterpret_cast<int64_t *>(workspace);
+    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256));
+    p.ntn = (int32_t)((N + bt - 1) / bt);
+    p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
+    p.tiles = ws;
+    p.sched = ws + gemm_tile_count(M, G);
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
+    if (mode == BSP_GEMM_DGRAD) {
+        if (bt == 256) launch_k<FMT_BF16, BSP_GEMM_DGRAD, 256>(p, bf, s);
+        else launch_k<FMT_BF16, BSP_GEMM_DGRAD, 128>(p, bf, s);
+    } else {
+        if (bt == 256) launch_k<FMT_BF16, BSP_GEMM_FPROP, 256>(p, bf, s);
+        else launch_k<FMT_BF16, BSP_GEMM_FPROP, 128>(p, bf, s);
     }
     return hipGetLastError();
 }

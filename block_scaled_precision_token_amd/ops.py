@@ -34,6 +34,7 @@ EXPORTED = [
     "bsp_version", "bsp_status_string", "bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize",
     "bsp_requant_transpose_sr", "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes",
     "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
+    "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size",
 ]
 
 
@@ -64,6 +65,10 @@ def _declare(lib):
     lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
     lib.bsp_moe_grouped_gemm_blockscaled.argtypes = [INT, INT, P, P, P, P, I64, P, I64, I64, I64, I64, P, P, P, P,
                                                      INT, I64, P, SZ, P]
+    lib.bsp_moe_grouped_gemm_bf16.argtypes = [INT, P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, INT, I64, P,
+                                              SZ, P]
+    lib.bsp_gemm_bf16_workspace_size.argtypes = [INT, I64, I64, I64, I64]
+    lib.bsp_gemm_bf16_workspace_size.restype = SZ
     lib.bsp_swiglu_quantize.argtypes = [P, INT, I64, I64, P, INT, P, P, P, U32, P]
     lib.bsp_nvfp4_sizes.argtypes = [I64, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     lib.bsp_mxfp8_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
@@ -74,7 +79,8 @@ def _declare(lib):
     lib.bsp_gemm_workspace_size.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.bsp_gemm_workspace_size.restype = SZ
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
-                 "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes"):
+                 "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
+                 "bsp_moe_grouped_gemm_bf16"):
         getattr(lib, name).restype = INT
 
 
@@ -263,6 +269,44 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
                                                      _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt,
                                                      ldc, _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "bsp_moe_grouped_gemm_blockscaled")
+    return out
+
+
+def gemm_bf16_workspace_size(mode: int, M: int, N: int, K: int, G: int) -> int:
+    return _lib_raw().bsp_gemm_bf16_workspace_size(mode, M, N, K, G)
+
+
+def moe_grouped_gemm_bf16(mode: int, a: torch.Tensor, b: torch.Tensor, group_offsets, N: int, K: int,
+                          M: int | None = None, gather=None, out_dtype=torch.float32, out=None, workspace=None):
+    """BF16 grouped GEMM; see bsp_moe_grouped_gemm_bf16 in include/bsp.h.
+
+    FPROP: a [src_rows, K], b [G*N, K] (or [G, N, K]); DGRAD: b [G*K, N] (or
+    [G, K, N]); C [M, N] with M = rows of C (gather length, else a's rows).
+    WGRAD: a [K, M] (K = grouped rows), b [src_rows, N]; C [G, M, N].
+    """
+    _need_cuda(a, "a")
+    dev = a.device
+    G = group_offsets.numel() - 1
+    if mode == GEMM_WGRAD:
+        M = a.shape[1] if M is None else M
+        src_rows = b.shape[0]
+    else:
+        src_rows = a.shape[0]
+        if M is None:
+            M = gather.numel() if gather is not None else src_rows
+    if out is None:
+        shape = (G, M, N) if mode == GEMM_WGRAD else (M, N)
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    ldc = out.shape[-1]
+    dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    if workspace is None:
+        need = gemm_bf16_workspace_size(mode, M, N, K, G)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = _lib_raw().bsp_moe_grouped_gemm_bf16(mode, _ptr(a), a.stride(0) if a.dim() == 2 else a.shape[-1], _ptr(b),
+                                              b.shape[-1], _ptr(gather), src_rows, _ptr(group_offsets), G, M, N,
+                                              K, _ptr(out), dt, ldc, _ptr(workspace), ws_bytes, _stream(dev))
+    _check(st, "bsp_moe_grouped_gemm_bf16")
     return out
 
 

@@ -15,7 +15,10 @@
  *   - dequantize -> transpose -> requantize with stochastic rounding for the
  *     backward path [nopree.com, same page, section 第二个决定];
  *   - the block-scaled grouped expert GEMM (gate/up/down; forward, data and
- *     weight gradient) [alphasignal.ai, Recipe 1 and Recipe 2].
+ *     weight gradient) [alphasignal.ai, Recipe 1 and Recipe 2];
+ *   - the BF16 grouped expert GEMM of the NVFP4 recipe's backward pass, on the
+ *     original or on dequantized operands [remio.ai, section "Entrambe le
+ *     ricette supportano ..."; alphasignal.ai, Recipe 2].
  *
  * Conventions shared by every call:
  *   - Pointers named in the comments as "device" point to GPU memory; sizes
@@ -219,6 +222,51 @@ bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_
                                             void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * BF16 grouped expert GEMM for the backward pass of the NVFP4 MoE recipe,
+ * which runs its data- and weight-gradient GEMMs in BF16 [remio.ai, section
+ * "Entrambe le ricette supportano ...": either on the original high-precision
+ * operands, or on operands dequantized (bsp_dequantize) from the exact NVFP4
+ * values of the forward pass, which keeps the backward consistent with the
+ * forward; alphasignal.ai, Recipe 2].  Both modes are this one call; they
+ * differ only in the operands passed.  Operands are bf16, row-major, with
+ * leading dimensions lda, ldb in elements (multiples of 8).
+ *
+ * FPROP and DGRAD, rows of C grouped by expert (e = group holding row r,
+ * t = gather[r], or r when gather is NULL):
+ *   FPROP: C[r, n] = sum_k A[t, k] * B_e[n, k],  B [G, N, ldb]: forward weight
+ *   DGRAD: C[r, n] = sum_k A[t, k] * B_e[k, n],  B [G, K, ldb]: the forward
+ *          weight as stored ([out, in] per expert), so no transposed copy is
+ *          needed: dX = dY * W_e
+ *     a        device bf16 [src_rows, lda >= K]; K % 8 == 0
+ *     gather   device int32 [M] or NULL (then src_rows == M); a row with an
+ *              index outside [0, src_rows) reads as zeros
+ *     DGRAD: N % 8 == 0
+ *     C        device [M, ldc] of c_dtype; group_offsets: rows of C per
+ *              group, off[G] == M
+ * WGRAD, reducing over the rows of each group:
+ *   C_g[m, n] = sum_{r in [off[g], off[g+1])} A[r, m] * B[t, n],
+ *   t = gather[r] (or r): dW_e = dY_e^T * X_e with the routed rows of X read
+ *   through the routing map, and no transposed copies
+ *     a        device bf16 [K, lda >= M] (K = off[G], rows in grouped order)
+ *     b        device bf16 [src_rows, ldb >= N]
+ *     gather   device int32 [K] or NULL (then src_rows == K); an index
+ *              outside [0, src_rows) contributes nothing
+ *     M % 8 == 0, N % 8 == 0; C device [G, M, ldc] (group stride M * ldc)
+ * Accumulation is f32 on the MFMA units (V_MFMA_F32_32X32X16_BF16); bf16
+ * output is the RNE of the f32 sum.  Sizes below 2^31, lda and ldb below
+ * 2^26, A (FPROP/DGRAD) and one expert's B (FPROP) below 4 GiB, else
+ * BSP_ERR_SHAPE.
+ *   workspace  device, >= bsp_gemm_bf16_workspace_size(mode, M, N, K, G)
+ *              bytes (the row-tile list; WGRAD needs none and accepts NULL),
+ *              rewritten by every call: calls sharing one workspace must be
+ *              stream-ordered
+ */
+bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+                                     const int32_t *gather, int64_t src_rows, const int64_t *group_offsets,
+                                     int64_t G, int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
+                                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * SwiGLU between the gate/up and down projections, then quantization of its
  * output for the down GEMM [hackernews.jp, baseline recipe: the activation
  * quantizer is fused with the per-token scale computation].
@@ -247,6 +295,9 @@ int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
  * scales per 2048 rows (at most 1024 partials); 0 for M <= 0. */
 size_t bsp_requant_workspace_size(int64_t M);
 size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
+/* Bytes of workspace for bsp_moe_grouped_gemm_bf16 (0 for WGRAD and for
+ * invalid arguments). */
+size_t bsp_gemm_bf16_workspace_size(int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 
 #ifdef __cplusplus
 }

@@ -127,6 +127,33 @@ def test_gemm_rejects_bad_arguments():
     assert g(1, 0, A, A, None, None, 32, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 2   # a_rows != M
 
 
+def test_bf16_gemm_workspace_and_bad_arguments():
+    def up(x, a):
+        return (x + a - 1) // a * a
+    ws = L.bsp_gemm_bf16_workspace_size
+    assert ws(0, 65536, 2048, 768, 128) == up(((65536 + 127) // 128 + 128 + 16) * 8, 256)
+    assert ws(1, 65536, 2048, 768, 128) == ws(0, 65536, 2048, 768, 128)
+    assert ws(2, 2048, 768, 65536, 128) == 0         # the weight-gradient form needs no workspace
+    assert ws(5, 64, 64, 64, 1) == 0 and ws(0, 0, 64, 64, 1) == 0
+    g = L.bsp_moe_grouped_gemm_bf16
+    W = 1 << 16
+    # (mode, a, lda, b, ldb, gather, src_rows, off, G, M, N, K, c, c_dtype, ldc, ws, ws_bytes, stream)
+    assert g(3, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 1        # unknown mode
+    assert g(0, None, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 1     # null operand
+    assert g(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 60, A, 0, 64, A, W, None) == 2        # K % 8
+    assert g(0, A, 64, A, 64, None, 32, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 2        # src_rows != M
+    assert g(1, A, 64, A, 64, None, 64, A, 2, 64, 60, 64, A, 0, 64, A, W, None) == 2        # DGRAD N % 8
+    assert g(1, A, 64, A, 32, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 2        # DGRAD ldb < N
+    assert g(2, A, 64, A, 64, None, 100, A, 2, 64, 64, 64, A, 0, 64, None, 0, None) == 2    # src_rows != K
+    assert g(2, A, 60, A, 64, None, 64, A, 2, 60, 64, 64, A, 0, 64, None, 0, None) == 2     # WGRAD M % 8
+    assert g(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, 8, None) == 5        # workspace too small
+    assert g(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, None, 0, None) == 5     # workspace missing
+    assert g(0, A, 68, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 3        # lda % 8
+    assert g(0, MIS, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 3      # misaligned
+    # 32-bit limits: A of 2^32 bytes or more
+    assert g(0, A, 1024, A, 1024, A, 1 << 21, A, 2, 64, 64, 1024, A, 0, 64, A, W, None) == 2
+
+
 def test_python_binding_fails_loudly_without_device_tensors():
     import torch
     with pytest.raises(ValueError):
