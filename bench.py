@@ -8,7 +8,8 @@ hidden 7168, 256 routed + 1 shared expert, top-8, expert projections
 columnwise copies: per step the expert weights and the activations are
 quantized (row + column copies), then the forward (gate/up, SwiGLU + quantize,
 down), data-gradient and weight-gradient grouped GEMMs run.  Other workloads
-(--workload) time the Qwen3-30B-A3B-shaped NVFP4 forward, the MXFP8
+(--workload) time the Qwen3-30B-A3B-shaped NVFP4 forward, its BF16 backward
+GEMMs in the high-precision and the dequantized mode, the MXFP8
 quantization of 8192 x 2048 activations plus 128 expert weights, the
 16384 x 2048 requant with stochastic rounding, and the 256 x 2048 round trip.
 
@@ -306,6 +307,133 @@ class Qwen3MoeNvfp4:
                           f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
 
 
+class Qwen3MoeNvfp4Bwd:
+    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward GEMMs in BF16 (configs[3]
+    shapes): data- and weight-gradient GEMMs of the down and gate/up
+    projections, on the original bf16 operands (high-precision mode) or on
+    dequantized copies of the forward's NVFP4 operands (dequantized mode, the
+    four dequantizations timed inside the step).  The upstream gradients dY
+    [routed rows, hidden] and dH13 [routed rows, 2 x intermediate] are
+    synthetic N(0,1) with outliers (the SwiGLU backward between them is not on
+    the path)."""
+    unit = "TFLOP/s"
+    dtype = "bf16"
+    mode = "hp"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        T, H, I, E, k = 8192, 2048, 768, 128, 8
+        N13 = 2 * I
+        self.shape = dict(T=T, H=H, I=I, E=E, k=k)
+        bias = synth.zipf_bias(SEED + 4, E, 1.1)
+        off, src = synth.route_topk(SEED + 5, T, E, k, bias)
+        R = int(off[-1])
+        self.R, self.counts, self.off_h, self.src_h = R, np.diff(off), off, src
+        off_d = torch.from_numpy(off).to(dev)
+        src_d = torch.from_numpy(src).to(dev)
+        X = synth.device_activations(SEED + 6, T, H, dev)
+        W13 = synth.device_weights(SEED + 7, E, N13, H, dev)
+        W2 = synth.device_weights(SEED + 8, E, H, I, dev)
+        h = synth.device_activations(SEED + 9, R, I, dev, std=0.5)          # SwiGLU output of the forward
+        dY = synth.device_activations(SEED + 10, R, H, dev)
+        dH13 = synth.device_activations(SEED + 11, R, N13, dev)
+        self.X, self.W13, self.dH13 = X, W13, dH13
+        bf = torch.bfloat16
+        emp = lambda *s_, dt=bf: torch.empty(s_, dtype=dt, device=dev)
+        dh, dX = emp(R, I), emp(R, H)
+        dW2, dW13 = emp(E, H, I), emp(E, N13, H)
+        ws = emp(max(ops.gemm_bf16_workspace_size(ops.GEMM_DGRAD, R, n, kk, E) for n, kk in ((I, H), (H, N13))),
+                 dt=torch.uint8)
+        gm, DG, WG = ops.moe_grouped_gemm_bf16, ops.GEMM_DGRAD, ops.GEMM_WGRAD
+        self.ops = []
+        if self.mode == "deq":
+            # the forward's NVFP4 operands (quantized once here, as the forward would have)
+            xq = ops.quantize_nvfp4_per_token(X, mode46=True)
+            hq = ops.quantize_nvfp4_per_token(h, mode46=True)
+            w13q = ops.quantize_nvfp4_per_token(W13, rows_per_scale=N13)
+            w2q = ops.quantize_nvfp4_per_token(W2, rows_per_scale=H)
+            X, h, W13, W2 = emp(T, H), emp(R, I), emp(E * N13, H), emp(E * H, I)
+            s4 = 0.5 + 1 / 16
+            NV = ops.FMT_NVFP4
+            self.ops += [
+                Op("dequant_x", lambda: ops.dequantize(NV, *xq, out=X), T * H * (s4 + 2) + T * 4),
+                Op("dequant_h", lambda: ops.dequantize(NV, *hq, out=h), R * I * (s4 + 2) + R * 4),
+                Op("dequant_w13", lambda: ops.dequantize(NV, *w13q, rows_per_scale=N13, out=W13),
+                   E * N13 * H * (s4 + 2) + E * 4),
+                Op("dequant_w2", lambda: ops.dequantize(NV, *w2q, rows_per_scale=H, out=W2),
+                   E * H * I * (s4 + 2) + E * 4),
+            ]
+        self.ops += [
+            Op("gemm_dgrad_down", lambda: gm(DG, dY, W2, off_d, I, H, out=dh, workspace=ws),
+               R * H * 2 + E * H * I * 2 + R * I * 2, 2.0 * R * I * H, "bf16"),
+            Op("gemm_wgrad_down", lambda: gm(WG, dY, h, off_d, I, R, out=dW2),
+               R * H * 2 + R * I * 2 + E * H * I * 2, 2.0 * R * H * I, "bf16"),
+            Op("gemm_dgrad_gate_up", lambda: gm(DG, dH13, W13, off_d, H, N13, out=dX, workspace=ws),
+               R * N13 * 2 + E * N13 * H * 2 + R * H * 2, 2.0 * R * H * N13, "bf16"),
+            Op("gemm_wgrad_gate_up", lambda: gm(WG, dH13, X, off_d, H, R, gather=src_d, out=dW13),
+               R * N13 * 2 + T * H * 2 + E * N13 * H * 2, 2.0 * R * N13 * H, "bf16"),
+        ]
+        self.gemm_flops = sum(o.flops for o in self.ops)
+
+    def config(self):
+        import numpy as np
+        c = self.counts
+        name = {"hp": "high_precision", "deq": "dequantized"}[self.mode]
+        return {"workload": f"qwen3_30b_a3b_moe_layer_nvfp4_backward_bf16_{name}", "tokens": self.shape["T"],
+                "hidden": self.shape["H"], "expert_intermediate": self.shape["I"], "experts": self.shape["E"],
+                "topk": self.shape["k"], "routed_rows": self.R, "backward_mode": name,
+                "gradient_dtype": "bf16",
+                "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(np.median(c)),
+                               "min": int(c.min()), "empty": int((c == 0).sum())},
+                "gemm_flops_per_step": self.gemm_flops}
+
+    def value(self, ms_per_step):
+        return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def cpu_baseline(self, budget_s=10.0):
+        """Oracle on a sample: experts from the median load up, the data-gradient GEMM of up
+        to 128 of the expert's rows against its gate/up weight in fp64 (dequantized mode:
+        after the oracle's NVFP4 quantize + dequantize of those operands)."""
+        import numpy as np
+        import torch
+        import oracle
+        H, N13 = self.shape["H"], 2 * self.shape["I"]
+        order = np.argsort(self.counts)
+        order = np.concatenate([order[len(order) // 2:], order[:len(order) // 2]])
+        it = iter(order.tolist())
+        deq = self.mode == "deq"
+
+        def unit():
+            e = next(it)
+            w = self.W13[e * N13:(e + 1) * N13].view(torch.int16).cpu().numpy().view(np.uint16)
+            lo = int(self.off_h[e])
+            n = min(int(self.off_h[e + 1]) - lo, 128)
+            a = self.dH13[lo:lo + n].view(torch.int16).cpu().numpy().view(np.uint16)
+            if deq:
+                w = oracle.dequantize_nvfp4(*oracle.quantize_nvfp4(w, rows_per_scale=N13), rows_per_scale=N13)[1]
+            off = np.array([0, n], np.int64)
+            oracle.gemm_bf16_rowgroup(oracle.GEMM_DGRAD, a, w, None, off, H, N13)
+            return 2.0 * n * N13 * H
+
+        flops, dt, reps = timed_until(unit, budget_s, max_reps=len(order))
+        what = "NVFP4 quantize + dequantize of each expert's 1536x2048 gate/up weight, then " if deq else ""
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{reps} experts from the median load up: {what}the data-gradient GEMM of up to 128 of "
+                          f"its rows (dH13 x W13_e) in fp64 ({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+class Qwen3MoeNvfp4BwdHp(Qwen3MoeNvfp4Bwd):
+    name = "qwen3_moe_nvfp4_bwd_hp"
+    mode = "hp"
+
+
+class Qwen3MoeNvfp4BwdDeq(Qwen3MoeNvfp4Bwd):
+    name = "qwen3_moe_nvfp4_bwd_deq"
+    mode = "deq"
+
+
 class Mxfp8Quant:
     """MXFP8 rowwise + columnwise quantization of 8192 x 2048 activations and rowwise
     quantization of 128 expert weights 2048 x 768 (configs[1])."""
@@ -523,7 +651,8 @@ class HbmCopy:
         return None
 
 
-WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Mxfp8Quant, RequantSr, RoundTrip, HbmCopy)}
+WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq, Mxfp8Quant,
+                                  RequantSr, RoundTrip, HbmCopy)}
 
 
 # ---------------------------------------------------------------------------
