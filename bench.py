@@ -368,11 +368,11 @@ class Qwen3MoeNvfp4Bwd:
         self.ops += [
             Op("gemm_dgrad_down", lambda: gm(DG, dY, W2, off_d, I, H, out=dh, workspace=ws),
                R * H * 2 + E * H * I * 2 + R * I * 2, 2.0 * R * I * H, "bf16"),
-            Op("gemm_wgrad_down", lambda: gm(WG, dY, h, off_d, I, R, out=dW2),
+            Op("gemm_wgrad_down", lambda: gm(WG, dY, h, off_d, I, R, out=dW2, workspace=ws),
                R * H * 2 + R * I * 2 + E * H * I * 2, 2.0 * R * H * I, "bf16"),
             Op("gemm_dgrad_gate_up", lambda: gm(DG, dH13, W13, off_d, H, N13, out=dX, workspace=ws),
                R * N13 * 2 + E * N13 * H * 2 + R * H * 2, 2.0 * R * H * N13, "bf16"),
-            Op("gemm_wgrad_gate_up", lambda: gm(WG, dH13, X, off_d, H, R, gather=src_d, out=dW13),
+            Op("gemm_wgrad_gate_up", lambda: gm(WG, dH13, X, off_d, H, R, gather=src_d, out=dW13, workspace=ws),
                R * N13 * 2 + T * H * 2 + E * N13 * H * 2, 2.0 * R * N13 * H, "bf16"),
         ]
         self.gemm_flops = sum(o.flops for o in self.ops)

@@ -224,11 +224,10 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int
         const int64_t tiles = wg ? G * ((M + 127) / 128) * ((N + 127) / 128) : ((M + 127) / 128 + G) * ((N + 127) / 128);
         if (tiles > lim31) return BSP_ERR_SHAPE;
     }
-    const size_t need = bsp_gemm_bf16_workspace_size(mode, M, N, K, G);
-    if (need > 0 && (!workspace || ws_bytes < need)) return BSP_ERR_WORKSPACE;
+    if (!workspace || ws_bytes < bsp_gemm_bf16_workspace_size(mode, M, N, K, G)) return BSP_ERR_WORKSPACE;
     if (lda % 8 || ldb % 8) return BSP_ERR_ALIGNMENT;
-    if (!aligned16(a) || !aligned16(b) || !aligned16(group_offsets) || !aligned16(c) ||
-        !aligned16_or_null(workspace) || !aligned16_or_null(gather))
+    if (!aligned16(a) || !aligned16(b) || !aligned16(group_offsets) || !aligned16(c) || !aligned16(workspace) ||
+        !aligned16_or_null(gather))
         return BSP_ERR_ALIGNMENT;
     return hip_status(bsp::launch_gemm_bf16(mode, a, lda, b, ldb, gather, src_rows, group_offsets, G, M, N, K, c,
                                             c_dtype, ldc, workspace, as_stream(stream)));

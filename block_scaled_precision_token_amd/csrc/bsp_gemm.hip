@@ -42,9 +42,12 @@
 // offsets, so no host synchronization is needed.  Persistent workgroups walk a
 // static tile sequence: for the row-grouped forms an XCD-contiguous chunk of
 // the row-major tile order (workgroups resident on one XCD share activation
-// rows and weight panels in that XCD's L2), for the weight-gradient form a
-// grid-strided order (every workgroup sees every expert, which balances
-// experts of very different token counts).
+// rows and weight panels in that XCD's L2).  In the weight-gradient form a
+// tile's cost is its expert's token count, which under skewed routing spans
+// three orders of magnitude: a setup kernel orders the experts by token
+// count, largest first, and workgroup b takes tiles b, 2P - 1 - b, 2P + b, ...
+// of that order (P workgroups), so the longest tiles are spread first and the
+// short ones fill in behind them.
 #include <stdlib.h>
 
 #include "bsp_device.hpp"
@@ -75,6 +78,7 @@ struct GemmArgs {
     const float *b_outer;
     void *c;
     const int64_t *tiles;     // row-grouped form: packed (group << 40) | first row; WGRAD: padded starts [G+1]
+    const int32_t *order;     // WGRAD: experts by decreasing token count
     int64_t *sched;           // [NXCD] spare counters, then (row-grouped form) the listed row-tile count
     // Sizes fit 32 bits (checked at the C ABI), as do all tile and stage
     // counts; byte offsets are formed in 64 bits where they can exceed that.
@@ -123,6 +127,28 @@ __global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t 
     for (int64_t t = carry + threadIdx.x; t < ntile_max; t += blockDim.x) tiles[t] = -1;
     if (threadIdx.x < NXCD) sched[threadIdx.x] = 0;
     if (threadIdx.x == 0) sched[NXCD] = carry < ntile_max ? carry : ntile_max;
+}
+
+// Weight-gradient form: the experts in order of decreasing token count (ties
+// by index), by rank counting over the counts staged in LDS; past 4096
+// experts the O(G^2) count is not worth it and the order stays the identity.
+constexpr int kOrderMaxG = 4096;
+__global__ __launch_bounds__(1024) void k_wgrad_order(const int64_t *__restrict__ off, int64_t G,
+                                                      int32_t *__restrict__ order) {
+    __shared__ int64_t cnt[kOrderMaxG];
+    if (G > kOrderMaxG) {
+        for (int64_t g = threadIdx.x; g < G; g += blockDim.x) order[g] = (int32_t)g;
+        return;
+    }
+    const int n = (int)G;
+    for (int g = threadIdx.x; g < n; g += blockDim.x) cnt[g] = off[g + 1] - off[g];
+    __syncthreads();
+    for (int g = threadIdx.x; g < n; g += blockDim.x) {
+        const int64_t c = cnt[g];
+        int rank = 0;
+        for (int h = 0; h < n; h++) rank += (cnt[h] > c) || (cnt[h] == c && h < g);
+        order[rank] = g;
+    }
 }
 
 // Padded group starts P (running sum of roundup32(n_g)) for the weight-gradient form.
@@ -353,6 +379,18 @@ struct Tile {
     int slot;   // row-tile index (row-grouped form: position in the tile list)
 };
 
+// Load of a wave-uniform element through the scalar cache.  The tables read
+// this way (tile list, group offsets, expert order, gathers) are written by
+// earlier kernels, so the scalar cache, invalidated at kernel start, is
+// coherent for them.  A vector load here would make the compiler wait for
+// every outstanding vector-memory operation, the pipeline's LDS-DMA loads
+// included, before using the value.
+template <typename T>
+__device__ __forceinline__ T sload(const T *p, int64_t i) {
+    typedef const __attribute__((address_space(4))) T cT;
+    return ((const cT *)p)[i];
+}
+
 template <int FMT, int MODE, int BT>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
     constexpr int BK = Geo<FMT, BT>::BK;
@@ -360,21 +398,22 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
     const int ty = lin / p.ntn, tx = lin - ty * p.ntn;
     if (MODE == BSP_GEMM_WGRAD) {
         const int mt_per_g = (p.M + BT - 1) / BT;
-        T.g = ty / mt_per_g;
-        T.row0 = (ty - T.g * mt_per_g) * BT;
+        const int rank = ty / mt_per_g;
+        T.g = __builtin_amdgcn_readfirstlane(sload(p.order, rank));
+        T.row0 = (ty - rank * mt_per_g) * BT;
         T.row_end = p.M;
         // MXFP8: the group's padded token columns; BF16: the group's rows
-        const int64_t kb = FMT == FMT_BF16 ? p.group_offsets[T.g] : p.tiles[T.g];
-        const int64_t ke = FMT == FMT_BF16 ? p.group_offsets[T.g + 1]
-                                           : kb + (p.group_offsets[T.g + 1] - p.group_offsets[T.g] + 31) / 32 * 32;
+        const int64_t o0 = sload(p.group_offsets, T.g), o1 = sload(p.group_offsets, T.g + 1);
+        const int64_t kb = FMT == FMT_BF16 ? o0 : sload(p.tiles, T.g);
+        const int64_t ke = FMT == FMT_BF16 ? o1 : kb + (o1 - o0 + 31) / 32 * 32;
         // offsets are trusted only up to the copies' width
         T.kbeg = (int)(kb < 0 ? 0 : kb < p.K ? kb : p.K);
         T.kend = (int)(ke < 0 ? 0 : ke < p.K ? ke : p.K);
     } else {
-        const int64_t tile = p.tiles[ty];   // valid: ty < the listed tile count
-        T.g = (int)(tile >> 40);
+        const int64_t tile = sload(p.tiles, ty);   // valid: ty < the listed tile count
+        T.g = __builtin_amdgcn_readfirstlane((int)(tile >> 40));
         T.row0 = (int)(tile & ((1ll << 40) - 1));
-        const int64_t re = p.group_offsets[T.g + 1];
+        const int64_t re = sload(p.group_offsets, T.g + 1);
         T.row_end = (int)(re < p.M ? re : p.M);   // never past the rows of C
         T.kbeg = 0;
         T.kend = p.K;
@@ -428,7 +467,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     int first, stride, last;
     if (WG) {
         first = blockIdx.x;
-        stride = gridDim.x;
+        stride = gridDim.x;   // P; the walk alternates direction every P tiles
         last = p.ntm * p.ntn;
     } else {
         const int total = (int)p.sched[NXCD] * p.ntn;   // listed row tiles x column tiles
@@ -439,6 +478,14 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const int e = (x + 1) * chunk;
         last = e < total ? e : total;
     }
+
+    // Next tile of this workgroup after `lin`: row-grouped forms lin + stride;
+    // weight-gradient form the serpentine walk (lin = r P + x, x = b for even
+    // rounds r and P - 1 - b for odd ones).
+    auto next_tile = [&](int lin) __attribute__((always_inline)) -> int {
+        if (!WG) return lin + stride;
+        return lin + 2 * stride - 1 - 2 * (lin % stride);
+    };
 
     // Fragment geometry (fixed per lane): LDS offsets inside a stage of the
     // code chunks and scale dwords this lane feeds to the MFMA.
@@ -547,7 +594,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         while (p_lin < last) {
             PT = decode_tile<FMT, MODE, BT>(p, p_lin);
             if (PT.nk > 0) break;
-            p_lin += stride;
+            p_lin = next_tile(p_lin);
             p_ord++;
         }
         if (p_lin >= last) {
@@ -938,7 +985,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 
     // Advance the consumer to its next tile.
     auto cons_next = [&]() __attribute__((always_inline)) {
-        c_lin += stride;
+        c_lin = next_tile(c_lin);
         c_ord++;
         if (c_lin >= last) {
             c_done = true;
@@ -962,7 +1009,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         issue(s);
         p_q++;
         if (++p_kt == p_nk) {
-            p_lin += stride;
+            p_lin = next_tile(p_lin);
             p_ord++;
             prod_seek();
         }
@@ -1005,7 +1052,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             if (!fl) fl = step(IC<3>{});
         }
         if (fl & SEEK) {
-            p_lin += stride;
+            p_lin = next_tile(p_lin);
             p_ord++;
             prod_seek();
         }
@@ -1036,7 +1083,8 @@ static WsLayout ws_layout(int fmt, int mode, int64_t M, int64_t N, int64_t K, in
     const int64_t nblk = K / sblk;
     L.nbp = (int32_t)(up(nblk, sps) + sps);   // K-tail stages read one padded step past the end
     const int64_t entries = (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G)) + kGemmSchedSlots;
-    L.head = up(entries * 8, 256);
+    // weight-gradient form: then the expert order, int32 [G]
+    L.head = up(entries * 8 + (mode == BSP_GEMM_WGRAD ? G * 4 : 0), 256);
     L.a_rp = (int32_t)(mode == BSP_GEMM_WGRAD ? up(M, 256) : ((M + 255) / 256 + G) * 256);
     L.b_rp = (int32_t)up(N, 256);
     L.a_off = L.head;
@@ -1122,6 +1170,9 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
         k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
+        int32_t *order = reinterpret_cast<int32_t *>(ws + G + 1 + kGemmSchedSlots);
+        k_wgrad_order<<<1, 1024, 0, s>>>(group_offsets, G, order);
+        p.order = order;
         PlaneArgs pa = {};
         pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
         pa.rows_z = (int32_t)M;
@@ -1152,9 +1203,9 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
 }
 
 // BF16 grouped GEMM.  Workspace: the row-tile list and counters of the
-// row-grouped forms; the weight-gradient form needs none.
+// row-grouped forms; the expert order of the weight-gradient form.
 int64_t gemm_bf16_workspace_bytes(int mode, int64_t M, int64_t G) {
-    if (mode == BSP_GEMM_WGRAD) return 0;
+    if (mode == BSP_GEMM_WGRAD) return up(G * 4, 256);
     return up((gemm_tile_count(M, G) + kGemmSchedSlots) * 8, 256);
 }
 
@@ -1179,6 +1230,9 @@ hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint
         const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
+        int32_t *order = reinterpret_cast<int32_t *>(workspace);
+        k_wgrad_order<<<1, 1024, 0, s>>>(group_offsets, G, order);
+        p.order = order;
         if (bt == 256) launch_k<FMT_BF16, BSP_GEMM_WGRAD, 256>(p, bf, s);
         else launch_k<FMT_BF16, BSP_GEMM_WGRAD, 128>(p, bf, s);
         return hipGetLastError();

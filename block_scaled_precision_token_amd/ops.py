@@ -300,9 +300,8 @@ def moe_grouped_gemm_bf16(mode: int, a: torch.Tensor, b: torch.Tensor, group_off
     ldc = out.shape[-1]
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
     if workspace is None:
-        need = gemm_bf16_workspace_size(mode, M, N, K, G)
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
-    ws_bytes = workspace.numel() if workspace is not None else 0
+        workspace = torch.empty((gemm_bf16_workspace_size(mode, M, N, K, G),), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel()
     st = _lib_raw().bsp_moe_grouped_gemm_bf16(mode, _ptr(a), a.stride(0) if a.dim() == 2 else a.shape[-1], _ptr(b),
                                               b.shape[-1], _ptr(gather), src_rows, _ptr(group_offsets), G, M, N,
                                               K, _ptr(out), dt, ldc, _ptr(workspace), ws_bytes, _stream(dev))

@@ -210,9 +210,11 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
  * Accumulation is f32 on the MFMA units; the epilogue applies gA * gB and
  * rounds to c_dtype (RNE for bf16).
  *   workspace  device, >= bsp_gemm_workspace_size(fmt, mode, M, N, K, G)
- *              bytes, 16-byte aligned; holds the tile list and block-major
- *              copies of both operands' scales, rewritten by every call, so
- *              calls sharing one workspace must be stream-ordered
+ *              bytes, 16-byte aligned; holds the tile list (WGRAD: the padded
+ *              group starts and the experts ordered by token count) and
+ *              block-major copies of both operands' scales, rewritten by
+ *              every call, so calls sharing one workspace must be
+ *              stream-ordered
  */
 bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales,
                                             const float *a_outer, const int32_t *a_gather, int64_t a_rows,
@@ -257,9 +259,9 @@ bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_
  * 2^26, A (FPROP/DGRAD) and one expert's B (FPROP) below 4 GiB, else
  * BSP_ERR_SHAPE.
  *   workspace  device, >= bsp_gemm_bf16_workspace_size(mode, M, N, K, G)
- *              bytes (the row-tile list; WGRAD needs none and accepts NULL),
- *              rewritten by every call: calls sharing one workspace must be
- *              stream-ordered
+ *              bytes (the row-tile list, or for WGRAD the experts ordered by
+ *              token count), rewritten by every call: calls sharing one
+ *              workspace must be stream-ordered
  */
 bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
                                      const int32_t *gather, int64_t src_rows, const int64_t *group_offsets,
@@ -295,8 +297,7 @@ int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
  * scales per 2048 rows (at most 1024 partials); 0 for M <= 0. */
 size_t bsp_requant_workspace_size(int64_t M);
 size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
-/* Bytes of workspace for bsp_moe_grouped_gemm_bf16 (0 for WGRAD and for
- * invalid arguments). */
+/* Bytes of workspace for bsp_moe_grouped_gemm_bf16 (0 for invalid arguments). */
 size_t bsp_gemm_bf16_workspace_size(int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 
 #ifdef __cplusplus

@@ -58,7 +58,7 @@ def test_size_helpers():
     a_plane = nbp * ((65536 + 255) // 256 + 128) * 256
     b_plane = 128 * nbp * up(1536, 256)
     assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) == head + up(a_plane, 256) + up(b_plane, 256)
-    head = up((258 + 16) * 8, 256)
+    head = up((258 + 16) * 8 + 257 * 4, 256)           # + the expert order
     nbp = 37120 // 32 + 2
     assert L.bsp_gemm_workspace_size(1, 2, 4096, 7168, 37120, 257) == head + nbp * 4096 + nbp * 7168
     assert L.bsp_gemm_workspace_size(7, 0, 64, 64, 64, 1) == 0
@@ -133,7 +133,7 @@ def test_bf16_gemm_workspace_and_bad_arguments():
     ws = L.bsp_gemm_bf16_workspace_size
     assert ws(0, 65536, 2048, 768, 128) == up(((65536 + 127) // 128 + 128 + 16) * 8, 256)
     assert ws(1, 65536, 2048, 768, 128) == ws(0, 65536, 2048, 768, 128)
-    assert ws(2, 2048, 768, 65536, 128) == 0         # the weight-gradient form needs no workspace
+    assert ws(2, 2048, 768, 65536, 128) == 512       # the weight-gradient form: the expert order
     assert ws(5, 64, 64, 64, 1) == 0 and ws(0, 0, 64, 64, 1) == 0
     g = L.bsp_moe_grouped_gemm_bf16
     W = 1 << 16
@@ -144,8 +144,9 @@ def test_bf16_gemm_workspace_and_bad_arguments():
     assert g(0, A, 64, A, 64, None, 32, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 2        # src_rows != M
     assert g(1, A, 64, A, 64, None, 64, A, 2, 64, 60, 64, A, 0, 64, A, W, None) == 2        # DGRAD N % 8
     assert g(1, A, 64, A, 32, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 2        # DGRAD ldb < N
-    assert g(2, A, 64, A, 64, None, 100, A, 2, 64, 64, 64, A, 0, 64, None, 0, None) == 2    # src_rows != K
-    assert g(2, A, 60, A, 64, None, 64, A, 2, 60, 64, 64, A, 0, 64, None, 0, None) == 2     # WGRAD M % 8
+    assert g(2, A, 64, A, 64, None, 100, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 2       # src_rows != K
+    assert g(2, A, 60, A, 64, None, 64, A, 2, 60, 64, 64, A, 0, 64, A, W, None) == 2        # WGRAD M % 8
+    assert g(2, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, None, 0, None) == 5     # WGRAD workspace
     assert g(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, 8, None) == 5        # workspace too small
     assert g(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, None, 0, None) == 5     # workspace missing
     assert g(0, A, 68, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, W, None) == 3        # lda % 8
