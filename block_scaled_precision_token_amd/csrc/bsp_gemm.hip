@@ -545,6 +545,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
 
     // A row of tile row r for the row-grouped form: its source row (or -1).
+    // A row of tile row r for the row-grouped form: its source row (or -1).
+    // (Vector loads: the compiler then waits for the pipeline's outstanding
+    // loads once per tile; resolving the gather through scalar loads instead
+    // measured slower, its code being much larger.)
     auto a_src = [&](const Tile &T, int r) __attribute__((always_inline)) -> int {
         const int gr = T.row0 + r;
         if (gr >= T.row_end) return -1;
