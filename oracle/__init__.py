@@ -84,6 +84,7 @@ def _declare(lib):
     lib.orc_e2m1_sr_mag.argtypes = [ctypes.c_float, ctypes.c_uint16]
     lib.orc_e2m1_sr_mag.restype = ctypes.c_uint8
     lib.orc_requant_transpose_sr.argtypes = [P, P, P, I64, I64, U64, ctypes.c_int, P, P, P]
+    lib.orc_requant_transpose_sr_batched.argtypes = [P, P, P, I64, I64, I64, I64, U64, ctypes.c_int, P, P, P]
     lib.orc_gemm_rowgroup.argtypes = [ctypes.c_int, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, I64, P, P]
     lib.orc_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
     lib.orc_gemm_bf16_rowgroup.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, P, I64, I64, I64, P, I64, P, P]
@@ -288,6 +289,25 @@ def requant_transpose_sr(codes, scales, outer, seed: int = 0, use_sr: bool = Tru
     G = np.empty(1, np.float32)
     _load().orc_requant_transpose_sr(_ptr(codes), _ptr(scales), _ptr(outer), M, K, seed, int(bool(use_sr)),
                                      _ptr(codesT), _ptr(scalesT), _ptr(G))
+    return codesT, scalesT, G
+
+
+def requant_transpose_sr_batched(codes, scales, outer, E: int, rows_per_scale: int, seed: int = 0,
+                                 use_sr: bool = True):
+    """E stacked rowwise NVFP4 tensors [E*M, K] -> each transposed and requantized
+    on its own: (codesT [E*K, M/2], scalesT [E*K, M/16], G [E]); random bits of
+    output element (e, k, m) at index e*K*M + k*M + m [nopree.com, section
+    第二个决定, applied per expert tensor]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    outer = _c(outer, np.float32)
+    M = codes.shape[0] // E
+    K = codes.shape[1] * 2
+    codesT = np.empty((E * K, M // 2), np.uint8)
+    scalesT = np.empty((E * K, M // 16), np.uint8)
+    G = np.empty(E, np.float32)
+    _load().orc_requant_transpose_sr_batched(_ptr(codes), _ptr(scales), _ptr(outer), rows_per_scale, E, M, K, seed,
+                                             int(bool(use_sr)), _ptr(codesT), _ptr(scalesT), _ptr(G))
     return codesT, scalesT, G
 
 

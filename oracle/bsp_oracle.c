@@ -428,9 +428,11 @@ ORC_API uint8_t orc_e2m1_sr_mag(float v, uint16_t u) {
  * intermediate is the f32 dequantized value, not rounded to bf16.  use_sr = 0
  * rounds to nearest even instead.  The random bits of output element (k, m)
  * use index k * M + m. */
-ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
-                                      int64_t M, int64_t K, uint64_t seed, int use_sr,
-                                      uint8_t *codesT, uint8_t *scalesT, float *outerT) {
+/* One [M, K] tensor; its output element (k, m) draws its random bits at
+ * index base + k * M + m. */
+static void requant_one(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M, int64_t K,
+                        uint64_t seed, int use_sr, uint64_t base, uint8_t *codesT, uint8_t *scalesT,
+                        float *outerT) {
     float G = 0.0f;
     for (int64_t m = 0; m < M; m++)
         if (outer[m] > G) G = outer[m];
@@ -460,8 +462,9 @@ ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scale
                 float r = 1.0f / eff;
                 for (int i = 0; i < 16; i++) {
                     float v = fabsf(d[i]) * r;
-                    uint8_t mag = use_sr ? orc_e2m1_sr_mag(v, orc_sr_bits(seed, (uint64_t)(k * M + 16 * j + i)))
-                                         : e2m1_mag_rne(v);
+                    uint8_t mag = use_sr
+                                      ? orc_e2m1_sr_mag(v, orc_sr_bits(seed, base + (uint64_t)(k * M + 16 * j + i)))
+                                      : e2m1_mag_rne(v);
                     q[i] = (uint8_t)((signbit(d[i]) ? 8u : 0u) | mag);
                 }
             }
@@ -469,6 +472,31 @@ ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scale
             for (int i = 0; i < 16; i += 2)
                 codesT[k * (M / 2) + (16 * j + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
         }
+}
+
+ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                      int64_t M, int64_t K, uint64_t seed, int use_sr,
+                                      uint8_t *codesT, uint8_t *scalesT, float *outerT) {
+    requant_one(codes, scales, outer, M, K, seed, use_sr, 0, codesT, scalesT, outerT);
+}
+
+/* E stacked tensors [E, M, K] (e.g. the per-expert weights of one projection,
+ * outer scales per rows_per_scale rows: one per expert for per-expert weight
+ * scaling), each dequantized, transposed and requantized on its own with its
+ * own G_e = max of its rows' outer scales.  The random bits of output element
+ * (e, k, m) are drawn at its index in the stacked output [E, K, M],
+ * e K M + k M + m, so the E outputs together use the counter stream of one
+ * [E K, M] tensor. */
+ORC_API void orc_requant_transpose_sr_batched(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                              int64_t rows_per_scale, int64_t E, int64_t M, int64_t K, uint64_t seed,
+                                              int use_sr, uint8_t *codesT, uint8_t *scalesT, float *outerT) {
+    float *g = (float *)malloc(sizeof(float) * (size_t)M);
+    for (int64_t e = 0; e < E; e++) {
+        for (int64_t m = 0; m < M; m++) g[m] = outer[(e * M + m) / rows_per_scale];
+        requant_one(codes + e * M * (K / 2), scales + e * M * (K / 16), g, M, K, seed, use_sr,
+                    (uint64_t)(e * K * M), codesT + e * K * (M / 2), scalesT + e * K * (M / 16), outerT + e);
+    }
+    free(g);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -430,3 +430,40 @@ def test_sr_deterministic_in_seed_and_index():
     assert oracle.sr_bits(123, 40) == (w[0] & 0xFFFF)
     assert oracle.sr_bits(123, 43) == (w[1] >> 16)
     assert oracle.sr_bits(123, 47) == (w[3] >> 16)
+
+
+def test_batched_requant_counter_stream_is_one_stacked_tensor():
+    """Batched requant of E per-expert tensors with equal outer scales equals,
+    bit for bit with stochastic rounding on, one requant of the tensors laid
+    side by side along K (input [M, E*K] -> output [E*K, M]): output element
+    (e, k, m) of the batch draws its bits at e*K*M + k*M + m."""
+    E, M, K = 3, 32, 48
+    w = synth.weights(31, E, M, K)
+    codes, scales, g = oracle.quantize_nvfp4(w, rows_per_scale=E * M)      # one scale: G_e all equal
+    outer_e = np.repeat(g, E)
+    cT, sT, G = oracle.requant_transpose_sr_batched(codes, scales, outer_e, E, rows_per_scale=M, seed=77)
+    side = lambda a: np.concatenate([a[e * M:(e + 1) * M] for e in range(E)], axis=1)
+    cT1, sT1, G1 = oracle.requant_transpose_sr(side(codes), side(scales), np.repeat(g, M), seed=77)
+    np.testing.assert_array_equal(cT, cT1)
+    np.testing.assert_array_equal(sT, sT1)
+    np.testing.assert_array_equal(G, np.repeat(G1, E))
+
+
+def test_batched_requant_scales_each_expert_by_its_own_outer():
+    """Per-expert weights (one outer scale per expert): each expert's output is
+    its own requant (G_e = its outer scale), not one shared G."""
+    E, M, K = 4, 32, 64
+    w = synth.weights(32, E, M, K)
+    wf = synth.f32_from_bf16_bits(w).reshape(E, M, K) * np.array([1, 10, 0.1, 3], np.float32)[:, None, None]
+    w = synth.bf16_bits_from_f32(wf.reshape(E * M, K))
+    codes, scales, g = oracle.quantize_nvfp4(w, rows_per_scale=M)
+    assert len(set(g.tolist())) == E
+    cT, sT, G = oracle.requant_transpose_sr_batched(codes, scales, g, E, rows_per_scale=M, use_sr=False)
+    np.testing.assert_array_equal(G, g)
+    for e in range(E):
+        rows = slice(e * M, (e + 1) * M)
+        c1, s1, G1 = oracle.requant_transpose_sr(codes[rows], scales[rows], np.full(M, g[e], np.float32),
+                                                 use_sr=False)
+        np.testing.assert_array_equal(cT[e * K:(e + 1) * K], c1)
+        np.testing.assert_array_equal(sT[e * K:(e + 1) * K], s1)
+        assert G1[0] == g[e]
