@@ -60,6 +60,12 @@ BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
     return (size_t)bsp::requant_partials(M) * sizeof(float);
 }
 
+BSP_EXPORT size_t bsp_requant_batched_workspace_size(int64_t E, int64_t M, int64_t rows_per_scale) {
+    if (E <= 0 || M <= 0 || rows_per_scale <= 0) return 0;
+    if (M % rows_per_scale && rows_per_scale % M) return 0;
+    return (size_t)bsp::requant_workspace_floats(E, M, rows_per_scale) * sizeof(float);
+}
+
 BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
     if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return 0;
@@ -133,20 +139,30 @@ BSP_EXPORT bsp_status bsp_dequantize(int fmt, const uint8_t *codes, const uint8_
                                              out, out_dtype, as_stream(stream)));
 }
 
+BSP_EXPORT bsp_status bsp_requant_transpose_sr_batched(const uint8_t *codes, const uint8_t *scales,
+                                                       const float *outer, int64_t rows_per_scale, int64_t E,
+                                                       int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT,
+                                                       float *outerT, uint64_t seed, uint32_t flags, void *workspace,
+                                                       size_t ws_bytes, void *stream) {
+    if (!codes || !scales || !outer || !codesT || !scalesT || !outerT) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_SR) return BSP_ERR_INVALID_ARG;
+    if (E <= 0 || M <= 0 || K <= 0 || M % 16 || K % 16 || rows_per_scale <= 0) return BSP_ERR_SHAPE;
+    if (E > 65535 || (M % rows_per_scale && rows_per_scale % M) || (E * M) % rows_per_scale) return BSP_ERR_SHAPE;
+    if (!workspace || ws_bytes < bsp_requant_batched_workspace_size(E, M, rows_per_scale)) return BSP_ERR_WORKSPACE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(outer) || !aligned16(codesT) || !aligned16(scalesT) ||
+        !aligned16(outerT) || !aligned16(workspace))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_requant(codes, scales, outer, rows_per_scale, E, M, K, codesT, scalesT, outerT,
+                                          seed, (flags & BSP_SR) != 0, reinterpret_cast<float *>(workspace),
+                                          as_stream(stream)));
+}
+
 BSP_EXPORT bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
                                                int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT,
                                                float *outerT, uint64_t seed, uint32_t flags, void *workspace,
                                                size_t ws_bytes, void *stream) {
-    if (!codes || !scales || !outer || !codesT || !scalesT || !outerT) return BSP_ERR_INVALID_ARG;
-    if (flags & ~BSP_SR) return BSP_ERR_INVALID_ARG;
-    if (M <= 0 || K <= 0 || M % 16 || K % 16) return BSP_ERR_SHAPE;
-    if (!workspace || ws_bytes < bsp_requant_workspace_size(M)) return BSP_ERR_WORKSPACE;
-    if (!aligned16(codes) || !aligned16(scales) || !aligned16(outer) || !aligned16(codesT) || !aligned16(scalesT) ||
-        !aligned16(outerT) || !aligned16(workspace))
-        return BSP_ERR_ALIGNMENT;
-    return hip_status(bsp::launch_requant(codes, scales, outer, M, K, codesT, scalesT, outerT, seed,
-                                          (flags & BSP_SR) != 0, reinterpret_cast<float *>(workspace),
-                                          as_stream(stream)));
+    return bsp_requant_transpose_sr_batched(codes, scales, outer, 1, 1, M, K, codesT, scalesT, outerT, seed, flags,
+                                            workspace, ws_bytes, stream);
 }
 
 BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes,

@@ -17,10 +17,11 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, i
                                  int64_t batch, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M,
                              int64_t K, int64_t rps, void *out, int out_dtype, hipStream_t s);
-int requant_partials(int64_t M);
-hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M, int64_t K,
-                          uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed, bool sr, float *part,
-                          hipStream_t s);
+int requant_partials(int64_t n);
+int64_t requant_workspace_floats(int64_t E, int64_t M, int64_t rps);
+hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t rps, int64_t E,
+                          int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed,
+                          bool sr, float *part, hipStream_t s);
 hipError_t launch_swiglu(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out, int fmt, bool m46,
                          uint8_t *codes, uint8_t *scales, float *outer, hipStream_t s);
 int64_t gemm_tile_count(int64_t M, int64_t G);

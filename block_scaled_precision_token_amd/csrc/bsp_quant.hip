@@ -634,16 +634,21 @@ constexpr int RQ_CS = RQ_TM + 4;      // word stride of the transposed code tile
 constexpr int RQ_MAXPART = 1024;      // partial maxima of the outer scales
 constexpr int RQ_PCHUNK = 2048;       // outer scales per partial-max block
 
-// Partial maxima of the per-row outer scales (G = max over all partials,
-// starting from 0).  Chunks are multiples of 4 floats, so every chunk starts
-// 16-byte aligned.
-__global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restrict__ outer, int64_t M,
+// Partial maxima of the outer scales of each tensor of a batch (G_e = max
+// over tensor e's partials, starting from 0).  Tensor e = blockIdx.y has rows
+// [e M, (e + 1) M) and outer scale outer[row / rps], i.e. the entries
+// [lo, hi) below.  Chunks are multiples of 4 floats; float4 loads where the
+// chunk start is 16-byte aligned.
+__global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restrict__ outer, int64_t M, int64_t rps,
                                                            float *__restrict__ part) {
-    const int64_t chunk = ((M + gridDim.x - 1) / gridDim.x + 3) & ~(int64_t)3;
-    const int64_t a = (int64_t)blockIdx.x * chunk, b = a + chunk < M ? a + chunk : M;
+    const int64_t e = blockIdx.y;
+    const int64_t lo = e * M / rps, hi = ((e + 1) * M - 1) / rps + 1, n = hi - lo;
+    const int64_t chunk = ((n + gridDim.x - 1) / gridDim.x + 3) & ~(int64_t)3;
+    const int64_t a = lo + (int64_t)blockIdx.x * chunk, b = a + chunk < hi ? a + chunk : hi;
+    const bool vec = (lo & 3) == 0;
     float m = 0.0f;
     for (int64_t i = a + 4 * (int64_t)threadIdx.x; i < b; i += 4 * (int64_t)blockDim.x) {
-        if (i + 4 <= b) {
+        if (vec && i + 4 <= b) {
             const float4 v = *reinterpret_cast<const float4 *>(outer + i);
             m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
         } else {
@@ -654,7 +659,7 @@ __global__ __launch_bounds__(256) void k_outer_partial_max(const float *__restri
     __shared__ float red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (threadIdx.x == 0) part[e * gridDim.x + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // a[15:0] * b[15:0] + c (low half of a) and a[31:16] * b[15:0] + c (high
@@ -797,9 +802,13 @@ __device__ __forceinline__ void requant_pair(const uint32_t (&cw)[16], const flo
 // then holds rows 16 j .. 16 j + 15 of its 8 columns and produces the 8
 // output blocks (k, 16-row block j): for each k, the 16 lanes of one k write
 // 128 contiguous bytes of output row k.
+// A batch of tensors runs on blockIdx.y: tensor e reads rows [e M, (e+1) M)
+// of the stacked input (outer scale of row r: outer[r / rps]) and writes
+// [e K, (e+1) K) of the stacked output with its own G_e; its random bits are
+// drawn at the element's index in the stacked output.
 template <bool SR>
 __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                                 const float *__restrict__ outer, int64_t M, int64_t K,
+                                                 const float *__restrict__ outer, int64_t rps, int64_t M, int64_t K,
                                                  uint8_t *__restrict__ codesT, uint8_t *__restrict__ scalesT,
                                                  float *__restrict__ outerT, const float *__restrict__ part, int npart,
                                                  uint32_t key0, uint32_t key1, int ntk, int ntiles) {
@@ -808,6 +817,13 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
     __shared__ float red[4];
     __shared__ float rlut[128];
     const int t = threadIdx.x;
+    const int64_t eb = blockIdx.y;
+    codes += eb * M * (K / 2);
+    scales += eb * M * (K / 16);
+    codesT += eb * K * (M / 2);
+    scalesT += eb * K * (M / 16);
+    outerT += eb;
+    part += eb * npart;
     // consecutive tiles (which share input cache lines) on one XCD
     int tile = (int)blockIdx.x;
     if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
@@ -877,7 +893,7 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
         for (int b = 0; b < RQ_TK / 16; b++) sb[b] = 0u;
         float g = 0.0f;
         if (m < M) {
-            g = outer[m];
+            g = outer[(eb * M + m) / rps];
             const int64_t sp = K / 16;
             const uint8_t *src = scales + m * sp + k0 / 16;
             const int64_t left = sp - k0 / 16;
@@ -920,7 +936,8 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
         cw[4 * q + 0] = c.x; cw[4 * q + 1] = c.y; cw[4 * q + 2] = c.z; cw[4 * q + 3] = c.w;
         sf[4 * q + 0] = f.x; sf[4 * q + 1] = f.y; sf[4 * q + 2] = f.z; sf[4 * q + 3] = f.w;
     }
-    const uint64_t blk0 = ((uint64_t)kbase * (uint64_t)M + (uint64_t)mb) >> 3, bstep = (uint64_t)M >> 3;
+    const uint64_t blk0 = (((uint64_t)eb * (uint64_t)K + (uint64_t)kbase) * (uint64_t)M + (uint64_t)mb) >> 3,
+                   bstep = (uint64_t)M >> 3;
     uint8_t *cp0 = codesT + kbase * (M / 2) + mb / 2;
     uint8_t *sp0 = scalesT + kbase * (M / 16) + mb / 16;
     requant_pair<SR, 0>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
@@ -929,26 +946,35 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
     requant_pair<SR, 3>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
 }
 
-int requant_partials(int64_t M) {
-    int64_t n = (M + RQ_PCHUNK - 1) / RQ_PCHUNK;
+// Outer scales per tensor of a batch of tensors of M rows, rps dividing M or
+// a multiple of it.
+static int64_t requant_scales_per_tensor(int64_t M, int64_t rps) { return M % rps == 0 ? M / rps : 1; }
+
+int requant_partials(int64_t n) {
+    n = (n + RQ_PCHUNK - 1) / RQ_PCHUNK;
     return (int)(n < 1 ? 1 : (n > RQ_MAXPART ? RQ_MAXPART : n));
 }
 
-hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M, int64_t K,
-                          uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed, bool sr, float *part,
-                          hipStream_t s) {
-    const int np = requant_partials(M);
-    k_outer_partial_max<<<np, 256, 0, s>>>(outer, M, part);
+int64_t requant_workspace_floats(int64_t E, int64_t M, int64_t rps) {
+    return E * requant_partials(requant_scales_per_tensor(M, rps));
+}
+
+hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t rps, int64_t E,
+                          int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed,
+                          bool sr, float *part, hipStream_t s) {
+    const int np = requant_partials(requant_scales_per_tensor(M, rps));
+    k_outer_partial_max<<<dim3(np, (unsigned)E), 256, 0, s>>>(outer, M, rps, part);
     const int64_t ntk = (K + RQ_TK - 1) / RQ_TK, ntm = (M + RQ_TM - 1) / RQ_TM;
     if (ntk * ntm > INT32_MAX) return hipErrorInvalidValue;
     const int nt = (int)(ntk * ntm);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    const dim3 grid((unsigned)nt, (unsigned)E);
     if (sr)
-        k_requant<true><<<nt, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1,
-                                           (int)ntk, nt);
+        k_requant<true><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, part, np, k0,
+                                             k1, (int)ntk, nt);
     else
-        k_requant<false><<<nt, 256, 0, s>>>(codes, scales, outer, M, K, codesT, scalesT, outerT, part, np, k0, k1,
-                                            (int)ntk, nt);
+        k_requant<false><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, part, np, k0,
+                                              k1, (int)ntk, nt);
     return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ EXPORTED = [
     "bsp_version", "bsp_status_string", "bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize",
     "bsp_requant_transpose_sr", "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes",
     "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
-    "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size",
+    "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size", "bsp_requant_transpose_sr_batched",
+    "bsp_requant_batched_workspace_size",
 ]
 
 
@@ -63,6 +64,9 @@ def _declare(lib):
     lib.bsp_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P, P, I64, P, I64, U32, P]
     lib.bsp_dequantize.argtypes = [INT, P, P, P, I64, I64, I64, P, INT, P]
     lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
+    lib.bsp_requant_transpose_sr_batched.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, U64, U32, P, SZ, P]
+    lib.bsp_requant_batched_workspace_size.argtypes = [I64, I64, I64]
+    lib.bsp_requant_batched_workspace_size.restype = SZ
     lib.bsp_moe_grouped_gemm_blockscaled.argtypes = [INT, INT, P, P, P, P, I64, P, I64, I64, I64, I64, P, P, P, P,
                                                      INT, I64, P, SZ, P]
     lib.bsp_moe_grouped_gemm_bf16.argtypes = [INT, P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, INT, I64, P,
@@ -80,7 +84,7 @@ def _declare(lib):
     lib.bsp_gemm_workspace_size.restype = SZ
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
-                 "bsp_moe_grouped_gemm_bf16"):
+                 "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched"):
         getattr(lib, name).restype = INT
 
 
@@ -215,6 +219,32 @@ def dequantize(fmt: int, codes, scales, outer=None, rows_per_scale: int = 1, out
 
 def requant_workspace_size(M: int) -> int:
     return int(_lib_raw().bsp_requant_workspace_size(M))
+
+
+def requant_batched_workspace_size(E: int, M: int, rows_per_scale: int) -> int:
+    return int(_lib_raw().bsp_requant_batched_workspace_size(E, M, rows_per_scale))
+
+
+def requant_transpose_sr_batched(codes, scales, outer, E: int, rows_per_scale: int, seed: int = 0, sr: bool = True,
+                                 workspace=None, out=None):
+    """E stacked rowwise NVFP4 tensors [E*M, K] -> (codesT [E*K, M/2], scalesT [E*K, M/16], outerT [E])."""
+    _need_cuda(codes, "codes")
+    EM, K = codes.shape[0], codes.shape[1] * 2
+    M = EM // E
+    dev = codes.device
+    if out is None:
+        out = (torch.empty((E * K, M // 2), dtype=torch.uint8, device=dev),
+               torch.empty((E * K, M // 16), dtype=torch.uint8, device=dev),
+               torch.empty((max(E, 4),), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty((max(requant_batched_workspace_size(E, M, rows_per_scale), 16),), dtype=torch.uint8,
+                                device=dev)
+    codesT, scalesT, outerT = out
+    st = _lib_raw().bsp_requant_transpose_sr_batched(_ptr(codes), _ptr(scales), _ptr(outer), rows_per_scale, E, M, K,
+                                                     _ptr(codesT), _ptr(scalesT), _ptr(outerT), seed, SR if sr else 0,
+                                                     _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "bsp_requant_transpose_sr_batched")
+    return codesT, scalesT, outerT
 
 
 def requant_transpose_sr(codes, scales, outer, seed: int = 0, sr: bool = True, workspace=None, out=None):

@@ -181,6 +181,32 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
                                     uint32_t flags, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The same for a batch of E tensors stacked along their rows, each on its
+ * own [nopree.com, section 第二个决定, applied per expert]: the per-expert
+ * weights of one projection become the data-gradient GEMM's B operand with
+ * 16-blocks along the forward's output dimension.
+ *   codes, scales  device rowwise NVFP4 of the stacked input [E*M, K]
+ *   outer    device f32 [E*M / rows_per_scale]: row r's outer scale is
+ *            outer[r / rows_per_scale] (rows_per_scale = M for per-expert
+ *            weights); rows_per_scale divides M or is a multiple of M
+ *            dividing E*M
+ *   codesT   device u8 [E*K, M/2], scalesT device u8 [E*K, M/16] (out):
+ *            tensor e's output at rows [e*K, (e+1)*K)
+ *   outerT   device f32 [E] (out): G_e = max over tensor e's rows' outer scales
+ *   E <= 65535; M % 16 == 0, K % 16 == 0
+ *   workspace  device, >= bsp_requant_batched_workspace_size(E, M,
+ *              rows_per_scale) bytes
+ * Each tensor is requantized exactly as by bsp_requant_transpose_sr with its
+ * own G_e; the SR bits of output element (e, k, m) are drawn at its index in
+ * the stacked output, i = (e*K + k)*M + m.  bsp_requant_transpose_sr is
+ * this call with E = 1, rows_per_scale = 1.
+ */
+bsp_status bsp_requant_transpose_sr_batched(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                            int64_t rows_per_scale, int64_t E, int64_t M, int64_t K, uint8_t *codesT,
+                                            uint8_t *scalesT, float *outerT, uint64_t seed, uint32_t flags,
+                                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Block-scaled grouped expert GEMM [alphasignal.ai, Recipe 1 (MXFP8 forward,
  * weight- and data-gradient GEMMs) and Recipe 2 (NVFP4 MoE experts, per-token
  * scaling fused into the GEMM epilogue); remio.ai, section "Un quantizzatore
@@ -296,6 +322,9 @@ int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
 /* Bytes of requant workspace for M rows: one f32 partial maximum of the outer
  * scales per 2048 rows (at most 1024 partials); 0 for M <= 0. */
 size_t bsp_requant_workspace_size(int64_t M);
+/* Bytes of workspace for the batched requant: per tensor, one f32 partial
+ * maximum per 2048 outer scales (at most 1024); 0 for invalid arguments. */
+size_t bsp_requant_batched_workspace_size(int64_t E, int64_t M, int64_t rows_per_scale);
 size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 /* Bytes of workspace for bsp_moe_grouped_gemm_bf16 (0 for invalid arguments). */
 size_t bsp_gemm_bf16_workspace_size(int mode, int64_t M, int64_t N, int64_t K, int64_t G);

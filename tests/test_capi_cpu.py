@@ -155,6 +155,25 @@ def test_bf16_gemm_workspace_and_bad_arguments():
     assert g(0, A, 1024, A, 1024, A, 1 << 21, A, 2, 64, 64, 1024, A, 0, 64, A, W, None) == 2
 
 
+def test_requant_batched_workspace_and_bad_arguments():
+    ws = L.bsp_requant_batched_workspace_size
+    assert ws(128, 2048, 2048) == 128 * 4           # one outer scale per expert: one partial each
+    assert ws(1, 16384, 1) == L.bsp_requant_workspace_size(16384)
+    assert ws(4, 8192, 1) == 4 * 4 * 4
+    assert ws(2, 256, 512) == 2 * 4                 # one scale over two tensors
+    assert ws(2, 256, 96) == 0 and ws(0, 256, 1) == 0
+    r = L.bsp_requant_transpose_sr_batched
+    W = 1 << 16
+    # (codes, scales, outer, rps, E, M, K, codesT, scalesT, outerT, seed, flags, ws, ws_bytes, stream)
+    assert r(A, A, A, 64, 2, 64, 64, A, A, A, 0, 0x4, A, W, None) == 1          # unknown flag
+    assert r(A, A, None, 64, 2, 64, 64, A, A, A, 0, 0, A, W, None) == 1         # null outer
+    assert r(A, A, A, 64, 2, 60, 64, A, A, A, 0, 0, A, W, None) == 2            # M % 16
+    assert r(A, A, A, 48, 2, 64, 64, A, A, A, 0, 0, A, W, None) == 2            # rps neither divides nor spans M
+    assert r(A, A, A, 64, 70000, 64, 64, A, A, A, 0, 0, A, W, None) == 2        # too many tensors
+    assert r(A, A, A, 1, 2, 64, 64, A, A, A, 0, 0, A, 4, None) == 5             # workspace too small
+    assert r(MIS, A, A, 64, 2, 64, 64, A, A, A, 0, 0, A, W, None) == 3          # misaligned
+
+
 def test_python_binding_fails_loudly_without_device_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -168,3 +168,25 @@ def test_qwen3_shaped_nvfp4_gate_up_sampled_rows():
     ref, refabs = oracle.gemm_rowgroup(oracle.FMT_NVFP4, ac, as_, ag, src, off, N, H, bc, bs, bg, rows=rows)
     got = host(c)[rows]
     assert_gemm_close(got, ref, refabs)
+
+
+@pytest.mark.parametrize("sr", [True, False])
+def test_nvfp4_dgrad_on_requantized_weights(sr):
+    # The 4-bit backward's data gradient: dX = dY W_e with the forward's NVFP4
+    # weight copy W_e [N, Kf] dequantized, transposed and requantized on the
+    # device (16-blocks along N, the reduction dim of dgrad; per-expert G_e).
+    G, N, Kf = 3, 96, 160
+    counts = [50, 0, 77]
+    off = offsets(counts)
+    R = int(off[-1])
+    w = synth.weights(43, G, N, Kf)
+    wc, ws, wg = oracle.quantize_nvfp4(w, rows_per_scale=N)
+    bct, bst, bgt = ops.requant_transpose_sr_batched(to_dev(wc), to_dev(ws), to_dev(wg), G, N, seed=99, sr=sr)
+    rct, rst, rgt = oracle.requant_transpose_sr_batched(wc, ws, wg, G, N, seed=99, use_sr=sr)
+    np.testing.assert_array_equal(host(bct), rct)
+    dy = synth.activations(44, R, N)
+    ac, as_, ag = oracle.quantize_nvfp4(dy)
+    c = ops.moe_grouped_gemm_blockscaled(ops.FMT_NVFP4, ops.GEMM_DGRAD, to_dev(ac), to_dev(as_), bct, bst,
+                                         to_dev(off), Kf, N, a_outer=to_dev(ag), b_outer=bgt)
+    ref, refabs = oracle.gemm_rowgroup(oracle.FMT_NVFP4, ac, as_, ag, None, off, Kf, N, rct, rst, rgt)
+    assert_gemm_close(host(c), ref, refabs)

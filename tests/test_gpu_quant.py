@@ -289,6 +289,26 @@ def test_requant_worked_example_on_device():
     assert int(host(ct)[17, 0] & 15) == 4 and int(host(st)[17, 0]) == 0x40   # element 2, scale 2
 
 
+@pytest.mark.parametrize("E,M,K,rps", [(3, 272, 144, 272), (4, 512, 256, 1), (2, 256, 2048, 512),
+                                        (128, 48, 32, 48)])
+@pytest.mark.parametrize("sr", [True, False])
+def test_requant_batched_parity(E, M, K, rps, sr):
+    """Per-expert tensors requantized on their own (own G_e; SR bits indexed in
+    the stacked output), against the oracle: per-expert weight scales
+    (rps = M), per-row scales (rps = 1) and one scale over two tensors."""
+    w = synth.weights(20261215 + M, E, M, K)
+    if rps == 1:
+        rc, rs, rg = oracle.quantize_nvfp4(w)
+    else:
+        rc, rs, rg = oracle.quantize_nvfp4(w, rows_per_scale=rps)
+    seed = 0xBA7C + E
+    ct, st, gt = ops.requant_transpose_sr_batched(to_dev(rc), to_dev(rs), to_dev(rg), E, rps, seed=seed, sr=sr)
+    rct, rst, rgt = oracle.requant_transpose_sr_batched(rc, rs, rg, E, rps, seed=seed, use_sr=sr)
+    assert_bytes_equal(host(gt)[:E], rgt, "outerT")
+    assert_bytes_equal(host(st), rst, "scalesT")
+    assert_bytes_equal(host(ct), rct, "codesT")
+
+
 # ---------------------------------------------------------------------------
 # SwiGLU + quantize
 # ---------------------------------------------------------------------------
