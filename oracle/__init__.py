@@ -87,6 +87,8 @@ def _declare(lib):
     lib.orc_requant_transpose_sr_batched.argtypes = [P, P, P, I64, I64, I64, I64, U64, ctypes.c_int, P, P, P]
     lib.orc_gemm_rowgroup.argtypes = [ctypes.c_int, P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, I64, P, P]
     lib.orc_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
+    lib.orc_gemm_wgrad_fmt.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
+    lib.orc_requant_transpose_sr_grouped.argtypes = [P, P, P, I64, P, P, I64, I64, I64, U64, ctypes.c_int, P, P, P]
     lib.orc_gemm_bf16_rowgroup.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, P, I64, I64, I64, P, I64, P, P]
     lib.orc_gemm_bf16_wgrad.argtypes = [P, I64, P, I64, P, I64, P, I64, P, I64, P, P]
     lib.orc_exp_f32.argtypes = [ctypes.c_float]
@@ -311,6 +313,29 @@ def requant_transpose_sr_batched(codes, scales, outer, E: int, rows_per_scale: i
     return codesT, scalesT, G
 
 
+def requant_transpose_sr_grouped(codes, scales, outer, gather, group_offsets, ldT: int, seed: int = 0,
+                                 use_sr: bool = True):
+    """Rowwise NVFP4 rows [src_rows, K], grouped (rows [off[g], off[g+1]) read
+    through gather) -> per group dequantized, transposed and requantized into
+    32-padded columns of [K, ldT] with G_g per group: (codesT [K, ldT/2],
+    scalesT [K, ldT/16], G [G]) [nopree.com, section 第二个决定, for the weight
+    gradient's token-blocked operands]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    outer = _c(outer, np.float32)
+    off = _c(group_offsets, np.int64)
+    gather = None if gather is None else _c(gather, np.int32)
+    G = off.size - 1
+    K = codes.shape[1] * 2
+    codesT = np.zeros((K, ldT // 2), np.uint8)
+    scalesT = np.zeros((K, ldT // 16), np.uint8)
+    Gs = np.empty(G, np.float32)
+    _load().orc_requant_transpose_sr_grouped(_ptr(codes), _ptr(scales), _ptr(outer), codes.shape[0], _ptr(gather),
+                                             _ptr(off), G, K, ldT, seed, int(bool(use_sr)), _ptr(codesT),
+                                             _ptr(scalesT), _ptr(Gs))
+    return codesT, scalesT, Gs
+
+
 # --- GEMM -------------------------------------------------------------------
 
 FMT_NVFP4 = 0
@@ -337,6 +362,28 @@ def gemm_rowgroup(fmt, a_codes, a_scales, a_outer, a_gather, group_offsets, N, K
     _load().orc_gemm_rowgroup(fmt, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer), _ptr(gather), _ptr(off), G, M,
                               N, K, _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(rows_arr), n, _ptr(c),
                               _ptr(cabs))
+    return c, cabs
+
+
+def gemm_wgrad_nvfp4(a_codesT, a_scalesT, a_outer, b_codesT, b_scalesT, b_outer, group_offsets, sel):
+    """Weight-gradient form on grouped NVFP4 columnwise copies (outer scale per
+    group and operand) in binary64, for the (g, n) pairs in sel."""
+    a_codesT = _c(a_codesT, np.uint8)
+    a_scalesT = _c(a_scalesT, np.uint8)
+    b_codesT = _c(b_codesT, np.uint8)
+    b_scalesT = _c(b_scalesT, np.uint8)
+    a_outer = _c(a_outer, np.float32)
+    b_outer = _c(b_outer, np.float32)
+    off = _c(group_offsets, np.int64)
+    G = off.size - 1
+    NA, ldk = a_codesT.shape[0], a_codesT.shape[1] * 2
+    NB = b_codesT.shape[0]
+    sel = _c(sel, np.int64).reshape(-1, 2)
+    c = np.empty((sel.shape[0], NB), np.float64)
+    cabs = np.empty((sel.shape[0], NB), np.float64)
+    _load().orc_gemm_wgrad_fmt(FMT_NVFP4, _ptr(a_codesT), _ptr(a_scalesT), _ptr(a_outer), _ptr(b_codesT),
+                               _ptr(b_scalesT), _ptr(b_outer), _ptr(off), G, NA, NB, ldk, _ptr(sel), sel.shape[0],
+                               _ptr(c), _ptr(cabs))
     return c, cabs
 
 

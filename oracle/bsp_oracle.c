@@ -428,10 +428,11 @@ ORC_API uint8_t orc_e2m1_sr_mag(float v, uint16_t u) {
  * intermediate is the f32 dequantized value, not rounded to bf16.  use_sr = 0
  * rounds to nearest even instead.  The random bits of output element (k, m)
  * use index k * M + m. */
-/* One [M, K] tensor; its output element (k, m) draws its random bits at
- * index base + k * M + m. */
+/* One [M, K] tensor into rows of ldo elements of the output ([K, ldo] codes
+ * [K, ldo/2], scales [K, ldo/16]); its output element (k, m) draws its random
+ * bits at index base + k * ldo + m. */
 static void requant_one(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t M, int64_t K,
-                        uint64_t seed, int use_sr, uint64_t base, uint8_t *codesT, uint8_t *scalesT,
+                        int64_t ldo, uint64_t seed, int use_sr, uint64_t base, uint8_t *codesT, uint8_t *scalesT,
                         float *outerT) {
     float G = 0.0f;
     for (int64_t m = 0; m < M; m++)
@@ -463,21 +464,21 @@ static void requant_one(const uint8_t *codes, const uint8_t *scales, const float
                 for (int i = 0; i < 16; i++) {
                     float v = fabsf(d[i]) * r;
                     uint8_t mag = use_sr
-                                      ? orc_e2m1_sr_mag(v, orc_sr_bits(seed, base + (uint64_t)(k * M + 16 * j + i)))
+                                      ? orc_e2m1_sr_mag(v, orc_sr_bits(seed, base + (uint64_t)(k * ldo + 16 * j + i)))
                                       : e2m1_mag_rne(v);
                     q[i] = (uint8_t)((signbit(d[i]) ? 8u : 0u) | mag);
                 }
             }
-            scalesT[k * (M / 16) + j] = s;
+            scalesT[k * (ldo / 16) + j] = s;
             for (int i = 0; i < 16; i += 2)
-                codesT[k * (M / 2) + (16 * j + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+                codesT[k * (ldo / 2) + (16 * j + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
         }
 }
 
 ORC_API void orc_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
                                       int64_t M, int64_t K, uint64_t seed, int use_sr,
                                       uint8_t *codesT, uint8_t *scalesT, float *outerT) {
-    requant_one(codes, scales, outer, M, K, seed, use_sr, 0, codesT, scalesT, outerT);
+    requant_one(codes, scales, outer, M, K, M, seed, use_sr, 0, codesT, scalesT, outerT);
 }
 
 /* E stacked tensors [E, M, K] (e.g. the per-expert weights of one projection,
@@ -493,10 +494,47 @@ ORC_API void orc_requant_transpose_sr_batched(const uint8_t *codes, const uint8_
     float *g = (float *)malloc(sizeof(float) * (size_t)M);
     for (int64_t e = 0; e < E; e++) {
         for (int64_t m = 0; m < M; m++) g[m] = outer[(e * M + m) / rows_per_scale];
-        requant_one(codes + e * M * (K / 2), scales + e * M * (K / 16), g, M, K, seed, use_sr,
+        requant_one(codes + e * M * (K / 2), scales + e * M * (K / 16), g, M, K, M, seed, use_sr,
                     (uint64_t)(e * K * M), codesT + e * K * (M / 2), scalesT + e * K * (M / 16), outerT + e);
     }
     free(g);
+}
+
+/* The weight-gradient operands of the 4-bit backward: rows [off[g], off[g+1])
+ * of a rowwise NVFP4 tensor (read through `gather`, or directly) are group g's
+ * tokens; each group is dequantized, transposed and requantized on its own
+ * (G_g = max of its rows' outer scales) into columns [P_g, P_g + pad32(n_g))
+ * of the output [K, ldT], P the running sum of the 32-padded group sizes;
+ * padding columns hold zero codes under zero scales.  The SR bits of output
+ * element (k, p) are drawn at its index in the output array, k * ldT + p.
+ * A gathered row outside [0, src_rows) reads as zeros. */
+ORC_API void orc_requant_transpose_sr_grouped(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                              int64_t src_rows, const int32_t *gather, const int64_t *off, int64_t G,
+                                              int64_t K, int64_t ldT, uint64_t seed, int use_sr, uint8_t *codesT,
+                                              uint8_t *scalesT, float *outerT) {
+    int64_t *P = (int64_t *)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    orc_padded_offsets(off, G, P);
+    for (int64_t g = 0; g < G; g++) {
+        const int64_t n = off[g + 1] - off[g], np = P[g + 1] - P[g];
+        /* the group's tokens as a rowwise tensor [np, K], padding rows zero */
+        uint8_t *c = (uint8_t *)calloc((size_t)(np * (K / 2) + 1), 1);
+        uint8_t *sc = (uint8_t *)calloc((size_t)(np * (K / 16) + 1), 1);
+        float *o = (float *)calloc((size_t)(np + 1), sizeof(float));
+        for (int64_t i = 0; i < n; i++) {
+            const int64_t r = off[g] + i;
+            const int64_t t = gather ? (int64_t)gather[r] : r;
+            if (t < 0 || t >= src_rows) continue;
+            memcpy(c + i * (K / 2), codes + t * (K / 2), (size_t)(K / 2));
+            memcpy(sc + i * (K / 16), scales + t * (K / 16), (size_t)(K / 16));
+            o[i] = outer[t];
+        }
+        requant_one(c, sc, o, np, K, ldT, seed, use_sr, (uint64_t)P[g], codesT + P[g] / 2, scalesT + P[g] / 16,
+                    outerT + g);
+        free(c);
+        free(sc);
+        free(o);
+    }
+    free(P);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -553,33 +591,45 @@ ORC_API void orc_gemm_rowgroup(int fmt, const uint8_t *a_codes, const uint8_t *a
     }
 }
 
-/* Weight-gradient form (MXFP8 only): for group g,
- * C_g[n, c] = sum over the group's padded token columns j of
+/* Weight-gradient form: for group g,
+ * C_g[n, c] = gA[g] gB[g] sum over the group's padded token columns j of
  * A[n, P[g] + j] * B[c, P[g] + j], with A [NA, ldk] and B [NB, ldk] the
- * grouped columnwise copies (padding columns hold zeros).  The (g, n) output
- * rows to compute are listed in sel (pairs); c and c_abs are [nsel, NB]. */
-ORC_API void orc_gemm_wgrad(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
-                            const uint8_t *b_scales, const int64_t *group_offsets, int64_t G, int64_t NA,
-                            int64_t NB, int64_t ldk, const int64_t *sel, int64_t nsel, double *c,
-                            double *c_abs) {
+ * grouped columnwise copies (padding columns hold zeros): MXFP8 (fmt 1, no
+ * outer scales) or NVFP4 (fmt 0) with one outer scale per group and operand
+ * (the grouped requant's G_g).  The (g, n) output rows to compute are listed
+ * in sel (pairs); c and c_abs (sum |A B| |gA gB|) are [nsel, NB]. */
+ORC_API void orc_gemm_wgrad_fmt(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
+                                const uint8_t *b_codes, const uint8_t *b_scales, const float *b_outer,
+                                const int64_t *group_offsets, int64_t G, int64_t NA, int64_t NB, int64_t ldk,
+                                const int64_t *sel, int64_t nsel, double *c, double *c_abs) {
     int64_t *P = (int64_t *)malloc(sizeof(int64_t) * (size_t)(G + 1));
     orc_padded_offsets(group_offsets, G, P);
     (void)NA;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < nsel; i++) {
         int64_t g = sel[2 * i], n = sel[2 * i + 1];
+        const double gab = fmt == 0 ? (double)a_outer[g] * (double)b_outer[g] : 1.0;
         for (int64_t cc = 0; cc < NB; cc++) {
             double s = 0.0, sa = 0.0;
             for (int64_t j = P[g]; j < P[g + 1]; j++) {
-                double p = exact_elem(1, a_codes, a_scales, ldk, n, j) * exact_elem(1, b_codes, b_scales, ldk, cc, j);
+                double p = exact_elem(fmt, a_codes, a_scales, ldk, n, j) *
+                           exact_elem(fmt, b_codes, b_scales, ldk, cc, j);
                 s += p;
                 sa += fabs(p);
             }
-            c[i * NB + cc] = s;
-            if (c_abs) c_abs[i * NB + cc] = sa;
+            c[i * NB + cc] = s * gab;
+            if (c_abs) c_abs[i * NB + cc] = sa * fabs(gab);
         }
     }
     free(P);
+}
+
+ORC_API void orc_gemm_wgrad(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                            const uint8_t *b_scales, const int64_t *group_offsets, int64_t G, int64_t NA,
+                            int64_t NB, int64_t ldk, const int64_t *sel, int64_t nsel, double *c,
+                            double *c_abs) {
+    orc_gemm_wgrad_fmt(1, a_codes, a_scales, NULL, b_codes, b_scales, NULL, group_offsets, G, NA, NB, ldk, sel, nsel,
+                       c, c_abs);
 }
 
 /* ------------------------------------------------------------------------ */

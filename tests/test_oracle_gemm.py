@@ -199,3 +199,28 @@ def test_swiglu_matches_float64_formula():
     # exact special values: silu(0) = 0, silu(-inf side) -> -0, silu(large) = z
     assert oracle.lib().orc_silu_f32(0.0) == 0.0
     assert oracle.lib().orc_silu_f32(100.0) == 100.0
+
+
+def test_nvfp4_wgrad_matches_float64_matmul_per_group():
+    """NVFP4 weight-gradient form on grouped columnwise copies with one outer
+    scale per group and operand: C_g = gA_g gB_g A_g B_g^T over the group's
+    padded columns (padding columns are zero codes)."""
+    G, NA, NB, ld = 3, 32, 48, 128
+    rng = np.random.default_rng(7)
+    ac = rng.integers(0, 256, (NA, ld // 2)).astype(np.uint8)
+    asc = rng.integers(0x20, 0x50, (NA, ld // 16)).astype(np.uint8)
+    bc = rng.integers(0, 256, (NB, ld // 2)).astype(np.uint8)
+    bsc = rng.integers(0x20, 0x50, (NB, ld // 16)).astype(np.uint8)
+    off = np.array([0, 20, 20, 70], np.int64)          # padded starts 0, 32, 32, 96
+    ag = np.array([0.5, 2.0, 0.125], np.float32)
+    bg = np.array([3.0, 1.0, 0.25], np.float32)
+    sel = np.array([[g, n] for g in range(G) for n in (0, 5, NA - 1)], np.int64)
+    c, cabs = oracle.gemm_wgrad_nvfp4(ac, asc, ag, bc, bsc, bg, off, sel)
+    A = nvfp4_exact(ac, asc, np.ones(NA, np.float32))
+    B = nvfp4_exact(bc, bsc, np.ones(NB, np.float32))
+    P = oracle.padded_offsets(off)
+    for i, (g, n) in enumerate(sel):
+        cols = slice(P[g], P[g + 1])
+        ref = ag[g] * bg[g] * (B[:, cols] @ A[n, cols])
+        np.testing.assert_allclose(c[i], ref, rtol=1e-12, atol=1e-12 * max(np.abs(ref).max(), 1e-300))
+    assert not c[3:6].any()                            # the empty group

@@ -467,3 +467,76 @@ def test_batched_requant_scales_each_expert_by_its_own_outer():
         np.testing.assert_array_equal(cT[e * K:(e + 1) * K], c1)
         np.testing.assert_array_equal(sT[e * K:(e + 1) * K], s1)
         assert G1[0] == g[e]
+
+
+def _stacked_padded(codes, scales, outer, src, off):
+    """The grouped rows laid out as one rowwise tensor: group g's rows (read
+    through src) then zero rows up to a multiple of 32."""
+    K2, K16 = codes.shape[1], scales.shape[1]
+    parts_c, parts_s, parts_o = [], [], []
+    for g in range(off.size - 1):
+        rows = src[off[g]:off[g + 1]]
+        n = rows.size
+        pad = (n + 31) // 32 * 32 - n
+        parts_c += [codes[rows], np.zeros((pad, K2), np.uint8)]
+        parts_s += [scales[rows], np.zeros((pad, K16), np.uint8)]
+        parts_o += [outer[rows], np.zeros(pad, np.float32)]
+    return np.concatenate(parts_c), np.concatenate(parts_s), np.concatenate(parts_o)
+
+
+def test_grouped_requant_is_requant_of_the_padded_group_layout():
+    """With every outer scale equal (so every G_g equals the single G), the
+    grouped, gathered requant with stochastic rounding equals, bit for bit, one
+    requant of the groups' rows laid out explicitly (gathered, each group
+    zero-padded to 32 rows) -- the counter of output element (k, p) being
+    k * ldT + p; columns past the padded total of a wider output stay
+    untouched."""
+    T, K = 40, 64
+    off = np.array([0, 21, 21, 60, 93], np.int64)
+    rng = np.random.default_rng(5)
+    src = rng.integers(0, T, int(off[-1])).astype(np.int32)
+    x = synth.activations(33, T, K)
+    codes, scales, g = oracle.quantize_nvfp4(x, rows_per_scale=T)        # one outer scale for all rows
+    outer = np.repeat(g, T)
+    c2, s2, o2 = _stacked_padded(codes, scales, outer, src, off)
+    P = c2.shape[0]
+    cT, sT, G = oracle.requant_transpose_sr_grouped(codes, scales, outer, src, off, P, seed=11)
+    cT1, sT1, G1 = oracle.requant_transpose_sr(c2, s2, np.where(o2 > 0, o2, g[0]), seed=11)
+    np.testing.assert_array_equal(cT, cT1)
+    np.testing.assert_array_equal(sT, sT1)
+    np.testing.assert_array_equal(G, np.where(np.diff(off) > 0, g[0], 0.0).astype(np.float32))
+    # a wider output: the counter follows the row length, so compare in RTN
+    cTn, sTn, _ = oracle.requant_transpose_sr_grouped(codes, scales, outer, src, off, P, use_sr=False)
+    cTw, sTw, _ = oracle.requant_transpose_sr_grouped(codes, scales, outer, src, off, P + 64, use_sr=False)
+    np.testing.assert_array_equal(cTw[:, :P // 2], cTn)
+    np.testing.assert_array_equal(sTw[:, :P // 16], sTn)
+    assert not cTw[:, P // 2:].any() and not sTw[:, P // 16:].any()
+
+
+def test_grouped_requant_scales_each_group_by_its_own_outer():
+    """Per-token outer scales: each group is requantized with G_g = the max of
+    its own rows' scales (RTN: equal to the single-tensor requant of that
+    group's padded rows alone); a bad gather index reads as a zero row."""
+    T, K = 50, 32
+    off = np.array([0, 7, 40, 40, 71], np.int64)
+    rng = np.random.default_rng(6)
+    src = rng.integers(0, T, int(off[-1])).astype(np.int32)
+    src[3] = -1
+    x = synth.activations(34, T, K)
+    codes, scales, outer = oracle.quantize_nvfp4(x)
+    cT, sT, G = oracle.requant_transpose_sr_grouped(codes, scales, outer, src, off, 160, use_sr=False)
+    Pg = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
+    codes_x = np.concatenate([codes, np.zeros((1, K // 2), np.uint8)])   # row T: the zero row of a bad index
+    scales_x = np.concatenate([scales, np.zeros((1, K // 16), np.uint8)])
+    outer_x = np.concatenate([outer, np.zeros(1, np.float32)])
+    src_x = np.where(src < 0, T, src)
+    for gi in range(off.size - 1):
+        rows = src_x[off[gi]:off[gi + 1]]
+        if rows.size == 0:
+            assert G[gi] == 0.0
+            continue
+        c1, s1, o1 = _stacked_padded(codes_x, scales_x, outer_x, rows, np.array([0, rows.size]))
+        r1c, r1s, r1g = oracle.requant_transpose_sr(c1, s1, o1, use_sr=False)
+        assert G[gi] == r1g[0] == outer_x[rows].max()
+        np.testing.assert_array_equal(cT[:, Pg[gi] // 2:Pg[gi + 1] // 2], r1c)
+        np.testing.assert_array_equal(sT[:, Pg[gi] // 16:Pg[gi + 1] // 16], r1s)
