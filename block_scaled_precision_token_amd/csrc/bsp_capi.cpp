@@ -157,6 +157,25 @@ BSP_EXPORT bsp_status bsp_requant_transpose_sr_batched(const uint8_t *codes, con
                                           as_stream(stream)));
 }
 
+BSP_EXPORT bsp_status bsp_requant_transpose_sr_grouped(const uint8_t *codes, const uint8_t *scales,
+                                                       const float *outer, int64_t src_rows, const int32_t *gather,
+                                                       const int64_t *group_offsets, int64_t G, int64_t R, int64_t K,
+                                                       uint8_t *codesT, uint8_t *scalesT, int64_t ldT, float *outerT,
+                                                       uint64_t seed, uint32_t flags, void *stream) {
+    if (!codes || !scales || !outer || !group_offsets || !codesT || !scalesT || !outerT) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_SR) return BSP_ERR_INVALID_ARG;
+    if (G < 1 || G > 2048 || R <= 0 || K <= 0 || K % 16 || src_rows <= 0) return BSP_ERR_SHAPE;
+    if (src_rows >= (1ll << 31) || R >= (1ll << 40)) return BSP_ERR_SHAPE;
+    if (!gather && src_rows != R) return BSP_ERR_SHAPE;
+    if (ldT % 32 || ldT < bsp_mxfp8_grouped_cols(R, G)) return BSP_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(outer) || !aligned16(group_offsets) ||
+        !aligned16(codesT) || !aligned16(scalesT) || !aligned16(outerT) || !aligned16_or_null(gather))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_requant_grouped(codes, scales, outer, src_rows, gather, group_offsets, G, R, K,
+                                                  codesT, scalesT, ldT, outerT, seed, (flags & BSP_SR) != 0,
+                                                  as_stream(stream)));
+}
+
 BSP_EXPORT bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales, const float *outer,
                                                int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT,
                                                float *outerT, uint64_t seed, uint32_t flags, void *workspace,
@@ -178,10 +197,7 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
     if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
     if (fmt == BSP_FMT_NVFP4 && (!a_outer || !b_outer)) return BSP_ERR_INVALID_ARG;
     if (fmt == BSP_FMT_MXFP8 && (a_outer || b_outer)) return BSP_ERR_INVALID_ARG;
-    if (mode == BSP_GEMM_WGRAD) {
-        if (fmt != BSP_FMT_MXFP8) return BSP_ERR_UNSUPPORTED;
-        if (a_gather) return BSP_ERR_INVALID_ARG;
-    }
+    if (mode == BSP_GEMM_WGRAD && a_gather) return BSP_ERR_INVALID_ARG;
     if (G < 1 || M <= 0 || N <= 0 || K <= 0 || ldc < N) return BSP_ERR_SHAPE;
     if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;

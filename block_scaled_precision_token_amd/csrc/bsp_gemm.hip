@@ -612,8 +612,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             bf_seek(ord);
             return;
         }
-        pca = p.a_codes + (WG ? PT.kbeg : 0);
-        pcb = p.b_codes + (WG ? (size_t)PT.kbeg : (size_t)PT.g * p.N * ldA);
+        // weight-gradient form: code bytes from the group's first column
+        pca = p.a_codes + (WG ? PT.kbeg / (MX ? 1 : 2) : 0);
+        pcb = p.b_codes + (WG ? (size_t)(PT.kbeg / (MX ? 1 : 2)) : (size_t)PT.g * p.N * ldA);
         // codes: unit u = 64 (w CIW + j) + l covers row u / CH, chunk position u % CH
 #pragma unroll
         for (int j = 0; j < GG::CIW; j++) {
@@ -921,6 +922,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const int ord = c_ord & 7;
         const bool vec_ok = (p.ldc % VEC) == 0;
         const int64_t goff = WG ? (int64_t)CT.g * p.M * p.ldc : 0;
+        // NVFP4 weight gradient: the group's outer scales of both operands
+        const float gab = (WG && NV) ? sload(p.a_outer, CT.g) * sload(p.b_outer, CT.g) : 1.0f;
         const int nv = live_blocks();
 #pragma unroll
         for (int i = 0; i < TI; i++) {
@@ -929,7 +932,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; e++) {
                 const int rt = wm * (BT / 2) + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
-                if (WG) mul[e] = 1.0f;
+                if (WG) mul[e] = gab;
                 else if (!NV) mul[e] = rowtok[ord][rt] >= 0 ? 1.0f : 0.0f;
                 else mul[e] = rowmul[NV ? ord : 0][rt];
             }
@@ -1182,8 +1185,13 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
         pa.rows_z = (int32_t)M;
         k_scale_plane<false><<<dim3((unsigned)(L.a_rp / 64), gy, 1), 256, 0, s>>>(pa);
         k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, 1), 256, 0, s>>>(pb);
-        if (bt == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>(p, bf, s);
-        else launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
+        if (fmt == BSP_FMT_MXFP8) {
+            if (bt == 256) launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>(p, bf, s);
+            else launch_k<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 128>(p, bf, s);
+        } else {
+            if (bt == 256) launch_k<BSP_FMT_NVFP4, BSP_GEMM_WGRAD, 256>(p, bf, s);
+            else launch_k<BSP_FMT_NVFP4, BSP_GEMM_WGRAD, 128>(p, bf, s);
+        }
         return hipGetLastError();
     }
     const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256));

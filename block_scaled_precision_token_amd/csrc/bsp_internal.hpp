@@ -22,6 +22,10 @@ int64_t requant_workspace_floats(int64_t E, int64_t M, int64_t rps);
 hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t rps, int64_t E,
                           int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed,
                           bool sr, float *part, hipStream_t s);
+hipError_t launch_requant_grouped(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t src_rows,
+                                  const int32_t *gather, const int64_t *group_offsets, int64_t G, int64_t R,
+                                  int64_t K, uint8_t *codesT, uint8_t *scalesT, int64_t ldT, float *outerT,
+                                  uint64_t seed, bool sr, hipStream_t s);
 hipError_t launch_swiglu(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out, int fmt, bool m46,
                          uint8_t *codes, uint8_t *scales, float *outer, hipStream_t s);
 int64_t gemm_tile_count(int64_t M, int64_t G);

@@ -720,8 +720,9 @@ __device__ __forceinline__ uint32_t e2m1_sr_code_hi(float d, float r, uint32_t n
 // mb + 15) and store its 8 code bytes at cp and its scale at sp.  blk is the
 // Philox block of the block's first element, (k * M + mb) / 8.  rlut[s] is
 // 1 / (E4M3(s) * G), or 0 where that product is below 2^-126 (the block is
-// flushed: scale 0, every code keeps only its sign).
-template <bool SR>
+// flushed: scale 0, every code keeps only its sign).  DIRECT: G differs
+// between the blocks of a workgroup and the same value is computed in place.
+template <bool SR, bool DIRECT = false>
 __device__ __forceinline__ void requant_block(const float (&d)[16], float G, const float *rlut, uint64_t blk,
                                               uint8_t *cp, uint8_t *sp, uint32_t key0, uint32_t key1) {
     float a = 0.0f;
@@ -731,7 +732,12 @@ __device__ __forceinline__ void requant_block(const float (&d)[16], float G, con
     float r = 0.0f;
     if (G > 0.0f) {
         s = e4m3x2_hw(a / (6.0f * G), 0.0f) & 0xFFu;  // a >= 0: s <= 0x7E
-        r = rlut[s];
+        if (DIRECT) {
+            const float eff = __builtin_amdgcn_cvt_f32_fp8((int)s, 0) * G;
+            r = eff >= kFlushBelow ? 1.0f / eff : 0.0f;
+        } else {
+            r = rlut[s];
+        }
         s = r == 0.0f ? 0u : s;
     }
     uint32_t lo = 0u, hi = 0u;
@@ -778,7 +784,7 @@ __device__ __forceinline__ void requant_block(const float (&d)[16], float G, con
 // and kbase + 2E + 1: decode both (exact at scale 1), scale, requantize.
 // Output row kbase + e starts at block blk0 + e * bstep, code byte cp0 + e *
 // cstep and scale byte sp0 + e * sstep.
-template <bool SR, int E>
+template <bool SR, int E, bool DIRECT = false>
 __device__ __forceinline__ void requant_pair(const uint32_t (&cw)[16], const float (&sf)[16], float G,
                                              const float *rlut, uint64_t blk0, uint64_t bstep, uint8_t *cp0,
                                              int64_t cstep, uint8_t *sp0, int64_t sstep, uint32_t key0,
@@ -790,10 +796,10 @@ __device__ __forceinline__ void requant_pair(const uint32_t (&cw)[16], const flo
         d0[i] = v[0] * sf[i];
         d1[i] = v[1] * sf[i];
     }
-    requant_block<SR>(d0, G, rlut, blk0 + (2 * E) * bstep, cp0 + (2 * E) * cstep, sp0 + (2 * E) * sstep, key0,
-                      key1);
-    requant_block<SR>(d1, G, rlut, blk0 + (2 * E + 1) * bstep, cp0 + (2 * E + 1) * cstep,
-                      sp0 + (2 * E + 1) * sstep, key0, key1);
+    requant_block<SR, DIRECT>(d0, G, rlut, blk0 + (2 * E) * bstep, cp0 + (2 * E) * cstep, sp0 + (2 * E) * sstep,
+                              key0, key1);
+    requant_block<SR, DIRECT>(d1, G, rlut, blk0 + (2 * E + 1) * bstep, cp0 + (2 * E + 1) * cstep,
+                              sp0 + (2 * E + 1) * sstep, key0, key1);
 }
 
 // One 256 (m) x 128 (k) input tile per workgroup.  The code tile is stored
@@ -944,6 +950,195 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
     requant_pair<SR, 1>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
     requant_pair<SR, 2>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
     requant_pair<SR, 3>(cw, sf, G, rlut, blk0, bstep, cp0, M / 2, sp0, M / 16, key0, key1);
+}
+
+// Grouped form, for the weight gradient's token-blocked operands: the rows of
+// group g (rows [off[g], off[g+1]) of the routed order, read through the
+// gather) become columns [P[g], P[g] + pad32(n_g)) of the output [K, ldT],
+// each group requantized with its own G_g.  G_g = max outer scale over the
+// group's rows, one workgroup per group.
+// (Offsets are trusted only up to R, the length of the routed order.)
+__global__ __launch_bounds__(256) void k_group_outer_max(const float *__restrict__ outer, int64_t src_rows,
+                                                         const int32_t *__restrict__ gather,
+                                                         const int64_t *__restrict__ off, int64_t R,
+                                                         float *__restrict__ outerT) {
+    const int64_t g = blockIdx.x, a = off[g], b = off[g + 1] < R ? off[g + 1] : R;
+    float m = 0.0f;
+    for (int64_t r = a + threadIdx.x; r < b; r += blockDim.x) {
+        const int64_t src = gather ? (int64_t)gather[r] : r;
+        if (src >= 0 && src < src_rows) m = fmaxf(m, outer[src]);
+    }
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) outerT[g] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One 256 (padded columns) x 128 (k) tile per workgroup, as k_requant, with
+// the tile's rows mapped through the groups: 32-row block b of the tile lies
+// in one group (P is 32-aligned), whose G_g every 16-block of it uses; rows
+// past a group's tokens (padding) and bad gather indices read as zeros.  The
+// SR bits of output element (k, p) are drawn at k * ldT + p.
+template <bool SR>
+__global__ __launch_bounds__(256) void k_requant_grouped(
+    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, const float *__restrict__ outer,
+    int64_t src_rows, const int32_t *__restrict__ gather, const int64_t *__restrict__ off, int G, int64_t R,
+    int64_t K, int64_t ldT, uint8_t *__restrict__ codesT, uint8_t *__restrict__ scalesT,
+    const float *__restrict__ outerT, uint32_t key0, uint32_t key1, int ntk) {
+    __shared__ uint32_t tc[RQ_TK / 8][RQ_CS];
+    __shared__ float tf[RQ_TK / 16][RQ_TM];
+    __shared__ int64_t sP[MX_MAXG + 1];
+    __shared__ int64_t wsum[4];
+    __shared__ int64_t blk_src0[RQ_TM / 32], blk_end[RQ_TM / 32];
+    __shared__ float blk_G[RQ_TM / 32];
+    __shared__ int64_t srow[RQ_TM];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t m0 = (int64_t)(blockIdx.x / ntk) * RQ_TM, k0 = (int64_t)(blockIdx.x % ntk) * RQ_TK;
+
+    // padded group starts P (thread t owns groups [t per, t per + per))
+    {
+        const int per = (G + 255) / 256;
+        const int g0 = t * per;
+        int64_t local = 0;
+        for (int g = g0; g < g0 + per && g < G; g++) local += (off[g + 1] - off[g] + 31) / 32 * 32;
+        const int64_t incl = wave_incl_scan(local, lane);
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        int64_t run = incl - local;
+        for (int w = 0; w < wv; w++) run += wsum[w];
+        for (int g = g0; g < g0 + per && g < G; g++) {
+            sP[g] = run;
+            run += (off[g + 1] - off[g] + 31) / 32 * 32;
+        }
+        if (t == 255) sP[G] = run;
+        __syncthreads();
+    }
+    const int64_t ptotal = sP[G] < ldT ? sP[G] : ldT;   // never past the output's rows
+    if (m0 >= ptotal) return;
+    if (t < RQ_TM / 32) {
+        const int64_t pb = m0 + 32 * t;
+        int64_t src0 = 0, end = 0;
+        float gG = 0.0f;
+        if (pb < ptotal) {
+            int lo = 0, hi = G - 1;  // last g with P[g] <= pb
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (sP[mid] <= pb) lo = mid;
+                else hi = mid - 1;
+            }
+            src0 = off[lo] + (pb - sP[lo]);
+            end = off[lo + 1] < R ? off[lo + 1] : R;
+            gG = outerT[lo];
+        }
+        blk_src0[t] = src0;
+        blk_end[t] = end;
+        blk_G[t] = gG;
+    }
+    __syncthreads();
+    {
+        const int b = t >> 5;
+        const int64_t r = blk_src0[b] + (t & 31);
+        int64_t src = -1;
+        if (m0 + t < ptotal && r < blk_end[b]) {
+            src = gather ? (int64_t)gather[r] : r;
+            if (src < 0 || src >= src_rows) src = -1;
+        }
+        srow[t] = src;
+    }
+    __syncthreads();
+
+    // codes of the tile's rows (16-byte pieces p = t & 3 of k0 + 32 p ..)
+    const int64_t rowb = K / 2;
+    {
+        const int p = t & 3;
+        const int64_t kb = k0 + 32 * p;
+#pragma unroll
+        for (int it = 0; it < 4; it++) {
+            const int r = (t >> 2) + 64 * it;
+            const int64_t src = srow[r];
+            uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
+            if (src >= 0) {
+                const uint8_t *sp = codes + src * rowb + kb / 2;
+                if (kb + 32 <= K) {
+                    if ((rowb & 15) == 0) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(sp);
+                        w0 = v.x; w1 = v.y; w2 = v.z; w3 = v.w;
+                    } else {
+                        const uint2 a = reinterpret_cast<const uint2 *>(sp)[0];
+                        const uint2 b = reinterpret_cast<const uint2 *>(sp)[1];
+                        w0 = a.x; w1 = a.y; w2 = b.x; w3 = b.y;
+                    }
+                } else if (kb + 16 <= K) {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(sp);
+                    w0 = a.x; w1 = a.y;
+                }
+            }
+            tc[4 * p + 0][r] = w0;
+            tc[4 * p + 1][r] = w1;
+            tc[4 * p + 2][r] = w2;
+            tc[4 * p + 3][r] = w3;
+        }
+    }
+    // effective scales of tile row t for the tile's 8 k blocks
+    {
+        const int64_t src = srow[t];
+        uint32_t sb[RQ_TK / 16];
+#pragma unroll
+        for (int b = 0; b < RQ_TK / 16; b++) sb[b] = 0u;
+        float g = 0.0f;
+        if (src >= 0) {
+            g = outer[src];
+            const int64_t sp = K / 16;
+            const uint8_t *srcp = scales + src * sp + k0 / 16;
+            const int64_t left = sp - k0 / 16;
+#pragma unroll
+            for (int b = 0; b < RQ_TK / 16; b++)
+                if (b < left) sb[b] = srcp[b];
+        }
+#pragma unroll
+        for (int b = 0; b < RQ_TK / 16; b++) tf[b][t] = e4m3_decode(sb[b]) * g;
+    }
+    __syncthreads();
+
+    const int j = lane & 15, kq = 4 * wv + (lane >> 4);
+    const int64_t mb = m0 + 16 * j, kbase = k0 + 8 * kq;
+    if (mb >= ptotal || kbase >= K) return;
+    const float G_ = blk_G[j >> 1];
+    uint32_t cw[16];
+    float sf[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(&tc[kq][16 * j + 4 * q]);
+        const float4 f = *reinterpret_cast<const float4 *>(&tf[kq >> 1][16 * j + 4 * q]);
+        cw[4 * q + 0] = c.x; cw[4 * q + 1] = c.y; cw[4 * q + 2] = c.z; cw[4 * q + 3] = c.w;
+        sf[4 * q + 0] = f.x; sf[4 * q + 1] = f.y; sf[4 * q + 2] = f.z; sf[4 * q + 3] = f.w;
+    }
+    const uint64_t blk0 = ((uint64_t)kbase * (uint64_t)ldT + (uint64_t)mb) >> 3, bstep = (uint64_t)ldT >> 3;
+    uint8_t *cp0 = codesT + kbase * (ldT / 2) + mb / 2;
+    uint8_t *sp0 = scalesT + kbase * (ldT / 16) + mb / 16;
+    requant_pair<SR, 0, true>(cw, sf, G_, nullptr, blk0, bstep, cp0, ldT / 2, sp0, ldT / 16, key0, key1);
+    requant_pair<SR, 1, true>(cw, sf, G_, nullptr, blk0, bstep, cp0, ldT / 2, sp0, ldT / 16, key0, key1);
+    requant_pair<SR, 2, true>(cw, sf, G_, nullptr, blk0, bstep, cp0, ldT / 2, sp0, ldT / 16, key0, key1);
+    requant_pair<SR, 3, true>(cw, sf, G_, nullptr, blk0, bstep, cp0, ldT / 2, sp0, ldT / 16, key0, key1);
+}
+
+hipError_t launch_requant_grouped(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t src_rows,
+                                  const int32_t *gather, const int64_t *group_offsets, int64_t G, int64_t R,
+                                  int64_t K, uint8_t *codesT, uint8_t *scalesT, int64_t ldT, float *outerT,
+                                  uint64_t seed, bool sr, hipStream_t s) {
+    k_group_outer_max<<<(unsigned)G, 256, 0, s>>>(outer, src_rows, gather, group_offsets, R, outerT);
+    const int64_t ntk = (K + RQ_TK - 1) / RQ_TK, ntm = (ldT + RQ_TM - 1) / RQ_TM;
+    if (ntk * ntm > INT32_MAX) return hipErrorInvalidValue;
+    const int nt = (int)(ntk * ntm);
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    if (sr)
+        k_requant_grouped<true><<<nt, 256, 0, s>>>(codes, scales, outer, src_rows, gather, group_offsets, (int)G, R,
+                                                   K, ldT, codesT, scalesT, outerT, k0, k1, (int)ntk);
+    else
+        k_requant_grouped<false><<<nt, 256, 0, s>>>(codes, scales, outer, src_rows, gather, group_offsets, (int)G, R,
+                                                    K, ldT, codesT, scalesT, outerT, k0, k1, (int)ntk);
+    return hipGetLastError();
 }
 
 // Outer scales per tensor of a batch of tensors of M rows, rps dividing M or

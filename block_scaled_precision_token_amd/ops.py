@@ -35,7 +35,7 @@ EXPORTED = [
     "bsp_requant_transpose_sr", "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes",
     "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
     "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size", "bsp_requant_transpose_sr_batched",
-    "bsp_requant_batched_workspace_size",
+    "bsp_requant_batched_workspace_size", "bsp_requant_transpose_sr_grouped",
 ]
 
 
@@ -66,6 +66,7 @@ def _declare(lib):
     lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
     lib.bsp_requant_transpose_sr_batched.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, U64, U32, P, SZ, P]
     lib.bsp_requant_batched_workspace_size.argtypes = [I64, I64, I64]
+    lib.bsp_requant_transpose_sr_grouped.argtypes = [P, P, P, I64, P, P, I64, I64, I64, P, P, I64, P, U64, U32, P]
     lib.bsp_requant_batched_workspace_size.restype = SZ
     lib.bsp_moe_grouped_gemm_blockscaled.argtypes = [INT, INT, P, P, P, P, I64, P, I64, I64, I64, I64, P, P, P, P,
                                                      INT, I64, P, SZ, P]
@@ -84,7 +85,7 @@ def _declare(lib):
     lib.bsp_gemm_workspace_size.restype = SZ
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
-                 "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched"):
+                 "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched", "bsp_requant_transpose_sr_grouped"):
         getattr(lib, name).restype = INT
 
 
@@ -244,6 +245,29 @@ def requant_transpose_sr_batched(codes, scales, outer, E: int, rows_per_scale: i
                                                      _ptr(codesT), _ptr(scalesT), _ptr(outerT), seed, SR if sr else 0,
                                                      _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, "bsp_requant_transpose_sr_batched")
+    return codesT, scalesT, outerT
+
+
+def requant_transpose_sr_grouped(codes, scales, outer, group_offsets, R: int, ldT: int | None = None, gather=None,
+                                 seed: int = 0, sr: bool = True, out=None):
+    """Rowwise NVFP4 [src_rows, K] grouped through `gather` -> (codesT [K, ldT/2],
+    scalesT [K, ldT/16], outerT [G]); columns past the padded total untouched
+    (zero when allocated here)."""
+    _need_cuda(codes, "codes")
+    src_rows, K = codes.shape[0], codes.shape[1] * 2
+    G = group_offsets.numel() - 1
+    dev = codes.device
+    if ldT is None:
+        ldT = mxfp8_grouped_cols(R, G)
+    if out is None:
+        out = (torch.zeros((K, ldT // 2), dtype=torch.uint8, device=dev),
+               torch.zeros((K, ldT // 16), dtype=torch.uint8, device=dev),
+               torch.empty((max(G, 4),), dtype=torch.float32, device=dev))
+    codesT, scalesT, outerT = out
+    st = _lib_raw().bsp_requant_transpose_sr_grouped(_ptr(codes), _ptr(scales), _ptr(outer), src_rows, _ptr(gather),
+                                                     _ptr(group_offsets), G, R, K, _ptr(codesT), _ptr(scalesT), ldT,
+                                                     _ptr(outerT), seed, SR if sr else 0, _stream(dev))
+    _check(st, "bsp_requant_transpose_sr_grouped")
     return codesT, scalesT, outerT
 
 

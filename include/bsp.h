@@ -181,6 +181,33 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
                                     uint32_t flags, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The same for the weight gradient's token-blocked operands: the rows of each
+ * expert group, read through the routing map, dequantized, transposed and
+ * requantized on their own [nopree.com, section 第二个决定, per expert].
+ *   codes, scales, outer  device rowwise NVFP4 [src_rows, K] with per-row
+ *            outer scales [src_rows] (e.g. the forward's per-token X, or dY)
+ *   gather   device int32 [R] or NULL (then src_rows == R): row r of the
+ *            routed order reads source row gather[r]; an index outside
+ *            [0, src_rows) reads as zeros
+ *   group_offsets  device int64 [G+1], rows of the routed order per group
+ *            (0 = off[0] <= ... <= off[G] = R); 1 <= G <= 2048
+ *   codesT   device u8 [K, ldT/2], scalesT device u8 [K, ldT/16] (out):
+ *            group g in columns [P[g], P[g] + pad32(n_g)), P the running sum
+ *            of the 32-padded group sizes; padding columns hold zero codes
+ *            and zero scales; columns from P[G] to ldT are left untouched
+ *   ldT      multiple of 32, >= bsp_mxfp8_grouped_cols(R, G)
+ *   outerT   device f32 [G] (out): G_g = max outer scale over group g's rows
+ *   K % 16 == 0
+ * Each group is requantized exactly as by bsp_requant_transpose_sr with its
+ * own G_g; the SR bits of output element (k, p) are drawn at its index in
+ * the output array, i = k*ldT + p.
+ */
+bsp_status bsp_requant_transpose_sr_grouped(const uint8_t *codes, const uint8_t *scales, const float *outer,
+                                            int64_t src_rows, const int32_t *gather, const int64_t *group_offsets,
+                                            int64_t G, int64_t R, int64_t K, uint8_t *codesT, uint8_t *scalesT,
+                                            int64_t ldT, float *outerT, uint64_t seed, uint32_t flags, void *stream);
+
+/*
  * The same for a batch of E tensors stacked along their rows, each on its
  * own [nopree.com, section 第二个决定, applied per expert]: the per-expert
  * weights of one projection become the data-gradient GEMM's B operand with
@@ -227,12 +254,15 @@ bsp_status bsp_requant_transpose_sr_batched(const uint8_t *codes, const uint8_t 
  *     b_codes/b_scales  device B [G, N, K] quantized along K
  *     b_outer   device f32 [G] (NVFP4 per-expert scales; NULL for MXFP8)
  *     c         device [M, ldc] of c_dtype (BSP_DTYPE_F32 or BSP_DTYPE_BF16)
- * WGRAD (MXFP8 only): per group g, C_g[n, j] = sum over the group's padded
- *   token columns t of A[n, P[g] + t] * B[j, P[g] + t], where A [M, K] and
- *   B [N, K] are the grouped columnwise copies made by bsp_quantize_mxfp8
- *   (K = their ld_colT) and P the padded group starts; group_offsets are the
- *   unpadded token offsets.  C is [G, M, ldc] (group stride M * ldc).
- *   a_gather, a_outer, b_outer must be NULL and a_rows == M.
+ * WGRAD: per group g, C_g[n, j] = gA[g] * gB[g] * sum over the group's
+ *   padded token columns t of A[n, P[g] + t] * B[j, P[g] + t], where A [M, K]
+ *   and B [N, K] are grouped columnwise copies (K = their ld_colT) and P the
+ *   32-padded group starts; group_offsets are the unpadded token offsets.
+ *   MXFP8: the copies made by bsp_quantize_mxfp8, a_outer and b_outer NULL.
+ *   NVFP4 (the 4-bit backward [nopree.com, section 第二个决定]): the copies
+ *   made by bsp_requant_transpose_sr_grouped, a_outer and b_outer their
+ *   per-group outer scales [G].  C is [G, M, ldc] (group stride M * ldc).
+ *   a_gather must be NULL and a_rows == M.
  * Accumulation is f32 on the MFMA units; the epilogue applies gA * gB and
  * rounds to c_dtype (RNE for bf16).
  *   workspace  device, >= bsp_gemm_workspace_size(fmt, mode, M, N, K, G)

@@ -115,8 +115,8 @@ def test_gemm_rejects_bad_arguments():
     # NVFP4 needs both outer scales; MXFP8 takes none
     assert g(0, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, A, ws, None) == 1
     assert g(1, 0, A, A, A, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 1
-    # NVFP4 weight gradient is not on the path
-    assert g(0, 2, A, A, A, None, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, A, ws, None) == 4
+    # the weight-gradient form takes no gather
+    assert g(0, 2, A, A, A, A, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, A, ws, None) == 1
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 48, A, A, None, A, 0, 64, A, ws, None) == 2
     # both formats fetch operand rows in 16-byte pieces: K % 32 == 0
     assert g(0, 0, A, A, A, None, 64, A, 2, 64, 64, 48, A, A, A, A, 0, 64, A, ws, None) == 2
@@ -172,6 +172,20 @@ def test_requant_batched_workspace_and_bad_arguments():
     assert r(A, A, A, 64, 70000, 64, 64, A, A, A, 0, 0, A, W, None) == 2        # too many tensors
     assert r(A, A, A, 1, 2, 64, 64, A, A, A, 0, 0, A, 4, None) == 5             # workspace too small
     assert r(MIS, A, A, 64, 2, 64, 64, A, A, A, 0, 0, A, W, None) == 3          # misaligned
+
+
+def test_requant_grouped_bad_arguments():
+    r = L.bsp_requant_transpose_sr_grouped
+    # (codes, scales, outer, src_rows, gather, off, G, R, K, codesT, scalesT, ldT, outerT, seed, flags, stream)
+    assert r(A, A, A, 64, None, A, 2, 64, 64, A, A, 128, A, 0, 0x4, None) == 1        # unknown flag
+    assert r(A, A, A, 64, None, None, 2, 64, 64, A, A, 128, A, 0, 0, None) == 1       # null offsets
+    assert r(A, A, A, 64, None, A, 0, 64, 64, A, A, 128, A, 0, 0, None) == 2          # G < 1
+    assert r(A, A, A, 64, None, A, 4096, 64, 64, A, A, 1 << 20, A, 0, 0, None) == 2   # G > 2048
+    assert r(A, A, A, 64, None, A, 2, 64, 40, A, A, 128, A, 0, 0, None) == 2          # K % 16
+    assert r(A, A, A, 50, None, A, 2, 64, 64, A, A, 128, A, 0, 0, None) == 2          # src_rows != R
+    assert r(A, A, A, 64, None, A, 2, 64, 64, A, A, 96, A, 0, 0, None) == 2           # ldT < grouped cols
+    assert r(A, A, A, 64, None, A, 2, 64, 64, A, A, 144, A, 0, 0, None) == 2          # ldT % 32
+    assert r(A, A, A, 64, MIS, A, 2, 64, 64, A, A, 128, A, 0, 0, None) == 3           # misaligned gather
 
 
 def test_python_binding_fails_loudly_without_device_tensors():

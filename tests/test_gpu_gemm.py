@@ -190,3 +190,35 @@ def test_nvfp4_dgrad_on_requantized_weights(sr):
                                          to_dev(off), Kf, N, a_outer=to_dev(ag), b_outer=bgt)
     ref, refabs = oracle.gemm_rowgroup(oracle.FMT_NVFP4, ac, as_, ag, None, off, Kf, N, rct, rst, rgt)
     assert_gemm_close(host(c), ref, refabs)
+
+
+@pytest.mark.parametrize("counts", [[50, 0, 64, 1, 100], [33, 200, 7]])
+@pytest.mark.parametrize("sr", [True, False])
+def test_nvfp4_wgrad_on_grouped_requantized_operands(counts, sr):
+    # The 4-bit backward's weight gradient: dW_e = dY_e^T X_e, both operands
+    # requantized on the device from rowwise per-token NVFP4 into token-blocked
+    # grouped copies (X through the routing map), one outer scale per group.
+    G = len(counts)
+    off = offsets(counts)
+    R = int(off[-1])
+    T, NA, NB = 90, 160, 96
+    rng = np.random.default_rng(R)
+    src = rng.integers(0, T, R).astype(np.int32)
+    dy = synth.activations(53, R, NA)
+    x = synth.activations(54, T, NB)
+    dyc, dys, dyg = oracle.quantize_nvfp4(dy)
+    xc, xs, xg = oracle.quantize_nvfp4(x, mode46=True)
+    ld = ops.mxfp8_grouped_cols(R, G)
+    offd = to_dev(off)
+    a = ops.requant_transpose_sr_grouped(to_dev(dyc), to_dev(dys), to_dev(dyg), offd, R, ldT=ld, seed=3, sr=sr)
+    b = ops.requant_transpose_sr_grouped(to_dev(xc), to_dev(xs), to_dev(xg), offd, R, ldT=ld, gather=to_dev(src),
+                                         seed=4, sr=sr)
+    ra = oracle.requant_transpose_sr_grouped(dyc, dys, dyg, None, off, ld, seed=3, use_sr=sr)
+    rb = oracle.requant_transpose_sr_grouped(xc, xs, xg, src, off, ld, seed=4, use_sr=sr)
+    for got, ref in zip(a + b, ra + rb):
+        np.testing.assert_array_equal(host(got)[:ref.shape[0]], ref)
+    c = ops.moe_grouped_gemm_blockscaled(ops.FMT_NVFP4, ops.GEMM_WGRAD, a[0], a[1], b[0], b[1], offd, NB, ld, M=NA,
+                                         a_outer=a[2], b_outer=b[2])
+    sel = np.array([[g, n] for g in range(G) for n in range(NA)], np.int64)
+    ref, refabs = oracle.gemm_wgrad_nvfp4(ra[0], ra[1], ra[2], rb[0], rb[1], rb[2], off, sel)
+    assert_gemm_close(host(c).reshape(G * NA, NB), ref, refabs)

@@ -309,6 +309,48 @@ def test_requant_batched_parity(E, M, K, rps, sr):
     assert_bytes_equal(host(ct), rct, "codesT")
 
 
+GROUPED_RQ_CASES = [
+    # (source rows, K, rows per group, gather)
+    (40, 64, [21, 0, 39, 33], True),
+    (300, 272, [129, 0, 128, 1, 142, 31, 32], True),
+    (256, 2048, [64, 64, 0, 128], False),
+    (8192, 2048, None, True),          # Qwen3-shaped: 65,536 routed rows of 8192 tokens, 128 experts
+]
+
+
+@pytest.mark.parametrize("T,K,counts,gathered", GROUPED_RQ_CASES)
+@pytest.mark.parametrize("sr", [True, False])
+def test_requant_grouped_parity(T, K, counts, gathered, sr):
+    """Token-blocked operands of the 4-bit weight gradient: rows of each group
+    (through the routing map, bad indices read as zeros), each group
+    requantized with its own G_g into 32-padded columns; bit-exact against the
+    oracle, columns past the padded total untouched."""
+    if counts is None:
+        off, src = synth.route_topk(20261205, T, 128, 8, synth.zipf_bias(20261204, 128))
+    else:
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+        rng = np.random.default_rng(T + K)
+        src = rng.integers(0, T, int(off[-1])).astype(np.int32)
+        if src.size > 8:
+            src[2] = -1
+            src[src.size // 2] = T + 5
+    R = int(off[-1])
+    if not gathered:
+        src = None
+        T = R
+    x = synth.activations(20261216 + K, T, K)
+    rc, rs, rg = oracle.quantize_nvfp4(x, mode46=True)
+    G = off.size - 1
+    ldT = ops.mxfp8_grouped_cols(R, G) + 32
+    seed = 0x6A0B + K
+    ct, st, gt = ops.requant_transpose_sr_grouped(to_dev(rc), to_dev(rs), to_dev(rg), to_dev(off), R, ldT=ldT,
+                                                  gather=None if src is None else to_dev(src), seed=seed, sr=sr)
+    rct, rst, rgt = oracle.requant_transpose_sr_grouped(rc, rs, rg, src, off, ldT, seed=seed, use_sr=sr)
+    assert_bytes_equal(host(gt)[:G], rgt, "outerT")
+    assert_bytes_equal(host(st), rst, "scalesT")
+    assert_bytes_equal(host(ct), rct, "codesT")
+
+
 # ---------------------------------------------------------------------------
 # SwiGLU + quantize
 # ---------------------------------------------------------------------------
