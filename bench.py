@@ -9,7 +9,8 @@ columnwise copies: per step the expert weights and the activations are
 quantized (row + column copies), then the forward (gate/up, SwiGLU + quantize,
 down), data-gradient and weight-gradient grouped GEMMs run.  Other workloads
 (--workload) time the Qwen3-30B-A3B-shaped NVFP4 forward, its BF16 backward
-GEMMs in the high-precision and the dequantized mode, the MXFP8
+GEMMs in the high-precision and the dequantized mode, its 4-bit backward on
+stochastically requantized operands, the MXFP8
 quantization of 8192 x 2048 activations plus 128 expert weights, the
 16384 x 2048 requant with stochastic rounding, and the 256 x 2048 round trip.
 
@@ -434,6 +435,136 @@ class Qwen3MoeNvfp4BwdDeq(Qwen3MoeNvfp4Bwd):
     mode = "deq"
 
 
+class Qwen3MoeNvfp4BwdFp4:
+    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward in 4 bits (configs[3]
+    shapes): the gradients dY and dH13 are quantized per token, the forward's
+    NVFP4 weights and activations are dequantized, transposed and requantized
+    with stochastic rounding (per expert for the weights, per expert group of
+    routed tokens for the activations and gradients), and the four data- and
+    weight-gradient GEMMs run on NVFP4 operands."""
+    name = "qwen3_moe_nvfp4_bwd_fp4"
+    unit = "TFLOP/s"
+    dtype = "fp16"
+
+    def __init__(self, dev):
+        import numpy as np
+        import torch
+        from block_scaled_precision_token_amd import ops, synth
+        T, H, I, E, k = 8192, 2048, 768, 128, 8
+        N13 = 2 * I
+        self.shape = dict(T=T, H=H, I=I, E=E, k=k)
+        bias = synth.zipf_bias(SEED + 4, E, 1.1)
+        off, src = synth.route_topk(SEED + 5, T, E, k, bias)
+        R = int(off[-1])
+        self.R, self.counts, self.off_h, self.src_h = R, np.diff(off), off, src
+        off_d = torch.from_numpy(off).to(dev)
+        src_d = torch.from_numpy(src).to(dev)
+        X = synth.device_activations(SEED + 6, T, H, dev)
+        W13 = synth.device_weights(SEED + 7, E, N13, H, dev)
+        W2 = synth.device_weights(SEED + 8, E, H, I, dev)
+        h = synth.device_activations(SEED + 9, R, I, dev, std=0.5)
+        dY = synth.device_activations(SEED + 10, R, H, dev)
+        dH13 = synth.device_activations(SEED + 11, R, N13, dev)
+        self.dH13, self.W13 = dH13, W13
+        # the forward's NVFP4 operands
+        xq = ops.quantize_nvfp4_per_token(X, mode46=True)
+        hq = ops.quantize_nvfp4_per_token(h, mode46=True)
+        w13q = ops.quantize_nvfp4_per_token(W13, rows_per_scale=N13)
+        w2q = ops.quantize_nvfp4_per_token(W2, rows_per_scale=H)
+        u8, bf, f32 = torch.uint8, torch.bfloat16, torch.float32
+        emp = lambda *s_, dt=u8: torch.empty(s_, dtype=dt, device=dev)
+        G = E
+        ld = ops.mxfp8_grouped_cols(R, G)
+        nvq = lambda M, K: (emp(M, K // 2), emp(M, K // 16), emp(M, dt=f32))
+        dyq, dhq = nvq(R, H), nvq(R, N13)
+        w2t = (emp(E * I, H // 2), emp(E * I, H // 16), emp(max(E, 4), dt=f32))
+        w13t = (emp(E * H, N13 // 2), emp(E * H, N13 // 16), emp(max(E, 4), dt=f32))
+        gq = lambda K: (torch.zeros((K, ld // 2), dtype=u8, device=dev), torch.zeros((K, ld // 16), dtype=u8, device=dev),
+                        emp(max(G, 4), dt=f32))
+        dyT, hT, dhT, xT = gq(H), gq(I), gq(N13), gq(H)
+        rq_ws = emp(max(ops.requant_batched_workspace_size(E, n, n) for n in (H, N13)))
+        dh, dX = emp(R, I, dt=bf), emp(R, H, dt=bf)
+        dW2, dW13 = emp(E, H, I, dt=bf), emp(E, N13, H, dt=bf)
+        gm, NV = ops.moe_grouped_gemm_blockscaled, ops.FMT_NVFP4
+        ws = emp(max(ops.gemm_workspace_size(NV, md, m, n, kk, E)
+                     for md, m, n, kk in ((ops.GEMM_DGRAD, R, I, H), (ops.GEMM_DGRAD, R, H, N13),
+                                          (ops.GEMM_WGRAD, H, I, ld), (ops.GEMM_WGRAD, N13, H, ld))))
+        s4 = 0.5 + 1 / 16
+        rqg = ops.requant_transpose_sr_grouped
+        self.ops = [
+            Op("quant_dy", lambda: ops.quantize_nvfp4_per_token(dY, out=dyq), R * H * (2 + s4) + R * 4),
+            Op("quant_dh13", lambda: ops.quantize_nvfp4_per_token(dH13, out=dhq), R * N13 * (2 + s4) + R * 4),
+            Op("requant_w2", lambda: ops.requant_transpose_sr_batched(*w2q, E, H, seed=1, workspace=rq_ws, out=w2t),
+               2 * E * H * I * s4),
+            Op("requant_w13", lambda: ops.requant_transpose_sr_batched(*w13q, E, N13, seed=2, workspace=rq_ws,
+                                                                       out=w13t),
+               2 * E * N13 * H * s4),
+            Op("requant_dy_grouped", lambda: rqg(*dyq, off_d, R, ldT=ld, seed=3, out=dyT), 2 * R * H * s4),
+            Op("requant_h_grouped", lambda: rqg(*hq, off_d, R, ldT=ld, seed=4, out=hT), 2 * R * I * s4),
+            Op("requant_dh13_grouped", lambda: rqg(*dhq, off_d, R, ldT=ld, seed=5, out=dhT), 2 * R * N13 * s4),
+            Op("requant_x_grouped", lambda: rqg(*xq, off_d, R, ldT=ld, gather=src_d, seed=6, out=xT),
+               T * H * s4 + R * H * s4),
+            Op("gemm_dgrad_down", lambda: gm(NV, ops.GEMM_DGRAD, dyq[0], dyq[1], w2t[0], w2t[1], off_d, I, H,
+                                             a_outer=dyq[2], b_outer=w2t[2], out=dh, workspace=ws),
+               R * H * s4 + E * H * I * s4 + R * I * 2, 2.0 * R * I * H, "fp16"),
+            Op("gemm_wgrad_down", lambda: gm(NV, ops.GEMM_WGRAD, dyT[0], dyT[1], hT[0], hT[1], off_d, I, ld, M=H,
+                                             a_outer=dyT[2], b_outer=hT[2], out=dW2, workspace=ws),
+               R * H * s4 + R * I * s4 + E * H * I * 2, 2.0 * R * H * I, "fp16"),
+            Op("gemm_dgrad_gate_up", lambda: gm(NV, ops.GEMM_DGRAD, dhq[0], dhq[1], w13t[0], w13t[1], off_d, H, N13,
+                                                a_outer=dhq[2], b_outer=w13t[2], out=dX, workspace=ws),
+               R * N13 * s4 + E * N13 * H * s4 + R * H * 2, 2.0 * R * H * N13, "fp16"),
+            Op("gemm_wgrad_gate_up", lambda: gm(NV, ops.GEMM_WGRAD, dhT[0], dhT[1], xT[0], xT[1], off_d, H, ld,
+                                                M=N13, a_outer=dhT[2], b_outer=xT[2], out=dW13, workspace=ws),
+               R * N13 * s4 + R * H * s4 + E * N13 * H * 2, 2.0 * R * N13 * H, "fp16"),
+        ]
+        self.gemm_flops = sum(o.flops for o in self.ops)
+
+    def config(self):
+        import numpy as np
+        c = self.counts
+        return {"workload": "qwen3_30b_a3b_moe_layer_nvfp4_backward_fp4_requant_sr", "tokens": self.shape["T"],
+                "hidden": self.shape["H"], "expert_intermediate": self.shape["I"], "experts": self.shape["E"],
+                "topk": self.shape["k"], "routed_rows": self.R, "backward_mode": "nvfp4_requant_sr",
+                "gradient_dtype": "bf16",
+                "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(np.median(c)),
+                               "min": int(c.min()), "empty": int((c == 0).sum())},
+                "gemm_flops_per_step": self.gemm_flops}
+
+    def value(self, ms_per_step):
+        return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def cpu_baseline(self, budget_s=10.0):
+        """Oracle on a sample: experts from the median load up, the NVFP4 quantize of up to 128
+        of the expert's dH13 rows, the requant (SR) of its gate/up weight, and their data-gradient
+        GEMM in fp64."""
+        import numpy as np
+        import torch
+        import oracle
+        H, N13 = self.shape["H"], 2 * self.shape["I"]
+        order = np.argsort(self.counts)
+        order = np.concatenate([order[len(order) // 2:], order[:len(order) // 2]])
+        it = iter(order.tolist())
+
+        def unit():
+            e = next(it)
+            w = self.W13[e * N13:(e + 1) * N13].view(torch.int16).cpu().numpy().view(np.uint16)
+            lo = int(self.off_h[e])
+            n = min(int(self.off_h[e + 1]) - lo, 128)
+            a = self.dH13[lo:lo + n].view(torch.int16).cpu().numpy().view(np.uint16)
+            wc, wsc, wg = oracle.quantize_nvfp4(w, rows_per_scale=N13)
+            bc, bs, bg = oracle.requant_transpose_sr_batched(wc, wsc, wg, 1, N13, seed=2)
+            ac, as_, ag = oracle.quantize_nvfp4(a)
+            off = np.array([0, n], np.int64)
+            oracle.gemm_rowgroup(oracle.FMT_NVFP4, ac, as_, ag, None, off, H, N13, bc, bs, bg)
+            return 2.0 * n * N13 * H
+
+        flops, dt, reps = timed_until(unit, budget_s, max_reps=len(order))
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{reps} experts from the median load up: NVFP4 quantize of the expert's 1536x2048 gate/up "
+                          f"weight and its requant with SR, NVFP4 quantize of up to 128 of its dH13 rows, then their "
+                          f"data-gradient GEMM in fp64 ({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
 class Mxfp8Quant:
     """MXFP8 rowwise + columnwise quantization of 8192 x 2048 activations and rowwise
     quantization of 128 expert weights 2048 x 768 (configs[1])."""
@@ -651,8 +782,8 @@ class HbmCopy:
         return None
 
 
-WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq, Mxfp8Quant,
-                                  RequantSr, RoundTrip, HbmCopy)}
+WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq,
+                                  Qwen3MoeNvfp4BwdFp4, Mxfp8Quant, RequantSr, RoundTrip, HbmCopy)}
 
 
 # ---------------------------------------------------------------------------
