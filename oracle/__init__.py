@@ -73,6 +73,9 @@ def _declare(lib):
     lib.orc_mxfp8_block_exponent.argtypes = [ctypes.c_float]
     lib.orc_mxfp8_block_exponent.restype = ctypes.c_int
     lib.orc_quantize_nvfp4.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P, P]
+    lib.orc_quantize_nvfp4_2d.argtypes = [P, I64, I64, P, P, P]
+    lib.orc_rht16.argtypes = [P, ctypes.c_uint32]
+    lib.orc_quantize_nvfp4_rht.argtypes = [P, I64, I64, ctypes.c_uint32, ctypes.c_int, P, P, P]
     lib.orc_dequantize_nvfp4.argtypes = [P, P, P, I64, I64, I64, P, P]
     lib.orc_quantize_mxfp8_rowwise.argtypes = [P, I64, I64, P, P]
     lib.orc_padded_offsets.argtypes = [P, I64, P]
@@ -195,6 +198,37 @@ def quantize_nvfp4(x_bf16: np.ndarray, rows_per_scale: int = 1, mode46: bool = F
     outer = np.empty((M // rows_per_scale,), np.float32)
     _load().orc_quantize_nvfp4(_ptr(x), M, K, rows_per_scale, int(bool(mode46)), _ptr(codes), _ptr(scales),
                                _ptr(outer))
+    return codes, scales, outer
+
+
+def quantize_nvfp4_2d(x_bf16: np.ndarray):
+    """NVFP4 with 16x16 2-D block scales and one per-tensor outer scale:
+    (codes [M, K/2], scales [M/16, K/16], outer [1])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M // 16, K // 16), np.uint8)
+    outer = np.empty(1, np.float32)
+    _load().orc_quantize_nvfp4_2d(_ptr(x), M, K, _ptr(codes), _ptr(scales), _ptr(outer))
+    return codes, scales, outer
+
+
+def rht16(v, signs: int):
+    """The 16-point random Hadamard transform of each row of v (f32 [n, 16])."""
+    v = np.array(v, dtype=np.float32, copy=True).reshape(-1, 16)
+    for row in v:
+        _load().orc_rht16(row.ctypes.data_as(ctypes.c_void_p), signs)
+    return v
+
+
+def quantize_nvfp4_rht(x_bf16: np.ndarray, signs: int, mode46: bool = False):
+    """Per-token NVFP4 of the rows after a 16-point RHT of each block."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M, K // 16), np.uint8)
+    outer = np.empty(M, np.float32)
+    _load().orc_quantize_nvfp4_rht(_ptr(x), M, K, signs, int(mode46), _ptr(codes), _ptr(scales), _ptr(outer))
     return codes, scales, outer
 
 

@@ -164,13 +164,9 @@ ORC_API int orc_mxfp8_block_exponent(float amax) {
 /* One candidate block scale with divisor D (6 = standard; 4 = the "4"
  * candidate of the 4/6 choice).  Writes 16 codes, returns the scale code and
  * the effective decode scale. */
-static uint8_t nvfp4_block_candidate(const float *xb, float g, float D, uint8_t q[NVFP4_BLOCK],
+/* Block scale from a given amax a (the block's own, or a 16x16 tile's). */
+static uint8_t nvfp4_block_with_amax(const float *xb, float a, float g, float D, uint8_t q[NVFP4_BLOCK],
                                      float *eff_out) {
-    float a = 0.0f;
-    for (int i = 0; i < NVFP4_BLOCK; i++) {
-        float m = fabsf(xb[i]);
-        if (m > a) a = m;
-    }
     uint8_t s = 0;
     float eff = 0.0f;
     if (g > 0.0f) {
@@ -187,6 +183,16 @@ static uint8_t nvfp4_block_candidate(const float *xb, float g, float D, uint8_t 
     for (int i = 0; i < NVFP4_BLOCK; i++) q[i] = orc_e2m1_encode(xb[i] * r);
     *eff_out = eff;
     return s;
+}
+
+static uint8_t nvfp4_block_candidate(const float *xb, float g, float D, uint8_t q[NVFP4_BLOCK],
+                                     float *eff_out) {
+    float a = 0.0f;
+    for (int i = 0; i < NVFP4_BLOCK; i++) {
+        float m = fabsf(xb[i]);
+        if (m > a) a = m;
+    }
+    return nvfp4_block_with_amax(xb, a, g, D, q, eff_out);
 }
 
 /* Sum of squared reconstruction errors of a candidate, accumulated in index
@@ -250,6 +256,99 @@ ORC_API void orc_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t
             for (int i = 0; i < NVFP4_BLOCK; i += 2)
                 codes[r * (K / 2) + (b * NVFP4_BLOCK + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
         }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Numerics variants of NVFP4 [nopree.com, section 第二个决定: 16x16 block     */
+/* scaling keeps the scales through a transpose but one outlier among 256    */
+/* values flattens the rest; hackernews.jp, recipe notes: the random Hadamard */
+/* transform option].                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* 16x16 2-D blocks: one per-tensor outer scale g = amax / 2688; the E4M3
+ * scale of tile (i, j) (rows 16i.., columns 16j..) from the tile's amax,
+ * s = E4M3(a / (6 g)); every 16-value row piece of the tile then quantized as
+ * a 1x16 block under that scale.  codes [M, K/2], scales [M/16, K/16],
+ * outer [1].  M % 16 == 0, K % 16 == 0. */
+ORC_API void orc_quantize_nvfp4_2d(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
+                                   float *outer) {
+    float A = 0.0f;
+    for (int64_t i = 0; i < M * K; i++) {
+        float m = fabsf(orc_bf16_to_f32(x[i]));
+        if (m > A) A = m;
+    }
+    const float g = (A == 0.0f) ? 0.0f : A / 2688.0f;
+    *outer = g;
+#pragma omp parallel for schedule(static)
+    for (int64_t ti = 0; ti < M / 16; ti++)
+        for (int64_t tj = 0; tj < K / 16; tj++) {
+            float a = 0.0f;
+            for (int r = 0; r < 16; r++)
+                for (int c = 0; c < 16; c++) {
+                    float m = fabsf(orc_bf16_to_f32(x[(16 * ti + r) * K + 16 * tj + c]));
+                    if (m > a) a = m;
+                }
+            uint8_t s = 0;
+            for (int r = 0; r < 16; r++) {
+                float xb[NVFP4_BLOCK];
+                uint8_t q[NVFP4_BLOCK];
+                float eff;
+                const int64_t row = 16 * ti + r;
+                for (int c = 0; c < 16; c++) xb[c] = orc_bf16_to_f32(x[row * K + 16 * tj + c]);
+                s = nvfp4_block_with_amax(xb, a, g, 6.0f, q, &eff);
+                for (int c = 0; c < 16; c += 2)
+                    codes[row * (K / 2) + (16 * tj + c) / 2] = (uint8_t)(q[c] | (q[c + 1] << 4));
+            }
+            scales[ti * (K / 16) + tj] = s;
+        }
+}
+
+/* 16-point random Hadamard transform of one block, in place, in f32: negate
+ * element i where bit i of `signs` is set, then the Walsh-Hadamard butterflies
+ * (a, b) -> (a + b, a - b) at distances 1, 2, 4, 8 in index order, then
+ * scale by 1/4 (exact), so the transform is orthonormal. */
+ORC_API void orc_rht16(float *v, uint32_t signs) {
+    for (int i = 0; i < 16; i++)
+        if ((signs >> i) & 1u) v[i] = -v[i];
+    for (int h = 1; h < 16; h *= 2)
+        for (int j = 0; j < 16; j += 2 * h)
+            for (int i = j; i < j + h; i++) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    for (int i = 0; i < 16; i++) v[i] *= 0.25f;
+}
+
+/* Per-token NVFP4 of the transformed rows: every 16-value block of row r goes
+ * through orc_rht16 (in f32, no rounding back to bf16), then the per-token
+ * quantization (standard or 4/6) of the transformed row.  A product of two
+ * operands transformed along their common K dimension with the same signs is
+ * unchanged (the transform is orthonormal), so the GEMM consumes them as
+ * they are. */
+ORC_API void orc_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, uint32_t signs, int mode46,
+                                    uint8_t *codes, uint8_t *scales, float *outer) {
+    const int64_t nblk = K / NVFP4_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < M; r++) {
+        float *y = (float *)malloc(sizeof(float) * (size_t)K);
+        for (int64_t k = 0; k < K; k++) y[k] = orc_bf16_to_f32(x[r * K + k]);
+        float A = 0.0f;
+        for (int64_t b = 0; b < nblk; b++) {
+            orc_rht16(y + b * NVFP4_BLOCK, signs);
+            for (int i = 0; i < NVFP4_BLOCK; i++)
+                if (fabsf(y[b * NVFP4_BLOCK + i]) > A) A = fabsf(y[b * NVFP4_BLOCK + i]);
+        }
+        const float g = (A == 0.0f) ? 0.0f : A / 2688.0f;
+        outer[r] = g;
+        for (int64_t b = 0; b < nblk; b++) {
+            uint8_t q[NVFP4_BLOCK];
+            scales[r * nblk + b] = nvfp4_quantize_block(y + b * NVFP4_BLOCK, g, mode46, q);
+            for (int i = 0; i < NVFP4_BLOCK; i += 2)
+                codes[r * (K / 2) + (b * NVFP4_BLOCK + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+        }
+        free(y);
     }
 }
 

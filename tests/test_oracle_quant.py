@@ -540,3 +540,98 @@ def test_grouped_requant_scales_each_group_by_its_own_outer():
         assert G[gi] == r1g[0] == outer_x[rows].max()
         np.testing.assert_array_equal(cT[:, Pg[gi] // 2:Pg[gi + 1] // 2], r1c)
         np.testing.assert_array_equal(sT[:, Pg[gi] // 16:Pg[gi + 1] // 16], r1s)
+
+
+# --- numerics variants: 16x16 2-D scaling and the random Hadamard transform ---
+
+def _nibble_transpose(codes, M, K):
+    q = np.empty((M, K), np.uint8)
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    qt = np.ascontiguousarray(q.T)
+    return (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_2d_scaling_is_transpose_invariant():
+    """16x16 blocks keep their scales through a transpose [nopree.com, section
+    第二个决定]: quantizing the transpose gives the transposed codes and scales."""
+    M, K = 64, 96
+    x = synth.activations(41, M, K)
+    c, s, g = oracle.quantize_nvfp4_2d(x)
+    ct, st, gt = oracle.quantize_nvfp4_2d(np.ascontiguousarray(x.T))
+    assert g[0] == gt[0]
+    np.testing.assert_array_equal(st, s.T)
+    np.testing.assert_array_equal(ct, _nibble_transpose(c, M, K))
+
+
+def test_2d_scaling_of_repeated_rows_equals_1x16_per_tensor():
+    """When the 16 rows of every band are equal, a tile's amax is its row
+    piece's amax, so 2-D scaling reduces to 1x16 blocks under one tensor scale."""
+    M, K = 48, 64
+    base = synth.activations(42, M // 16, K)
+    x = np.repeat(base, 16, axis=0)
+    c, s, g = oracle.quantize_nvfp4_2d(x)
+    c1, s1, g1 = oracle.quantize_nvfp4(x, rows_per_scale=M)
+    assert g[0] == g1[0]
+    np.testing.assert_array_equal(c, c1)
+    np.testing.assert_array_equal(np.repeat(s, 16, axis=0), s1)
+
+
+def test_2d_scaling_one_outlier_flattens_its_tile():
+    """The pages' warning about 16x16 blocks: one large value among 256 and the
+    other 255 quantize to zero, where 1x16 blocks keep the other rows."""
+    x = np.full((16, 16), 0.75, np.float32)
+    x[::2] *= -1
+    x[0, 0] = 2688.0                    # g = 1, tile scale E4M3(2688 / 6) = 448
+    xb = synth.bf16_bits_from_f32(x)
+    c, s, g = oracle.quantize_nvfp4_2d(xb)
+    assert g[0] == 1.0 and s[0, 0] == oracle.e4m3_encode(448.0)
+    mags = np.stack([c & 7, (c >> 4) & 7], axis=-1).reshape(16, 16)
+    assert mags[0, 0] == 7 and np.count_nonzero(mags) == 1
+    c1, s1, g1 = oracle.quantize_nvfp4(xb, rows_per_scale=16)
+    mags1 = np.stack([c1 & 7, (c1 >> 4) & 7], axis=-1).reshape(16, 16)
+    assert np.count_nonzero(mags1[1:]) == 15 * 16
+
+
+def test_rht16_matches_the_hadamard_matrix():
+    """The transform is (1/4) H16 D with H16 the Sylvester Hadamard matrix
+    (scipy) and D the sign flips: exact on small integers, and inverted by
+    D H16 / 4."""
+    from scipy.linalg import hadamard
+    Hm = hadamard(16).astype(np.float64)
+    rng = np.random.default_rng(3)
+    v = rng.integers(-64, 65, (50, 16)).astype(np.float32)
+    for signs in (0, 0xA5C3, 0xFFFF):
+        d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+        got = oracle.rht16(v, signs).astype(np.float64)
+        ref = (v.astype(np.float64) * d) @ Hm.T / 4
+        np.testing.assert_array_equal(got, ref)
+        back = (got @ Hm.T / 4) * d
+        np.testing.assert_array_equal(back, v)
+
+
+def test_rht_quantize_is_quantize_of_the_transformed_rows():
+    """Rows built from signed Hadamard columns transform to scaled unit
+    vectors, exact in bf16: RHT-then-quantize equals the plain per-token
+    quantizer on the transformed rows."""
+    from scipy.linalg import hadamard
+    Hm = hadamard(16).astype(np.float64)
+    signs = 0x3C5A
+    d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    rng = np.random.default_rng(4)
+    M, K = 8, 64
+    y = np.zeros((M, K), np.float64)
+    for r in range(M):
+        for b in range(K // 16):
+            y[r, 16 * b + rng.integers(0, 16)] = 4.0 * rng.choice([0.5, 1.0, 1.5, 3.0, -2.0, 6.0])
+    x = np.empty_like(y)
+    for b in range(K // 16):
+        x[:, 16 * b:16 * b + 16] = (y[:, 16 * b:16 * b + 16] @ Hm / 4) * d   # the inverse transform
+    xb = synth.bf16_bits_from_f32(x.astype(np.float32))
+    assert np.array_equal(synth.f32_from_bf16_bits(xb).astype(np.float64), x)
+    for m46 in (False, True):
+        c, s, g = oracle.quantize_nvfp4_rht(xb, signs, mode46=m46)
+        c1, s1, g1 = oracle.quantize_nvfp4(synth.bf16_bits_from_f32(y.astype(np.float32)), mode46=m46)
+        np.testing.assert_array_equal(g, g1)
+        np.testing.assert_array_equal(s, s1)
+        np.testing.assert_array_equal(c, c1)
