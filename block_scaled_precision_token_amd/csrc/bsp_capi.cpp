@@ -90,6 +90,29 @@ BSP_EXPORT bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M,
                                                  (flags & BSP_NVFP4_46) != 0, as_stream(stream)));
 }
 
+BSP_EXPORT bsp_status bsp_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint32_t signs,
+                                             uint8_t *codes, uint8_t *scales, float *outer, uint32_t flags,
+                                             void *stream) {
+    if (!x || !codes || !scales || !outer) return BSP_ERR_INVALID_ARG;
+    if (flags & ~BSP_NVFP4_46) return BSP_ERR_INVALID_ARG;
+    if (signs > 0xFFFFu) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K < 16 || K % 16 || K > 8192 || ldx < K) return BSP_ERR_SHAPE;
+    if (!aligned16(x) || ldx % 8 || !aligned16(codes) || !aligned16(scales) || !aligned16(outer))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_quantize_nvfp4_rht(x, M, K, ldx, signs, codes, scales, outer,
+                                                     (flags & BSP_NVFP4_46) != 0, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_quantize_nvfp4_2d(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes,
+                                            uint8_t *scales, float *outer, void *stream) {
+    if (!x || !codes || !scales || !outer) return BSP_ERR_INVALID_ARG;
+    if (M <= 0 || K <= 0 || M % 16 || K % 16 || ldx < K) return BSP_ERR_SHAPE;
+    if (M / 16 > 65535) return BSP_ERR_SHAPE;
+    if (!aligned16(x) || ldx % 8 || !aligned16(codes) || !aligned16(scales) || !aligned16(outer))
+        return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_quantize_nvfp4_2d(x, M, K, ldx, codes, scales, outer, as_stream(stream)));
+}
+
 BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx,
                                          const int32_t *row_gather, int64_t M, int64_t batch, uint8_t *codes_row,
                                          uint8_t *scales_row, uint8_t *codes_colT, uint8_t *scales_colT,

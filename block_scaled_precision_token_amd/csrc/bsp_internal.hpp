@@ -11,6 +11,10 @@ namespace bsp {
 
 hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, uint8_t *codes,
                                  uint8_t *scales, float *outer, bool m46, hipStream_t s);
+hipError_t launch_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint32_t signs,
+                                     uint8_t *codes, uint8_t *scales, float *outer, bool m46, hipStream_t s);
+hipError_t launch_quantize_nvfp4_2d(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes,
+                                    uint8_t *scales, float *outer, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int64_t ldx, const int32_t *gather,
                                  int64_t M, uint8_t *codes_row, uint8_t *scales_row, uint8_t *codes_colT,
                                  uint8_t *scales_colT, int64_t ld_colT, const int64_t *group_offsets, int64_t G,

@@ -98,12 +98,37 @@ __device__ __forceinline__ Nvfp4Block nvfp4_block(const float (&xf)[16], float g
     return (e4 < e6) ? b4 : b6;
 }
 
+// 16-point random Hadamard transform of one block in f32: negate the
+// elements whose bit is set in `signs`, Walsh-Hadamard butterflies (a, b) ->
+// (a + b, a - b) at distances 1, 2, 4, 8, then scale by 1/4 (exact): an
+// orthonormal transform, so two operands transformed along their common K
+// give the same product.
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        if ((signs >> i) & 1u) v[i] = -v[i];
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int j = 0; j < 16; j += 2 * h)
+#pragma unroll
+            for (int i = j; i < j + h; i++) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] *= 0.25f;
+}
+
 // Outer scope = one row, whole row kept in registers: one wavefront per row,
-// lane l owns the 16-value blocks starting at k = 1024 j + 16 l.
-template <bool M46, int MAXIT>
+// lane l owns the 16-value blocks starting at k = 1024 j + 16 l.  RHT: every
+// block transformed first (the row's scale from the transformed values).
+template <bool M46, int MAXIT, bool RHT = false>
 __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                    int64_t ldx, uint8_t *__restrict__ codes,
-                                                   uint8_t *__restrict__ scales, float *__restrict__ outer) {
+                                                   uint8_t *__restrict__ scales, float *__restrict__ outer,
+                                                   uint32_t signs = 0) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
@@ -118,6 +143,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ 
             v[j][1] = *reinterpret_cast<const uint4 *>(xr + k0 + 8);
             float xf[16];
             unpack16(v[j], xf);
+            if (RHT) rht16(xf, signs);
             amax = fmaxf(amax, absmax16(xf));
         }
     }
@@ -130,11 +156,40 @@ __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ 
         if (k0 < K) {
             float xf[16];
             unpack16(v[j], xf);
+            if (RHT) rht16(xf, signs);
             Nvfp4Block b = nvfp4_block<M46>(xf, g);
             *reinterpret_cast<uint2 *>(codes + row * (K / 2) + k0 / 2) = make_uint2(b.lo, b.hi);
             scales[row * (K / 16) + k0 / 16] = (uint8_t)b.s;
         }
     }
+}
+
+// 16x16 2-D blocks under one per-tensor outer scale (outer[0], computed
+// before): workgroup (column tile of 256, band of 16 rows); thread 16 j + r
+// owns row r of tile j (16 values), the tile's amax is a 16-lane maximum, and
+// each row piece is quantized as a 1x16 block under the tile's scale.
+__global__ __launch_bounds__(256) void k_nvfp4_2d(const uint16_t *__restrict__ x, int64_t K, int64_t ldx,
+                                                  uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                  const float *__restrict__ outer) {
+    const int t = threadIdx.x, j = t >> 4, r = t & 15;
+    const int64_t row = (int64_t)blockIdx.y * 16 + r, k0 = (int64_t)blockIdx.x * 256 + 16 * j;
+    const bool live = k0 < K;
+    float xf[16];
+    float a = 0.0f;
+    if (live) {
+        uint4 v[2];
+        v[0] = *reinterpret_cast<const uint4 *>(x + row * ldx + k0);
+        v[1] = *reinterpret_cast<const uint4 *>(x + row * ldx + k0 + 8);
+        unpack16(v, xf);
+        a = absmax16(xf);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if (!live) return;
+    float eff;
+    const Nvfp4Block b = nvfp4_candidate(xf, a, outer[0], 6.0f, eff);
+    *reinterpret_cast<uint2 *>(codes + row * (K / 2) + k0 / 2) = make_uint2(b.lo, b.hi);
+    if (r == 0) scales[(int64_t)blockIdx.y * (K / 16) + k0 / 16] = (uint8_t)b.s;
 }
 
 // Scope amax for scopes of several rows (or rows too long to keep in
@@ -210,6 +265,45 @@ static int grid_for(int64_t work, int per_block = 256, int cap = 65536) {
     return (int)(g > cap ? cap : g);
 }
 
+hipError_t launch_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint32_t signs,
+                                     uint8_t *codes, uint8_t *scales, float *outer, bool m46, hipStream_t s) {
+    dim3 grid((unsigned)((M + 3) / 4)), block(256);
+    if (K <= 2048) {
+        if (m46) k_nvfp4_row<true, 2, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
+        else k_nvfp4_row<false, 2, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
+    } else {
+        if (m46) k_nvfp4_row<true, 8, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
+        else k_nvfp4_row<false, 8, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
+    }
+    return hipGetLastError();
+}
+
+static hipError_t launch_scope_outer(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, float *outer,
+                                     hipStream_t s);
+
+hipError_t launch_quantize_nvfp4_2d(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes,
+                                    uint8_t *scales, float *outer, hipStream_t s) {
+    const hipError_t e = launch_scope_outer(x, M, K, ldx, M, outer, s);
+    if (e != hipSuccess) return e;
+    k_nvfp4_2d<<<dim3((unsigned)((K + 255) / 256), (unsigned)(M / 16)), 256, 0, s>>>(x, K, ldx, codes, scales, outer);
+    return hipGetLastError();
+}
+
+// Outer scales of scopes of rps rows: amax per scope, then g = amax / 2688.
+static hipError_t launch_scope_outer(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, float *outer,
+                                     hipStream_t s) {
+    const int64_t nscope = M / rps;
+    k_fill_f32<<<grid_for(nscope), 256, 0, s>>>(outer, nscope, 0.0f);
+    const int64_t per_scope = rps * (K / 16);
+    int64_t slices = (2048 + nscope - 1) / nscope;                     // about 2048 blocks in flight
+    const int64_t max_slices = (per_scope + 1023) / 1024;              // at least 1024 16-blocks each
+    slices = slices < max_slices ? slices : max_slices;
+    slices = slices < 1 ? 1 : (slices > 65535 ? 65535 : slices);
+    k_scope_amax<<<dim3((unsigned)nscope, (unsigned)slices), 256, 0, s>>>(x, K, ldx, rps, outer);
+    k_amax_to_g<<<grid_for(nscope), 256, 0, s>>>(outer, nscope);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, uint8_t *codes,
                                  uint8_t *scales, float *outer, bool m46, hipStream_t s) {
     if (rps == 1 && K <= 8192) {
@@ -223,16 +317,9 @@ hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_
         }
         return hipGetLastError();
     }
-    const int64_t nscope = M / rps;
-    k_fill_f32<<<grid_for(nscope), 256, 0, s>>>(outer, nscope, 0.0f);
+    const hipError_t e = launch_scope_outer(x, M, K, ldx, rps, outer, s);
+    if (e != hipSuccess) return e;
     const int64_t nblk = M * (K / 16);
-    const int64_t per_scope = rps * (K / 16);
-    int64_t slices = (2048 + nscope - 1) / nscope;                     // about 2048 blocks in flight
-    const int64_t max_slices = (per_scope + 1023) / 1024;              // at least 1024 16-blocks each
-    slices = slices < max_slices ? slices : max_slices;
-    slices = slices < 1 ? 1 : (slices > 65535 ? 65535 : slices);
-    k_scope_amax<<<dim3((unsigned)nscope, (unsigned)slices), 256, 0, s>>>(x, K, ldx, rps, outer);
-    k_amax_to_g<<<grid_for(nscope), 256, 0, s>>>(outer, nscope);
     if (m46) k_nvfp4_blocks<true><<<grid_for(nblk, 256, 16384), 256, 0, s>>>(x, M, K, ldx, rps, codes, scales, outer);
     else k_nvfp4_blocks<false><<<grid_for(nblk, 256, 16384), 256, 0, s>>>(x, M, K, ldx, rps, codes, scales, outer);
     return hipGetLastError();

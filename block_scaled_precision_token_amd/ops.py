@@ -35,7 +35,8 @@ EXPORTED = [
     "bsp_requant_transpose_sr", "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes",
     "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
     "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size", "bsp_requant_transpose_sr_batched",
-    "bsp_requant_batched_workspace_size", "bsp_requant_transpose_sr_grouped",
+    "bsp_requant_batched_workspace_size", "bsp_requant_transpose_sr_grouped", "bsp_quantize_nvfp4_rht",
+    "bsp_quantize_nvfp4_2d",
 ]
 
 
@@ -61,6 +62,8 @@ def _declare(lib):
     lib.bsp_status_string.argtypes = [INT]
     lib.bsp_status_string.restype = ctypes.c_char_p
     lib.bsp_quantize_nvfp4_per_token.argtypes = [P, I64, I64, I64, I64, P, P, P, U32, P]
+    lib.bsp_quantize_nvfp4_rht.argtypes = [P, I64, I64, I64, U32, P, P, P, U32, P]
+    lib.bsp_quantize_nvfp4_2d.argtypes = [P, I64, I64, I64, P, P, P, P]
     lib.bsp_quantize_mxfp8.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P, P, I64, P, I64, U32, P]
     lib.bsp_dequantize.argtypes = [INT, P, P, P, I64, I64, I64, P, INT, P]
     lib.bsp_requant_transpose_sr.argtypes = [P, P, P, I64, I64, P, P, P, U64, U32, P, SZ, P]
@@ -85,7 +88,8 @@ def _declare(lib):
     lib.bsp_gemm_workspace_size.restype = SZ
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
-                 "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched", "bsp_requant_transpose_sr_grouped"):
+                 "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched", "bsp_requant_transpose_sr_grouped",
+                 "bsp_quantize_nvfp4_rht", "bsp_quantize_nvfp4_2d"):
         getattr(lib, name).restype = INT
 
 
@@ -203,6 +207,40 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
                                        ld_colT or 0, _ptr(group_offsets), G, 0, _stream(dev))
     _check(st, "bsp_quantize_mxfp8")
     return res
+
+
+def quantize_nvfp4_rht(x: torch.Tensor, signs: int, mode46: bool = False, out=None):
+    """bf16 [M, K] -> per-token NVFP4 of the 16-point-RHT'd rows (codes, scales, outer [M])."""
+    _need_cuda(x, "x")
+    _rowmajor(x, "x")
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+               torch.empty((M,), dtype=torch.float32, device=dev))
+    codes, scales, outer = out
+    st = _lib_raw().bsp_quantize_nvfp4_rht(_ptr(x), M, K, x.stride(0), signs, _ptr(codes), _ptr(scales), _ptr(outer),
+                                           NVFP4_46 if mode46 else 0, _stream(dev))
+    _check(st, "bsp_quantize_nvfp4_rht")
+    return codes, scales, outer
+
+
+def quantize_nvfp4_2d(x: torch.Tensor, out=None):
+    """bf16 [M, K] -> NVFP4 with 16x16 block scales (codes [M, K/2], scales [M/16, K/16], outer [1])."""
+    _need_cuda(x, "x")
+    _rowmajor(x, "x")
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M // 16, K // 16), dtype=torch.uint8, device=dev),
+               torch.empty((4,), dtype=torch.float32, device=dev))
+    codes, scales, outer = out
+    st = _lib_raw().bsp_quantize_nvfp4_2d(_ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales), _ptr(outer),
+                                          _stream(dev))
+    _check(st, "bsp_quantize_nvfp4_2d")
+    return codes, scales, outer
 
 
 def dequantize(fmt: int, codes, scales, outer=None, rows_per_scale: int = 1, out_dtype=torch.float32, out=None):

@@ -139,6 +139,34 @@ bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, int6
                               uint32_t flags, void *stream);
 
 /*
+ * NVFP4 numerics variants [nopree.com, section 第二个决定: 16x16 block scales
+ * survive a transpose, but one outlier among 256 values flattens the other
+ * 255; hackernews.jp, recipe notes: the random Hadamard transform option].
+ *
+ * bsp_quantize_nvfp4_rht: per-token NVFP4 (standard, or 4/6 with
+ * BSP_NVFP4_46) of the rows after a 16-point random Hadamard transform of
+ * every 16-value block, in f32: negate element i where bit i of `signs`
+ * (< 2^16) is set, Walsh-Hadamard butterflies (a, b) -> (a + b, a - b) at
+ * distances 1, 2, 4, 8, scale by 1/4.  The transform is orthonormal, so two
+ * operands transformed with the same signs along their common K multiply as
+ * the originals (the GEMM takes them as they are); the outer scale is the
+ * transformed row's.  Outputs as bsp_quantize_nvfp4_per_token with
+ * rows_per_scale = 1; 16 <= K <= 8192, K % 16 == 0.
+ *
+ * bsp_quantize_nvfp4_2d: 16x16 2-D blocks under one per-tensor outer scale
+ * g = amax / 2688 (outer [1]); tile (i, j)'s E4M3 scale s = E4M3(a / (6 g))
+ * from the tile's amax, stored at scales[i * (K/16) + j] ([M/16, K/16]);
+ * every 16-value row piece of the tile is then coded as a 1x16 block under
+ * that scale (codes [M, K/2] as usual).  The transposed tensor's
+ * quantization is the nibble transpose of the codes with the transposed
+ * scales.  M % 16 == 0 (M/16 <= 65535), K % 16 == 0.
+ */
+bsp_status bsp_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint32_t signs,
+                                  uint8_t *codes, uint8_t *scales, float *outer, uint32_t flags, void *stream);
+bsp_status bsp_quantize_nvfp4_2d(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes,
+                                 uint8_t *scales, float *outer, void *stream);
+
+/*
  * Dequantize NVFP4 or MXFP8 to f32 or bf16 [remio.ai, section "Entrambe le
  * ricette supportano ...": the dequantized backward rebuilds BF16 from the
  * exact low-precision values used in the forward; alphasignal.ai, Recipe 2].

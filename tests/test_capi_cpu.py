@@ -188,6 +188,20 @@ def test_requant_grouped_bad_arguments():
     assert r(A, A, A, 64, MIS, A, 2, 64, 64, A, A, 128, A, 0, 0, None) == 3           # misaligned gather
 
 
+def test_nvfp4_variants_reject_bad_arguments():
+    r = L.bsp_quantize_nvfp4_rht
+    assert r(A, 64, 64, 64, 0x10000, A, A, A, 0, None) == 1       # signs past 16 bits
+    assert r(A, 64, 64, 64, 0x1234, A, A, A, 0x2, None) == 1      # unknown flag
+    assert r(A, 64, 16384, 16384, 1, A, A, A, 0, None) == 2       # rows longer than 8192
+    assert r(A, 64, 72, 64, 1, A, A, A, 0, None) == 2             # ldx < K
+    assert r(A, 64, 64, 68, 1, A, A, A, 0, None) == 3             # ldx % 8
+    d = L.bsp_quantize_nvfp4_2d
+    assert d(A, 40, 64, 64, A, A, A, None) == 2                   # M % 16
+    assert d(A, 64, 40, 64, A, A, A, None) == 2                   # K % 16
+    assert d(None, 64, 64, 64, A, A, A, None) == 1
+    assert d(MIS, 64, 64, 64, A, A, A, None) == 3
+
+
 def test_python_binding_fails_loudly_without_device_tensors():
     import torch
     with pytest.raises(ValueError):

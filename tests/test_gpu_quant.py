@@ -351,6 +351,38 @@ def test_requant_grouped_parity(T, K, counts, gathered, sr):
     assert_bytes_equal(host(ct), rct, "codesT")
 
 
+@pytest.mark.parametrize("M,K", [(64, 2048), (37, 4096), (8, 16), (16, 8192)])
+@pytest.mark.parametrize("m46", [False, True])
+def test_nvfp4_rht_parity(M, K, m46):
+    x = synth.activations(20261222 + K, M, K)
+    signs = 0x9C35 ^ K
+    c, s, g = ops.quantize_nvfp4_rht(to_dev_bf16(x), signs, mode46=m46)
+    rc, rs, rg = oracle.quantize_nvfp4_rht(x, signs, mode46=m46)
+    assert_bytes_equal(host(g), rg, "outer")
+    assert_bytes_equal(host(s), rs, "scales")
+    assert_bytes_equal(host(c), rc, "codes")
+
+
+@pytest.mark.parametrize("M,K", [(64, 2048), (48, 272), (16, 16), (256, 7168)])
+def test_nvfp4_2d_parity(M, K):
+    x = synth.activations(20261223 + K, M, K)
+    c, s, g = ops.quantize_nvfp4_2d(to_dev_bf16(x))
+    rc, rs, rg = oracle.quantize_nvfp4_2d(x)
+    assert_bytes_equal(host(g)[:1], rg, "outer")
+    assert_bytes_equal(host(s), rs, "scales")
+    assert_bytes_equal(host(c), rc, "codes")
+
+
+def test_nvfp4_2d_outlier_tile_on_device():
+    # the pages' example: one large value among 256 flattens the other 255
+    x = np.full((16, 32), 0.75, np.float32)
+    x[0, 0] = 2688.0
+    c, s, g = ops.quantize_nvfp4_2d(to_dev_bf16(synth.bf16_bits_from_f32(x)))
+    c = host(c)
+    mags = np.stack([c & 7, (c >> 4) & 7], axis=-1).reshape(16, 32)
+    assert mags[0, 0] == 7 and np.count_nonzero(mags[:, :16]) == 1 and np.count_nonzero(mags[:, 16:]) == 256
+
+
 # ---------------------------------------------------------------------------
 # SwiGLU + quantize
 # ---------------------------------------------------------------------------
