@@ -788,15 +788,27 @@ WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp
 
 # ---------------------------------------------------------------------------
 
-def kernel_source_digest():
-    """sha256 over the HIP sources the library is built from (file names and
-    code with comments and whitespace runs removed, so that documentation edits
-    keep the measurements valid)."""
+# The source files an op's kernels are compiled from (the shared device and
+# launch headers included): the grouped GEMMs, and everything else.
+KERNEL_SOURCES = {"gemm": ("bsp_gemm.hip", "bsp_device.hpp", "bsp_internal.hpp"),
+                  "other": ("bsp_quant.hip", "bsp_device.hpp", "bsp_internal.hpp")}
+
+
+def kernel_sources_of(op):
+    return KERNEL_SOURCES["gemm" if op.startswith("gemm") else "other"]
+
+
+def kernel_source_digest(files=None):
+    """sha256 over HIP sources the library is built from (all of them, or the
+    given files): file names and code with comments and whitespace runs
+    removed, so that documentation edits keep the measurements valid."""
     import hashlib
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_precision_token_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if files is not None and name not in files:
+            continue
         if name.endswith((".hip", ".hpp", ".cpp", ".h")):
             with open(os.path.join(csrc, name)) as f:
                 text = f.read()
@@ -819,7 +831,7 @@ def measured_traffic(workload, op):
     except (OSError, ValueError):
         return None
     ent = table.get("ops", {}).get(f"{workload}/{op}")
-    if not ent or ent.get("source_sha256") != kernel_source_digest():
+    if not ent or ent.get("source_sha256") != kernel_source_digest(kernel_sources_of(op)):
         return None
     return ent.get("bytes_per_launch")
 
