@@ -409,17 +409,30 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
         // offsets are trusted only up to the copies' width
         T.kbeg = (int)(kb < 0 ? 0 : kb < p.K ? kb : p.K);
         T.kend = (int)(ke < 0 ? 0 : ke < p.K ? ke : p.K);
+        T.col0 = tx * BT;
+        T.slot = ty;
     } else {
+        // An expert's tiles occupy [t0 ntn, (t0 + nt) ntn) of the tile order
+        // (t0: its first row tile, nt: its row-tile count); inside that range
+        // the row tiles vary fastest, so the workgroups running an expert's
+        // tiles at one time share its weight panels.
         const int64_t tile = sload(p.tiles, ty);   // valid: ty < the listed tile count
         T.g = __builtin_amdgcn_readfirstlane((int)(tile >> 40));
-        T.row0 = (int)(tile & ((1ll << 40) - 1));
-        const int64_t re = sload(p.group_offsets, T.g + 1);
+        const int64_t r0 = tile & ((1ll << 40) - 1);
+        const int64_t rb = sload(p.group_offsets, T.g), re = sload(p.group_offsets, T.g + 1);
+        // the row-tile count as the tile list counts it (rows clamped to M)
+        const int64_t lo = rb < p.M ? rb : p.M, hi = re < p.M ? re : p.M;
+        const int t0 = ty - (int)((r0 - rb) / BT);
+        const int nt = hi > lo ? (int)((hi - lo + BT - 1) / BT) : 1;
+        const int local = lin - t0 * p.ntn;
+        const int tyc = t0 + local % nt;
+        T.col0 = (local / nt) * BT;
+        T.slot = tyc;
+        T.row0 = (int)(rb + (int64_t)(tyc - t0) * BT);
         T.row_end = (int)(re < p.M ? re : p.M);   // never past the rows of C
         T.kbeg = 0;
         T.kend = p.K;
     }
-    T.col0 = tx * BT;
-    T.slot = ty;
     T.nk = T.kend > T.kbeg ? (T.kend - T.kbeg + BK - 1) / BK : 0;
     return T;
 }
