@@ -632,11 +632,41 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, i
 // Dequantize
 // --------------------------------------------------------------------------
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t *__restrict__ codes,
-                                                       const uint8_t *__restrict__ scales,
-                                                       const float *__restrict__ outer, int64_t M, int64_t K,
-                                                       int64_t rps, void *__restrict__ out) {
+// bf16 output: one lane per half block (8 values), so that a store
+// instruction covers 1 KB of output contiguously; values decoded two at a
+// time by V_CVT_SCALEF32_PK_F32_FP4 at scale 1 (exact), scaled in f32 and
+// rounded to bf16 (RNE) in pairs, stored non-temporally (the output is a
+// stream the GEMM reads later, far beyond the caches).
+__global__ __launch_bounds__(256) void k_dequant_nvfp4_bf16(const uint8_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            const float *__restrict__ outer, int64_t M, int64_t K,
+                                                            int64_t rps, uint16_t *__restrict__ out) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const int64_t nb = K / 16, total = 2 * M * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t blk = i >> 1, r = blk / nb;
+        const float eff = e4m3_decode(scales[blk]) * outer[r / rps];
+        const uint32_t c = reinterpret_cast<const uint32_t *>(codes)[i];
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const auto v = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)
+                         : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1)
+                         : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2)
+                                  : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+            w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[0] * eff, v[1] * eff}, bf2));
+        }
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(out + i * 8));
+    }
+}
+
+// f32 output: one lane per 16-value block.
+__global__ __launch_bounds__(256) void k_dequant_nvfp4_f32(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales,
+                                                           const float *__restrict__ outer, int64_t M, int64_t K,
+                                                           int64_t rps, float *__restrict__ out) {
     const int64_t nb = K / 16, total = M * nb;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -649,18 +679,9 @@ __global__ __launch_bounds__(256) void k_dequant_nvfp4(const uint8_t *__restrict
             y[j] = e2m1_value((c.x >> (4 * j)) & 15u) * eff;
             y[8 + j] = e2m1_value((c.y >> (4 * j)) & 15u) * eff;
         }
-        if (BF16) {
-            uint32_t w[8];
+        float4 *d = reinterpret_cast<float4 *>(out + i * 16);
 #pragma unroll
-            for (int j = 0; j < 8; j++) w[j] = f32_to_bf16(y[2 * j]) | (f32_to_bf16(y[2 * j + 1]) << 16);
-            uint4 *d = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + i * 16);
-            d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        } else {
-            float4 *d = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + i * 16);
-#pragma unroll
-            for (int j = 0; j < 4; j++) d[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
-        }
+        for (int j = 0; j < 4; j++) d[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
     }
 }
 
@@ -700,9 +721,12 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
                              int64_t K, int64_t rps, void *out, int out_dtype, hipStream_t s) {
     const bool bf = out_dtype == 1;
     if (fmt == 0) {
-        const int grid = grid_for(M * (K / 16), 256, 1 << 20);
-        if (bf) k_dequant_nvfp4<true><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, rps, out);
-        else k_dequant_nvfp4<false><<<grid, 256, 0, s>>>(codes, scales, outer, M, K, rps, out);
+        if (bf)
+            k_dequant_nvfp4_bf16<<<grid_for(2 * M * (K / 16), 256, 1 << 20), 256, 0, s>>>(
+                codes, scales, outer, M, K, rps, reinterpret_cast<uint16_t *>(out));
+        else
+            k_dequant_nvfp4_f32<<<grid_for(M * (K / 16), 256, 1 << 20), 256, 0, s>>>(
+                codes, scales, outer, M, K, rps, reinterpret_cast<float *>(out));
     } else {
         const int grid = grid_for(M * (K / 32), 256, 1 << 20);
         if (bf) k_dequant_mxfp8<true><<<grid, 256, 0, s>>>(codes, scales, M, K, out);

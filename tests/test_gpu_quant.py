@@ -219,12 +219,14 @@ def test_dequantize_parity(out_dtype):
     assert_bytes_equal(host(f), rf if out_dtype == torch.float32 else rb, "mxfp8 dequant")
 
 
-def test_dequantize_per_expert_scope():
-    w = synth.weights(31, 3, 32, 64)
-    rc, rs, rg = oracle.quantize_nvfp4(w, rows_per_scale=32)
-    f = ops.dequantize(ops.FMT_NVFP4, to_dev(rc), to_dev(rs), to_dev(rg), rows_per_scale=32)
-    rf, _ = oracle.dequantize_nvfp4(rc, rs, rg, rows_per_scale=32)
-    assert_bytes_equal(host(f), rf, "dequant per expert")
+@pytest.mark.parametrize("E,N,K", [(3, 32, 64), (8, 256, 2048)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_per_expert_scope(E, N, K, out_dtype):
+    w = synth.weights(31 + K, E, N, K)
+    rc, rs, rg = oracle.quantize_nvfp4(w, rows_per_scale=N)
+    f = ops.dequantize(ops.FMT_NVFP4, to_dev(rc), to_dev(rs), to_dev(rg), rows_per_scale=N, out_dtype=out_dtype)
+    rf, rb = oracle.dequantize_nvfp4(rc, rs, rg, rows_per_scale=N)
+    assert_bytes_equal(host(f), rf if out_dtype == torch.float32 else rb, "dequant per expert")
 
 
 # ---------------------------------------------------------------------------
