@@ -42,59 +42,80 @@ __device__ __forceinline__ float absmax16(const float (&xf)[16]) {
     return a;
 }
 
-// One candidate block scale with divisor D (6: standard; 4: the "4" of 4/6).
-__device__ __forceinline__ Nvfp4Block nvfp4_candidate(const float (&xf)[16], float a, float g, float D,
-                                                      float &eff) {
+// Codes of one block at effective decode scale eff = E4M3(s) * g: each value
+// times one correctly rounded reciprocal of eff, converted by
+// V_CVT_SCALEF32_PK_FP4_F32 at scale 1 (byte i of the word written in place).
+// A zero or subnormal eff flushes the block: reciprocal 0, so every code
+// keeps only its sign, and scale 0.
+__device__ __forceinline__ Nvfp4Block nvfp4_codes(const float (&xf)[16], uint32_t s, float &eff) {
+    const bool ok = eff >= kFlushBelow;
+    const float r = ok ? 1.0f / eff : 0.0f;
     Nvfp4Block b;
-    b.s = 0u;
-    eff = 0.0f;
-    if (g > 0.0f) {
-        float denom = D * g;
-        b.s = e4m3_encode(a / denom);
-        eff = e4m3_decode(b.s) * g;
-    }
+    b.s = ok ? s : 0u;
+    eff = ok ? eff : 0.0f;
     b.lo = 0u;
     b.hi = 0u;
-    if (!(g > 0.0f) || eff < kFlushBelow) {
-        b.s = 0u;
-        eff = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            b.lo |= ((__float_as_uint(xf[i]) >> 28) & 8u) << (4 * i);
-            b.hi |= ((__float_as_uint(xf[8 + i]) >> 28) & 8u) << (4 * i);
-        }
-        return b;
-    }
-    float r = 1.0f / eff;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        b.lo |= e2m1x2_hw(xf[2 * i] * r, xf[2 * i + 1] * r) << (8 * i);
-        b.hi |= e2m1x2_hw(xf[8 + 2 * i] * r, xf[8 + 2 * i + 1] * r) << (8 * i);
-    }
+#define BSP_FP4_PAIR(W, I, J) W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, xf[I] * r, xf[I + 1] * r, 1.0f, J)
+    BSP_FP4_PAIR(b.lo, 0, 0);
+    BSP_FP4_PAIR(b.lo, 2, 1);
+    BSP_FP4_PAIR(b.lo, 4, 2);
+    BSP_FP4_PAIR(b.lo, 6, 3);
+    BSP_FP4_PAIR(b.hi, 8, 0);
+    BSP_FP4_PAIR(b.hi, 10, 1);
+    BSP_FP4_PAIR(b.hi, 12, 2);
+    BSP_FP4_PAIR(b.hi, 14, 3);
+#undef BSP_FP4_PAIR
     return b;
 }
 
+// One candidate block scale with divisor D (6: standard; 4: the "4" of 4/6):
+// s = E4M3(a / (D g)) by V_CVT_PK_FP8_F32 (identical to e4m3_encode on the
+// clamped input), decoded by V_CVT_F32_FP8 (exact).  g = 0 gives s = 0.
+__device__ __forceinline__ Nvfp4Block nvfp4_candidate(const float (&xf)[16], float a, float g, float D,
+                                                      float &eff) {
+    const uint32_t s = g > 0.0f ? e4m3x2_hw(a / (D * g), 0.0f) & 0xFFu : 0u;
+    eff = __builtin_amdgcn_cvt_f32_fp8((int)s, 0) * g;
+    return nvfp4_codes(xf, s, eff);
+}
+
+// Sum of squared reconstruction errors in index order with fused
+// multiply-adds, d_i = x_i - value(q_i) * eff; the codes are decoded two at a
+// time by V_CVT_SCALEF32_PK_F32_FP4 at scale 1 (exact).
 __device__ __forceinline__ float nvfp4_sse(const float (&xf)[16], const Nvfp4Block &b, float eff) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 v[8];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.lo, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.lo, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.lo, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.lo, 1.0f, 3);
+    v[4] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.hi, 1.0f, 0);
+    v[5] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.hi, 1.0f, 1);
+    v[6] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.hi, 1.0f, 2);
+    v[7] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.hi, 1.0f, 3);
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        uint32_t c = ((i < 8 ? b.lo : b.hi) >> (4 * (i & 7))) & 15u;
-        float d = __builtin_fmaf(-e2m1_value(c), eff, xf[i]);
-        acc = __builtin_fmaf(d, d, acc);
+    for (int i = 0; i < 8; i++) {
+        const float d0 = __builtin_fmaf(-v[i].x, eff, xf[2 * i]);
+        acc = __builtin_fmaf(d0, d0, acc);
+        const float d1 = __builtin_fmaf(-v[i].y, eff, xf[2 * i + 1]);
+        acc = __builtin_fmaf(d1, d1, acc);
     }
     return acc;
 }
 
+// 4/6: both candidate scales come from one two-value conversion.
 template <bool M46>
 __device__ __forceinline__ Nvfp4Block nvfp4_block(const float (&xf)[16], float g) {
-    float a = absmax16(xf);
+    const float a = absmax16(xf);
     float eff6;
-    Nvfp4Block b6 = nvfp4_candidate(xf, a, g, 6.0f, eff6);
-    if (!M46) return b6;
-    float eff4;
-    Nvfp4Block b4 = nvfp4_candidate(xf, a, g, 4.0f, eff4);
-    float e6 = nvfp4_sse(xf, b6, eff6);
-    float e4 = nvfp4_sse(xf, b4, eff4);
+    if (!M46) return nvfp4_candidate(xf, a, g, 6.0f, eff6);
+    const uint32_t s2 = g > 0.0f ? e4m3x2_hw(a / (6.0f * g), a / (4.0f * g)) : 0u;
+    eff6 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 0) * g;
+    float eff4 = __builtin_amdgcn_cvt_f32_fp8((int)s2, 1) * g;
+    const Nvfp4Block b6 = nvfp4_codes(xf, s2 & 0xFFu, eff6);
+    const Nvfp4Block b4 = nvfp4_codes(xf, (s2 >> 8) & 0xFFu, eff4);
+    const float e6 = nvfp4_sse(xf, b6, eff6);
+    const float e4 = nvfp4_sse(xf, b4, eff4);
     return (e4 < e6) ? b4 : b6;
 }
 
@@ -121,23 +142,25 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
     for (int i = 0; i < 16; i++) v[i] *= 0.25f;
 }
 
-// Outer scope = one row, whole row kept in registers: one wavefront per row,
-// lane l owns the 16-value blocks starting at k = 1024 j + 16 l.  RHT: every
-// block transformed first (the row's scale from the transformed values).
-template <bool M46, int MAXIT, bool RHT = false>
+// Outer scope = one row, whole row kept in registers: LPR lanes per row (64,
+// or 32 / 16 for short rows so that few lanes idle), lane l of a row owning
+// the 16-value blocks starting at k = 16 LPR j + 16 l.  RHT: every block
+// transformed first (the row's scale from the transformed values).
+template <bool M46, int MAXIT, bool RHT = false, int LPR = 64>
 __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                    int64_t ldx, uint8_t *__restrict__ codes,
                                                    uint8_t *__restrict__ scales, float *__restrict__ outer,
                                                    uint32_t signs = 0) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
+    constexpr int RPW = 64 / LPR;               // rows per wavefront
+    const int lane = threadIdx.x & (LPR - 1);
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + (threadIdx.x & 63) / LPR;
+    if (row >= M) return;                       // whole row groups leave together
     const uint16_t *xr = x + row * ldx;
     uint4 v[MAXIT][2];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < MAXIT; j++) {
-        const int64_t k0 = (int64_t)j * 1024 + lane * 16;
+        const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
         if (k0 < K) {
             v[j][0] = *reinterpret_cast<const uint4 *>(xr + k0);
             v[j][1] = *reinterpret_cast<const uint4 *>(xr + k0 + 8);
@@ -147,12 +170,13 @@ __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ 
             amax = fmaxf(amax, absmax16(xf));
         }
     }
-    amax = wave_max(amax);
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
     if (lane == 0) outer[row] = g;
 #pragma unroll
     for (int j = 0; j < MAXIT; j++) {
-        const int64_t k0 = (int64_t)j * 1024 + lane * 16;
+        const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
         if (k0 < K) {
             float xf[16];
             unpack16(v[j], xf);
@@ -162,6 +186,28 @@ __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ 
             scales[row * (K / 16) + k0 / 16] = (uint8_t)b.s;
         }
     }
+}
+
+// Per-token launch: lanes per row and blocks per lane from the block count
+// nb = K / 16 (K <= 8192), so that at most a quarter of the lanes idle for
+// the row lengths of the MoE layers (768 ... 8192).
+template <bool M46, bool RHT>
+static void launch_nvfp4_row(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes, uint8_t *scales,
+                             float *outer, uint32_t signs, hipStream_t s) {
+    const int64_t nb = K / 16;
+    auto go = [&](auto kern, int lpr) {
+        const int64_t rows_per_wg = 4 * (64 / lpr);
+        kern<<<dim3((unsigned)((M + rows_per_wg - 1) / rows_per_wg)), 256, 0, s>>>(x, M, K, ldx, codes, scales,
+                                                                                     outer, signs);
+    };
+    if (nb <= 16) go(k_nvfp4_row<M46, 1, RHT, 16>, 16);
+    else if (nb <= 32) go(k_nvfp4_row<M46, 1, RHT, 32>, 32);
+    else if (nb <= 48) go(k_nvfp4_row<M46, 3, RHT, 16>, 16);
+    else if (nb <= 64) go(k_nvfp4_row<M46, 1, RHT, 64>, 64);
+    else if (nb <= 96) go(k_nvfp4_row<M46, 3, RHT, 32>, 32);
+    else if (nb <= 128) go(k_nvfp4_row<M46, 2, RHT, 64>, 64);
+    else if (nb <= 192) go(k_nvfp4_row<M46, 3, RHT, 64>, 64);
+    else go(k_nvfp4_row<M46, 8, RHT, 64>, 64);
 }
 
 // 16x16 2-D blocks under one per-tensor outer scale (outer[0], computed
@@ -267,14 +313,8 @@ static int grid_for(int64_t work, int per_block = 256, int cap = 65536) {
 
 hipError_t launch_quantize_nvfp4_rht(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint32_t signs,
                                      uint8_t *codes, uint8_t *scales, float *outer, bool m46, hipStream_t s) {
-    dim3 grid((unsigned)((M + 3) / 4)), block(256);
-    if (K <= 2048) {
-        if (m46) k_nvfp4_row<true, 2, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
-        else k_nvfp4_row<false, 2, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
-    } else {
-        if (m46) k_nvfp4_row<true, 8, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
-        else k_nvfp4_row<false, 8, true><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer, signs);
-    }
+    if (m46) launch_nvfp4_row<true, true>(x, M, K, ldx, codes, scales, outer, signs, s);
+    else launch_nvfp4_row<false, true>(x, M, K, ldx, codes, scales, outer, signs, s);
     return hipGetLastError();
 }
 
@@ -307,14 +347,8 @@ static hipError_t launch_scope_outer(const uint16_t *x, int64_t M, int64_t K, in
 hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int64_t rps, uint8_t *codes,
                                  uint8_t *scales, float *outer, bool m46, hipStream_t s) {
     if (rps == 1 && K <= 8192) {
-        dim3 grid((unsigned)((M + 3) / 4)), block(256);
-        if (K <= 2048) {
-            if (m46) k_nvfp4_row<true, 2><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
-            else k_nvfp4_row<false, 2><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
-        } else {
-            if (m46) k_nvfp4_row<true, 8><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
-            else k_nvfp4_row<false, 8><<<grid, block, 0, s>>>(x, M, K, ldx, codes, scales, outer);
-        }
+        if (m46) launch_nvfp4_row<true, false>(x, M, K, ldx, codes, scales, outer, 0u, s);
+        else launch_nvfp4_row<false, false>(x, M, K, ldx, codes, scales, outer, 0u, s);
         return hipGetLastError();
     }
     const hipError_t e = launch_scope_outer(x, M, K, ldx, rps, outer, s);
@@ -1290,20 +1324,24 @@ hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const flo
 
 // exp(x) in f32 by one fixed sequence: n = rint(x / ln 2), r = x - n ln 2 with
 // ln 2 split in a 16-bit head (n * head is exact) and a tail, e^r by its
-// degree-7 Taylor polynomial in Horner form, then the exact scaling by 2^n.
+// degree-7 Taylor polynomial in Horner form (reduction and Horner steps one
+// fused multiply-add each), then the exact scaling by 2^n.  Results are inf
+// from x = 89 and 0 up to x = -104; the sequence itself gives exactly those
+// at both ends, so the argument is clamped to [-104, 89] (one V_MED3_F32, no
+// branch) instead of testing the two cut-offs (finite x).
 __device__ __forceinline__ float exp_cw(float x) {
-    if (x >= 89.0f) return __builtin_huge_valf();
-    if (x <= -104.0f) return 0.0f;
+    x = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
     const float n = rintf(x * 1.44269504088896341f);
-    const float r = (x - n * 0.693145751953125f) - n * 1.428606765330187e-06f;
+    float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+    r = __builtin_fmaf(-n, 1.428606765330187e-06f, r);
     float p = 1.0f / 5040.0f;
-    p = p * r + 1.0f / 720.0f;
-    p = p * r + 1.0f / 120.0f;
-    p = p * r + 1.0f / 24.0f;
-    p = p * r + 1.0f / 6.0f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
+    p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
     return ldexpf(p, (int)n);
 }
 
@@ -1344,7 +1382,7 @@ __device__ __forceinline__ void load32<uint16_t>(const uint16_t *p, float (&v)[3
     }
 }
 
-// LPR lanes per row of h (64, or 32 / 16 for short rows so that lanes are
+// LPR lanes per row of h (64, or 32 / 16 / 8 for short rows so that lanes are
 // not left idle); lane l of a row owns the 32-value chunks starting at
 // i = 32 LPR j + 32 l (whole quantization blocks per lane).  Outputs whose
 // per-lane pieces are not contiguous across lanes (h, MXFP8 codes) go through
@@ -1465,9 +1503,14 @@ static void swiglu_dispatch_it(const void *h13, int64_t R, int64_t I, uint16_t *
                                uint8_t *scales, float *outer, hipStream_t s) {
     const T *in = reinterpret_cast<const T *>(h13);
     auto grid = [&](int lpr) { return dim3((unsigned)((R + 4 * (64 / lpr) - 1) / (4 * (64 / lpr)))); };
-    if (I <= 512) k_swiglu<T, FMT, M46, 1, 16><<<grid(16), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
-    else if (I <= 1024) k_swiglu<T, FMT, M46, 1, 32><<<grid(32), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
-    else if (I <= 2048) k_swiglu<T, FMT, M46, 1, 64><<<grid(64), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    // 32-value chunks per row: lanes per row and chunks per lane chosen so
+    // that at most a third of the lanes idle (none for I = 768, 1536, 2048)
+    const int64_t nc = (I + 31) / 32;
+    if (nc <= 16) k_swiglu<T, FMT, M46, 1, 16><<<grid(16), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (nc <= 24) k_swiglu<T, FMT, M46, 3, 8><<<grid(8), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (nc <= 32) k_swiglu<T, FMT, M46, 1, 32><<<grid(32), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (nc <= 48) k_swiglu<T, FMT, M46, 3, 16><<<grid(16), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
+    else if (nc <= 64) k_swiglu<T, FMT, M46, 1, 64><<<grid(64), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
     else k_swiglu<T, FMT, M46, 4, 64><<<grid(64), 256, 0, s>>>(in, R, I, h_out, codes, scales, outer);
 }
 

@@ -808,8 +808,9 @@ ORC_API void orc_gemm_bf16_wgrad(const uint16_t *a, int64_t lda, const uint16_t 
 /* with silu(z) = z / (1 + exp(-z)), gate = columns [0, I) and up = columns  */
 /* [I, 2I) of the fused gate/up output, and h stored as bf16 (RNE).  Because  */
 /* h feeds a bit-exact quantizer, exp is fixed to one explicit f32 algorithm  */
-/* (Cody-Waite reduction by ln 2, degree-7 Taylor polynomial, exact 2^n       */
-/* scaling) instead of a libm whose last bit may differ.                      */
+/* (Cody-Waite reduction by ln 2, degree-7 Taylor polynomial in Horner form,  */
+/* both with fused multiply-adds, exact 2^n scaling) instead of a libm whose  */
+/* last bit may differ.                                                       */
 /* ------------------------------------------------------------------------ */
 
 ORC_API float orc_exp_f32(float x) {
@@ -819,16 +820,18 @@ ORC_API float orc_exp_f32(float x) {
     const float ln2_hi = 0.693145751953125f;     /* ln 2 to 16 bits: n * ln2_hi is exact */
     const float ln2_lo = 1.428606765330187e-06f; /* ln 2 - ln2_hi */
     float n = nearbyintf(x * log2e);
-    float r = (x - n * ln2_hi) - n * ln2_lo;
-    /* e^r = sum_{j=0..7} r^j / j!, Horner, each step rounded */
+    /* r = x - n ln 2: the head product is exact, each step one fused multiply-add */
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    /* e^r = sum_{j=0..7} r^j / j!, Horner, one fused multiply-add per step */
     float p = 1.0f / 5040.0f;
-    p = p * r + 1.0f / 720.0f;
-    p = p * r + 1.0f / 120.0f;
-    p = p * r + 1.0f / 24.0f;
-    p = p * r + 1.0f / 6.0f;
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
     return ldexpf(p, (int)n);
 }
 

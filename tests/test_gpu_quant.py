@@ -44,7 +44,10 @@ def edge_tensor(M, K, seed=0):
 # NVFP4
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(1, 16), (7, 32), (37, 48), (256, 2048), (130, 768), (33, 7168), (9, 8208)])
+# K spans every lanes-per-row choice of the per-token kernel (16-value blocks
+# per row: 1, 25, 3, 48, 63, 96, 128, 160, 448) and the scope kernel (8208)
+@pytest.mark.parametrize("M,K", [(1, 16), (19, 400), (37, 48), (130, 768), (66, 1008), (45, 1536), (256, 2048),
+                                 (11, 2560), (33, 7168), (9, 8208)])
 @pytest.mark.parametrize("mode46", [False, True])
 def test_nvfp4_per_token_parity(M, K, mode46):
     x = edge_tensor(M, K, seed=M * 31 + K)
@@ -353,7 +356,7 @@ def test_requant_grouped_parity(T, K, counts, gathered, sr):
     assert_bytes_equal(host(ct), rct, "codesT")
 
 
-@pytest.mark.parametrize("M,K", [(64, 2048), (37, 4096), (8, 16), (16, 8192)])
+@pytest.mark.parametrize("M,K", [(64, 2048), (37, 4096), (8, 16), (16, 8192), (24, 768), (13, 1536)])
 @pytest.mark.parametrize("m46", [False, True])
 def test_nvfp4_rht_parity(M, K, m46):
     x = synth.activations(20261222 + K, M, K)
@@ -389,12 +392,16 @@ def test_nvfp4_2d_outlier_tile_on_device():
 # SwiGLU + quantize
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,I", [(5, 32), (37, 480), (130, 768), (21, 992), (17, 2048), (9, 4096)])
+@pytest.mark.parametrize("R,I", [(5, 32), (37, 480), (19, 640), (130, 768), (21, 992), (7, 1280), (44, 1536),
+                                 (17, 2048), (9, 4096)])
 @pytest.mark.parametrize("fmt,m46", [(-1, False), (0, True), (0, False), (1, False)])
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
 def test_swiglu_quantize_parity(R, I, fmt, m46, in_dtype):
     h13 = synth.fp32_matrix(R * 7 + I, R, 2 * I, std=2.5)
-    h13[0, :4] = [0.0, -0.0, 90.0, -120.0]
+    # gate values at and past the ends of exp's range (exp(-z) is inf from
+    # z = -89 and 0 from z = 104), signed zeros, large magnitudes
+    h13[0, :16] = [0.0, -0.0, 90.0, -120.0, 89.0, -89.0, 104.0, -104.0, 88.5, -103.5, 1e4, -1e4,
+                   -88.75, 103.75, 0.5, -0.5]
     if in_dtype == "bf16":
         hb = synth.bf16_bits_from_f32(h13)
         h13 = synth.f32_from_bf16_bits(hb)
