@@ -84,10 +84,15 @@ def bf16_dev(bits, dev):
 # ---------------------------------------------------------------------------
 
 class Dsv3MoeMxfp8:
-    """DeepSeek-V3-shaped MoE layer, MXFP8 forward + dgrad + wgrad (configs[4])."""
+    """DeepSeek-V3-shaped MoE layer, MXFP8 forward + dgrad + wgrad.  SwiGLU runs
+    in the gate/up GEMM's epilogue, which writes h in bf16, and one pass makes
+    h's rowwise and grouped columnwise copies; or (swiglu_epilogue False) it
+    runs with h's rowwise quantization as one kernel after the GEMM and a
+    second pass makes the columnwise copy.  Both give the same h and copies."""
     name = "dsv3_moe_mxfp8"
     unit = "TFLOP/s"
     dtype = "fp8_e4m3"
+    swiglu_epilogue = True
 
     def __init__(self, dev):
         import numpy as np
@@ -124,6 +129,8 @@ class Dsv3MoeMxfp8:
         h13 = emp(R, N13, dt=bf)
         hq = (emp(R, I, dt=bf), emp(R, I), emp(R, I // 32), None)
         hcq = {"codes_colT": emp(I, ld), "scales_colT": emp(I, ld // 32)}
+        # SwiGLU in the GEMM epilogue: h's rowwise and grouped columnwise copies in one pass
+        hrcq = {"codes_row": hq[1], "scales_row": hq[2], **hcq}
         y = emp(R, H, dt=bf)
         dyq = {"codes_row": emp(R, H), "scales_row": emp(R, H // 32), "codes_colT": emp(H, ld),
                "scales_colT": emp(H, ld // 32)}
@@ -146,12 +153,21 @@ class Dsv3MoeMxfp8:
             Op("quant_x_row", lambda: q(X, True, False, out=xq), T * H * (2 + s8)),
             Op("quant_xg_col_grouped", lambda: q(X, False, True, group_offsets=off_d, row_gather=src_d, out=xgq),
                T * H * 2 + R * H * s8),
+        ] + ([
+            Op("gemm_fprop_gate_up_swiglu", lambda: gm(M8, ops.GEMM_FPROP_SWIGLU, xq["codes_row"], xq["scales_row"],
+                                                        w13q["codes_row"], w13q["scales_row"], off_d, N13, H, M=R,
+                                                        a_gather=src_d, out=hq[0], workspace=ws),
+               G * N13 * H * s8 + T * H * s8 + R * I * 2, 2.0 * R * N13 * H, "fp8"),
+            Op("quant_h_row_col_grouped", lambda: q(hq[0], True, True, group_offsets=off_d, out=hrcq),
+               R * I * (2 + 2 * s8)),
+        ] if self.swiglu_epilogue else [
             Op("gemm_fprop_gate_up", lambda: gm(M8, F, xq["codes_row"], xq["scales_row"], w13q["codes_row"],
                                                  w13q["scales_row"], off_d, N13, H, M=R, a_gather=src_d, out=h13,
                                                  workspace=ws),
                G * N13 * H * s8 + T * H * s8 + R * N13 * 2, 2.0 * R * N13 * H, "fp8"),
             Op("swiglu_quant_h", lambda: ops.swiglu_quantize(h13, ops.FMT_MXFP8, out=hq), R * N13 * 2 + R * I * (2 + s8)),
             Op("quant_h_col_grouped", lambda: q(hq[0], False, True, group_offsets=off_d, out=hcq), R * I * (2 + s8)),
+        ]) + [
             Op("gemm_fprop_down", lambda: gm(M8, F, hq[1], hq[2], w2q["codes_row"], w2q["scales_row"], off_d, H, I,
                                               M=R, out=y, workspace=ws),
                G * H * I * s8 + R * I * s8 + R * H * 2, 2.0 * R * H * I, "fp8"),
@@ -180,7 +196,9 @@ class Dsv3MoeMxfp8:
                 "experts": self.shape["E"], "shared_experts": 1, "topk": self.shape["k"], "routed_rows": self.R,
                 "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(__import__("numpy").median(c)),
                                "min": int(c.min()), "empty": int((c == 0).sum()), "shared": int(self.counts[-1])},
-                "weights_quantized_per_step": True, "gemm_flops_per_step": self.gemm_flops}
+                "weights_quantized_per_step": True,
+                "swiglu": "gemm_epilogue" if self.swiglu_epilogue else "separate_kernel",
+                "gemm_flops_per_step": self.gemm_flops}
 
     def value(self, ms_per_step):
         return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -217,11 +235,21 @@ class Dsv3MoeMxfp8:
                           f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, weight quantization included in the time)"}
 
 
+class Dsv3MoeMxfp8SwigluSeparate(Dsv3MoeMxfp8):
+    name = "dsv3_moe_mxfp8_swiglu_separate"
+    swiglu_epilogue = False
+
+
 class Qwen3MoeNvfp4:
-    """Qwen3-30B-A3B-shaped MoE layer forward in NVFP4 (configs[3])."""
+    """Qwen3-30B-A3B-shaped MoE layer forward in NVFP4 (8192 tokens, top-8 of
+    128 experts).  SwiGLU runs in the gate/up GEMM's epilogue, which writes h
+    in bf16, and h is quantized per token (4/6) by the per-token quantizer;
+    or (swiglu_epilogue False) SwiGLU and the 4/6 quantization of h run as
+    one kernel after the GEMM.  Both give the same h codes."""
     name = "qwen3_moe_nvfp4"
     unit = "TFLOP/s"
     dtype = "fp16"
+    swiglu_epilogue = True
 
     def __init__(self, dev):
         import numpy as np
@@ -248,18 +276,28 @@ class Qwen3MoeNvfp4:
         xq = (emp(T, H // 2), emp(T, H // 16), emp(T, dt=f32))
         h13 = emp(R, N13, dt=bf)
         hq = (None, emp(R, I // 2), emp(R, I // 16), emp(R, dt=f32))
+        hb = emp(R, I, dt=bf)     # h in bf16 (SwiGLU in the gate/up GEMM's epilogue)
         y = emp(R, H, dt=bf)
         ws = emp(max(ops.gemm_workspace_size(ops.FMT_NVFP4, 0, R, n, k, E) for n, k in ((N13, H), (H, I))))
         gm, F, NV = ops.moe_grouped_gemm_blockscaled, ops.GEMM_FPROP, ops.FMT_NVFP4
         s4 = 0.5 + 1 / 16
         self.ops = [
             Op("quant_x_nvfp4_46", lambda: ops.quantize_nvfp4_per_token(X, mode46=True, out=xq), T * H * (2 + s4) + T * 4),
+        ] + ([
+            Op("gemm_fprop_gate_up_swiglu", lambda: gm(NV, ops.GEMM_FPROP_SWIGLU, xq[0], xq[1], w13[0], w13[1], off_d,
+                                                        N13, H, M=R, a_outer=xq[2], b_outer=w13[2], a_gather=src_d,
+                                                        out=hb, workspace=ws),
+               E * N13 * H * s4 + T * H * s4 + R * I * 2, 2.0 * R * N13 * H, "fp16"),
+            Op("quant_h_nvfp4_46", lambda: ops.quantize_nvfp4_per_token(hb, mode46=True, out=hq[1:]),
+               R * I * (2 + s4) + R * 4),
+        ] if self.swiglu_epilogue else [
             Op("gemm_fprop_gate_up", lambda: gm(NV, F, xq[0], xq[1], w13[0], w13[1], off_d, N13, H, M=R,
                                                  a_outer=xq[2], b_outer=w13[2], a_gather=src_d, out=h13, workspace=ws),
                E * N13 * H * s4 + T * H * s4 + R * N13 * 2, 2.0 * R * N13 * H, "fp16"),
             Op("swiglu_quant_h_nvfp4_46", lambda: ops.swiglu_quantize(h13, ops.FMT_NVFP4, mode46=True, return_h=False,
                                                                         out=hq),
                R * N13 * 2 + R * I * s4 + R * 4),
+        ]) + [
             Op("gemm_fprop_down", lambda: gm(NV, F, hq[1], hq[2], w2[0], w2[1], off_d, H, I, M=R, a_outer=hq[3],
                                               b_outer=w2[2], out=y, workspace=ws),
                E * H * I * s4 + R * I * s4 + R * H * 2, 2.0 * R * H * I, "fp16"),
@@ -272,6 +310,7 @@ class Qwen3MoeNvfp4:
         return {"workload": "qwen3_30b_a3b_moe_layer_nvfp4_forward", "tokens": self.shape["T"],
                 "hidden": self.shape["H"], "expert_intermediate": self.shape["I"], "experts": self.shape["E"],
                 "topk": self.shape["k"], "routed_rows": self.R, "activation_46": True,
+                "swiglu": "gemm_epilogue" if self.swiglu_epilogue else "separate_kernel",
                 "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(np.median(c)),
                                "min": int(c.min()), "empty": int((c == 0).sum())},
                 "gemm_flops_per_step": self.gemm_flops}
@@ -308,9 +347,14 @@ class Qwen3MoeNvfp4:
                           f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
 
 
+class Qwen3MoeNvfp4SwigluSeparate(Qwen3MoeNvfp4):
+    name = "qwen3_moe_nvfp4_swiglu_separate"
+    swiglu_epilogue = False
+
+
 class Qwen3MoeNvfp4Bwd:
-    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward GEMMs in BF16 (configs[3]
-    shapes): data- and weight-gradient GEMMs of the down and gate/up
+    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward GEMMs in BF16 (the forward
+    workload's shapes): data- and weight-gradient GEMMs of the down and gate/up
     projections, on the original bf16 operands (high-precision mode) or on
     dequantized copies of the forward's NVFP4 operands (dequantized mode, the
     four dequantizations timed inside the step).  The upstream gradients dY
@@ -436,8 +480,8 @@ class Qwen3MoeNvfp4BwdDeq(Qwen3MoeNvfp4Bwd):
 
 
 class Qwen3MoeNvfp4BwdFp4:
-    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward in 4 bits (configs[3]
-    shapes): the gradients dY and dH13 are quantized per token, the forward's
+    """Qwen3-30B-A3B-shaped NVFP4 MoE layer, backward in 4 bits (the forward
+    workload's shapes): the gradients dY and dH13 are quantized per token, the forward's
     NVFP4 weights and activations are dequantized, transposed and requantized
     with stochastic rounding (per expert for the weights, per expert group of
     routed tokens for the activations and gradients), and the four data- and
@@ -567,7 +611,7 @@ class Qwen3MoeNvfp4BwdFp4:
 
 class Mxfp8Quant:
     """MXFP8 rowwise + columnwise quantization of 8192 x 2048 activations and rowwise
-    quantization of 128 expert weights 2048 x 768 (configs[1])."""
+    quantization of 128 expert weights 2048 x 768."""
     name = "mxfp8_quant"
     unit = "GB/s"
     dtype = "f32"
@@ -627,7 +671,7 @@ class Mxfp8Quant:
 
 
 class RequantSr:
-    """Dequantize -> transpose -> requantize with SR of a 16384 x 2048 NVFP4 tensor (configs[2])."""
+    """Dequantize -> transpose -> requantize with SR of a 16384 x 2048 NVFP4 tensor."""
     name = "requant_sr"
     unit = "GB/s"
     dtype = "f32"
@@ -693,7 +737,7 @@ class RequantSr:
 
 
 class RoundTrip:
-    """256 x 2048 activation round trip + small GEMM against a 2048 x 768 weight (configs[0])."""
+    """256 x 2048 activation round trip + small GEMM against a 2048 x 768 weight."""
     name = "roundtrip"
     unit = "us"
     dtype = "f32"
@@ -782,8 +826,9 @@ class HbmCopy:
         return None
 
 
-WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq,
-                                  Qwen3MoeNvfp4BwdFp4, Mxfp8Quant, RequantSr, RoundTrip, HbmCopy)}
+WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Dsv3MoeMxfp8SwigluSeparate, Qwen3MoeNvfp4, Qwen3MoeNvfp4SwigluSeparate,
+                                  Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq, Qwen3MoeNvfp4BwdFp4, Mxfp8Quant,
+                                  RequantSr, RoundTrip, HbmCopy)}
 
 
 # ---------------------------------------------------------------------------

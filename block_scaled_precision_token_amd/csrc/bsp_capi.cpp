@@ -216,12 +216,15 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
                                                        void *workspace, size_t ws_bytes, void *stream) {
     if (!a_codes || !a_scales || !b_codes || !b_scales || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
-    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return BSP_ERR_INVALID_ARG;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD && mode != BSP_GEMM_FPROP_SWIGLU)
+        return BSP_ERR_INVALID_ARG;
     if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
+    if (mode == BSP_GEMM_FPROP_SWIGLU && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_UNSUPPORTED;
     if (fmt == BSP_FMT_NVFP4 && (!a_outer || !b_outer)) return BSP_ERR_INVALID_ARG;
     if (fmt == BSP_FMT_MXFP8 && (a_outer || b_outer)) return BSP_ERR_INVALID_ARG;
     if (mode == BSP_GEMM_WGRAD && a_gather) return BSP_ERR_INVALID_ARG;
-    if (G < 1 || M <= 0 || N <= 0 || K <= 0 || ldc < N) return BSP_ERR_SHAPE;
+    if (G < 1 || M <= 0 || N <= 0 || K <= 0) return BSP_ERR_SHAPE;
+    if (mode == BSP_GEMM_FPROP_SWIGLU ? (N % 64 || ldc < N / 2) : ldc < N) return BSP_ERR_SHAPE;
     if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_NVFP4 && K % 32) return BSP_ERR_SHAPE;   // rows of codes 16-byte aligned

@@ -1322,29 +1322,6 @@ hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const flo
 // SwiGLU + quantization of its output
 // --------------------------------------------------------------------------
 
-// exp(x) in f32 by one fixed sequence: n = rint(x / ln 2), r = x - n ln 2 with
-// ln 2 split in a 16-bit head (n * head is exact) and a tail, e^r by its
-// degree-7 Taylor polynomial in Horner form (reduction and Horner steps one
-// fused multiply-add each), then the exact scaling by 2^n.  Results are inf
-// from x = 89 and 0 up to x = -104; the sequence itself gives exactly those
-// at both ends, so the argument is clamped to [-104, 89] (one V_MED3_F32, no
-// branch) instead of testing the two cut-offs (finite x).
-__device__ __forceinline__ float exp_cw(float x) {
-    x = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
-    const float n = rintf(x * 1.44269504088896341f);
-    float r = __builtin_fmaf(-n, 0.693145751953125f, x);
-    r = __builtin_fmaf(-n, 1.428606765330187e-06f, r);
-    float p = 1.0f / 5040.0f;
-    p = __builtin_fmaf(p, r, 1.0f / 720.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    return ldexpf(p, (int)n);
-}
-
 template <typename T>
 __device__ __forceinline__ float load_elem(const T *p);
 template <>
@@ -1415,8 +1392,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const T *__restrict__ h13, int64
             load32<T>(up + i0, u);
 #pragma unroll
             for (int i = 0; i < 32; i++) {
-                const float silu = z[i] / (1.0f + exp_cw(-z[i]));
-                hv[j][i] = __uint_as_float(f32_to_bf16(silu * u[i]) << 16);
+                hv[j][i] = __uint_as_float(swiglu_bf16(z[i], u[i]) << 16);
                 amax = fmaxf(amax, fabsf(hv[j][i]));
             }
         } else {

@@ -24,6 +24,7 @@ DTYPE_BF16 = 1
 GEMM_FPROP = 0
 GEMM_DGRAD = 1
 GEMM_WGRAD = 2
+GEMM_FPROP_SWIGLU = 3     # forward gate/up GEMM with SwiGLU in the epilogue: C = h [M, N/2] bf16
 NVFP4_46 = 0x1
 SR = 0x2
 
@@ -341,6 +342,8 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
 
     FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
     with M = rows of A (the columnwise copies' K dimension is their ld).
+    FPROP_SWIGLU: B the fused [gate; up] weight (N = 2I rows per expert),
+    C = h [M, I] in bf16.
     """
     _need_cuda(a_codes, "a_codes")
     dev = a_codes.device
@@ -349,8 +352,10 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
     if M is None:
         M = a_gather.numel() if a_gather is not None else a_rows
     if out is None:
-        shape = (G, M, N) if mode == GEMM_WGRAD else (M, N)
-        out = torch.empty(shape, dtype=out_dtype, device=dev)
+        if mode == GEMM_FPROP_SWIGLU:
+            out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty((G, M, N) if mode == GEMM_WGRAD else (M, N), dtype=out_dtype, device=dev)
     ldc = out.shape[-1] if out.dim() >= 2 else N
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
     if workspace is None:

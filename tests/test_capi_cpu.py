@@ -125,6 +125,11 @@ def test_gemm_rejects_bad_arguments():
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 32, A, ws, None) == 2   # ldc < N
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, 8, None) == 5
     assert g(1, 0, A, A, None, None, 32, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 2   # a_rows != M
+    # SwiGLU epilogue form: bf16 output only, N % 64 == 0, ldc >= N / 2; mode 4 is unknown
+    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 0, 64, A, ws, None) == 4
+    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 96, 64, A, A, None, A, 1, 48, A, ws, None) == 2
+    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 32, A, ws, None) == 2
+    assert g(1, 4, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 64, A, ws, None) == 1
 
 
 def test_bf16_gemm_workspace_and_bad_arguments():
