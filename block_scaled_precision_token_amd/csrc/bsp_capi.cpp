@@ -69,6 +69,8 @@ BSP_EXPORT size_t bsp_requant_batched_workspace_size(int64_t E, int64_t M, int64
 BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
     if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return 0;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD && mode != BSP_GEMM_FPROP_SWIGLU)
+        return 0;
     return (size_t)bsp::gemm_workspace_bytes(fmt, mode, M, N, K, G);
 }
 

@@ -396,6 +396,8 @@ size_t bsp_requant_workspace_size(int64_t M);
 /* Bytes of workspace for the batched requant: per tensor, one f32 partial
  * maximum per 2048 outer scales (at most 1024); 0 for invalid arguments. */
 size_t bsp_requant_batched_workspace_size(int64_t E, int64_t M, int64_t rows_per_scale);
+/* Bytes of workspace for bsp_moe_grouped_gemm_blockscaled (0 for an unknown
+ * format or mode, or sizes below 1). */
 size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G);
 /* Bytes of workspace for bsp_moe_grouped_gemm_bf16 (0 for invalid arguments). */
 size_t bsp_gemm_bf16_workspace_size(int mode, int64_t M, int64_t N, int64_t K, int64_t G);

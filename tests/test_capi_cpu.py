@@ -58,6 +58,9 @@ def test_size_helpers():
     a_plane = nbp * ((65536 + 255) // 256 + 128) * 256
     b_plane = 128 * nbp * up(1536, 256)
     assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) == head + up(a_plane, 256) + up(b_plane, 256)
+    # the SwiGLU epilogue form needs what the forward form needs; unknown modes size to 0
+    assert L.bsp_gemm_workspace_size(0, 3, 65536, 1536, 2048, 128) == L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128)
+    assert L.bsp_gemm_workspace_size(0, 7, 65536, 1536, 2048, 128) == 0
     head = up((258 + 16) * 8 + 257 * 4, 256)           # + the expert order
     nbp = 37120 // 32 + 2
     assert L.bsp_gemm_workspace_size(1, 2, 4096, 7168, 37120, 257) == head + nbp * 4096 + nbp * 7168
