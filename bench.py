@@ -705,7 +705,7 @@ class RequantSr:
         nbytes = M * K * (0.5 + 1 / 16) * 2 + M * 4 + 4
         # The generator alone fixes the VALU floor: Philox4x32-10 gives 8 elements
         # their 16 bits with 19 32x32->64 products (V_MAD_U64_U32, quarter rate: 4
-        # each; round 1 has one, two counter words being zero) and 20 three-input
+        # each; the first Philox round has one, two counter words being zero) and 20 three-input
         # xors (1 each), 96 lane-operations; plus the dequantizing and the rescaling
         # multiply of every element: 14 per element.
         valu = M * K * (96 / 8 + 2)
@@ -963,8 +963,8 @@ def main():
                     help="time HIP-graph replays instead of Python launches (auto: for the short-step workloads)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
