@@ -907,54 +907,37 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             auto word = [](const uint4 &u, int q) __attribute__((always_inline)) -> uint32_t {
                 return q == 0 ? u.x : q == 1 ? u.y : q == 2 ? u.z : u.w;
             };
-            if constexpr (WG) {
-                // Weight-gradient form, every block live: B's fragments for
-                // step q + 1 are converted during step q and each A fragment
-                // right before its two MFMAs, one MFMA then six conversions
-                // at a time, so that the vector ALU and the matrix core of one
-                // wavefront overlap (few extra registers: the accumulators
-                // take half of them).
-                v8h fb[2][2];
+            // B's fragments for step q + 1 are converted during step q and
+            // each A fragment right before its two MFMAs, so that the
+            // conversions issue between MFMAs and overlap them (a wavefront
+            // issuing its MFMAs back to back could not convert meanwhile).
+            // Block 0 is always live (nv >= 1 here); blocks past the group's
+            // rows skip their conversions and MFMAs.
+            v8h fb[2][2];
 #pragma unroll
-                for (int j = 0; j < 2; j++) fb[0][j] = nv_frag(word(ub[j], 0), sb[j][0]);
+            for (int j = 0; j < 2; j++) fb[0][j] = nv_frag(word(ub[j], 0), sb[j][0]);
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int c = q & 1;
-                    if (q < 3) {
+            for (int q = 0; q < 4; q++) {
+                const int c = q & 1;
+                if (q < 3) {
 #pragma unroll
-                        for (int j = 0; j < 2; j++) fb[c ^ 1][j] = nv_frag(word(ub[j], q + 1), sb[j][(q + 1) >> 1]);
-                    }
+                    for (int j = 0; j < 2; j++) fb[c ^ 1][j] = nv_frag(word(ub[j], q + 1), sb[j][(q + 1) >> 1]);
+                }
 #pragma unroll
-                    for (int i = 0; i < TI; i++) {
-                        const v8h fa = nv_frag(word(ua[i], q), sa[i][q >> 1]);
+                for (int i = 0; i < TI; i++) {
+                    if (i > 0 && i >= nv) break;
+                    const v8h fa = nv_frag(word(ua[i], q), sa[i][q >> 1]);
 #pragma unroll
-                        for (int j = 0; j < 2; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[c][j], acc[i][j], 0, 0, 0);
-                    }
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[c][j], acc[i][j], 0, 0, 0);
+                }
+                if constexpr (WG) {
+                    // every block live: request the interleave explicitly
 #pragma unroll
                     for (int m = 0; m < 2 * TI; m++) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
                     }
-                }
-                return;
-            }
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                v8h fa[TI], fb[2];
-#pragma unroll
-                for (int i = 0; i < TI; i++) {
-                    if (i >= nv) break;
-                    fa[i] = nv_frag(word(ua[i], q), sa[i][q >> 1]);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; j++) fb[j] = nv_frag(word(ub[j], q), sb[j][q >> 1]);
-#pragma unroll
-                for (int i = 0; i < TI; i++) {
-                    if (i >= nv) break;
-#pragma unroll
-                    for (int j = 0; j < 2; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
                 }
             }
         }
