@@ -272,7 +272,12 @@ def quantize_mxfp8_colwise(x_bf16, group_offsets=None, ldT=None):
     x = _c(x_bf16, np.uint16)
     M, K = x.shape
     if group_offsets is None:
+        if M % 32:
+            raise ValueError("an ungrouped columnwise copy needs M % 32 == 0 (whole 32-row blocks); "
+                             "pass group_offsets to pad a group to 32 rows")
         ldT = M if ldT is None else ldT
+        if ldT < M or ldT % 32:
+            raise ValueError("ldT must be a multiple of 32 and at least M")
         off = None
         G = 1
     else:

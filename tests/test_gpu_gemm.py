@@ -305,3 +305,131 @@ def test_nvfp4_wgrad_on_grouped_requantized_operands(counts, sr):
     sel = np.array([[g, n] for g in range(G) for n in range(NA)], np.int64)
     ref, refabs = oracle.gemm_wgrad_nvfp4(ra[0], ra[1], ra[2], rb[0], rb[1], rb[2], off, sel)
     assert_gemm_close(host(c).reshape(G * NA, NB), ref, refabs)
+
+
+# --- the DeepSeek-V3-shaped MXFP8 GEMMs at full size, sampled ---------------
+# 4096 tokens, hidden 7168, expert intermediate 2048, top-8 of 256 routed
+# experts plus one shared expert (36,864 rows), as in the timed step.  The
+# weights (7.5 G values per projection) are generated and quantized on the
+# device; the sampled experts' codes are then replaced by the oracle's codes
+# of the same bf16 values, and only rows (or weight-gradient groups) of those
+# experts are checked, so every checked output depends on oracle inputs only.
+
+T_D, H_D, I_D, E_D, TOPK_D = 4096, 7168, 2048, 256, 8
+N13_D = 2 * I_D
+
+
+@pytest.fixture(scope="module")
+def dsv3_routing():
+    off, src = synth.route_topk(20261210, T_D, E_D, TOPK_D, synth.zipf_bias(20261209, E_D, 1.1, uniform_mix=0.5),
+                                shared_expert=True)
+    counts = np.diff(off)
+    rng = np.random.default_rng(20261211)
+    sampled = sorted({int(np.argmax(counts[:-1])), int(np.argmin(counts[:-1])), E_D,
+                      *rng.integers(0, E_D, 2).tolist()})
+    rows = {}
+    for e in sampled:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows[e] = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 3)]))
+    return off, src, sampled, rows
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_dsv3_shaped_mxfp8_gate_up_swiglu_sampled(dsv3_routing, gemm_tile):
+    if gemm_tile != "auto":
+        pytest.skip("full size: the library's tile choice only (the one bench.py times)")
+    off, src, sampled, rows = dsv3_routing
+    G, R = E_D + 1, int(off[-1])
+    x = synth.activations(20261212, T_D, H_D)
+    ac, as_ = oracle.quantize_mxfp8_rowwise(x)
+    w13 = synth.device_weights(20261213, G, N13_D, H_D, device=DEV)
+    wq = ops.quantize_mxfp8(w13.view(G, N13_D, H_D), True, False)
+    bc, bs = {}, {}
+    for e in sampled:
+        bc[e], bs[e] = oracle.quantize_mxfp8_rowwise(host_bits(w13[e * N13_D:(e + 1) * N13_D]))
+        wq["codes_row"][e].copy_(to_dev(bc[e]))
+        wq["scales_row"][e].copy_(to_dev(bs[e]))
+    del w13
+    h = ops.moe_grouped_gemm_blockscaled(ops.FMT_MXFP8, ops.GEMM_FPROP_SWIGLU, to_dev(ac), to_dev(as_),
+                                         wq["codes_row"], wq["scales_row"], to_dev(off), N13_D, H_D, M=R,
+                                         a_gather=to_dev(src))
+    got = host(h.float())
+    for e in sampled:
+        sel = rows[e]
+        ref, refabs = oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac, as_, None, src[sel], np.array([0, sel.size]),
+                                           N13_D, H_D, bc[e], bs[e], None)
+        href, bound = swiglu_reference(ref, refabs)
+        d = np.abs(got[sel].astype(np.float64) - href)
+        assert np.all(d <= bound), (e, float((d / bound).max()))
+
+
+def test_dsv3_shaped_mxfp8_dgrad_gate_up_sampled(dsv3_routing, gemm_tile):
+    if gemm_tile != "auto":
+        pytest.skip("full size: the library's tile choice only (the one bench.py times)")
+    # dX = dH13 W13_e through W13's columnwise copy [H, 2I] per expert
+    off, src, sampled, rows = dsv3_routing
+    G, R = E_D + 1, int(off[-1])
+    dh = synth.device_activations(20261214, R, N13_D, device=DEV)
+    dq = ops.quantize_mxfp8(dh, True, False)
+    w13 = synth.device_weights(20261215, G, N13_D, H_D, device=DEV)
+    wq = ops.quantize_mxfp8(w13.view(G, N13_D, H_D), False, True)
+    bc, bs, ac, as_ = {}, {}, {}, {}
+    for e in sampled:
+        bc[e], bs[e] = oracle.quantize_mxfp8_colwise(host_bits(w13[e * N13_D:(e + 1) * N13_D]))
+        wq["codes_colT"][e].copy_(to_dev(bc[e]))
+        wq["scales_colT"][e].copy_(to_dev(bs[e]))
+        sel = torch.from_numpy(rows[e]).to(DEV)
+        ac[e], as_[e] = oracle.quantize_mxfp8_rowwise(host_bits(dh[sel]))
+        dq["codes_row"][sel] = to_dev(ac[e])
+        dq["scales_row"][sel] = to_dev(as_[e])
+    del w13, dh
+    dx = ops.moe_grouped_gemm_blockscaled(ops.FMT_MXFP8, ops.GEMM_DGRAD, dq["codes_row"], dq["scales_row"],
+                                          wq["codes_colT"], wq["scales_colT"], to_dev(off), H_D, N13_D, M=R,
+                                          out_dtype=torch.bfloat16)
+    got = host(dx.float())
+    for e in sampled:
+        ref, refabs = oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac[e], as_[e], None, None,
+                                           np.array([0, rows[e].size]), H_D, N13_D, bc[e], bs[e], None)
+        assert_gemm_close(got[rows[e]], ref, refabs, bf16=True)
+
+
+def test_dsv3_shaped_mxfp8_wgrad_gate_up_sampled(dsv3_routing, gemm_tile):
+    if gemm_tile != "auto":
+        pytest.skip("full size: the library's tile choice only (the one bench.py times)")
+    # dW13_e = dH13_e^T X_e over the routed rows of expert e, both operands in
+    # their grouped columnwise copies (X read through the routing map)
+    off, src, sampled, rows = dsv3_routing
+    G, R = E_D + 1, int(off[-1])
+    offd = to_dev(off)
+    dh = synth.device_activations(20261216, R, N13_D, device=DEV)
+    x = synth.device_activations(20261217, T_D, H_D, device=DEV)
+    qa = ops.quantize_mxfp8(dh, False, True, group_offsets=offd)
+    qb = ops.quantize_mxfp8(x, False, True, group_offsets=offd, row_gather=to_dev(src))
+    P = oracle.padded_offsets(off)
+    ref_ops = {}
+    for e in sampled:
+        lo, hi = int(off[e]), int(off[e + 1])
+        one = np.array([0, hi - lo], np.int64)   # one group: padded to 32 rows like the grouped copies
+        a_e = oracle.quantize_mxfp8_colwise(host_bits(dh[lo:hi]), one)
+        b_e = oracle.quantize_mxfp8_colwise(host_bits(x[torch.from_numpy(src[lo:hi].astype(np.int64)).to(DEV)]), one)
+        w = a_e[0].shape[1]                      # the group's 32-padded width
+        qa["codes_colT"][:, P[e]:P[e] + w].copy_(to_dev(a_e[0]))
+        qa["scales_colT"][:, P[e] // 32:(P[e] + w) // 32].copy_(to_dev(a_e[1]))
+        qb["codes_colT"][:, P[e]:P[e] + w].copy_(to_dev(b_e[0]))
+        qb["scales_colT"][:, P[e] // 32:(P[e] + w) // 32].copy_(to_dev(b_e[1]))
+        ref_ops[e] = (a_e, b_e, hi - lo)
+    del dh, x
+    ld = qa["codes_colT"].shape[1]
+    dw = ops.moe_grouped_gemm_blockscaled(ops.FMT_MXFP8, ops.GEMM_WGRAD, qa["codes_colT"], qa["scales_colT"],
+                                          qb["codes_colT"], qb["scales_colT"], offd, H_D, ld, M=N13_D,
+                                          out_dtype=torch.bfloat16)
+    rng = np.random.default_rng(20261218)
+    for e in sampled:
+        (ac, as_), (bc, bs), n = ref_ops[e]
+        ms = np.unique(np.concatenate([[0, N13_D - 1], rng.integers(0, N13_D, 4)]))
+        sel = np.stack([np.zeros_like(ms), ms], 1)
+        ref, refabs = oracle.gemm_wgrad(ac, as_, bc, bs, np.array([0, n]), sel)
+        assert_gemm_close(host(dw[e].float())[ms], ref, refabs, bf16=True)

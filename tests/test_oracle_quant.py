@@ -308,6 +308,15 @@ def test_mxfp8_columnwise_is_rowwise_of_transpose():
     np.testing.assert_array_equal(sT, sr)
 
 
+def test_mxfp8_columnwise_rejects_partial_blocks_without_groups():
+    # an ungrouped copy has whole 32-row blocks only; one group pads instead
+    x = synth.activations(17, 19, 64)
+    with pytest.raises(ValueError):
+        oracle.quantize_mxfp8_colwise(x)
+    cT, sT = oracle.quantize_mxfp8_colwise(x, np.array([0, 19], np.int64))
+    assert cT.shape == (64, 32) and sT.shape == (64, 1) and not cT[:, 19:].any()
+
+
 def test_mxfp8_grouped_columnwise_pads_each_group():
     x = synth.activations(16, 100, 64)
     off = np.array([0, 5, 5, 40, 100], np.int64)      # includes an empty group
