@@ -389,8 +389,9 @@ class Qwen3MoeNvfp4Bwd:
         emp = lambda *s_, dt=bf: torch.empty(s_, dtype=dt, device=dev)
         dh, dX = emp(R, I), emp(R, H)
         dW2, dW13 = emp(E, H, I), emp(E, N13, H)
-        ws = emp(max(ops.gemm_bf16_workspace_size(ops.GEMM_DGRAD, R, n, kk, E) for n, kk in ((I, H), (H, N13))),
-                 dt=torch.uint8)
+        ws = emp(max(ops.gemm_bf16_workspace_size(md, m, n, kk, E)
+                     for md, m, n, kk in ((ops.GEMM_DGRAD, R, I, H), (ops.GEMM_DGRAD, R, H, N13),
+                                          (ops.GEMM_WGRAD, H, I, R), (ops.GEMM_WGRAD, N13, H, R))), dt=torch.uint8)
         gm, DG, WG = ops.moe_grouped_gemm_bf16, ops.GEMM_DGRAD, ops.GEMM_WGRAD
         self.ops = []
         if self.mode == "deq":
