@@ -931,13 +931,11 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[c][j], acc[i][j], 0, 0, 0);
                 }
-                if constexpr (WG) {
-                    // every block live: request the interleave explicitly
+                // request the interleave from the scheduler as well
 #pragma unroll
-                    for (int m = 0; m < 2 * TI; m++) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
-                    }
+                for (int m = 0; m < 2 * TI; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
                 }
             }
         }
