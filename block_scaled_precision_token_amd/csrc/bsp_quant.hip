@@ -146,44 +146,66 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
 // or 32 / 16 for short rows so that few lanes idle), lane l of a row owning
 // the 16-value blocks starting at k = 16 LPR j + 16 l.  RHT: every block
 // transformed first (the row's scale from the transformed values).
-template <bool M46, int MAXIT, bool RHT = false, int LPR = 64>
+template <bool M46, int MAXIT, bool RHT = false, int LPR = 64, int NR = 1>
 __global__ __launch_bounds__(256) void k_nvfp4_row(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                    int64_t ldx, uint8_t *__restrict__ codes,
                                                    uint8_t *__restrict__ scales, float *__restrict__ outer,
                                                    uint32_t signs = 0) {
-    constexpr int RPW = 64 / LPR;               // rows per wavefront
+    // NR rows per lane group, RPW apart, all loaded before the first is
+    // quantized (straight-line code): the later rows' loads overlap the
+    // earlier rows' arithmetic, which matters when every workgroup of the
+    // launch is resident at once (short tensors).
+    constexpr int RPW = 64 / LPR;               // rows per wavefront and pass
     const int lane = threadIdx.x & (LPR - 1);
-    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + (threadIdx.x & 63) / LPR;
-    if (row >= M) return;                       // whole row groups leave together
-    const uint16_t *xr = x + row * ldx;
-    uint4 v[MAXIT][2];
-    float amax = 0.0f;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW * NR + (threadIdx.x & 63) / LPR;
+    if (row0 >= M) return;                      // whole row groups leave together
+    uint4 v[NR][MAXIT][2];
 #pragma unroll
-    for (int j = 0; j < MAXIT; j++) {
-        const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
-        if (k0 < K) {
-            v[j][0] = *reinterpret_cast<const uint4 *>(xr + k0);
-            v[j][1] = *reinterpret_cast<const uint4 *>(xr + k0 + 8);
-            float xf[16];
-            unpack16(v[j], xf);
-            if (RHT) rht16(xf, signs);
-            amax = fmaxf(amax, absmax16(xf));
+    for (int q = 0; q < NR; q++) {
+        // NR > 1: every load is issued, from a clamped (valid) address, so
+        // that the count of loads in flight does not depend on the path and
+        // the first row's wait leaves the later rows' loads outstanding;
+        // pieces past M or K are never used
+        const int64_t rq = row0 + q * RPW, row = NR > 1 && rq >= M ? M - 1 : rq;
+#pragma unroll
+        for (int j = 0; j < MAXIT; j++) {
+            const int64_t kq = (int64_t)j * 16 * LPR + lane * 16, k0 = NR > 1 && kq >= K ? K - 16 : kq;
+            if (NR > 1 || (row < M && k0 < K)) {
+                v[q][j][0] = *reinterpret_cast<const uint4 *>(x + row * ldx + k0);
+                v[q][j][1] = *reinterpret_cast<const uint4 *>(x + row * ldx + k0 + 8);
+            }
         }
     }
 #pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
-    if (lane == 0) outer[row] = g;
+    for (int q = 0; q < NR; q++) {
+        const int64_t row = row0 + q * RPW;
+        if (row >= M) break;                    // uniform within the lane group
+        float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MAXIT; j++) {
-        const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
-        if (k0 < K) {
-            float xf[16];
-            unpack16(v[j], xf);
-            if (RHT) rht16(xf, signs);
-            Nvfp4Block b = nvfp4_block<M46>(xf, g);
-            *reinterpret_cast<uint2 *>(codes + row * (K / 2) + k0 / 2) = make_uint2(b.lo, b.hi);
-            scales[row * (K / 16) + k0 / 16] = (uint8_t)b.s;
+        for (int j = 0; j < MAXIT; j++) {
+            const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
+            if (k0 < K) {
+                float xf[16];
+                unpack16(v[q][j], xf);
+                if (RHT) rht16(xf, signs);
+                amax = fmaxf(amax, absmax16(xf));
+            }
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float g = (amax == 0.0f) ? 0.0f : amax / 2688.0f;
+        if (lane == 0) outer[row] = g;
+#pragma unroll
+        for (int j = 0; j < MAXIT; j++) {
+            const int64_t k0 = (int64_t)j * 16 * LPR + lane * 16;
+            if (k0 < K) {
+                float xf[16];
+                unpack16(v[q][j], xf);
+                if (RHT) rht16(xf, signs);
+                Nvfp4Block b = nvfp4_block<M46>(xf, g);
+                *reinterpret_cast<uint2 *>(codes + row * (K / 2) + k0 / 2) = make_uint2(b.lo, b.hi);
+                scales[row * (K / 16) + k0 / 16] = (uint8_t)b.s;
+            }
         }
     }
 }
@@ -195,19 +217,26 @@ template <bool M46, bool RHT>
 static void launch_nvfp4_row(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint8_t *codes, uint8_t *scales,
                              float *outer, uint32_t signs, hipStream_t s) {
     const int64_t nb = K / 16;
-    auto go = [&](auto kern, int lpr) {
-        const int64_t rows_per_wg = 4 * (64 / lpr);
+    auto go = [&](auto kern, int lpr, int nr) {
+        const int64_t rows_per_wg = 4 * (64 / lpr) * nr;
         kern<<<dim3((unsigned)((M + rows_per_wg - 1) / rows_per_wg)), 256, 0, s>>>(x, M, K, ldx, codes, scales,
                                                                                      outer, signs);
     };
-    if (nb <= 16) go(k_nvfp4_row<M46, 1, RHT, 16>, 16);
-    else if (nb <= 32) go(k_nvfp4_row<M46, 1, RHT, 32>, 32);
-    else if (nb <= 48) go(k_nvfp4_row<M46, 3, RHT, 16>, 16);
-    else if (nb <= 64) go(k_nvfp4_row<M46, 1, RHT, 64>, 64);
-    else if (nb <= 96) go(k_nvfp4_row<M46, 3, RHT, 32>, 32);
-    else if (nb <= 128) go(k_nvfp4_row<M46, 2, RHT, 64>, 64);
-    else if (nb <= 192) go(k_nvfp4_row<M46, 3, RHT, 64>, 64);
-    else go(k_nvfp4_row<M46, 8, RHT, 64>, 64);
+    // K = 1537..2048 (the activations of the MoE layers): two rows per
+    // wavefront while one each would keep at most ~8 workgroups per CU
+    if (nb > 96 && nb <= 128) {
+        if ((M + 3) / 4 <= 2048) go(k_nvfp4_row<M46, 2, RHT, 64, 2>, 64, 2);
+        else go(k_nvfp4_row<M46, 2, RHT, 64>, 64, 1);
+        return;
+    }
+    auto go1 = [&](auto kern, int lpr) { go(kern, lpr, 1); };
+    if (nb <= 16) go1(k_nvfp4_row<M46, 1, RHT, 16>, 16);
+    else if (nb <= 32) go1(k_nvfp4_row<M46, 1, RHT, 32>, 32);
+    else if (nb <= 48) go1(k_nvfp4_row<M46, 3, RHT, 16>, 16);
+    else if (nb <= 64) go1(k_nvfp4_row<M46, 1, RHT, 64>, 64);
+    else if (nb <= 96) go1(k_nvfp4_row<M46, 3, RHT, 32>, 32);
+    else if (nb <= 192) go1(k_nvfp4_row<M46, 3, RHT, 64>, 64);
+    else go1(k_nvfp4_row<M46, 8, RHT, 64>, 64);
 }
 
 // 16x16 2-D blocks under one per-tensor outer scale (outer[0], computed

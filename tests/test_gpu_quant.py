@@ -45,9 +45,10 @@ def edge_tensor(M, K, seed=0):
 # ---------------------------------------------------------------------------
 
 # K spans every lanes-per-row choice of the per-token kernel (16-value blocks
-# per row: 1, 25, 3, 48, 63, 96, 128, 160, 448) and the scope kernel (8208)
+# per row: 1, 25, 3, 48, 63, 96, 128, 97, 160, 448; 13 and 21 rows leave the
+# two-rows-per-wavefront form a partial last pair) and the scope kernel (8208)
 @pytest.mark.parametrize("M,K", [(1, 16), (19, 400), (37, 48), (130, 768), (66, 1008), (45, 1536), (256, 2048),
-                                 (11, 2560), (33, 7168), (9, 8208)])
+                                 (13, 2048), (21, 1552), (11, 2560), (33, 7168), (9, 8208)])
 @pytest.mark.parametrize("mode46", [False, True])
 def test_nvfp4_per_token_parity(M, K, mode46):
     x = edge_tensor(M, K, seed=M * 31 + K)
