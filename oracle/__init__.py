@@ -98,6 +98,8 @@ def _declare(lib):
     lib.orc_exp_f32.restype = ctypes.c_float
     lib.orc_silu_f32.argtypes = [ctypes.c_float]
     lib.orc_silu_f32.restype = ctypes.c_float
+    lib.orc_silu_f64.argtypes = [ctypes.c_double]
+    lib.orc_silu_f64.restype = ctypes.c_double
     lib.orc_swiglu.argtypes = [P, I64, I64, P]
     for name in ("orc_e2m1_encode_array", "orc_e4m3_encode_array", "orc_mxfp8_block_exponent_array",
                  "orc_f32_to_bf16_array", "orc_exp_f32_array"):
@@ -486,8 +488,19 @@ def gemm_bf16_wgrad(a, b, gather, group_offsets, sel):
 
 # --- SwiGLU -------------------------------------------------------------------
 
+def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Units in the last place between two bf16 arrays (bit patterns mapped to
+    an ordered integer line, so +0 and -0 are one unit apart)."""
+    def ordered(x):
+        x = np.asarray(x, np.uint16).astype(np.int32)
+        return np.where(x & 0x8000, 0x7FFF - (x & 0x7FFF), x + 0x8000)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
 def swiglu(h13: np.ndarray) -> np.ndarray:
-    """h13 f32 [R, 2I] -> h bf16 bits [R, I]."""
+    """h13 f32 [R, 2I] -> h bf16 bits [R, I]: bf16(f32(silu(gate) * up)) with
+    silu evaluated in binary64 (the pages give no SwiGLU arithmetic; this is
+    the plain definition, independent of any kernel's exp)."""
     h13 = _c(h13, np.float32)
     R, I2 = h13.shape
     h = np.empty((R, I2 // 2), np.uint16)

@@ -52,3 +52,23 @@ def assert_gemm_close(c, ref, refabs, bf16=False, tol=1e-3):
     e_norm, e_wise = gemm_errors(c, ref, refabs)
     assert e_norm <= tol, e_norm
     assert e_wise <= tol, e_wise
+
+
+def assert_swiglu_close(h_dev_bits, h13_f32):
+    """Stage one of the SwiGLU contract: the device's bf16 h within one bf16 unit
+    of the oracle's binary64 SwiGLU.  Both round a value that f32 arithmetic
+    gets to a few f32 units, so they can straddle one bf16 rounding boundary
+    but not two.  The one exception is f32's range: exp(-z) overflows f32 for
+    z < -88.72, where an f32 evaluation of z / (1 + exp(-z)) gives -0 against
+    a true magnitude below 89 e^-88.72 |up| < 3e-37 |up|; such elements may
+    differ by that much instead."""
+    import oracle
+    h_ref = oracle.swiglu(h13_f32)
+    dist = oracle.bf16_ulp_distance(h_dev_bits, h_ref)
+    I = h_ref.shape[1]
+    up = np.abs(h13_f32[:, I:].astype(np.float64))
+    f = lambda b: (np.asarray(b, np.uint32) << 16).view(np.float32).astype(np.float64)
+    absdiff = np.abs(f(h_dev_bits) - f(h_ref))
+    ok = (dist <= 1) | (absdiff <= 3e-37 * up)
+    bad = np.argwhere(~ok)
+    assert bad.size == 0, f"h: {len(bad)} elements beyond one bf16 unit, first at {bad[:5].tolist()}"

@@ -3,8 +3,8 @@
 GEMM: numpy float64 matmul (a library routine) on operands decoded
 independently (the pages' E2M1 value set, torch's float8 and bfloat16
 decodes), and identity-weight cases whose result is known in closed form.
-SwiGLU: the explicit f32 exp against numpy's exp (within 2 ulp), the silu
-formula in float64, and exact special values.
+SwiGLU: exp against Python's decimal exp and its own identities; silu by
+closed forms (silu(z) - silu(-z) = z, its limits and signs).
 """
 import numpy as np
 import torch
@@ -175,28 +175,73 @@ def test_bf16_wgrad_matches_float64_matmul_per_group():
     np.testing.assert_allclose(c3, ref3[[0, 11, M - 1]], rtol=1e-12, atol=1e-12 * np.abs(ref3).max())
 
 
-def test_exp_f32_within_two_ulp_of_numpy():
+def _decimal_exp_f32(x: float) -> np.float32:
+    """exp(x) to 40 significant digits by Python's decimal module (correctly
+    rounded at that precision), then rounded to f32: an independent reference."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 40
+        return np.float32(float(decimal.Decimal(float(x)).exp()))
+
+
+def test_exp_f32_against_decimal_and_identities():
     rng = np.random.default_rng(1)
-    x = np.concatenate([rng.uniform(-87, 88, 400000), np.linspace(-20, 20, 20001)]).astype(np.float32)
-    got = oracle.exp_f32_array(x).astype(np.float64)
-    ref = np.exp(x.astype(np.float64))
-    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
-    assert np.max(np.abs(got - ref) / ulp) <= 2.0
+    x = np.concatenate([rng.uniform(-87, 88, 3000), np.linspace(-20, 20, 2001)]).astype(np.float32)
+    got = oracle.exp_f32_array(x)
+    ref = np.array([_decimal_exp_f32(v) for v in x], np.float32)
+    # at most one f32 unit apart (both sides round the exact value once or twice)
+    ulp = np.spacing(np.maximum(np.abs(got), np.abs(ref))).astype(np.float64)
+    assert np.max(np.abs(got.astype(np.float64) - ref) / ulp) <= 1.0
+    # exp(x) exp(-x) = 1 and exp(a) exp(b) = exp(a + b), to f32 rounding
+    y = rng.uniform(-40, 40, 2000).astype(np.float32)
+    prod = oracle.exp_f32_array(y).astype(np.float64) * oracle.exp_f32_array(-y)
+    assert np.max(np.abs(prod - 1.0)) <= 4 * 2.0 ** -24
+    a, b = y[:1000] / 2, y[1000:] / 2
+    s = (a.astype(np.float64) + b).astype(np.float32)          # exact: a and b have equal-scale halves
+    lhs = oracle.exp_f32_array(a).astype(np.float64) * oracle.exp_f32_array(b)
+    rhs = oracle.exp_f32_array(s).astype(np.float64)
+    keep = s == a.astype(np.float64) + b
+    assert np.all(np.abs(lhs[keep] - rhs[keep]) <= 4 * 2.0 ** -24 * rhs[keep])
+    # monotone, and the ends of f32: overflow from 89, underflow to zero by -104
+    xs = np.sort(rng.uniform(-110, 95, 5000).astype(np.float32))
+    e = oracle.exp_f32_array(xs).astype(np.float64)
+    assert np.all((e[1:] >= e[:-1]) | (np.isinf(e[1:]) & np.isinf(e[:-1])))
     assert oracle.exp_f32(0.0) == 1.0
-    assert oracle.exp_f32(100.0) == np.inf and oracle.exp_f32(-200.0) == 0.0
+    assert oracle.exp_f32(89.0) == np.inf and oracle.exp_f32(-104.0) == 0.0
 
 
-def test_swiglu_matches_float64_formula():
-    R, I = 64, 96
-    h13 = synth.fp32_matrix(2, R, 2 * I, std=3.0)
-    h = oracle.swiglu(h13)
-    gate = h13[:, :I].astype(np.float64)
-    up = h13[:, I:].astype(np.float64)
-    ref = gate / (1.0 + np.exp(-gate)) * up
-    got = synth.f32_from_bf16_bits(h).astype(np.float64)
-    # bf16 rounding (2^-9 relative) plus a few f32 ulps
-    np.testing.assert_allclose(got, ref, rtol=2.0 ** -8, atol=1e-30)
-    # exact special values: silu(0) = 0, silu(-inf side) -> -0, silu(large) = z
+def _swiglu_scalar(gate, up):
+    h13 = np.array([[gate, up]], np.float32)
+    return oracle.swiglu(h13)[0, 0]
+
+
+def test_swiglu_closed_forms():
+    """SwiGLU pinned by properties of silu(z) = z sigma(z), not by its formula:
+    sigma(z) + sigma(-z) = 1 gives silu(z) - silu(-z) = z; silu(z) / z -> 1/2 at
+    0 and -> 1 for large z; silu(z) has the sign of z and tends to -0 for large negative z; up
+    scales h linearly."""
+    bf = synth.f32_from_bf16_bits
+    rng = np.random.default_rng(7)
+    R, I = 50, 64
+    z = rng.uniform(-12, 12, (R, I)).astype(np.float32)
+    one = np.ones_like(z)
+    hp = bf(oracle.swiglu(np.concatenate([z, one], 1))).astype(np.float64)
+    hm = bf(oracle.swiglu(np.concatenate([-z, one], 1))).astype(np.float64)
+    # each of hp, hm carries its bf16 rounding (half a unit: <= 2^-8 relative)
+    assert np.all(np.abs(hp - hm - z) <= 2.0 ** -8 * (np.abs(hp) + np.abs(hm)) * 1.0001)
+    # sign: silu(z) has the sign of z (z sigma(z), sigma > 0)
+    assert np.all(np.sign(hp) == np.sign(z))
+    # small z: silu(z) = z/2 + z^2/4 + O(z^4), so bf16(z/2) exactly at z = 2^-20
+    assert _swiglu_scalar(2.0 ** -20, 1.0) == synth.bf16_bits_from_f32(np.float32([2.0 ** -21]))[0]
+    # large z: silu(z) = z to within e^-z
+    for v in (30.0, 1e4):
+        assert _swiglu_scalar(v, 1.0) == synth.bf16_bits_from_f32(np.float32([v]))[0]
+    # large negative z: -z e^-|z| underflows; the sign survives as -0
+    assert _swiglu_scalar(-1e4, 1.0) == 0x8000 and _swiglu_scalar(-1e4, -1.0) == 0x0000
+    assert _swiglu_scalar(0.0, 5.0) == 0x0000
+    # up is a plain factor: power-of-two scaling of up is exact through bf16
+    hz = oracle.swiglu(np.concatenate([z, one * 4.0], 1))
+    assert np.array_equal(bf(hz).astype(np.float64), 4.0 * hp)
     assert oracle.lib().orc_silu_f32(0.0) == 0.0
     assert oracle.lib().orc_silu_f32(100.0) == 100.0
 
