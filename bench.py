@@ -38,6 +38,7 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0, "bf16": 2500.0, "fp4": 10100.
 # second (a quarter-rate instruction counts 4)
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 SEED = 20261201
+GRAPH_REPLAYS = 5
 
 
 class Op:
@@ -71,6 +72,104 @@ def timed_until(unit_fn, min_seconds=10.0, max_reps=10000):
         if time.perf_counter() - t0 >= min_seconds:
             break
     return work, time.perf_counter() - t0, reps
+
+
+def percentiles(times):
+    """Median, 10th and 90th percentile of per-launch times (ms)."""
+    import numpy as np
+    t = np.asarray(times, np.float64)
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def host_facts():
+    """The CPU the oracle baseline ran on: logical CPUs, the affinity set this
+    process may use, the model name and the OpenMP setting."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "model": model,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline_both(wl, budget_s=8.0):
+    """The oracle leg at one thread and at all the threads OpenMP uses, each on
+    its own bounded sample (about budget_s of CPU work)."""
+    import oracle
+    n_all = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        one = wl.cpu_baseline(budget_s)
+    finally:
+        oracle.set_num_threads(n_all)
+    res = wl.cpu_baseline(budget_s)
+    if res is None:
+        return None
+    res = dict(res)
+    if one is not None:
+        res["one_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
+    res["host"] = host_facts()
+    return res
+
+
+def requant_size_sweep(dev, sizes=(16384, 65536, 262144), K=2048, launches=20):
+    """Requant + SR at growing M (K = 2048): mean per launch over HIP-graph
+    replays, input copies rotated so that at least 600 MB are cycled (beyond the
+    256 MB MALL).  Returns one entry per size with GB/s and fractions of the
+    HBM peak and of the VALU issue rate (14 lane-operations per element)."""
+    import torch
+    from block_scaled_precision_token_amd import ops, synth
+    stream = torch.cuda.current_stream(dev)
+    out = []
+    for M in sizes:
+        nbytes = M * K * (0.5 + 1 / 16) * 2 + M * 4 + 4
+        copies = max(1, min(8, int(-(-600e6 // nbytes))))
+        x = synth.device_activations(SEED + 90 + M // 16384, M, K, dev)
+        ins = [ops.quantize_nvfp4_per_token(x)]
+        for _ in range(copies - 1):
+            ins.append(tuple(t.clone() for t in ins[0]))
+        del x
+        outs = [(torch.empty((K, M // 2), dtype=torch.uint8, device=dev),
+                 torch.empty((K, M // 16), dtype=torch.uint8, device=dev),
+                 torch.empty((4,), dtype=torch.float32, device=dev)) for _ in range(copies)]
+        ws = torch.empty((max(ops.requant_workspace_size(M), 16),), dtype=torch.uint8, device=dev)
+        for i in range(copies):
+            ops.requant_transpose_sr(*ins[i], seed=i, workspace=ws, out=outs[i])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(launches):
+                i = j % copies
+                ops.requant_transpose_sr(*ins[i], seed=0x5EED + j, workspace=ws, out=outs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(GRAPH_REPLAYS):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / launches)
+        med, p10, p90 = percentiles(times)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        valu = M * K * (96 / 8 + 2)
+        out.append({"M": M, "K": K, "us_median": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2),
+                    "us_p90": round(p90 * 1e3, 2), "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "alu_frac": round(valu / (med * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4), "input_copies": copies})
+        del g, ins, outs, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bf16_dev(bits, dev):
@@ -912,8 +1011,9 @@ def time_eager(wl, steps, dev):
 def time_graphed(wl, steps, dev):
     """Short steps are bound by the Python launch rate, not by the GPU: capture the
     launches in HIP graphs and time their replay.  Each op is timed alone (a graph
-    of `steps` launches of it), then the whole step (a graph of `steps` steps);
-    every graph is replayed once untimed first.  Returns (wall ms per step of the
+    of `steps` launches of it, replayed GRAPH_REPLAYS times: one mean per replay),
+    then the whole step (a graph of `steps` steps); every graph is replayed once
+    untimed first.  Returns (wall ms per step of the
     step graph's timed replay, event ms per step of it)."""
     import torch
     stream = torch.cuda.current_stream(dev)
@@ -931,13 +1031,14 @@ def time_graphed(wl, steps, dev):
 
     for op in wl.ops:
         g = capture([op.fn])
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        op.times.append(a.elapsed_time(b) / steps)
+        for _ in range(GRAPH_REPLAYS):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            op.times.append(a.elapsed_time(b) / steps)
         del g
     g = capture([op.fn for op in wl.ops])
     e_start = torch.cuda.Event(enable_timing=True)
@@ -959,6 +1060,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the requant size sweep")
     ap.add_argument("--only", default=None, help="time just this op of the workload (for profiler runs)")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
                     help="time HIP-graph replays instead of Python launches (auto: for the short-step workloads)")
@@ -1001,7 +1103,9 @@ def main():
     comps = {}
     for op in wl.ops:
         ms = sum(op.times) / len(op.times)
-        d = {"ms": round(ms, 4), "GB_s": round(op.nbytes / (ms * 1e-3) / 1e9, 1),
+        med, p10, p90 = percentiles(op.times)
+        d = {"ms": round(ms, 4), "ms_median": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+             "samples": len(op.times), "GB_s": round(op.nbytes / (ms * 1e-3) / 1e9, 1),
              "hbm_frac": round(op.nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bound": op.bound()}
         if op.flops:
             tf = op.flops / (ms * 1e-3) / 1e12
@@ -1029,11 +1133,16 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom.name}
 
+    sweep = None
+    if not args.no_sweep and not args.only and wl.name in ("dsv3_moe_mxfp8", "requant_sr"):
+        print("[bench] requant size sweep", file=sys.stderr, flush=True)
+        sweep = requant_size_sweep(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on a sample (one thread, then all)", file=sys.stderr, flush=True)
         try:
-            cpu = wl.cpu_baseline()
+            cpu = cpu_baseline_both(wl)
         except Exception as exc:  # the baseline is reported, never required
             cpu = {"error": repr(exc)}
 
@@ -1047,6 +1156,8 @@ def main():
                        **({"timing": "hip_graph_replay"} if use_graph else {})), "roofline": roof,
         "cpu_baseline": cpu, "components": comps,
     }
+    if sweep is not None:
+        line["requant_size_sweep"] = sweep
     print(json.dumps(line), flush=True)
 
 

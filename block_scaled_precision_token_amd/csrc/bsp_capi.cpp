@@ -209,13 +209,14 @@ BSP_EXPORT bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8
                                             workspace, ws_bytes, stream);
 }
 
-BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes,
-                                                       const uint8_t *a_scales, const float *a_outer,
-                                                       const int32_t *a_gather, int64_t a_rows,
-                                                       const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
-                                                       int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
-                                                       const float *b_outer, void *c, int c_dtype, int64_t ldc,
-                                                       void *workspace, size_t ws_bytes, void *stream) {
+namespace {
+
+// Argument checks shared by the grouped GEMM entry points (everything but the
+// workspace), before any HIP call.
+bsp_status gemm_args_status(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
+                            const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G,
+                            int64_t M, int64_t N, int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                            const float *b_outer, void *c, int c_dtype, int64_t ldc) {
     if (!a_codes || !a_scales || !b_codes || !b_scales || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
     if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD && mode != BSP_GEMM_FPROP_SWIGLU)
@@ -243,20 +244,53 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const 
     if (mode != BSP_GEMM_WGRAD && !a_gather && a_rows != M) return BSP_ERR_SHAPE;
     if (mode == BSP_GEMM_WGRAD && a_rows != M) return BSP_ERR_SHAPE;
     if (a_rows <= 0) return BSP_ERR_SHAPE;
-    if (!workspace || ws_bytes < bsp_gemm_workspace_size(fmt, mode, M, N, K, G)) return BSP_ERR_WORKSPACE;
     if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) || !aligned16(b_scales) ||
-        !aligned16(group_offsets) || !aligned16(c) || !aligned16(workspace) || !aligned16_or_null(a_outer) ||
+        !aligned16(group_offsets) || !aligned16(c) || !aligned16_or_null(a_outer) ||
         !aligned16_or_null(b_outer) || !aligned16_or_null(a_gather))
         return BSP_ERR_ALIGNMENT;
-    return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
-                                       b_codes, b_scales, b_outer, c, c_dtype, ldc, workspace, as_stream(stream)));
+    return BSP_OK;
 }
 
-BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b,
-                                                int64_t ldb, const int32_t *gather, int64_t src_rows,
-                                                const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
-                                                int64_t K, void *c, int c_dtype, int64_t ldc, void *workspace,
-                                                size_t ws_bytes, void *stream) {
+}  // namespace
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled_tiled(int fmt, int mode, const uint8_t *a_codes,
+                                                             const uint8_t *a_scales, const float *a_outer,
+                                                             const int32_t *a_gather, int64_t a_rows,
+                                                             const int64_t *group_offsets, int64_t G, int64_t M,
+                                                             int64_t N, int64_t K, const uint8_t *b_codes,
+                                                             const uint8_t *b_scales, const float *b_outer, void *c,
+                                                             int c_dtype, int64_t ldc, void *workspace,
+                                                             size_t ws_bytes, int tile, void *stream) {
+    if (tile != 0 && tile != 128 && tile != 256) return BSP_ERR_INVALID_ARG;
+    const bsp_status st = gemm_args_status(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G,
+                                           M, N, K, b_codes, b_scales, b_outer, c, c_dtype, ldc);
+    if (st != BSP_OK) return st;
+    if (!workspace || ws_bytes < bsp_gemm_workspace_size(fmt, mode, M, N, K, G)) return BSP_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return BSP_ERR_ALIGNMENT;
+    return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
+                                       b_codes, b_scales, b_outer, c, c_dtype, ldc, workspace, tile,
+                                       as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes,
+                                                       const uint8_t *a_scales, const float *a_outer,
+                                                       const int32_t *a_gather, int64_t a_rows,
+                                                       const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                       int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                                                       const float *b_outer, void *c, int c_dtype, int64_t ldc,
+                                                       void *workspace, size_t ws_bytes, void *stream) {
+    return bsp_moe_grouped_gemm_blockscaled_tiled(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows,
+                                                  group_offsets, G, M, N, K, b_codes, b_scales, b_outer, c, c_dtype,
+                                                  ldc, workspace, ws_bytes, 0, stream);
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16_tiled(int mode, const uint16_t *a, int64_t lda,
+                                                      const uint16_t *b, int64_t ldb, const int32_t *gather,
+                                                      int64_t src_rows, const int64_t *group_offsets, int64_t G,
+                                                      int64_t M, int64_t N, int64_t K, void *c, int c_dtype,
+                                                      int64_t ldc, void *workspace, size_t ws_bytes, int tile,
+                                                      void *stream) {
+    if (tile != 0 && tile != 128 && tile != 256) return BSP_ERR_INVALID_ARG;
     if (!a || !b || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
     if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return BSP_ERR_INVALID_ARG;
     if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
@@ -290,7 +324,16 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int
         !aligned16_or_null(gather))
         return BSP_ERR_ALIGNMENT;
     return hip_status(bsp::launch_gemm_bf16(mode, a, lda, b, ldb, gather, src_rows, group_offsets, G, M, N, K, c,
-                                            c_dtype, ldc, workspace, as_stream(stream)));
+                                            c_dtype, ldc, workspace, tile, as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b,
+                                                int64_t ldb, const int32_t *gather, int64_t src_rows,
+                                                const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                int64_t K, void *c, int c_dtype, int64_t ldc, void *workspace,
+                                                size_t ws_bytes, void *stream) {
+    return bsp_moe_grouped_gemm_bf16_tiled(mode, a, lda, b, ldb, gather, src_rows, group_offsets, G, M, N, K, c,
+                                           c_dtype, ldc, workspace, ws_bytes, 0, stream);
 }
 
 BSP_EXPORT bsp_status bsp_swiglu_quantize(const void *h13, int in_dtype, int64_t R, int64_t I, uint16_t *h_out,

@@ -50,6 +50,8 @@
 // short ones fill in behind them.
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "bsp_device.hpp"
 #include "bsp_internal.hpp"
 
@@ -1167,24 +1169,29 @@ int64_t gemm_workspace_bytes(int fmt, int mode, int64_t M, int64_t N, int64_t K,
 }
 
 // Workgroups resident per XCD for one instantiation on the current device
-// (compute units per XCD times workgroups per compute unit), cached per device.
+// (compute units per XCD times workgroups per compute unit).  The value is a
+// property of the device and the compiled kernel, so it is computed on first
+// use per device and kept: every caller computes the same number, and the
+// atomic store makes concurrent first calls harmless.
 template <typename Kern>
-static int64_t resident_per_xcd(Kern kern, int threads, int *cache) {
+static int64_t resident_per_xcd(Kern kern, int threads, std::atomic<int> *cache) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-    if (cache[dev] == 0) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0, occ = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess || occ <= 0) occ = 1;
-        cache[dev] = (cus + NXCD - 1) / NXCD * occ;
+        v = (cus + NXCD - 1) / NXCD * occ;
+        cache[dev].store(v, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return v;
 }
 
 template <int FMT, int MODE, bool BF, int BT>
 static void launch_one(const GemmArgs &p, hipStream_t s) {
-    static int cache[kMaxDevices] = {};
+    static std::atomic<int> cache[kMaxDevices];
     const int64_t per_xcd_max = resident_per_xcd(k_gemm<FMT, MODE, BF, BT>, 2 * BT, cache);
     const int64_t total = (int64_t)p.ntm * p.ntn;   // upper bound of the tile count
     const int64_t per_xcd_need = (total + NXCD - 1) / NXCD;
@@ -1201,12 +1208,8 @@ static void launch_k(const GemmArgs &p, bool bf, hipStream_t s) {
 
 // Tile edge: 256 (eight wavefronts, half the operand traffic per output of a
 // 128 tile) once there are enough tiles to occupy every compute unit twice
-// over, else 128.
-// BSP_GEMM_TILE=128 or 256 in the environment pins the choice (tests use it
-// to run both tile shapes on small problems).
-static int pick_tile(int64_t tiles256) {
-    const char *e = getenv("BSP_GEMM_TILE");
-    const int forced = e ? atoi(e) : 0;
+// over, else 128; `forced` (128 or 256, from the caller) pins the choice.
+static int pick_tile(int64_t tiles256, int forced) {
     if (forced == 128 || forced == 256) return forced;
     return tiles256 >= 512 ? 256 : 128;
 }
@@ -1214,7 +1217,8 @@ static int pick_tile(int64_t tiles256) {
 hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_outer,
                        const int32_t *a_gather, int64_t a_rows, const int64_t *group_offsets, int64_t G,
                        int64_t M, int64_t N, int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
-                       const float *b_outer, void *c, int c_dtype, int64_t ldc, void *workspace, hipStream_t s) {
+                       const float *b_outer, void *c, int c_dtype, int64_t ldc, void *workspace, int tile,
+                       hipStream_t s) {
     const WsLayout L = ws_layout(fmt, mode, M, N, K, G);
     GemmArgs p = {};
     p.a_codes = a_codes; p.a_scales = a_scales; p.a_outer = a_outer; p.a_gather = a_gather;
@@ -1236,7 +1240,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     PlaneArgs pb = {};
     pb.src = b_scales; pb.sr = sr; pb.plane = wsb + L.b_off; pb.nbp = L.nbp; pb.rp = L.b_rp; pb.rows_z = (int32_t)N;
     if (mode == BSP_GEMM_WGRAD) {
-        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
+        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256), tile);
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
         k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
@@ -1257,7 +1261,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
         }
         return hipGetLastError();
     }
-    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256));
+    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256), tile);
     p.ntn = (int32_t)((N + bt - 1) / bt);
     p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
     k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
@@ -1298,7 +1302,7 @@ int64_t gemm_bf16_workspace_bytes(int mode, int64_t M, int64_t G) {
 hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
                             const int32_t *gather, int64_t src_rows, const int64_t *group_offsets, int64_t G,
                             int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc, void *workspace,
-                            hipStream_t s) {
+                            int tile, hipStream_t s) {
     GemmArgs p = {};
     const bool wg = mode == BSP_GEMM_WGRAD;
     p.a_codes = reinterpret_cast<const uint8_t *>(a);
@@ -1313,7 +1317,7 @@ hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint
     p.c = c; p.G = (int32_t)G; p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K; p.ldc = (int32_t)ldc;
     const bool bf = c_dtype == BSP_DTYPE_BF16;
     if (wg) {
-        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256));
+        const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256), tile);
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
         int32_t *order = reinterpret_cast<int32_t *>(workspace);
@@ -1324,7 +1328,7 @@ hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint
         return hipGetLastError();
     }
     int64_t *ws = reinterpret_cast<int64_t *>(workspace);
-    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256));
+    const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256), tile);
     p.ntn = (int32_t)((N + bt - 1) / bt);
     p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
     p.tiles = ws;

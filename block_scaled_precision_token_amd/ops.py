@@ -37,7 +37,7 @@ EXPORTED = [
     "bsp_mxfp8_sizes", "bsp_mxfp8_grouped_cols", "bsp_requant_workspace_size", "bsp_gemm_workspace_size",
     "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size", "bsp_requant_transpose_sr_batched",
     "bsp_requant_batched_workspace_size", "bsp_requant_transpose_sr_grouped", "bsp_quantize_nvfp4_rht",
-    "bsp_quantize_nvfp4_2d",
+    "bsp_quantize_nvfp4_2d", "bsp_moe_grouped_gemm_blockscaled_tiled", "bsp_moe_grouped_gemm_bf16_tiled",
 ]
 
 
@@ -76,6 +76,8 @@ def _declare(lib):
                                                      INT, I64, P, SZ, P]
     lib.bsp_moe_grouped_gemm_bf16.argtypes = [INT, P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P, INT, I64, P,
                                               SZ, P]
+    lib.bsp_moe_grouped_gemm_blockscaled_tiled.argtypes = lib.bsp_moe_grouped_gemm_blockscaled.argtypes[:-1] + [INT, P]
+    lib.bsp_moe_grouped_gemm_bf16_tiled.argtypes = lib.bsp_moe_grouped_gemm_bf16.argtypes[:-1] + [INT, P]
     lib.bsp_gemm_bf16_workspace_size.argtypes = [INT, I64, I64, I64, I64]
     lib.bsp_gemm_bf16_workspace_size.restype = SZ
     lib.bsp_swiglu_quantize.argtypes = [P, INT, I64, I64, P, INT, P, P, P, U32, P]
@@ -90,7 +92,8 @@ def _declare(lib):
     for name in ("bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize", "bsp_requant_transpose_sr",
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
                  "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched", "bsp_requant_transpose_sr_grouped",
-                 "bsp_quantize_nvfp4_rht", "bsp_quantize_nvfp4_2d"):
+                 "bsp_quantize_nvfp4_rht", "bsp_quantize_nvfp4_2d", "bsp_moe_grouped_gemm_blockscaled_tiled",
+                 "bsp_moe_grouped_gemm_bf16_tiled"):
         getattr(lib, name).restype = INT
 
 
@@ -124,8 +127,16 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# Device type the tensor arguments must live on.  The CPU tests of the
+# argument checks rebind it (with the library stubbed out) so that the checks
+# can be exercised without a GPU; nothing is launched on that path.
+DEVICE_TYPE = "cuda"
+
+_DT = {"u8": torch.uint8, "bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32, "i64": torch.int64}
+
+
 def _need_cuda(t, name):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or t.device.type != DEVICE_TYPE:
         raise ValueError(f"{name} must be a device tensor")
 
 
@@ -134,24 +145,73 @@ def _rowmajor(t, name):
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
 
 
+def _arg(t, name, dev, dtype, numel=None, optional=False, contiguous=True):
+    """Check one tensor argument before its pointer goes to the library: a
+    device tensor on `dev` of the given dtype ("u8", "bf16", "f32", "i32",
+    "i64" or a tuple of them), contiguous, with at least `numel` elements.
+    Raises ValueError; returns t."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    _need_cuda(t, name)
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    kinds = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in tuple(_DT[k] for k in kinds):
+        raise ValueError(f"{name} must have dtype {' or '.join(kinds)}, not {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {int(numel)}")
+    return t
+
+
+def _rows_arg(t, name, dev, dtype, cols):
+    """A 2-D operand read row by row with its row stride: unit column stride,
+    at least `cols` columns, 16-byte aligned rows."""
+    _arg(t, name, dev, dtype, contiguous=False)
+    _rowmajor(t, name)
+    if t.shape[1] < cols:
+        raise ValueError(f"{name} has {t.shape[1]} columns, needs {cols}")
+    return t
+
+
+def _offsets_arg(off, dev):
+    _arg(off, "group_offsets", dev, "i64")
+    if off.dim() != 1 or off.numel() < 2:
+        raise ValueError("group_offsets must be a 1-D int64 tensor of G + 1 >= 2 entries")
+    return off.numel() - 1
+
+
 # ---------------------------------------------------------------------------
 # ops
 # ---------------------------------------------------------------------------
 
+def _x_arg(x, name="x"):
+    """The bf16 input of a quantizer: a 2-D device tensor with unit column stride."""
+    _need_cuda(x, name)
+    _rowmajor(x, name)
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16")
+    return x
+
+
 def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1, mode46: bool = False, out=None):
     """bf16 [M, K] -> (codes u8 [M, K/2], scales u8 [M, K/16], outer f32 [M / rows_per_scale])."""
-    _need_cuda(x, "x")
-    _rowmajor(x, "x")
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bfloat16")
+    _x_arg(x)
     M, K = x.shape
     dev = x.device
+    nscope = max(M // max(rows_per_scale, 1), 1)
     if out is None:
         codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
-        outer = torch.empty((max(M // max(rows_per_scale, 1), 1),), dtype=torch.float32, device=dev)
+        outer = torch.empty((nscope,), dtype=torch.float32, device=dev)
     else:
         codes, scales, outer = out
+        _arg(codes, "codes", dev, "u8", M * (K // 2))
+        _arg(scales, "scales", dev, "u8", M * (K // 16))
+        _arg(outer, "outer", dev, "f32", nscope)
     flags = NVFP4_46 if mode46 else 0
     st = _lib_raw().bsp_quantize_nvfp4_per_token(_ptr(x), M, K, x.stride(0), rows_per_scale, _ptr(codes),
                                                  _ptr(scales), _ptr(outer), flags, _stream(dev))
@@ -184,8 +244,11 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
         _rowmajor(x, "x")
         x2 = x
     x_rows, K = x2.shape
-    M = x_rows if row_gather is None else row_gather.numel()
     dev = x.device
+    if row_gather is not None:
+        _arg(row_gather, "row_gather", dev, "i32")
+    M = x_rows if row_gather is None else row_gather.numel()
+    G = 0 if group_offsets is None else _offsets_arg(group_offsets, dev)
     lead = (batch,) if x.dim() == 3 else ()
     res = {"codes_row": None, "scales_row": None, "codes_colT": None, "scales_colT": None}
     if out is not None:
@@ -196,12 +259,17 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
             res["scales_row"] = torch.empty(lead + (M, K // 32), dtype=torch.uint8, device=dev)
         if colwise:
             if ld_colT is None:
-                ld_colT = M if group_offsets is None else mxfp8_grouped_cols(M, group_offsets.numel() - 1)
+                ld_colT = M if group_offsets is None else mxfp8_grouped_cols(M, G)
             res["codes_colT"] = torch.empty(lead + (K, ld_colT), dtype=torch.uint8, device=dev)
             res["scales_colT"] = torch.empty(lead + (K, ld_colT // 32), dtype=torch.uint8, device=dev)
-    if res["codes_colT"] is not None:
+    if res["codes_row"] is not None or res["scales_row"] is not None:
+        _arg(res["codes_row"], "codes_row", dev, "u8", batch * M * K)
+        _arg(res["scales_row"], "scales_row", dev, "u8", batch * M * (K // 32))
+    if res["codes_colT"] is not None or res["scales_colT"] is not None:
+        _arg(res["codes_colT"], "codes_colT", dev, "u8")
         ld_colT = res["codes_colT"].shape[-1]
-    G = 0 if group_offsets is None else group_offsets.numel() - 1
+        _arg(res["codes_colT"], "codes_colT", dev, "u8", batch * K * ld_colT)
+        _arg(res["scales_colT"], "scales_colT", dev, "u8", batch * K * (ld_colT // 32))
     st = _lib_raw().bsp_quantize_mxfp8(_ptr(x), x_rows, K, x2.stride(0), _ptr(row_gather), M, batch,
                                        _ptr(res["codes_row"]),
                                        _ptr(res["scales_row"]), _ptr(res["codes_colT"]), _ptr(res["scales_colT"]),
@@ -210,17 +278,24 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
     return res
 
 
+def _nvfp4_out(out, M, K, nouter, dev):
+    if out is None:
+        return (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                torch.empty((nouter,), dtype=torch.float32, device=dev))
+    codes, scales, outer = out
+    _arg(codes, "codes", dev, "u8", M * (K // 2))
+    _arg(scales, "scales", dev, "u8", M * (K // 16))
+    _arg(outer, "outer", dev, "f32", nouter)
+    return out
+
+
 def quantize_nvfp4_rht(x: torch.Tensor, signs: int, mode46: bool = False, out=None):
     """bf16 [M, K] -> per-token NVFP4 of the 16-point-RHT'd rows (codes, scales, outer [M])."""
-    _need_cuda(x, "x")
-    _rowmajor(x, "x")
+    _x_arg(x)
     M, K = x.shape
     dev = x.device
-    if out is None:
-        out = (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
-               torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
-               torch.empty((M,), dtype=torch.float32, device=dev))
-    codes, scales, outer = out
+    codes, scales, outer = out = _nvfp4_out(out, M, K, M, dev)
     st = _lib_raw().bsp_quantize_nvfp4_rht(_ptr(x), M, K, x.stride(0), signs, _ptr(codes), _ptr(scales), _ptr(outer),
                                            NVFP4_46 if mode46 else 0, _stream(dev))
     _check(st, "bsp_quantize_nvfp4_rht")
@@ -229,8 +304,7 @@ def quantize_nvfp4_rht(x: torch.Tensor, signs: int, mode46: bool = False, out=No
 
 def quantize_nvfp4_2d(x: torch.Tensor, out=None):
     """bf16 [M, K] -> NVFP4 with 16x16 block scales (codes [M, K/2], scales [M/16, K/16], outer [1])."""
-    _need_cuda(x, "x")
-    _rowmajor(x, "x")
+    _x_arg(x)
     M, K = x.shape
     dev = x.device
     if out is None:
@@ -238,6 +312,9 @@ def quantize_nvfp4_2d(x: torch.Tensor, out=None):
                torch.empty((M // 16, K // 16), dtype=torch.uint8, device=dev),
                torch.empty((4,), dtype=torch.float32, device=dev))
     codes, scales, outer = out
+    _arg(codes, "codes", dev, "u8", M * (K // 2))
+    _arg(scales, "scales", dev, "u8", (M // 16) * (K // 16))
+    _arg(outer, "outer", dev, "f32", 1)
     st = _lib_raw().bsp_quantize_nvfp4_2d(_ptr(x), M, K, x.stride(0), _ptr(codes), _ptr(scales), _ptr(outer),
                                           _stream(dev))
     _check(st, "bsp_quantize_nvfp4_2d")
@@ -245,14 +322,21 @@ def quantize_nvfp4_2d(x: torch.Tensor, out=None):
 
 
 def dequantize(fmt: int, codes, scales, outer=None, rows_per_scale: int = 1, out_dtype=torch.float32, out=None):
-    _need_cuda(codes, "codes")
+    _arg(codes, "codes", codes.device if isinstance(codes, torch.Tensor) else None, "u8")
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D [M, K/2] (NVFP4) or [M, K] (MXFP8)")
+    dev = codes.device
     M = codes.shape[0]
     K = codes.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
+    _arg(scales, "scales", dev, "u8", M * (K // (16 if fmt == FMT_NVFP4 else 32)))
+    if fmt == FMT_NVFP4:
+        _arg(outer, "outer", dev, "f32", M // max(rows_per_scale, 1))
     if out is None:
-        out = torch.empty((M, K), dtype=out_dtype, device=codes.device)
+        out = torch.empty((M, K), dtype=out_dtype, device=dev)
+    _arg(out, "out", dev, ("f32", "bf16"), M * K)
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
     st = _lib_raw().bsp_dequantize(fmt, _ptr(codes), _ptr(scales), _ptr(outer), M, K, rows_per_scale, _ptr(out), dt,
-                                   _stream(codes.device))
+                                   _stream(dev))
     _check(st, "bsp_dequantize")
     return out
 
@@ -265,21 +349,35 @@ def requant_batched_workspace_size(E: int, M: int, rows_per_scale: int) -> int:
     return int(_lib_raw().bsp_requant_batched_workspace_size(E, M, rows_per_scale))
 
 
+def _nvfp4_in(codes, scales, outer, nouter):
+    """Rowwise NVFP4 operand [rows, K/2] + [rows, K/16] + f32 [nouter]."""
+    _arg(codes, "codes", codes.device if isinstance(codes, torch.Tensor) else None, "u8")
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D [rows, K/2]")
+    dev = codes.device
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    _arg(scales, "scales", dev, "u8", rows * (K // 16))
+    _arg(outer, "outer", dev, "f32", nouter(rows))
+    return dev, rows, K
+
+
 def requant_transpose_sr_batched(codes, scales, outer, E: int, rows_per_scale: int, seed: int = 0, sr: bool = True,
                                  workspace=None, out=None):
     """E stacked rowwise NVFP4 tensors [E*M, K] -> (codesT [E*K, M/2], scalesT [E*K, M/16], outerT [E])."""
-    _need_cuda(codes, "codes")
-    EM, K = codes.shape[0], codes.shape[1] * 2
+    dev, EM, K = _nvfp4_in(codes, scales, outer, lambda r: r // max(rows_per_scale, 1))
     M = EM // E
-    dev = codes.device
     if out is None:
         out = (torch.empty((E * K, M // 2), dtype=torch.uint8, device=dev),
                torch.empty((E * K, M // 16), dtype=torch.uint8, device=dev),
                torch.empty((max(E, 4),), dtype=torch.float32, device=dev))
-    if workspace is None:
-        workspace = torch.empty((max(requant_batched_workspace_size(E, M, rows_per_scale), 16),), dtype=torch.uint8,
-                                device=dev)
     codesT, scalesT, outerT = out
+    _arg(codesT, "codesT", dev, "u8", E * K * (M // 2))
+    _arg(scalesT, "scalesT", dev, "u8", E * K * (M // 16))
+    _arg(outerT, "outerT", dev, "f32", E)
+    need = requant_batched_workspace_size(E, M, rows_per_scale)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", dev, "u8", need)
     st = _lib_raw().bsp_requant_transpose_sr_batched(_ptr(codes), _ptr(scales), _ptr(outer), rows_per_scale, E, M, K,
                                                      _ptr(codesT), _ptr(scalesT), _ptr(outerT), seed, SR if sr else 0,
                                                      _ptr(workspace), workspace.numel(), _stream(dev))
@@ -292,10 +390,9 @@ def requant_transpose_sr_grouped(codes, scales, outer, group_offsets, R: int, ld
     """Rowwise NVFP4 [src_rows, K] grouped through `gather` -> (codesT [K, ldT/2],
     scalesT [K, ldT/16], outerT [G]); columns past the padded total untouched
     (zero when allocated here)."""
-    _need_cuda(codes, "codes")
-    src_rows, K = codes.shape[0], codes.shape[1] * 2
-    G = group_offsets.numel() - 1
-    dev = codes.device
+    dev, src_rows, K = _nvfp4_in(codes, scales, outer, lambda r: r)
+    G = _offsets_arg(group_offsets, dev)
+    _arg(gather, "gather", dev, "i32", R, optional=True)
     if ldT is None:
         ldT = mxfp8_grouped_cols(R, G)
     if out is None:
@@ -303,6 +400,9 @@ def requant_transpose_sr_grouped(codes, scales, outer, group_offsets, R: int, ld
                torch.zeros((K, ldT // 16), dtype=torch.uint8, device=dev),
                torch.empty((max(G, 4),), dtype=torch.float32, device=dev))
     codesT, scalesT, outerT = out
+    _arg(codesT, "codesT", dev, "u8", K * (ldT // 2))
+    _arg(scalesT, "scalesT", dev, "u8", K * (ldT // 16))
+    _arg(outerT, "outerT", dev, "f32", G)
     st = _lib_raw().bsp_requant_transpose_sr_grouped(_ptr(codes), _ptr(scales), _ptr(outer), src_rows, _ptr(gather),
                                                      _ptr(group_offsets), G, R, K, _ptr(codesT), _ptr(scalesT), ldT,
                                                      _ptr(outerT), seed, SR if sr else 0, _stream(dev))
@@ -312,17 +412,20 @@ def requant_transpose_sr_grouped(codes, scales, outer, group_offsets, R: int, ld
 
 def requant_transpose_sr(codes, scales, outer, seed: int = 0, sr: bool = True, workspace=None, out=None):
     """Rowwise NVFP4 [M, K] -> (codesT [K, M/2], scalesT [K, M/16], outerT [1])."""
-    _need_cuda(codes, "codes")
-    M, K = codes.shape[0], codes.shape[1] * 2
-    dev = codes.device
+    dev, M, K = _nvfp4_in(codes, scales, outer, lambda r: r)
     if out is None:
         codesT = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
         scalesT = torch.empty((K, M // 16), dtype=torch.uint8, device=dev)
         outerT = torch.empty((4,), dtype=torch.float32, device=dev)
     else:
         codesT, scalesT, outerT = out
+    _arg(codesT, "codesT", dev, "u8", K * (M // 2))
+    _arg(scalesT, "scalesT", dev, "u8", K * (M // 16))
+    _arg(outerT, "outerT", dev, "f32", 1)
+    need = requant_workspace_size(M)
     if workspace is None:
-        workspace = torch.empty((requant_workspace_size(M),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", dev, "u8", need)
     st = _lib_raw().bsp_requant_transpose_sr(_ptr(codes), _ptr(scales), _ptr(outer), M, K, _ptr(codesT),
                                              _ptr(scalesT), _ptr(outerT), seed & (2 ** 64 - 1), SR if sr else 0,
                                              _ptr(workspace), workspace.numel(), _stream(dev))
@@ -337,34 +440,62 @@ def gemm_workspace_size(fmt: int, mode: int, M: int, N: int, K: int, G: int) -> 
 
 def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets, N: int,
                                  K: int, M: int | None = None, a_outer=None, b_outer=None, a_gather=None,
-                                 out_dtype=torch.float32, out=None, workspace=None):
+                                 out_dtype=torch.float32, out=None, workspace=None, tile: int = 0):
     """Grouped block-scaled GEMM; see bsp_moe_grouped_gemm_blockscaled in include/bsp.h.
 
     FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
     with M = rows of A (the columnwise copies' K dimension is their ld).
     FPROP_SWIGLU: B the fused [gate; up] weight (N = 2I rows per expert),
-    C = h [M, I] in bf16.
+    C = h [M, I] in bf16.  tile: 0 (the library's choice), 128 or 256.
     """
-    _need_cuda(a_codes, "a_codes")
+    _arg(a_codes, "a_codes", a_codes.device if isinstance(a_codes, torch.Tensor) else None, "u8")
     dev = a_codes.device
-    G = group_offsets.numel() - 1
+    G = _offsets_arg(group_offsets, dev)
+    if a_codes.dim() != 2:
+        raise ValueError("a_codes must be 2-D")
     a_rows = a_codes.shape[0]
+    wg = mode == GEMM_WGRAD
+    nv = fmt == FMT_NVFP4
+    rowb = K // 2 if nv else K                      # code bytes per operand row
+    sblk = 16 if nv else 32
+    if a_codes.shape[1] * (2 if nv else 1) != K:
+        raise ValueError(f"a_codes has {a_codes.shape[1]} bytes per row, K = {K} needs {rowb}")
+    _arg(a_gather, "a_gather", dev, "i32", optional=True)
     if M is None:
         M = a_gather.numel() if a_gather is not None else a_rows
+    if a_gather is not None and a_gather.numel() < M:
+        raise ValueError(f"a_gather has {a_gather.numel()} entries, needs {M}")
+    _arg(a_scales, "a_scales", dev, "u8", a_rows * (K // sblk))
+    nb_rows = N if wg else G * N                    # rows of B
+    _arg(b_codes, "b_codes", dev, "u8", nb_rows * rowb)
+    _arg(b_scales, "b_scales", dev, "u8", nb_rows * (K // sblk))
+    if nv:
+        _arg(a_outer, "a_outer", dev, "f32", G if wg else a_rows)
+        _arg(b_outer, "b_outer", dev, "f32", G)
+    elif a_outer is not None or b_outer is not None:
+        raise ValueError("MXFP8 takes no outer scales")
     if out is None:
         if mode == GEMM_FPROP_SWIGLU:
             out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
         else:
-            out = torch.empty((G, M, N) if mode == GEMM_WGRAD else (M, N), dtype=out_dtype, device=dev)
+            out = torch.empty((G, M, N) if wg else (M, N), dtype=out_dtype, device=dev)
+    _arg(out, "out", dev, ("f32", "bf16"))
     ldc = out.shape[-1] if out.dim() >= 2 else N
+    if ldc < (N // 2 if mode == GEMM_FPROP_SWIGLU else N):
+        raise ValueError(f"out has rows of {ldc} elements, fewer than the {N} columns of C")
+    _arg(out, "out", dev, ("f32", "bf16"), (G * M if wg else M) * ldc)
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    need = gemm_workspace_size(fmt, mode, M, N, K, G)
     if workspace is None:
-        workspace = torch.empty((max(gemm_workspace_size(fmt, mode, M, N, K, G), 16),), dtype=torch.uint8,
-                                device=dev)
-    st = _lib_raw().bsp_moe_grouped_gemm_blockscaled(fmt, mode, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer),
-                                                     _ptr(a_gather), a_rows, _ptr(group_offsets), G, M, N, K,
-                                                     _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt,
-                                                     ldc, _ptr(workspace), workspace.numel(), _stream(dev))
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", dev, "u8", need)
+    args = (fmt, mode, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer), _ptr(a_gather), a_rows, _ptr(group_offsets), G,
+            M, N, K, _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt, ldc, _ptr(workspace),
+            workspace.numel())
+    if tile:
+        st = _lib_raw().bsp_moe_grouped_gemm_blockscaled_tiled(*args, tile, _stream(dev))
+    else:
+        st = _lib_raw().bsp_moe_grouped_gemm_blockscaled(*args, _stream(dev))
     _check(st, "bsp_moe_grouped_gemm_blockscaled")
     return out
 
@@ -374,41 +505,66 @@ def gemm_bf16_workspace_size(mode: int, M: int, N: int, K: int, G: int) -> int:
 
 
 def moe_grouped_gemm_bf16(mode: int, a: torch.Tensor, b: torch.Tensor, group_offsets, N: int, K: int,
-                          M: int | None = None, gather=None, out_dtype=torch.float32, out=None, workspace=None):
+                          M: int | None = None, gather=None, out_dtype=torch.float32, out=None, workspace=None,
+                          tile: int = 0):
     """BF16 grouped GEMM; see bsp_moe_grouped_gemm_bf16 in include/bsp.h.
 
     FPROP: a [src_rows, K], b [G*N, K] (or [G, N, K]); DGRAD: b [G*K, N] (or
     [G, K, N]); C [M, N] with M = rows of C (gather length, else a's rows).
     WGRAD: a [K, M] (K = grouped rows), b [src_rows, N]; C [G, M, N].
+    tile: 0 (the library's choice), 128 or 256.
     """
-    _need_cuda(a, "a")
+    _arg(a, "a", a.device if isinstance(a, torch.Tensor) else None, "bf16", contiguous=False)
+    _rowmajor(a, "a")
     dev = a.device
-    G = group_offsets.numel() - 1
+    G = _offsets_arg(group_offsets, dev)
+    _arg(b, "b", dev, "bf16")
+    lda, ldb = a.stride(0), b.shape[-1]
+    _arg(gather, "gather", dev, "i32", optional=True)
     if mode == GEMM_WGRAD:
         M = a.shape[1] if M is None else M
-        src_rows = b.shape[0]
+        src_rows = b.shape[0] if b.dim() == 2 else b.numel() // ldb
+        if a.shape[0] < K:
+            raise ValueError(f"a has {a.shape[0]} rows, needs K = {K}")
+        if gather is not None and gather.numel() < K:
+            raise ValueError(f"gather has {gather.numel()} entries, needs {K}")
+        b_need = src_rows * ldb
     else:
         src_rows = a.shape[0]
         if M is None:
             M = gather.numel() if gather is not None else src_rows
+        if gather is not None and gather.numel() < M:
+            raise ValueError(f"gather has {gather.numel()} entries, needs {M}")
+        b_need = G * (N if mode == GEMM_FPROP else K) * ldb
+    _arg(b, "b", dev, "bf16", b_need)
     if out is None:
         shape = (G, M, N) if mode == GEMM_WGRAD else (M, N)
         out = torch.empty(shape, dtype=out_dtype, device=dev)
+    _arg(out, "out", dev, ("f32", "bf16"))
     ldc = out.shape[-1]
+    if ldc < N:
+        raise ValueError(f"out has rows of {ldc} elements, fewer than the {N} columns of C")
+    _arg(out, "out", dev, ("f32", "bf16"), (G * M if mode == GEMM_WGRAD else M) * ldc)
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    need = gemm_bf16_workspace_size(mode, M, N, K, G)
     if workspace is None:
-        workspace = torch.empty((gemm_bf16_workspace_size(mode, M, N, K, G),), dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel()
-    st = _lib_raw().bsp_moe_grouped_gemm_bf16(mode, _ptr(a), a.stride(0) if a.dim() == 2 else a.shape[-1], _ptr(b),
-                                              b.shape[-1], _ptr(gather), src_rows, _ptr(group_offsets), G, M, N,
-                                              K, _ptr(out), dt, ldc, _ptr(workspace), ws_bytes, _stream(dev))
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", dev, "u8", need)
+    args = (mode, _ptr(a), lda, _ptr(b), ldb, _ptr(gather), src_rows, _ptr(group_offsets), G, M, N, K, _ptr(out), dt,
+            ldc, _ptr(workspace), workspace.numel())
+    if tile:
+        st = _lib_raw().bsp_moe_grouped_gemm_bf16_tiled(*args, tile, _stream(dev))
+    else:
+        st = _lib_raw().bsp_moe_grouped_gemm_bf16(*args, _stream(dev))
     _check(st, "bsp_moe_grouped_gemm_bf16")
     return out
 
 
 def swiglu_quantize(h13: torch.Tensor, fmt: int = -1, mode46: bool = False, return_h: bool = True, out=None):
     """h13 [R, 2I] (f32 or bf16) -> (h bf16 [R, I] or None, codes, scales, outer)."""
-    _need_cuda(h13, "h13")
+    _arg(h13, "h13", h13.device if isinstance(h13, torch.Tensor) else None, ("f32", "bf16"))
+    if h13.dim() != 2:
+        raise ValueError("h13 must be 2-D [R, 2I]")
     R, I2 = h13.shape
     I = I2 // 2
     dev = h13.device
@@ -425,6 +581,12 @@ def swiglu_quantize(h13: torch.Tensor, fmt: int = -1, mode46: bool = False, retu
         elif fmt == FMT_MXFP8:
             codes = torch.empty((R, I), dtype=torch.uint8, device=dev)
             scales = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+    _arg(h, "h", dev, "bf16", R * I, optional=fmt >= 0)
+    if fmt >= 0:
+        nv = fmt == FMT_NVFP4
+        _arg(codes, "codes", dev, "u8", R * (I // 2 if nv else I))
+        _arg(scales, "scales", dev, "u8", R * (I // (16 if nv else 32)))
+        _arg(outer, "outer", dev, "f32", R, optional=not nv)
     dt = DTYPE_BF16 if h13.dtype == torch.bfloat16 else DTYPE_F32
     st = _lib_raw().bsp_swiglu_quantize(_ptr(h13), dt, R, I, _ptr(h), fmt, _ptr(codes), _ptr(scales), _ptr(outer),
                                         NVFP4_46 if mode46 else 0, _stream(dev))

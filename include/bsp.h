@@ -23,7 +23,11 @@
  * Conventions shared by every call:
  *   - Pointers named in the comments as "device" point to GPU memory; sizes
  *     and scalars are host values.  The caller allocates and owns every buffer;
- *     the library keeps no state between calls and allocates nothing.
+ *     the library allocates nothing.  Its one piece of state is a per-device
+ *     cache of the grouped GEMM kernels' occupancy (workgroups per compute
+ *     unit), a property of the device and the compiled code filled on first
+ *     use and stored atomically: results never depend on it, and concurrent
+ *     callers may share the library.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and never synchronize; results are ready when the
  *     stream reaches that point.  Calls on one stream are ordered.
@@ -321,6 +325,23 @@ bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_
                                             void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The same call with the GEMM's output tile edge chosen by the caller:
+ * tile 0 is the library's choice (what bsp_moe_grouped_gemm_blockscaled
+ * does: 256 once the problem has at least 512 such tiles, else 128), 128 or
+ * 256 pins it; any other value returns BSP_ERR_INVALID_ARG.  Results do not
+ * depend on the tile (the contract holds for every launch geometry); the pin
+ * exists for tests, which run small problems with both tile shapes, and for
+ * tuning.
+ */
+bsp_status bsp_moe_grouped_gemm_blockscaled_tiled(int fmt, int mode, const uint8_t *a_codes,
+                                                  const uint8_t *a_scales, const float *a_outer,
+                                                  const int32_t *a_gather, int64_t a_rows,
+                                                  const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                  int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                                                  const float *b_outer, void *c, int c_dtype, int64_t ldc,
+                                                  void *workspace, size_t ws_bytes, int tile, void *stream);
+
+/*
  * BF16 grouped expert GEMM for the backward pass of the NVFP4 MoE recipe,
  * which runs its data- and weight-gradient GEMMs in BF16 [remio.ai, section
  * "Entrambe le ricette supportano ...": either on the original high-precision
@@ -364,6 +385,13 @@ bsp_status bsp_moe_grouped_gemm_bf16(int mode, const uint16_t *a, int64_t lda, c
                                      const int32_t *gather, int64_t src_rows, const int64_t *group_offsets,
                                      int64_t G, int64_t M, int64_t N, int64_t K, void *c, int c_dtype, int64_t ldc,
                                      void *workspace, size_t ws_bytes, void *stream);
+/* The same with the tile edge chosen by the caller (0, 128 or 256), as
+ * bsp_moe_grouped_gemm_blockscaled_tiled. */
+bsp_status bsp_moe_grouped_gemm_bf16_tiled(int mode, const uint16_t *a, int64_t lda, const uint16_t *b,
+                                           int64_t ldb, const int32_t *gather, int64_t src_rows,
+                                           const int64_t *group_offsets, int64_t G, int64_t M, int64_t N, int64_t K,
+                                           void *c, int c_dtype, int64_t ldc, void *workspace, size_t ws_bytes,
+                                           int tile, void *stream);
 
 /*
  * SwiGLU between the gate/up and down projections, then quantization of its

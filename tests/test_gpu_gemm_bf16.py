@@ -9,6 +9,8 @@ out-of-range entries, N, M and K tails (K a multiple of 8 but not of the
 32-value stage), all three forms, both tile edges, and the full
 Qwen3-30B-A3B-shaped backward GEMMs on sampled rows.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -20,13 +22,15 @@ from tests.gpu_util import DEV, assert_gemm_close, host, to_dev, to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 
+_GEMM = ops.moe_grouped_gemm_bf16
+
+
 @pytest.fixture(params=["auto", "128", "256"], autouse=True)
 def gemm_tile(request, monkeypatch):
-    """Every case with the library's tile choice and with each tile edge pinned."""
-    if request.param == "auto":
-        monkeypatch.delenv("BSP_GEMM_TILE", raising=False)
-    else:
-        monkeypatch.setenv("BSP_GEMM_TILE", request.param)
+    """Every case with the library's tile choice and with each tile edge
+    pinned through the tiled entry point."""
+    if request.param != "auto":
+        monkeypatch.setattr(ops, "moe_grouped_gemm_bf16", functools.partial(_GEMM, tile=int(request.param)))
     return request.param
 
 
