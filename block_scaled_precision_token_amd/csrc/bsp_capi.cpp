@@ -28,6 +28,7 @@ BSP_EXPORT const char *bsp_status_string(int status) {
         case BSP_ERR_UNSUPPORTED: return "unsupported combination";
         case BSP_ERR_WORKSPACE: return "workspace missing or too small";
         case BSP_ERR_HIP: return "HIP runtime error at launch";
+        case BSP_ERR_SCRATCH_LIMIT: return "problem needs more workspace than the allocation-free call's static scratch";
         default: return "unknown status";
     }
 }
@@ -270,6 +271,23 @@ BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled_tiled(int fmt, int mode, 
     return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
                                        b_codes, b_scales, b_outer, c, c_dtype, ldc, workspace, tile,
                                        as_stream(stream)));
+}
+
+BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled_noalloc(int fmt, int mode, const uint8_t *a_codes,
+                                                               const uint8_t *a_scales, const float *a_outer,
+                                                               const int32_t *a_gather, int64_t a_rows,
+                                                               const int64_t *group_offsets, int64_t G, int64_t M,
+                                                               int64_t N, int64_t K, const uint8_t *b_codes,
+                                                               const uint8_t *b_scales, const float *b_outer,
+                                                               void *c, int c_dtype, int64_t ldc, void *stream) {
+    const bsp_status st = gemm_args_status(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G,
+                                           M, N, K, b_codes, b_scales, b_outer, c, c_dtype, ldc);
+    if (st != BSP_OK) return st;
+    if (bsp_gemm_workspace_size(fmt, mode, M, N, K, G) > (size_t)BSP_GEMM_SCRATCH_BYTES) return BSP_ERR_SCRATCH_LIMIT;
+    void *scratch = bsp::gemm_scratch();
+    if (scratch == nullptr) return BSP_ERR_HIP;
+    return hip_status(bsp::launch_gemm(fmt, mode, a_codes, a_scales, a_outer, a_gather, a_rows, group_offsets, G, M, N, K,
+                                       b_codes, b_scales, b_outer, c, c_dtype, ldc, scratch, 0, as_stream(stream)));
 }
 
 BSP_EXPORT bsp_status bsp_moe_grouped_gemm_blockscaled(int fmt, int mode, const uint8_t *a_codes,

@@ -1292,6 +1292,29 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     return hipGetLastError();
 }
 
+// Device scratch of the allocation-free GEMM entry point: the workspace
+// (tile list, counters, scale planes) of one call lives in this array instead
+// of caller memory.  Each device holds its own copy, at its own address, for
+// the life of the process; every call on a device rewrites the parts it reads
+// (the setup kernels clear the counters), so nothing carries over between
+// calls, and calls that overlap on one device race on it.
+static __device__ __align__(256) uint8_t scratch[BSP_GEMM_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device.  The host-side name is
+// only a stand-in for the symbol, so the address is looked up once per device
+// (with that device current) and kept; nullptr when the lookup fails.
+void *gemm_scratch() {
+    static std::atomic<void *> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 // BF16 grouped GEMM.  Workspace: the row-tile list and counters of the
 // row-grouped forms; the expert order of the weight-gradient form.
 int64_t gemm_bf16_workspace_bytes(int mode, int64_t M, int64_t G) {

@@ -40,6 +40,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
                        int64_t M, int64_t N,
                        int64_t K, const uint8_t *b_codes, const uint8_t *b_scales, const float *b_outer, void *c,
                        int c_dtype, int64_t ldc, void *workspace, int tile, hipStream_t s);
+void *gemm_scratch();   // device address of the static GEMM scratch on the current device (nullptr: failed)
 int64_t gemm_bf16_workspace_bytes(int mode, int64_t M, int64_t G);
 hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
                             const int32_t *gather, int64_t src_rows, const int64_t *group_offsets, int64_t G,

@@ -29,7 +29,8 @@ NVFP4_46 = 0x1
 SR = 0x2
 
 STATUS = {0: "BSP_OK", 1: "BSP_ERR_INVALID_ARG", 2: "BSP_ERR_SHAPE", 3: "BSP_ERR_ALIGNMENT",
-          4: "BSP_ERR_UNSUPPORTED", 5: "BSP_ERR_WORKSPACE", 6: "BSP_ERR_HIP"}
+          4: "BSP_ERR_UNSUPPORTED", 5: "BSP_ERR_WORKSPACE", 6: "BSP_ERR_HIP", 7: "BSP_ERR_SCRATCH_LIMIT"}
+GEMM_SCRATCH_BYTES = 64 << 20   # static device scratch of the allocation-free GEMM (BSP_GEMM_SCRATCH_BYTES)
 
 EXPORTED = [
     "bsp_version", "bsp_status_string", "bsp_quantize_nvfp4_per_token", "bsp_quantize_mxfp8", "bsp_dequantize",
@@ -38,6 +39,7 @@ EXPORTED = [
     "bsp_moe_grouped_gemm_bf16", "bsp_gemm_bf16_workspace_size", "bsp_requant_transpose_sr_batched",
     "bsp_requant_batched_workspace_size", "bsp_requant_transpose_sr_grouped", "bsp_quantize_nvfp4_rht",
     "bsp_quantize_nvfp4_2d", "bsp_moe_grouped_gemm_blockscaled_tiled", "bsp_moe_grouped_gemm_bf16_tiled",
+    "bsp_moe_grouped_gemm_blockscaled_noalloc",
 ]
 
 
@@ -78,6 +80,7 @@ def _declare(lib):
                                               SZ, P]
     lib.bsp_moe_grouped_gemm_blockscaled_tiled.argtypes = lib.bsp_moe_grouped_gemm_blockscaled.argtypes[:-1] + [INT, P]
     lib.bsp_moe_grouped_gemm_bf16_tiled.argtypes = lib.bsp_moe_grouped_gemm_bf16.argtypes[:-1] + [INT, P]
+    lib.bsp_moe_grouped_gemm_blockscaled_noalloc.argtypes = lib.bsp_moe_grouped_gemm_blockscaled.argtypes[:18] + [P]
     lib.bsp_gemm_bf16_workspace_size.argtypes = [INT, I64, I64, I64, I64]
     lib.bsp_gemm_bf16_workspace_size.restype = SZ
     lib.bsp_swiglu_quantize.argtypes = [P, INT, I64, I64, P, INT, P, P, P, U32, P]
@@ -93,7 +96,7 @@ def _declare(lib):
                  "bsp_moe_grouped_gemm_blockscaled", "bsp_swiglu_quantize", "bsp_nvfp4_sizes", "bsp_mxfp8_sizes",
                  "bsp_moe_grouped_gemm_bf16", "bsp_requant_transpose_sr_batched", "bsp_requant_transpose_sr_grouped",
                  "bsp_quantize_nvfp4_rht", "bsp_quantize_nvfp4_2d", "bsp_moe_grouped_gemm_blockscaled_tiled",
-                 "bsp_moe_grouped_gemm_bf16_tiled"):
+                 "bsp_moe_grouped_gemm_bf16_tiled", "bsp_moe_grouped_gemm_blockscaled_noalloc"):
         getattr(lib, name).restype = INT
 
 
@@ -438,16 +441,10 @@ def gemm_workspace_size(fmt: int, mode: int, M: int, N: int, K: int, G: int) -> 
     return int(_lib_raw().bsp_gemm_workspace_size(fmt, mode, M, N, K, G))
 
 
-def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets, N: int,
-                                 K: int, M: int | None = None, a_outer=None, b_outer=None, a_gather=None,
-                                 out_dtype=torch.float32, out=None, workspace=None, tile: int = 0):
-    """Grouped block-scaled GEMM; see bsp_moe_grouped_gemm_blockscaled in include/bsp.h.
-
-    FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
-    with M = rows of A (the columnwise copies' K dimension is their ld).
-    FPROP_SWIGLU: B the fused [gate; up] weight (N = 2I rows per expert),
-    C = h [M, I] in bf16.  tile: 0 (the library's choice), 128 or 256.
-    """
+def _gemm_blockscaled_args(fmt, mode, a_codes, a_scales, b_codes, b_scales, group_offsets, N, K, M, a_outer,
+                           b_outer, a_gather, out_dtype, out):
+    """Checks and output allocation shared by the grouped GEMM wrappers; returns
+    (device, G, M, a_rows, out, ldc, c_dtype)."""
     _arg(a_codes, "a_codes", a_codes.device if isinstance(a_codes, torch.Tensor) else None, "u8")
     dev = a_codes.device
     G = _offsets_arg(group_offsets, dev)
@@ -485,6 +482,22 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
         raise ValueError(f"out has rows of {ldc} elements, fewer than the {N} columns of C")
     _arg(out, "out", dev, ("f32", "bf16"), (G * M if wg else M) * ldc)
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    return dev, G, M, a_rows, out, ldc, dt
+
+
+def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets, N: int,
+                                 K: int, M: int | None = None, a_outer=None, b_outer=None, a_gather=None,
+                                 out_dtype=torch.float32, out=None, workspace=None, tile: int = 0):
+    """Grouped block-scaled GEMM; see bsp_moe_grouped_gemm_blockscaled in include/bsp.h.
+
+    FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
+    with M = rows of A (the columnwise copies' K dimension is their ld).
+    FPROP_SWIGLU: B the fused [gate; up] weight (N = 2I rows per expert),
+    C = h [M, I] in bf16.  tile: 0 (the library's choice), 128 or 256.
+    """
+    dev, G, M, a_rows, out, ldc, dt = _gemm_blockscaled_args(fmt, mode, a_codes, a_scales, b_codes, b_scales,
+                                                             group_offsets, N, K, M, a_outer, b_outer, a_gather,
+                                                             out_dtype, out)
     need = gemm_workspace_size(fmt, mode, M, N, K, G)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
@@ -497,6 +510,25 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
     else:
         st = _lib_raw().bsp_moe_grouped_gemm_blockscaled(*args, _stream(dev))
     _check(st, "bsp_moe_grouped_gemm_blockscaled")
+    return out
+
+
+def moe_grouped_gemm_blockscaled_noalloc(fmt: int, mode: int, a_codes, a_scales, b_codes, b_scales, group_offsets,
+                                         N: int, K: int, M: int | None = None, a_outer=None, b_outer=None,
+                                         a_gather=None, out=None):
+    """The allocation-free grouped GEMM (bsp_moe_grouped_gemm_blockscaled_noalloc):
+    no workspace, and `out` must be given -- nothing is allocated on this path.
+    Problems whose workspace exceeds GEMM_SCRATCH_BYTES raise BspError
+    (BSP_ERR_SCRATCH_LIMIT).  Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("out is required: the allocation-free call allocates nothing")
+    dev, G, M, a_rows, out, ldc, dt = _gemm_blockscaled_args(fmt, mode, a_codes, a_scales, b_codes, b_scales,
+                                                             group_offsets, N, K, M, a_outer, b_outer, a_gather,
+                                                             None, out)
+    st = _lib_raw().bsp_moe_grouped_gemm_blockscaled_noalloc(
+        fmt, mode, _ptr(a_codes), _ptr(a_scales), _ptr(a_outer), _ptr(a_gather), a_rows, _ptr(group_offsets), G, M,
+        N, K, _ptr(b_codes), _ptr(b_scales), _ptr(b_outer), _ptr(out), dt, ldc, _stream(dev))
+    _check(st, "bsp_moe_grouped_gemm_blockscaled_noalloc")
     return out
 
 

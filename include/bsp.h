@@ -59,7 +59,8 @@ typedef enum bsp_status {
     BSP_ERR_ALIGNMENT = 3,   /* device pointer or leading dimension misaligned */
     BSP_ERR_UNSUPPORTED = 4, /* valid combination that is not implemented */
     BSP_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-    BSP_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+    BSP_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    BSP_ERR_SCRATCH_LIMIT = 7 /* allocation-free call: the problem's workspace exceeds the static scratch */
 } bsp_status;
 
 enum { BSP_FMT_NVFP4 = 0, BSP_FMT_MXFP8 = 1 };
@@ -340,6 +341,34 @@ bsp_status bsp_moe_grouped_gemm_blockscaled_tiled(int fmt, int mode, const uint8
                                                   int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
                                                   const float *b_outer, void *c, int c_dtype, int64_t ldc,
                                                   void *workspace, size_t ws_bytes, int tile, void *stream);
+
+/*
+ * Allocation-free form of bsp_moe_grouped_gemm_blockscaled, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * bsp_moe_grouped_gemm_blockscaled with the library's tile choice, minus the
+ * workspace: the tile list, counters and scale planes live in a static
+ * device array of BSP_GEMM_SCRATCH_BYTES (64 MiB) that each GPU the library
+ * runs on holds until the process ends.  The call allocates nothing (no
+ * hipMalloc or allocating library routine); on its first call on a device
+ * it looks up that device's copy of the array (a HIP symbol query).
+ *   - A problem whose bsp_gemm_workspace_size exceeds BSP_GEMM_SCRATCH_BYTES
+ *     returns BSP_ERR_SCRATCH_LIMIT and enqueues nothing (e.g. the
+ *     Qwen3-30B-A3B-shaped expert GEMMs fit, 18-37 MiB; a DeepSeek-V3 layer's
+ *     257-expert forward GEMMs on one GPU, 122-249 MiB, do not).
+ *   - Every call on a GPU shares that GPU's array and rewrites what it reads,
+ *     so consecutive calls need nothing cleared; calls that overlap in time on
+ *     one GPU (different streams without ordering, or several host threads)
+ *     race on it and must be serialized by the caller.
+ */
+#define BSP_GEMM_SCRATCH_BYTES (64u << 20)
+bsp_status bsp_moe_grouped_gemm_blockscaled_noalloc(int fmt, int mode, const uint8_t *a_codes,
+                                                    const uint8_t *a_scales, const float *a_outer,
+                                                    const int32_t *a_gather, int64_t a_rows,
+                                                    const int64_t *group_offsets, int64_t G, int64_t M, int64_t N,
+                                                    int64_t K, const uint8_t *b_codes, const uint8_t *b_scales,
+                                                    const float *b_outer, void *c, int c_dtype, int64_t ldc,
+                                                    void *stream);
 
 /*
  * BF16 grouped expert GEMM for the backward pass of the NVFP4 MoE recipe,

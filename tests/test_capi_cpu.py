@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     assert L.bsp_version() == 100
-    for s in range(7):
+    for s in range(8):
         assert len(L.bsp_status_string(s)) > 0
     assert L.bsp_status_string(99) == b"unknown status"
 
@@ -133,6 +133,33 @@ def test_gemm_rejects_bad_arguments():
     assert g(1, 3, A, A, None, None, 64, A, 2, 64, 96, 64, A, A, None, A, 1, 48, A, ws, None) == 2
     assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 32, A, ws, None) == 2
     assert g(1, 4, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 64, A, ws, None) == 1
+
+
+def test_tiled_gemm_rejects_unknown_tile():
+    g = L.bsp_moe_grouped_gemm_blockscaled_tiled
+    ws = 1 << 16
+    for tile in (64, 192, -1, 512):
+        assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, tile, None) == 1
+    b = L.bsp_moe_grouped_gemm_bf16_tiled
+    assert b(0, A, 64, A, 64, None, 64, A, 2, 64, 64, 64, A, 0, 64, A, ws, 100, None) == 1
+
+
+def test_noalloc_gemm_checks_before_any_hip_call():
+    g = L.bsp_moe_grouped_gemm_blockscaled_noalloc
+    # the same argument errors as the workspace form
+    assert g(0, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, A, A, 0, 64, None) == 1
+    assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 48, A, A, None, A, 0, 64, None) == 2
+    assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 32, None) == 2
+    assert g(1, 0, MIS, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, None) == 3
+    # a valid problem whose workspace exceeds the static scratch: the DeepSeek-V3
+    # gate/up forward GEMM of 257 experts (about 249 MiB) is refused, nothing enqueued
+    need = L.bsp_gemm_workspace_size(1, 0, 36864, 4096, 7168, 257)
+    assert need > ops.GEMM_SCRATCH_BYTES
+    assert g(1, 0, A, A, None, A, 4096, A, 257, 36864, 4096, 7168, A, A, None, A, 1, 4096, None) == 7
+    assert L.bsp_status_string(7) != b"unknown status"
+    # the Qwen3-30B-A3B-shaped expert GEMMs fit
+    assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) <= ops.GEMM_SCRATCH_BYTES
+    assert L.bsp_gemm_workspace_size(0, 0, 65536, 2048, 768, 128) <= ops.GEMM_SCRATCH_BYTES
 
 
 def test_bf16_gemm_workspace_and_bad_arguments():
