@@ -409,7 +409,6 @@ __device__ __forceinline__ uint32_t mxfp8_block(const float (&xf)[32], uint32_t 
 
 constexpr int MX_TR = 128;  // tile rows (padded row space)
 constexpr int MX_TC = 128;  // tile columns
-constexpr int MX_MAXG = 2048;
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
@@ -427,7 +426,12 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 // and written back in whole 128-byte rows.
 // Grouped: tile rows live in the padded row space; 32-row block b belongs to
 // the group g with P[g] <= 32 b < P[g + 1] and reads source row
-// off[g] + (p - P[g]) (zero past the group).
+// off[g] + (p - P[g]) (zero past the group).  The grouped grid is 1-D and
+// XCD-aware: workgroup L runs tile v = (L % 8) * chunk + L / 8 of the
+// column-major tile order (all row tiles of a column tile, then the next),
+// so each XCD works through its own run of column tiles and the workgroups
+// resident on it share one column slab of x in its L2 -- what a gathered
+// input re-reads (every token appears once per routed copy).
 template <bool ROW, bool COL, bool GROUPED>
 __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                     int64_t ldx, uint8_t *__restrict__ codes_row,
@@ -436,13 +440,21 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
                                                     const int64_t *__restrict__ group_offsets, int G,
                                                     const int32_t *__restrict__ gather, int64_t x_rows) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[MX_TR][MX_TC + 8];
-    __shared__ int64_t sP[GROUPED ? MX_MAXG + 1 : 1];
     __shared__ int64_t rsrc[ROW ? MX_TR : 1];   // destination row of each tile row in codes_row (-1: none)
     __shared__ int64_t blk_src0[MX_TR / 32], blk_end[MX_TR / 32];
     __shared__ int64_t wsum[4];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int64_t p0 = (int64_t)blockIdx.y * MX_TR;
-    const int64_t k0 = (int64_t)blockIdx.x * MX_TC;
+    int64_t p0, k0;
+    if (GROUPED) {
+        const int64_t gx = (K + MX_TC - 1) / MX_TC, gy = (ld_colT + MX_TR - 1) / MX_TR, n = gx * gy;
+        const int64_t chunk = (n + 7) / 8, v = (int64_t)(blockIdx.x % 8) * chunk + blockIdx.x / 8;
+        if (v >= n) return;
+        k0 = (v / gy) * MX_TC;
+        p0 = (v % gy) * MX_TR;
+    } else {
+        p0 = (int64_t)blockIdx.y * MX_TR;
+        k0 = (int64_t)blockIdx.x * MX_TC;
+    }
     int64_t ptotal = M;
     if (!GROUPED && gridDim.z > 1) {  // stacked independent matrices (no gather, no groups)
         const int64_t b = blockIdx.z;
@@ -456,38 +468,38 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     }
 
     if (GROUPED) {
-        // padded group starts P: thread t owns groups [t*per, t*per + per)
+        // Thread t owns groups [t per, t per + per): a block-wide scan of their
+        // padded sizes gives the padded start of its first group, and the
+        // thread whose groups cover one of this tile's four 32-row blocks
+        // resolves that block's first source row and group end.
         const int per = (G + 255) / 256;
-        const int g0 = t * per;
+        const int g0 = t * per, g1 = g0 + per < G ? g0 + per : G;
         int64_t local = 0;
-        for (int g = g0; g < g0 + per && g < G; g++) local += (group_offsets[g + 1] - group_offsets[g] + 31) / 32 * 32;
+        for (int g = g0; g < g1; g++) local += (group_offsets[g + 1] - group_offsets[g] + 31) / 32 * 32;
         const int64_t incl = wave_incl_scan(local, lane);
         if (lane == 63) wsum[wv] = incl;
+        if (t < MX_TR / 32) {
+            blk_src0[t] = 0;
+            blk_end[t] = 0;
+        }
         __syncthreads();
         int64_t run = incl - local;
         for (int w = 0; w < wv; w++) run += wsum[w];
-        for (int g = g0; g < g0 + per && g < G; g++) {
-            sP[g] = run;
-            run += (group_offsets[g + 1] - group_offsets[g] + 31) / 32 * 32;
-        }
-        if (t == 255) sP[G] = run;
-        __syncthreads();
-        ptotal = sP[G];
-        if (t < MX_TR / 32) {
-            const int64_t pb = p0 + 32 * t;
-            int64_t src0 = 0, end = 0;
-            if (pb < ptotal) {
-                int lo = 0, hi = G - 1;  // last g with P[g] <= pb
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) / 2;
-                    if (sP[mid] <= pb) lo = mid;
-                    else hi = mid - 1;
+        ptotal = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        if (local > 0 && run < p0 + MX_TR && run + local > p0) {
+            for (int g = g0; g < g1; g++) {
+                const int64_t o0 = group_offsets[g], o1 = group_offsets[g + 1];
+                const int64_t pn = (o1 - o0 + 31) / 32 * 32;
+#pragma unroll
+                for (int b = 0; b < MX_TR / 32; b++) {
+                    const int64_t pb = p0 + 32 * b;
+                    if (pb >= run && pb < run + pn) {
+                        blk_src0[b] = o0 + (pb - run);
+                        blk_end[b] = o1 < M ? o1 : M;   // offsets past M are never read
+                    }
                 }
-                src0 = group_offsets[lo] + (pb - sP[lo]);
-                end = group_offsets[lo + 1] < M ? group_offsets[lo + 1] : M;  // offsets past M are never read
+                run += pn;
             }
-            blk_src0[t] = src0;
-            blk_end[t] = end;
         }
         __syncthreads();
         if (p0 >= ptotal) return;
@@ -668,15 +680,17 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, i
     }
     const unsigned gx = (unsigned)((K + MX_TC - 1) / MX_TC);
     if (group_offsets) {
-        const unsigned gy = (unsigned)((ld_colT + MX_TR - 1) / MX_TR);
+        // 1-D XCD-aware grid: 8 runs of ceil(tiles / 8) workgroups
+        const int64_t tiles = (int64_t)gx * ((ld_colT + MX_TR - 1) / MX_TR);
+        const unsigned nwg = (unsigned)(8 * ((tiles + 7) / 8));
         if (row)
-            k_mxfp8_tile<true, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
-                                                                        codes_colT, scales_colT, ld_colT,
-                                                                        group_offsets, (int)G, gather, x_rows);
+            k_mxfp8_tile<true, true, true><<<dim3(nwg), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                     codes_colT, scales_colT, ld_colT,
+                                                                     group_offsets, (int)G, gather, x_rows);
         else
-            k_mxfp8_tile<false, true, true><<<dim3(gx, gy), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
-                                                                         codes_colT, scales_colT, ld_colT,
-                                                                         group_offsets, (int)G, gather, x_rows);
+            k_mxfp8_tile<false, true, true><<<dim3(nwg), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                      codes_colT, scales_colT, ld_colT,
+                                                                      group_offsets, (int)G, gather, x_rows);
     } else {
         const unsigned gy = (unsigned)((M + MX_TR - 1) / MX_TR);
         if (row)
@@ -1162,7 +1176,6 @@ __global__ __launch_bounds__(256) void k_requant_grouped(
     const float *__restrict__ outerT, uint32_t key0, uint32_t key1, int ntk) {
     __shared__ uint32_t tc[RQ_TK / 8][RQ_CS];
     __shared__ float tf[RQ_TK / 16][RQ_TM];
-    __shared__ int64_t sP[MX_MAXG + 1];
     __shared__ int64_t wsum[4];
     __shared__ int64_t blk_src0[RQ_TM / 32], blk_end[RQ_TM / 32];
     __shared__ float blk_G[RQ_TM / 32];
@@ -1170,46 +1183,47 @@ __global__ __launch_bounds__(256) void k_requant_grouped(
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t m0 = (int64_t)(blockIdx.x / ntk) * RQ_TM, k0 = (int64_t)(blockIdx.x % ntk) * RQ_TK;
 
-    // padded group starts P (thread t owns groups [t per, t per + per))
+    // Padded group starts: thread t owns groups [t per, t per + per); a
+    // block-wide scan of their padded sizes gives the start of its first
+    // group, and the thread whose groups cover one of the tile's 32-row
+    // blocks resolves that block's first source row, group end and G_g.
+    int64_t ptotal;
     {
         const int per = (G + 255) / 256;
-        const int g0 = t * per;
+        const int g0 = t * per, g1 = g0 + per < G ? g0 + per : G;
         int64_t local = 0;
-        for (int g = g0; g < g0 + per && g < G; g++) local += (off[g + 1] - off[g] + 31) / 32 * 32;
+        for (int g = g0; g < g1; g++) local += (off[g + 1] - off[g] + 31) / 32 * 32;
         const int64_t incl = wave_incl_scan(local, lane);
         if (lane == 63) wsum[wv] = incl;
+        if (t < RQ_TM / 32) {
+            blk_src0[t] = 0;
+            blk_end[t] = 0;
+            blk_G[t] = 0.0f;
+        }
         __syncthreads();
         int64_t run = incl - local;
         for (int w = 0; w < wv; w++) run += wsum[w];
-        for (int g = g0; g < g0 + per && g < G; g++) {
-            sP[g] = run;
-            run += (off[g + 1] - off[g] + 31) / 32 * 32;
+        const int64_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        ptotal = total < ldT ? total : ldT;   // never past the output's rows
+        if (local > 0 && run < m0 + RQ_TM && run + local > m0) {
+            for (int g = g0; g < g1; g++) {
+                const int64_t o0 = off[g], o1 = off[g + 1];
+                const int64_t pn = (o1 - o0 + 31) / 32 * 32;
+#pragma unroll
+                for (int b = 0; b < RQ_TM / 32; b++) {
+                    const int64_t pb = m0 + 32 * b;
+                    if (pb >= run && pb < run + pn && pb < ptotal) {
+                        blk_src0[b] = o0 + (pb - run);
+                        blk_end[b] = o1 < R ? o1 : R;
+                        blk_G[b] = outerT[g];
+                    }
+                }
+                run += pn;
+            }
         }
-        if (t == 255) sP[G] = run;
         __syncthreads();
     }
-    const int64_t ptotal = sP[G] < ldT ? sP[G] : ldT;   // never past the output's rows
     if (m0 >= ptotal) return;
-    if (t < RQ_TM / 32) {
-        const int64_t pb = m0 + 32 * t;
-        int64_t src0 = 0, end = 0;
-        float gG = 0.0f;
-        if (pb < ptotal) {
-            int lo = 0, hi = G - 1;  // last g with P[g] <= pb
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) / 2;
-                if (sP[mid] <= pb) lo = mid;
-                else hi = mid - 1;
-            }
-            src0 = off[lo] + (pb - sP[lo]);
-            end = off[lo + 1] < R ? off[lo + 1] : R;
-            gG = outerT[lo];
-        }
-        blk_src0[t] = src0;
-        blk_end[t] = end;
-        blk_G[t] = gG;
-    }
-    __syncthreads();
     {
         const int b = t >> 5;
         const int64_t r = blk_src0[b] + (t & 31);
