@@ -184,14 +184,11 @@ def bf16_dev(bits, dev):
 
 class Dsv3MoeMxfp8:
     """DeepSeek-V3-shaped MoE layer, MXFP8 forward + dgrad + wgrad.  SwiGLU runs
-    in the gate/up GEMM's epilogue, which writes h in bf16, and one pass makes
-    h's rowwise and grouped columnwise copies; or (swiglu_epilogue False) it
-    runs with h's rowwise quantization as one kernel after the GEMM and a
-    second pass makes the columnwise copy.  Both give the same h and copies."""
+    as its own kernel on the gate/up GEMM's bf16 output, fused with h's rowwise
+    MXFP8 quantization; a second pass makes h's grouped columnwise copy."""
     name = "dsv3_moe_mxfp8"
     unit = "TFLOP/s"
     dtype = "fp8_e4m3"
-    swiglu_epilogue = True
 
     def __init__(self, dev):
         import numpy as np
@@ -215,7 +212,7 @@ class Dsv3MoeMxfp8:
         W2 = synth.device_weights(SEED + 9, G, H, I, dev)
         dY = synth.device_activations(SEED + 10, R, H, dev)
         dH13 = synth.device_activations(SEED + 11, R, N13, dev)
-        self.X, self.W13, self.W2 = X, W13, W2
+        self.X, self.W13, self.W2, self.dH13 = X, W13, W2, dH13
         u8, bf = torch.uint8, torch.bfloat16
         ld = ops.mxfp8_grouped_cols(R, G)
         emp = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=dev)
@@ -228,8 +225,6 @@ class Dsv3MoeMxfp8:
         h13 = emp(R, N13, dt=bf)
         hq = (emp(R, I, dt=bf), emp(R, I), emp(R, I // 32), None)
         hcq = {"codes_colT": emp(I, ld), "scales_colT": emp(I, ld // 32)}
-        # SwiGLU in the GEMM epilogue: h's rowwise and grouped columnwise copies in one pass
-        hrcq = {"codes_row": hq[1], "scales_row": hq[2], **hcq}
         y = emp(R, H, dt=bf)
         dyq = {"codes_row": emp(R, H), "scales_row": emp(R, H // 32), "codes_colT": emp(H, ld),
                "scales_colT": emp(H, ld // 32)}
@@ -252,21 +247,12 @@ class Dsv3MoeMxfp8:
             Op("quant_x_row", lambda: q(X, True, False, out=xq), T * H * (2 + s8)),
             Op("quant_xg_col_grouped", lambda: q(X, False, True, group_offsets=off_d, row_gather=src_d, out=xgq),
                T * H * 2 + R * H * s8),
-        ] + ([
-            Op("gemm_fprop_gate_up_swiglu", lambda: gm(M8, ops.GEMM_FPROP_SWIGLU, xq["codes_row"], xq["scales_row"],
-                                                        w13q["codes_row"], w13q["scales_row"], off_d, N13, H, M=R,
-                                                        a_gather=src_d, out=hq[0], workspace=ws),
-               G * N13 * H * s8 + T * H * s8 + R * I * 2, 2.0 * R * N13 * H, "fp8"),
-            Op("quant_h_row_col_grouped", lambda: q(hq[0], True, True, group_offsets=off_d, out=hrcq),
-               R * I * (2 + 2 * s8)),
-        ] if self.swiglu_epilogue else [
             Op("gemm_fprop_gate_up", lambda: gm(M8, F, xq["codes_row"], xq["scales_row"], w13q["codes_row"],
                                                  w13q["scales_row"], off_d, N13, H, M=R, a_gather=src_d, out=h13,
                                                  workspace=ws),
                G * N13 * H * s8 + T * H * s8 + R * N13 * 2, 2.0 * R * N13 * H, "fp8"),
             Op("swiglu_quant_h", lambda: ops.swiglu_quantize(h13, ops.FMT_MXFP8, out=hq), R * N13 * 2 + R * I * (2 + s8)),
             Op("quant_h_col_grouped", lambda: q(hq[0], False, True, group_offsets=off_d, out=hcq), R * I * (2 + s8)),
-        ]) + [
             Op("gemm_fprop_down", lambda: gm(M8, F, hq[1], hq[2], w2q["codes_row"], w2q["scales_row"], off_d, H, I,
                                               M=R, out=y, workspace=ws),
                G * H * I * s8 + R * I * s8 + R * H * 2, 2.0 * R * H * I, "fp8"),
@@ -295,60 +281,123 @@ class Dsv3MoeMxfp8:
                 "experts": self.shape["E"], "shared_experts": 1, "topk": self.shape["k"], "routed_rows": self.R,
                 "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(__import__("numpy").median(c)),
                                "min": int(c.min()), "empty": int((c == 0).sum()), "shared": int(self.counts[-1])},
-                "weights_quantized_per_step": True,
-                "swiglu": "gemm_epilogue" if self.swiglu_epilogue else "separate_kernel",
+                "weights_quantized_per_step": True, "swiglu": "kernel_fused_with_h_quantization",
                 "gemm_flops_per_step": self.gemm_flops}
 
     def value(self, ms_per_step):
         return self.gemm_flops / (ms_per_step * 1e-3) / 1e12
 
     def cpu_baseline(self, budget_s=10.0):
-        """Oracle on a sample: for experts taken in order of load from the median up,
-        MXFP8 quantize of the expert's gate/up weights and up to 64 of its token rows,
-        then those rows' fp64 forward GEMM; repeated until about 10 s of CPU work."""
+        """The oracle on a bounded sample of the same step, op kind by op kind, and
+        the whole step extrapolated from those rates.  Samples (about a quarter
+        of the budget each): the rowwise + columnwise MXFP8 quantization of
+        experts' gate/up weights; and the three GEMM directions in fp64 on the
+        experts with the largest, median and smallest routed loads and the
+        shared expert -- forward gate/up and data gradient on at most 8 evenly
+        spaced rows of each, weight gradient on 64 output rows over at most 256
+        of the expert's tokens.  The step's quantization bytes and each
+        GEMM's flops are divided by the matching rate."""
         import numpy as np
         import torch
         import oracle
         H, N13 = self.shape["H"], 2 * self.shape["I"]
-        order = np.argsort(self.counts[:-1])
-        order = np.concatenate([order[len(order) // 2:], order[:len(order) // 2]])
-        it = iter(order.tolist())
-        used = []
+        routed = self.counts[:-1]
+        order = np.argsort(routed)
+        subset = [int(order[-1]), int(order[len(order) // 2]), int(order[0]), len(routed)]   # largest, median, smallest, shared
+        host = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        share = budget_s / 4
 
-        def unit():
-            e = next(it)
-            used.append(e)
-            w = self.W13[e * N13:(e + 1) * N13].view(torch.int16).cpu().numpy().view(np.uint16)
-            rows = self.src_h[self.off_h[e]:self.off_h[e + 1]][:64]
-            x = self.X[rows.tolist()].view(torch.int16).cpu().numpy().view(np.uint16)
-            off = np.array([0, len(rows)], np.int64)
-            bc, bs = oracle.quantize_mxfp8_rowwise(w)
+        def rows_of(e, cap=8):
+            lo, hi = int(self.off_h[e]), int(self.off_h[e + 1])
+            n = hi - lo
+            return lo + (np.arange(min(n, cap)) * n) // min(n, cap)
+
+        qi = iter(subset * 4)
+
+        def quant_unit():
+            e = next(qi)
+            w = host(self.W13[e * N13:(e + 1) * N13])
+            oracle.quantize_mxfp8_rowwise(w)
+            oracle.quantize_mxfp8_colwise(w)
+            return w.size * (2 + 2 * (1 + 1 / 32))
+
+        qb, qt, qn = timed_until(quant_unit, share, max_reps=len(subset) * 4)
+        w13 = {e: host(self.W13[e * N13:(e + 1) * N13]) for e in subset}
+        fi = iter(subset)
+
+        def fprop_unit():
+            e = next(fi)
+            r = rows_of(e)
+            x = host(self.X[torch.from_numpy(self.src_h[r].astype(np.int64)).to(self.X.device)])
             ac, as_ = oracle.quantize_mxfp8_rowwise(x)
-            oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac, as_, None, None, off, N13, H, bc, bs, None)
-            return 2.0 * len(rows) * N13 * H
+            bc, bs = oracle.quantize_mxfp8_rowwise(w13[e])
+            t0 = time.perf_counter()
+            oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac, as_, None, None, np.array([0, len(r)]), N13, H, bc, bs, None)
+            fprop_unit.gemm_s += time.perf_counter() - t0
+            return 2.0 * len(r) * N13 * H
+        fprop_unit.gemm_s = 0.0
+        ff, _, fn = timed_until(fprop_unit, share, max_reps=len(subset))
+        di = iter(subset)
 
-        flops, dt, reps = timed_until(unit, budget_s, max_reps=len(order))
-        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-                "sample": f"{reps} experts from the median load up: MXFP8 quantize of each expert's 4096x7168 "
-                          f"gate/up weights and up to 64 of its token rows, then those rows' forward GEMM in fp64 "
-                          f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, weight quantization included in the time)"}
+        def dgrad_unit():
+            e = next(di)
+            r = rows_of(e)
+            dh = host(self.dH13[torch.from_numpy(r.astype(np.int64)).to(self.dH13.device)])
+            ac, as_ = oracle.quantize_mxfp8_rowwise(dh)
+            bc, bs = oracle.quantize_mxfp8_colwise(w13[e])
+            t0 = time.perf_counter()
+            oracle.gemm_rowgroup(oracle.FMT_MXFP8, ac, as_, None, None, np.array([0, len(r)]), H, N13, bc, bs, None)
+            dgrad_unit.gemm_s += time.perf_counter() - t0
+            return 2.0 * len(r) * N13 * H
+        dgrad_unit.gemm_s = 0.0
+        df, _, dn = timed_until(dgrad_unit, share, max_reps=len(subset))
+        wi = iter([subset[2], subset[1], subset[0], subset[3]])   # by increasing load, the shared expert last
 
-
-class Dsv3MoeMxfp8SwigluSeparate(Dsv3MoeMxfp8):
-    name = "dsv3_moe_mxfp8_swiglu_separate"
-    swiglu_epilogue = False
+        def wgrad_unit():
+            e = next(wi)
+            lo = int(self.off_h[e])
+            hi = min(int(self.off_h[e + 1]), lo + 256)
+            one = np.array([0, hi - lo], np.int64)
+            dh = host(self.dH13[lo:hi])
+            x = host(self.X[torch.from_numpy(self.src_h[lo:hi].astype(np.int64)).to(self.X.device)])
+            ac, as_ = oracle.quantize_mxfp8_colwise(dh, one)
+            bc, bs = oracle.quantize_mxfp8_colwise(x, one)
+            sel = np.stack([np.zeros(64, np.int64), (np.arange(64) * N13) // 64], 1)
+            t0 = time.perf_counter()
+            oracle.gemm_wgrad(ac, as_, bc, bs, one, sel)
+            wgrad_unit.gemm_s += time.perf_counter() - t0
+            return 2.0 * (hi - lo) * 64 * H
+        wgrad_unit.gemm_s = 0.0
+        wf, _, wn = timed_until(wgrad_unit, share, max_reps=len(subset))
+        rate = {"quant_GB_s": qb / qt / 1e9, "fprop_GFLOP_s": ff / fprop_unit.gemm_s / 1e9,
+                "dgrad_GFLOP_s": df / dgrad_unit.gemm_s / 1e9, "wgrad_GFLOP_s": wf / wgrad_unit.gemm_s / 1e9}
+        step_s = 0.0
+        for op in self.ops:
+            if op.flops:
+                kind = "wgrad" if "wgrad" in op.name else "dgrad" if "dgrad" in op.name else "fprop"
+                step_s += op.flops / (rate[f"{kind}_GFLOP_s"] * 1e9)
+            else:
+                step_s += op.nbytes / (rate["quant_GB_s"] * 1e9)
+        qbytes = sum(o.nbytes for o in self.ops if not o.flops)
+        return {"value": self.gemm_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                "kind": "oracle", "rates": {k: round(v, 4) for k, v in rate.items()},
+                "extrapolated_step_s": round(step_s, 1),
+                "sample": f"quantization of {qn} experts' 4096x7168 gate/up weights (row + column); GEMMs in fp64 "
+                          f"on the largest/median/smallest-load and shared experts ({fn} forward, {dn} data-gradient "
+                          f"on at most 8 evenly spaced rows each; {wn} weight-gradient, 64 output rows over at most "
+                          f"256 tokens); the step extrapolated from the four rates: GEMM flops x"
+                          f"{self.gemm_flops / (ff + df + wf):.0f} and quantization bytes x{qbytes / qb:.0f} "
+                          f"of the sampled ones"}
 
 
 class Qwen3MoeNvfp4:
     """Qwen3-30B-A3B-shaped MoE layer forward in NVFP4 (8192 tokens, top-8 of
-    128 experts).  SwiGLU runs in the gate/up GEMM's epilogue, which writes h
-    in bf16, and h is quantized per token (4/6) by the per-token quantizer;
-    or (swiglu_epilogue False) SwiGLU and the 4/6 quantization of h run as
-    one kernel after the GEMM.  Both give the same h codes."""
+    128 experts): per-token 4/6 quantization of X, gate/up GEMM (bf16 output),
+    SwiGLU fused with the per-token 4/6 quantization of h in one kernel, down
+    GEMM."""
     name = "qwen3_moe_nvfp4"
     unit = "TFLOP/s"
     dtype = "fp16"
-    swiglu_epilogue = True
 
     def __init__(self, dev):
         import numpy as np
@@ -375,28 +424,18 @@ class Qwen3MoeNvfp4:
         xq = (emp(T, H // 2), emp(T, H // 16), emp(T, dt=f32))
         h13 = emp(R, N13, dt=bf)
         hq = (None, emp(R, I // 2), emp(R, I // 16), emp(R, dt=f32))
-        hb = emp(R, I, dt=bf)     # h in bf16 (SwiGLU in the gate/up GEMM's epilogue)
         y = emp(R, H, dt=bf)
         ws = emp(max(ops.gemm_workspace_size(ops.FMT_NVFP4, 0, R, n, k, E) for n, k in ((N13, H), (H, I))))
         gm, F, NV = ops.moe_grouped_gemm_blockscaled, ops.GEMM_FPROP, ops.FMT_NVFP4
         s4 = 0.5 + 1 / 16
         self.ops = [
             Op("quant_x_nvfp4_46", lambda: ops.quantize_nvfp4_per_token(X, mode46=True, out=xq), T * H * (2 + s4) + T * 4),
-        ] + ([
-            Op("gemm_fprop_gate_up_swiglu", lambda: gm(NV, ops.GEMM_FPROP_SWIGLU, xq[0], xq[1], w13[0], w13[1], off_d,
-                                                        N13, H, M=R, a_outer=xq[2], b_outer=w13[2], a_gather=src_d,
-                                                        out=hb, workspace=ws),
-               E * N13 * H * s4 + T * H * s4 + R * I * 2, 2.0 * R * N13 * H, "fp16"),
-            Op("quant_h_nvfp4_46", lambda: ops.quantize_nvfp4_per_token(hb, mode46=True, out=hq[1:]),
-               R * I * (2 + s4) + R * 4),
-        ] if self.swiglu_epilogue else [
             Op("gemm_fprop_gate_up", lambda: gm(NV, F, xq[0], xq[1], w13[0], w13[1], off_d, N13, H, M=R,
                                                  a_outer=xq[2], b_outer=w13[2], a_gather=src_d, out=h13, workspace=ws),
                E * N13 * H * s4 + T * H * s4 + R * N13 * 2, 2.0 * R * N13 * H, "fp16"),
             Op("swiglu_quant_h_nvfp4_46", lambda: ops.swiglu_quantize(h13, ops.FMT_NVFP4, mode46=True, return_h=False,
                                                                         out=hq),
                R * N13 * 2 + R * I * s4 + R * 4),
-        ]) + [
             Op("gemm_fprop_down", lambda: gm(NV, F, hq[1], hq[2], w2[0], w2[1], off_d, H, I, M=R, a_outer=hq[3],
                                               b_outer=w2[2], out=y, workspace=ws),
                E * H * I * s4 + R * I * s4 + R * H * 2, 2.0 * R * H * I, "fp16"),
@@ -409,7 +448,7 @@ class Qwen3MoeNvfp4:
         return {"workload": "qwen3_30b_a3b_moe_layer_nvfp4_forward", "tokens": self.shape["T"],
                 "hidden": self.shape["H"], "expert_intermediate": self.shape["I"], "experts": self.shape["E"],
                 "topk": self.shape["k"], "routed_rows": self.R, "activation_46": True,
-                "swiglu": "gemm_epilogue" if self.swiglu_epilogue else "separate_kernel",
+                "swiglu": "kernel_fused_with_h_quantization",
                 "group_rows": {"max": int(c.max()), "mean": float(c.mean()), "median": float(np.median(c)),
                                "min": int(c.min()), "empty": int((c == 0).sum())},
                 "gemm_flops_per_step": self.gemm_flops}
@@ -444,11 +483,6 @@ class Qwen3MoeNvfp4:
                 "sample": f"{reps} experts from the median load up: NVFP4 quantize of each expert's 1536x2048 "
                           f"gate/up weights and up to 128 of its token rows (4/6), then their forward GEMM in fp64 "
                           f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
-
-
-class Qwen3MoeNvfp4SwigluSeparate(Qwen3MoeNvfp4):
-    name = "qwen3_moe_nvfp4_swiglu_separate"
-    swiglu_epilogue = False
 
 
 class Qwen3MoeNvfp4Bwd:
@@ -926,9 +960,8 @@ class HbmCopy:
         return None
 
 
-WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Dsv3MoeMxfp8SwigluSeparate, Qwen3MoeNvfp4, Qwen3MoeNvfp4SwigluSeparate,
-                                  Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq, Qwen3MoeNvfp4BwdFp4, Mxfp8Quant,
-                                  RequantSr, RoundTrip, HbmCopy)}
+WORKLOADS = {c.name: c for c in (Dsv3MoeMxfp8, Qwen3MoeNvfp4, Qwen3MoeNvfp4BwdHp, Qwen3MoeNvfp4BwdDeq,
+                                  Qwen3MoeNvfp4BwdFp4, Mxfp8Quant, RequantSr, RoundTrip, HbmCopy)}
 
 
 # ---------------------------------------------------------------------------

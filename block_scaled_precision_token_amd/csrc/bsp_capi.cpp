@@ -70,8 +70,7 @@ BSP_EXPORT size_t bsp_requant_batched_workspace_size(int64_t E, int64_t M, int64
 BSP_EXPORT size_t bsp_gemm_workspace_size(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
     if (M < 1 || N < 1 || K < 1 || G < 1) return 0;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return 0;
-    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD && mode != BSP_GEMM_FPROP_SWIGLU)
-        return 0;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return 0;
     return (size_t)bsp::gemm_workspace_bytes(fmt, mode, M, N, K, G);
 }
 
@@ -220,15 +219,13 @@ bsp_status gemm_args_status(int fmt, int mode, const uint8_t *a_codes, const uin
                             const float *b_outer, void *c, int c_dtype, int64_t ldc) {
     if (!a_codes || !a_scales || !b_codes || !b_scales || !group_offsets || !c) return BSP_ERR_INVALID_ARG;
     if (fmt != BSP_FMT_NVFP4 && fmt != BSP_FMT_MXFP8) return BSP_ERR_INVALID_ARG;
-    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD && mode != BSP_GEMM_FPROP_SWIGLU)
-        return BSP_ERR_INVALID_ARG;
+    if (mode != BSP_GEMM_FPROP && mode != BSP_GEMM_DGRAD && mode != BSP_GEMM_WGRAD) return BSP_ERR_INVALID_ARG;
     if (c_dtype != BSP_DTYPE_F32 && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_INVALID_ARG;
-    if (mode == BSP_GEMM_FPROP_SWIGLU && c_dtype != BSP_DTYPE_BF16) return BSP_ERR_UNSUPPORTED;
     if (fmt == BSP_FMT_NVFP4 && (!a_outer || !b_outer)) return BSP_ERR_INVALID_ARG;
     if (fmt == BSP_FMT_MXFP8 && (a_outer || b_outer)) return BSP_ERR_INVALID_ARG;
     if (mode == BSP_GEMM_WGRAD && a_gather) return BSP_ERR_INVALID_ARG;
     if (G < 1 || M <= 0 || N <= 0 || K <= 0) return BSP_ERR_SHAPE;
-    if (mode == BSP_GEMM_FPROP_SWIGLU ? (N % 64 || ldc < N / 2) : ldc < N) return BSP_ERR_SHAPE;
+    if (ldc < N) return BSP_ERR_SHAPE;
     if (G >= (1ll << 23) || M >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_MXFP8 && K % 32) return BSP_ERR_SHAPE;
     if (fmt == BSP_FMT_NVFP4 && K % 32) return BSP_ERR_SHAPE;   // rows of codes 16-byte aligned

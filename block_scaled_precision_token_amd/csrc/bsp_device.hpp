@@ -156,8 +156,8 @@ __device__ __forceinline__ float exp_cw(float x) {
 
 // SwiGLU of one element: bf16 bits of silu(gate) * up with silu(z) =
 // z / (1 + exp(-z)) (correctly rounded division), product rounded to bf16
-// (nearest even).  Shared by the SwiGLU kernel and the GEMM's SwiGLU
-// epilogue, which give the same h for the same bf16 gate and up.
+// (nearest even).  Within a few f32 units of the exact value before the
+// final rounding, so h is within one bf16 unit of the exactly rounded one.
 __device__ __forceinline__ uint32_t swiglu_bf16(float gate, float up) {
     const float silu = gate / (1.0f + exp_cw(-gate));
     return f32_to_bf16(silu * up);

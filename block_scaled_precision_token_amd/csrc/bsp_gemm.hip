@@ -173,14 +173,6 @@ __global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int6
 // K step for the tile's rows are contiguous: a few lines per operand.
 // plane[(z * nbp + b) * rp + r] = scale b of the source row of (z, r), or 0
 // where (z, r) has no source row or b is past the row's blocks.
-// SwiGLU epilogue form: column n of the product is B row swi_row(n, I) of
-// the expert's fused [gate; up] matrix (I = N / 2): every 64-column span holds
-// 32 gate rows followed by the up rows of the same 32 h columns, so one
-// wavefront's two 32-column blocks pair gate and up element by element.
-__host__ __device__ __forceinline__ int swi_row(int n, int half) {
-    return ((n & 32) ? half : 0) + ((n >> 6) << 5) + (n & 31);
-}
-
 struct PlaneArgs {
     const uint8_t *src;
     int64_t src_rows;          // rows of src
@@ -188,7 +180,6 @@ struct PlaneArgs {
     uint8_t *plane;
     int32_t nbp, rp;           // padded blocks, row pitch of the plane
     int32_t rows_z;            // direct map: source row of (z, r) = z * rows_z + r for r < rows_z
-    int32_t swi_half;          // SwiGLU form: source row z * rows_z + swi_row(r, swi_half) (0: off)
     // tile-list map (row-grouped A): plane row r = slot * bt + i
     const int64_t *tiles, *sched, *off;
     const int32_t *gather;
@@ -216,7 +207,7 @@ __global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
                 }
             }
         } else if (r < a.rows_z) {
-            srow = (int64_t)z * a.rows_z + (a.swi_half ? swi_row(r, a.swi_half) : r);
+            srow = (int64_t)z * a.rows_z + r;
         }
         const int bb = b0 + 16 * part;
         const uint8_t *src = a.src + srow * a.sr + bb;
@@ -462,8 +453,6 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
-    constexpr bool SWI = MODE == BSP_GEMM_FPROP_SWIGLU;   // forward form, SwiGLU epilogue (bf16 h)
-    static_assert(!SWI || (BF16OUT && !BF), "SwiGLU epilogue: block-scaled operands, bf16 output");
     // BF16 operand layouts: the forward form takes both operands K-major; the
     // data-gradient form takes B as the forward weight is stored ([K, N] per
     // expert, N contiguous); the weight-gradient form reduces over rows, so
@@ -660,7 +649,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             }
             const int n = PT.col0 + r < p.N ? PT.col0 + r : p.N - 1;
             poa[j] = (uint32_t)ar * ldA + 16 * c;
-            pob[j] = (uint32_t)(SWI ? swi_row(n, p.N >> 1) : n) * ldA + 16 * c;
+            pob[j] = (uint32_t)n * ldA + 16 * c;
         }
         {
             const int b0 = WG ? PT.kbeg / GG::SBLK : 0;
@@ -949,12 +938,11 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     auto epilogue = [&](uint8_t *slot) __attribute__((always_inline)) {
         // Each wavefront stages a 32-row slice of its outputs in its own LDS
         // patch and writes it back in whole 128-byte row pieces: 32 x 64
-        // columns for bf16 (both column blocks at once), 32 x 32 for f32; the
-        // SwiGLU form stages 32 x 32 h values (64-byte row pieces).
+        // columns for bf16 (both column blocks at once), 32 x 32 for f32.
         constexpr int ESZ = BF16OUT ? 2 : 4;
         constexpr int VEC = 16 / ESZ;                  // elements per 16-byte store
-        constexpr int NJ = (BF16OUT && !SWI) ? 2 : 1;  // column blocks per staged slice
-        constexpr int RB = 32 * NJ * ESZ;              // bytes of a staged row piece (128; SwiGLU: 64)
+        constexpr int NJ = BF16OUT ? 2 : 1;            // column blocks per staged slice
+        constexpr int RB = 32 * NJ * ESZ;              // bytes of a staged row piece (128)
         constexpr int STR = RB + 16;                   // padded LDS row stride
         constexpr int CPR = RB / 16;                   // 16-byte chunks per row piece
         uint8_t *ep = slot + w * (32 * STR);
@@ -964,8 +952,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         // NVFP4 weight gradient: the group's outer scales of both operands
         const float gab = (WG && NV) ? sload(p.a_outer, CT.g) * sload(p.b_outer, CT.g) : 1.0f;
         const int nv = live_blocks();
-        // SwiGLU form: h columns, the wavefront's 32 starting at (col0 + 64 wn) / 2
-        const int ncol = SWI ? p.N >> 1 : p.N;
+        const int ncol = p.N;
 #pragma unroll
         for (int i = 0; i < TI; i++) {
             if (i >= nv) break;
@@ -978,30 +965,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 else mul[e] = rowmul[NV ? ord : 0][rt];
             }
 #pragma unroll
-            for (int j0 = 0; j0 < (SWI ? 1 : 2); j0 += NJ) {
-                if constexpr (SWI) {
-                    // gate (block 0) and up (block 1) of the same h column,
-                    // each rounded to bf16 as the forward form's bf16 output
-                    // (V_CVT_PK_BF16_F32, nearest even), then SwiGLU
-#pragma unroll
-                    for (int e = 0; e < 16; e += 2) {
-                        const int rin = 8 * (e >> 2) + 4 * lh + (e & 3);   // rows rin, rin + 1
-                        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-                        typedef float f2 __attribute__((ext_vector_type(2)));
-                        float g[2], u[2];
-#pragma unroll
-                        for (int q = 0; q < 2; q++) {
-                            g[q] = mul[e + q] == 0.0f ? 0.0f : acc[i][0][e + q] * mul[e + q];
-                            u[q] = mul[e + q] == 0.0f ? 0.0f : acc[i][1][e + q] * mul[e + q];
-                        }
-                        const uint32_t gp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{g[0], g[1]}, bf2));
-                        const uint32_t upk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{u[0], u[1]}, bf2));
-                        *reinterpret_cast<uint16_t *>(ep + rin * STR + lr * 2) =
-                            (uint16_t)swiglu_bf16(bf16_lo(gp), bf16_lo(upk));
-                        *reinterpret_cast<uint16_t *>(ep + (rin + 1) * STR + lr * 2) =
-                            (uint16_t)swiglu_bf16(bf16_hi(gp), bf16_hi(upk));
-                    }
-                } else {
+            for (int j0 = 0; j0 < 2; j0 += NJ) {
+                {
 #pragma unroll
                     for (int jj = 0; jj < NJ; jj++) {
                         const int j = j0 + jj;
@@ -1031,7 +996,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     const int idx = pass * 64 + l;
                     const int rin = idx / CPR, ch = idx % CPR;
                     const int r = CT.row0 + wm * (BT / 2) + 32 * i + rin;
-                    const int cn = SWI ? ((CT.col0 + wn * 64) >> 1) + ch * VEC : CT.col0 + wn * 64 + 32 * j0 + ch * VEC;
+                    const int cn = CT.col0 + wn * 64 + 32 * j0 + ch * VEC;
                     const uint4 v = *reinterpret_cast<const uint4 *>(ep + rin * STR + ch * 16);
                     if (r < CT.row_end && cn < ncol) {
                         char *dst = reinterpret_cast<char *>(p.c) + (goff + (int64_t)r * p.ldc + cn) * ESZ;
@@ -1270,18 +1235,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     pa.tiles = ws; pa.sched = p.sched + NXCD; pa.off = group_offsets; pa.gather = a_gather;
     pa.bt = bt; pa.M = (int32_t)M; pa.a_rows = (int32_t)a_rows;
     k_scale_plane<true><<<dim3((unsigned)((int64_t)p.ntm * bt / 64), gy, 1), 256, 0, s>>>(pa);
-    if (mode == BSP_GEMM_FPROP_SWIGLU) pb.swi_half = (int32_t)(N / 2);   // plane rows in product-column order
     k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, (unsigned)G), 256, 0, s>>>(pb);
-    if (mode == BSP_GEMM_FPROP_SWIGLU) {   // bf16 output only (checked by the caller)
-        if (bt == 256) {
-            if (fmt == BSP_FMT_MXFP8) launch_one<BSP_FMT_MXFP8, BSP_GEMM_FPROP_SWIGLU, true, 256>(p, s);
-            else launch_one<BSP_FMT_NVFP4, BSP_GEMM_FPROP_SWIGLU, true, 256>(p, s);
-        } else {
-            if (fmt == BSP_FMT_MXFP8) launch_one<BSP_FMT_MXFP8, BSP_GEMM_FPROP_SWIGLU, true, 128>(p, s);
-            else launch_one<BSP_FMT_NVFP4, BSP_GEMM_FPROP_SWIGLU, true, 128>(p, s);
-        }
-        return hipGetLastError();
-    }
     if (bt == 256) {
         if (fmt == BSP_FMT_MXFP8) launch_k<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>(p, bf, s);
         else launch_k<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>(p, bf, s);

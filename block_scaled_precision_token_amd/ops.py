@@ -24,7 +24,6 @@ DTYPE_BF16 = 1
 GEMM_FPROP = 0
 GEMM_DGRAD = 1
 GEMM_WGRAD = 2
-GEMM_FPROP_SWIGLU = 3     # forward gate/up GEMM with SwiGLU in the epilogue: C = h [M, N/2] bf16
 NVFP4_46 = 0x1
 SR = 0x2
 
@@ -472,13 +471,10 @@ def _gemm_blockscaled_args(fmt, mode, a_codes, a_scales, b_codes, b_scales, grou
     elif a_outer is not None or b_outer is not None:
         raise ValueError("MXFP8 takes no outer scales")
     if out is None:
-        if mode == GEMM_FPROP_SWIGLU:
-            out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
-        else:
-            out = torch.empty((G, M, N) if wg else (M, N), dtype=out_dtype, device=dev)
+        out = torch.empty((G, M, N) if wg else (M, N), dtype=out_dtype, device=dev)
     _arg(out, "out", dev, ("f32", "bf16"))
     ldc = out.shape[-1] if out.dim() >= 2 else N
-    if ldc < (N // 2 if mode == GEMM_FPROP_SWIGLU else N):
+    if ldc < N:
         raise ValueError(f"out has rows of {ldc} elements, fewer than the {N} columns of C")
     _arg(out, "out", dev, ("f32", "bf16"), (G * M if wg else M) * ldc)
     dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
@@ -492,8 +488,7 @@ def moe_grouped_gemm_blockscaled(fmt: int, mode: int, a_codes, a_scales, b_codes
 
     FPROP/DGRAD: C [M, N] with M = rows of C (grouped rows).  WGRAD: C [G, M, N]
     with M = rows of A (the columnwise copies' K dimension is their ld).
-    FPROP_SWIGLU: B the fused [gate; up] weight (N = 2I rows per expert),
-    C = h [M, I] in bf16.  tile: 0 (the library's choice), 128 or 256.
+    tile: 0 (the library's choice), 128 or 256.
     """
     dev, G, M, a_rows, out, ldc, dt = _gemm_blockscaled_args(fmt, mode, a_codes, a_scales, b_codes, b_scales,
                                                              group_offsets, N, K, M, a_outer, b_outer, a_gather,

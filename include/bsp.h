@@ -65,7 +65,7 @@ typedef enum bsp_status {
 
 enum { BSP_FMT_NVFP4 = 0, BSP_FMT_MXFP8 = 1 };
 enum { BSP_DTYPE_F32 = 0, BSP_DTYPE_BF16 = 1 };
-enum { BSP_GEMM_FPROP = 0, BSP_GEMM_DGRAD = 1, BSP_GEMM_WGRAD = 2, BSP_GEMM_FPROP_SWIGLU = 3 };
+enum { BSP_GEMM_FPROP = 0, BSP_GEMM_DGRAD = 1, BSP_GEMM_WGRAD = 2 };
 
 /* flags */
 #define BSP_NVFP4_46 0x1u /* NVFP4: choose between the "6" and "4" block scales */
@@ -296,19 +296,6 @@ bsp_status bsp_requant_transpose_sr_batched(const uint8_t *codes, const uint8_t 
  *   made by bsp_requant_transpose_sr_grouped, a_outer and b_outer their
  *   per-group outer scales [G].  C is [G, M, ldc] (group stride M * ldc).
  *   a_gather must be NULL and a_rows == M.
- * FPROP_SWIGLU: the gate/up projection with SwiGLU applied in the epilogue
- *   [alphasignal.ai, "Results on Qwen3-30B-A3B": the NVFP4 training path
- *   measured there ran its per-token scaling outside the GEMM kernels;
- *   remio.ai, "Le curve delle ricompense spostano l'onere della prova"].
- *   B is each expert's fused [gate; up] weight, N = 2I rows (gate
- *   rows [0, I), up rows [I, 2I)), exactly as for FPROP; N % 64 == 0.  C
- *   receives h [M, I] in bf16 (c_dtype must be BSP_DTYPE_BF16, ldc >= I):
- *   h[r, i] = bf16(silu(g) * u), silu(z) = z / (1 + exp(-z)) in f32, with
- *   g = C[r, i] and u = C[r, I + i] of FPROP rounded to bf16, and exp the
- *   same f32 sequence as bsp_swiglu_quantize's: the result is bit-identical
- *   to FPROP with bf16 output followed by bsp_swiglu_quantize (fmt -1).  The
- *   per-token quantization of h is a separate call: its outer scale needs
- *   the whole row of h, which spans several output tiles.
  * Accumulation is f32 on the MFMA units; the epilogue applies gA * gB and
  * rounds to c_dtype (RNE for bf16).
  *   workspace  device, >= bsp_gemm_workspace_size(fmt, mode, M, N, K, G)

@@ -22,12 +22,9 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
 
 def test_workload_registry():
     # the default workload and every documented alternative are registered
-    for name in ("dsv3_moe_mxfp8", "dsv3_moe_mxfp8_swiglu_separate", "qwen3_moe_nvfp4",
-                 "qwen3_moe_nvfp4_swiglu_separate", "qwen3_moe_nvfp4_bwd_hp", "qwen3_moe_nvfp4_bwd_deq",
+    for name in ("dsv3_moe_mxfp8", "qwen3_moe_nvfp4", "qwen3_moe_nvfp4_bwd_hp", "qwen3_moe_nvfp4_bwd_deq",
                  "qwen3_moe_nvfp4_bwd_fp4", "mxfp8_quant", "requant_sr", "roundtrip", "hbm_copy"):
         assert name in bench.WORKLOADS, name
-    assert bench.WORKLOADS["dsv3_moe_mxfp8"].swiglu_epilogue
-    assert not bench.WORKLOADS["dsv3_moe_mxfp8_swiglu_separate"].swiglu_epilogue
 
 
 def test_kernel_source_digest_ignores_comments_and_layout(tmp_path, monkeypatch):

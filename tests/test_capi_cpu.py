@@ -58,8 +58,8 @@ def test_size_helpers():
     a_plane = nbp * ((65536 + 255) // 256 + 128) * 256
     b_plane = 128 * nbp * up(1536, 256)
     assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) == head + up(a_plane, 256) + up(b_plane, 256)
-    # the SwiGLU epilogue form needs what the forward form needs; unknown modes size to 0
-    assert L.bsp_gemm_workspace_size(0, 3, 65536, 1536, 2048, 128) == L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128)
+    # unknown modes size to 0
+    assert L.bsp_gemm_workspace_size(0, 3, 65536, 1536, 2048, 128) == 0
     assert L.bsp_gemm_workspace_size(0, 7, 65536, 1536, 2048, 128) == 0
     head = up((258 + 16) * 8 + 257 * 4, 256)           # + the expert order
     nbp = 37120 // 32 + 2
@@ -128,11 +128,9 @@ def test_gemm_rejects_bad_arguments():
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 32, A, ws, None) == 2   # ldc < N
     assert g(1, 0, A, A, None, None, 64, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, 8, None) == 5
     assert g(1, 0, A, A, None, None, 32, A, 2, 64, 64, 64, A, A, None, A, 0, 64, A, ws, None) == 2   # a_rows != M
-    # SwiGLU epilogue form: bf16 output only, N % 64 == 0, ldc >= N / 2; mode 4 is unknown
-    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 0, 64, A, ws, None) == 4
-    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 96, 64, A, A, None, A, 1, 48, A, ws, None) == 2
-    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 32, A, ws, None) == 2
-    assert g(1, 4, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 64, A, ws, None) == 1
+    # modes 3 and 4 are unknown
+    assert g(1, 3, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 128, A, ws, None) == 1
+    assert g(1, 4, A, A, None, None, 64, A, 2, 64, 128, 64, A, A, None, A, 1, 128, A, ws, None) == 1
 
 
 def test_tiled_gemm_rejects_unknown_tile():
