@@ -432,17 +432,22 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 // so each XCD works through its own run of column tiles and the workgroups
 // resident on it share one column slab of x in its L2 -- what a gathered
 // input re-reads (every token appears once per routed copy).
-template <bool ROW, bool COL, bool GROUPED>
+template <bool ROW, bool COL, bool GROUPED, bool GATHER = GROUPED>
 __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__ x, int64_t M, int64_t K,
                                                     int64_t ldx, uint8_t *__restrict__ codes_row,
                                                     uint8_t *__restrict__ scales_row, uint8_t *__restrict__ codes_colT,
                                                     uint8_t *__restrict__ scales_colT, int64_t ld_colT,
                                                     const int64_t *__restrict__ group_offsets, int G,
                                                     const int32_t *__restrict__ gather, int64_t x_rows) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[MX_TR][MX_TC + 8];
-    __shared__ int64_t rsrc[ROW ? MX_TR : 1];   // destination row of each tile row in codes_row (-1: none)
-    __shared__ int64_t blk_src0[MX_TR / 32], blk_end[MX_TR / 32];
-    __shared__ int64_t wsum[4];
+    // Tile rows map to rows of x through LDS tables only when they are not
+    // the identity (groups or a gather); the plain form then needs 32 KB of
+    // LDS in all, so five workgroups fit a compute unit.
+    constexpr bool MAP = GROUPED || GATHER;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[MX_TR][MX_TC];
+    __shared__ int64_t rsrc[ROW && MAP ? MX_TR : 1];   // destination row of each tile row in codes_row (-1: none)
+    __shared__ int64_t xsrc[MAP ? MX_TR : 1];           // row of x of each tile row (-1: zeros)
+    __shared__ int64_t blk_src0[GROUPED ? MX_TR / 32 : 1], blk_end[GROUPED ? MX_TR / 32 : 1];
+    __shared__ int64_t wsum[GROUPED ? 4 : 1];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     int64_t p0, k0;
     if (GROUPED) {
@@ -506,8 +511,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     }
 
     // ---- per-row sources: destination row of codes_row and row of x ----
-    __shared__ int64_t xsrc[MX_TR];
-    if (t < MX_TR) {
+    if constexpr (MAP) {
+      if (t < MX_TR) {
         const int64_t p = p0 + t;
         int64_t src = -1;
         if (GROUPED) {
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
         } else {
             if (p < M) src = p;
         }
-        if (ROW) rsrc[t] = src;
+        if constexpr (ROW) rsrc[t] = src;
         // physical row of x: the gathered row (out-of-range indices read as zeros)
         int64_t xrow = src;
         if (src >= 0 && gather) {
@@ -525,8 +530,12 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             if (xrow < 0 || xrow >= x_rows) xrow = -1;
         }
         xsrc[t] = xrow;
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    // identity map: tile row r is row p0 + r (none past M)
+    auto x_row = [&](int r) -> int64_t { return MAP ? xsrc[r] : (p0 + r < M ? p0 + r : -1); };
+    auto dst_row = [&](int r) -> int64_t { return MAP ? rsrc[ROW && MAP ? r : 0] : (p0 + r < M ? p0 + r : -1); };
 
     // ---- load: lane l of wavefront w reads 16-byte chunk l % 16 of tile row
     // 32 w + 4 i + l / 16 (i = 0..7), so each load covers four whole 256-byte
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     uint4 raw[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const int64_t xr = xsrc[32 * wv + 4 * i + rq];
+        const int64_t xr = x_row(32 * wv + 4 * i + rq);
         raw[i] = make_uint4(0u, 0u, 0u, 0u);
         if (xr >= 0 && col_ok) {
             const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + xr * ldx + kc));
@@ -563,7 +572,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             const float inv = exp2i(-k);   // see mxfp8_block
             const uint32_t q0 = e4m3x4_hw(xf[0] * inv, xf[1] * inv, xf[2] * inv, xf[3] * inv);
             const uint32_t q1 = e4m3x4_hw(xf[4] * inv, xf[5] * inv, xf[6] * inv, xf[7] * inv);
-            const int64_t dr = rsrc[32 * wv + 4 * i + rq];
+            const int64_t dr = dst_row(32 * wv + 4 * i + rq);
             if (dr >= 0 && col_ok) {
                 __builtin_nontemporal_store(u32x2{q0, q1}, reinterpret_cast<u32x2 *>(codes_row + dr * K + kc));
                 if ((ch & 3) == 0) scales_row[dr * (K / 32) + kc / 32] = (uint8_t)(k + 127);
@@ -611,17 +620,22 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     // ---- stage the column codes in LDS, then write them back with every
     // store instruction covering whole 128-byte rows (8 lanes per row):
     // lane-scattered 16-byte stores would cost one L2 request each ----
+    // (16-byte piece q of staged row c sits at piece q ^ ((c >> 1) & 7): the
+    // 64 lanes of a wavefront write rows 128 bytes apart, which without the
+    // swizzle would put every lane's piece on the same two groups of banks)
     uint8_t *stage = reinterpret_cast<uint8_t *>(&tile[0][0]);
     {
-        uint4 *d = reinterpret_cast<uint4 *>(stage + c * 128 + 64 * rh);
+        const int sw = (c >> 1) & 7;
 #pragma unroll
-        for (int i = 0; i < 4; i++) d[i] = make_uint4(qcol[4 * i], qcol[4 * i + 1], qcol[4 * i + 2], qcol[4 * i + 3]);
+        for (int i = 0; i < 4; i++)
+            *reinterpret_cast<uint4 *>(stage + c * 128 + 16 * ((4 * rh + i) ^ sw)) =
+                make_uint4(qcol[4 * i], qcol[4 * i + 1], qcol[4 * i + 2], qcol[4 * i + 3]);
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int id = 256 * i + t, r = id >> 3, piece = id & 7;
-        const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * piece);
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
         if (k0 + r < K && p0 + 16 * piece < plimit)
             __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
                                         reinterpret_cast<u32x4 *>(codes_colT + (k0 + r) * ld_colT + p0 + 16 * piece));
@@ -693,14 +707,26 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, i
                                                                       group_offsets, (int)G, gather, x_rows);
     } else {
         const unsigned gy = (unsigned)((M + MX_TR - 1) / MX_TR);
-        if (row)
-            k_mxfp8_tile<true, true, false><<<dim3(gx, gy, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
-                                                                         codes_colT, scales_colT, ld_colT, nullptr, 1,
-                                                                         gather, x_rows);
-        else
-            k_mxfp8_tile<false, true, false><<<dim3(gx, gy, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+        const dim3 grid(gx, gy, (unsigned)batch);
+        if (gather) {
+            if (row)
+                k_mxfp8_tile<true, true, false, true><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
                                                                           codes_colT, scales_colT, ld_colT, nullptr,
                                                                           1, gather, x_rows);
+            else
+                k_mxfp8_tile<false, true, false, true><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                           codes_colT, scales_colT, ld_colT, nullptr,
+                                                                           1, gather, x_rows);
+        } else {
+            if (row)
+                k_mxfp8_tile<true, true, false, false><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                           codes_colT, scales_colT, ld_colT,
+                                                                           nullptr, 1, nullptr, x_rows);
+            else
+                k_mxfp8_tile<false, true, false, false><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row,
+                                                                            codes_colT, scales_colT, ld_colT,
+                                                                            nullptr, 1, nullptr, x_rows);
+        }
     }
     return hipGetLastError();
 }
