@@ -543,13 +543,18 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     const int ch = lane & 15, rq = lane >> 4;
     const int64_t kc = k0 + 8 * ch;
     const bool col_ok = kc < K;   // K % 32 == 0: a block's four lanes agree
+    // A gathered x is read once per routed copy of each row: those loads keep
+    // the default cache policy so the copies after the first hit in L2; an
+    // x read once streams past the caches (non-temporal).
+    const bool reread = GATHER && gather != nullptr;
     uint4 raw[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int64_t xr = x_row(32 * wv + 4 * i + rq);
         raw[i] = make_uint4(0u, 0u, 0u, 0u);
         if (xr >= 0 && col_ok) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + xr * ldx + kc));
+            const u32x4 *px = reinterpret_cast<const u32x4 *>(x + xr * ldx + kc);
+            const u32x4 v = reread ? *px : __builtin_nontemporal_load(px);
             raw[i] = make_uint4(v.x, v.y, v.z, v.w);
         }
     }
