@@ -169,6 +169,31 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a 256-thread workgroup of each thread's value,
+// plus the workgroup total.  `wsum` holds four words of LDS; every thread
+// must call this (it contains barriers).
+__device__ __forceinline__ int64_t block256_excl_scan(int64_t v, int64_t *wsum, int64_t &total) {
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t incl = wave_incl_scan(v, lane);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int64_t run = incl - v;
+    for (int w = 0; w < wv; w++) run += wsum[w];
+    total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();   // wsum may be rewritten by the next call
+    return run;
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds of two
 // 32x32->64 multiplies with the Philox constants, high halves xor-ed into
 // the other words with the round key, key advanced by the Weyl constants.

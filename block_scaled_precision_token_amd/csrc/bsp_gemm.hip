@@ -99,36 +99,43 @@ struct GemmArgs {
 };
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
-__global__ void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t M, int64_t bm, int64_t ntile_max,
-                            int64_t *__restrict__ tiles, int64_t *__restrict__ sched) {
-    __shared__ int64_t base[1025];
+// One workgroup of 256 threads: per pass of 1024 groups each thread counts
+// the row tiles of four groups and a workgroup scan places them.
+__global__ __launch_bounds__(256) void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t M,
+                                                   int64_t bm, int64_t ntile_max, int64_t *__restrict__ tiles,
+                                                   int64_t *__restrict__ sched) {
+    __shared__ int64_t wsum[4];
+    const int t = threadIdx.x;
     int64_t carry = 0;
     for (int64_t g0 = 0; g0 < G; g0 += 1024) {
-        const int64_t n = (G - g0) < 1024 ? (G - g0) : 1024;
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            int64_t lo = off[g0 + i], hi = off[g0 + i + 1];
-            lo = lo < M ? lo : M;
-            hi = hi < M ? hi : M;
-            base[i + 1] = hi > lo ? (hi - lo + bm - 1) / bm : 0;
+        int64_t cnt[4], r0[4], local = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            cnt[q] = 0;
+            r0[q] = 0;
+            if (g < G) {
+                int64_t lo = off[g], hi = off[g + 1];
+                r0[q] = lo;
+                lo = lo < M ? lo : M;
+                hi = hi < M ? hi : M;
+                cnt[q] = hi > lo ? (hi - lo + bm - 1) / bm : 0;
+            }
+            local += cnt[q];
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            base[0] = carry;
-            for (int i = 1; i <= n; i++) base[i] += base[i - 1];
+        int64_t total;
+        int64_t base = carry + block256_excl_scan(local, wsum, total);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            for (int64_t i = 0; i < cnt[q] && base + i < ntile_max; i++) tiles[base + i] = (g << 40) | (r0[q] + i * bm);
+            base += cnt[q];
         }
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int64_t g = g0 + i;
-            const int64_t r0 = off[g];
-            for (int64_t t = base[i]; t < base[i + 1] && t < ntile_max; t++)
-                tiles[t] = (g << 40) | (r0 + (t - base[i]) * bm);
-        }
-        carry = base[n];
-        __syncthreads();
+        carry += total;
     }
-    for (int64_t t = carry + threadIdx.x; t < ntile_max; t += blockDim.x) tiles[t] = -1;
-    if (threadIdx.x < NXCD) sched[threadIdx.x] = 0;
-    if (threadIdx.x == 0) sched[NXCD] = carry < ntile_max ? carry : ntile_max;
+    for (int64_t i = carry + t; i < ntile_max; i += blockDim.x) tiles[i] = -1;
+    if (t < NXCD) sched[t] = 0;
+    if (t == 0) sched[NXCD] = carry < ntile_max ? carry : ntile_max;
 }
 
 // Weight-gradient form: the experts in order of decreasing token count (ties
@@ -153,18 +160,33 @@ __global__ __launch_bounds__(1024) void k_wgrad_order(const int64_t *__restrict_
     }
 }
 
-// Padded group starts P (running sum of roundup32(n_g)) for the weight-gradient form.
-__global__ void k_padded_starts(const int64_t *__restrict__ off, int64_t G, int64_t *__restrict__ P,
-                                int64_t *__restrict__ sched) {
-    if (threadIdx.x < NXCD) sched[threadIdx.x] = 0;
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        int64_t run = 0;
-        for (int64_t g = 0; g < G; g++) {
-            P[g] = run;
-            run += (off[g + 1] - off[g] + 31) / 32 * 32;
+// Padded group starts P (running sum of roundup32(n_g)) for the weight-gradient
+// form, by a workgroup scan over passes of 1024 groups (256 threads).
+__global__ __launch_bounds__(256) void k_padded_starts(const int64_t *__restrict__ off, int64_t G,
+                                                       int64_t *__restrict__ P, int64_t *__restrict__ sched) {
+    __shared__ int64_t wsum[4];
+    const int t = threadIdx.x;
+    if (t < NXCD) sched[t] = 0;
+    int64_t carry = 0;
+    for (int64_t g0 = 0; g0 < G; g0 += 1024) {
+        int64_t pn[4], local = 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            pn[q] = g < G ? (off[g + 1] - off[g] + 31) / 32 * 32 : 0;
+            local += pn[q];
         }
-        P[G] = run;
+        int64_t total;
+        int64_t run = carry + block256_excl_scan(local, wsum, total);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            if (g < G) P[g] = run;
+            run += pn[q];
+        }
+        carry += total;
     }
+    if (t == 0) P[G] = carry;
 }
 
 // Scale planes.  The operands' scales arrive row-major ([rows][K / SBLK]);
@@ -1208,7 +1230,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
         const int bt = pick_tile(G * ((M + 255) / 256) * ((N + 255) / 256), tile);
         p.ntn = (int32_t)((N + bt - 1) / bt);
         p.ntm = (int32_t)(G * ((M + bt - 1) / bt));
-        k_padded_starts<<<1, 64, 0, s>>>(group_offsets, G, ws, p.sched);
+        k_padded_starts<<<1, 256, 0, s>>>(group_offsets, G, ws, p.sched);
         int32_t *order = reinterpret_cast<int32_t *>(ws + G + 1 + kGemmSchedSlots);
         k_wgrad_order<<<1, 1024, 0, s>>>(group_offsets, G, order);
         p.order = order;

@@ -410,15 +410,6 @@ __device__ __forceinline__ uint32_t mxfp8_block(const float (&xf)[32], uint32_t 
 constexpr int MX_TR = 128;  // tile rows (padded row space)
 constexpr int MX_TC = 128;  // tile columns
 
-__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int64_t u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
-    return v;
-}
-
 // One 128 x 128 tile: rowwise blocks (32 along K) straight from registers and
 // columnwise blocks (32 along rows) through LDS, from a single read of x.
 // Loads and rowwise stores cover whole rows per instruction (16 lanes per
@@ -1182,10 +1173,20 @@ __global__ __launch_bounds__(256) void k_group_outer_max(const float *__restrict
                                                          const int64_t *__restrict__ off, int64_t R,
                                                          float *__restrict__ outerT) {
     const int64_t g = blockIdx.x, a = off[g], b = off[g + 1] < R ? off[g + 1] : R;
+    // eight rows per thread and pass, their loads issued together: a large
+    // group is a long chain of dependent (gather, then outer) loads otherwise
+    constexpr int U = 8;
     float m = 0.0f;
-    for (int64_t r = a + threadIdx.x; r < b; r += blockDim.x) {
-        const int64_t src = gather ? (int64_t)gather[r] : r;
-        if (src >= 0 && src < src_rows) m = fmaxf(m, outer[src]);
+    for (int64_t r0 = a + threadIdx.x; r0 < b; r0 += U * (int64_t)blockDim.x) {
+        int64_t src[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t r = r0 + u * (int64_t)blockDim.x;
+            src[u] = r < b ? (gather ? (int64_t)gather[r] : r) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            if (src[u] >= 0 && src[u] < src_rows) m = fmaxf(m, outer[src[u]]);
     }
     m = wave_max(m);
     __shared__ float red[4];
