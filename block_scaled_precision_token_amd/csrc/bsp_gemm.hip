@@ -19,23 +19,27 @@
 //
 // Data movement.  Operand tiles stream from global memory straight into LDS
 // with the gfx950 LDS-DMA loads (GLOBAL_LOAD_LDS_DWORDX4 for codes, _DWORD
-// for scales): no registers are spent on staging, so a ring of four LDS
-// stages keeps three K steps (48 KB per workgroup for MXFP8) in flight while
-// the fourth is multiplied.  The ring runs across tile boundaries: the first
-// stages of a workgroup's next tile are fetched while the current tile is
-// finished and written back.  Completion is tracked with explicit vmcnt waits
-// (loads retire in order, so "at most 2 stages outstanding" means the oldest
-// stage has landed) followed by a workgroup barrier; the epilogue's stores are
-// issued so that the compiler's own counter model stays exact.
+// for scales): no registers are spent on staging.  A ring of LDS stages
+// keeps the next stages in flight while one is multiplied: four stages of 64
+// K values (32 for BF16), or, for the MXFP8 forward and data-gradient forms,
+// two stages of 128 K values, whose loads fetch whole 128-byte lines of every
+// operand row (the per-CU count of outstanding memory requests is what bounds
+// these loads, so bytes per request matter; 8 % faster on the DeepSeek-V3
+// shapes than four stages of 64).  The ring runs across tile boundaries: the
+// first stages of a workgroup's next tile are fetched while the current tile
+// is finished and written back.  Completion is tracked with explicit vmcnt
+// waits (loads retire in order, so "at most n stages outstanding" means the
+// oldest stage has landed) followed by a workgroup barrier; the epilogue's
+// stores are issued so that the compiler's own counter model stays exact.
 //
-// LDS layout of a stage: per operand BT rows of 64 (MXFP8) or 32 (NVFP4)
-// code bytes, the 16-byte chunks of row r stored at position chunk ^ swz(r)
+// LDS layout of a stage: per operand BT rows of 64 or 128 (MXFP8) or 32
+// (NVFP4) code bytes, the 16-byte chunks of row r stored at position chunk ^ swz(r)
 // so that the 32 rows read by one fragment load hit distinct banks; then the
 // stage's scale bytes, block-major ([scale block][row]) as copied from the
 // scale planes a setup kernel builds in the workspace.
 //
 // Tiling: output tiles of BT x BT (256 on eight wavefronts, or 128 on four),
-// each wavefront (BT / 2) x 64 outputs, 64 K values per stage; wavefronts skip
+// each wavefront (BT / 2) x 64 outputs; wavefronts skip
 // the 32-row blocks of a tile past its expert's rows.  Row tiles never
 // straddle two experts: a setup kernel lists
 // the (expert, first row) of every row tile from the device-side group
@@ -270,21 +274,21 @@ __global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
 // BF16 stages hold 32 K values in the MXFP8 geometry (64 bytes per K-major
 // row); an operand stored with its M or N dimension contiguous (MN-major,
 // BF16 only) occupies the same bytes as 32 K rows of BT elements.
-template <int FMT, int BT>
+template <int FMT, int BT, bool WIDE = false>
 struct Geo {
     static constexpr bool MX = FMT == BSP_FMT_MXFP8;
     static constexpr bool BF = FMT == FMT_BF16;
-    static constexpr int BK = BF ? 32 : GBK;           // K values per stage
+    static constexpr int BK = BF ? 32 : WIDE ? 2 * GBK : GBK;   // K values per stage
     static constexpr int NW = BT / 32;                 // wavefronts
     static constexpr int TI = BT / 64;                 // 32-row MFMA blocks per wavefront
-    static constexpr int ROWB = (MX || BF) ? 64 : 32;  // code bytes per row per stage
+    static constexpr int ROWB = MX ? BK : BF ? 64 : BK / 2;     // code bytes per row per stage
     static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
     static constexpr int CODE = BT * ROWB;             // one operand's codes per stage
     static constexpr int CIW = CODE / 1024 / NW;       // 1 KB DMA loads per wavefront per operand
     static constexpr int RPI = 64 / (BT / 8);          // MN-major K rows per wavefront DMA load
     static constexpr int KPW = CIW * RPI;              // MN-major K rows per wavefront per stage
     static constexpr int SBLK = MX ? 32 : 16;          // values per scale
-    static constexpr int SPS = BF ? 0 : GBK / SBLK;    // scales per row per stage
+    static constexpr int SPS = BF ? 0 : BK / SBLK;     // scales per row per stage
     static constexpr int SCLB = SPS * BT;              // scale bytes per operand per stage: [SPS][BT]
     static constexpr int A_SCL = 2 * CODE;
     static constexpr int B_SCL = 2 * CODE + SCLB;
@@ -292,15 +296,26 @@ struct Geo {
     static constexpr int OPS = 2 * CIW;                // code DMA loads per wavefront per stage (+1 for w < SCI)
     // a ring stage also serves as the epilogue's transpose patch (32 x 144 bytes per wavefront)
     static constexpr int SLOT = (2 * CODE + 2 * SCLB) > NW * 4608 ? (2 * CODE + 2 * SCLB) : NW * 4608;
+    // ring stages: four where they fit the LDS, else two (the wide stage)
+    static constexpr int NS = 4 * SLOT <= 152 * 1024 ? 4 : 2;
+    static constexpr int VPC = MX ? 16 : 32;           // K values per 16-byte code chunk (block-scaled)
     static_assert(CIW >= 1 && SCI <= NW && SCI % 2 == 0, "DMA split over the wavefronts");
 };
+
+// The geometry of each GEMM form: MXFP8 row-grouped forms (forward, data
+// gradient) stage 128 K values, every other form 64 (BF16: 32).  Every use
+// (tile decoding, the kernel, the workspace layout) goes through this one
+// definition, so the stage count of a tile and the stages the kernel loads
+// agree.
+template <int FMT, int MODE, int BT>
+using GeoOf = Geo<FMT, BT, FMT == BSP_FMT_MXFP8 && MODE != BSP_GEMM_WGRAD>;
 
 // Chunk position of chunk c of row r is c ^ swz(r): a fragment load reads one
 // chunk from each of 32 consecutive rows, and with this swizzle every group
 // of 8 (or 16) rows served together lands on distinct LDS banks.
-template <int FMT>
+template <int CH>
 __device__ __forceinline__ int swz(int r) {
-    return FMT == BSP_FMT_NVFP4 ? (((r >> 2) ^ (r >> 3)) & 1) : (((r >> 1) ^ (r >> 3)) & 3);
+    return CH == 8 ? (r & 7) : CH == 4 ? (((r >> 1) ^ (r >> 3)) & 3) : (((r >> 2) ^ (r >> 3)) & 1);
 }
 // MN-major stages: K row k holds BT / 8 chunks of 8 elements, chunk c stored
 // at position c ^ swz_mn(k).  A transposed fragment read (below) touches 8 K
@@ -417,7 +432,7 @@ __device__ __forceinline__ T sload(const T *p, int64_t i) {
 
 template <int FMT, int MODE, int BT>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs &p, int lin) {
-    constexpr int BK = Geo<FMT, BT>::BK;
+    constexpr int BK = GeoOf<FMT, MODE, BT>::BK;
     Tile T;
     const int ty = lin / p.ntn, tx = lin - ty * p.ntn;
     if (MODE == BSP_GEMM_WGRAD) {
@@ -471,7 +486,14 @@ struct IC {
 
 template <int FMT, int MODE, bool BF16OUT, int BT>
 __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
-    using GG = Geo<FMT, BT>;
+    // MXFP8 row-grouped forms stage 128 K values (128 bytes of every operand
+    // row, whole 128-byte L2 lines: half the memory requests per byte of a
+    // 64-value stage, and the per-CU count of outstanding requests is what
+    // bounds these loads) in a ring of two stages; the other forms stage 64
+    // (32 for BF16) in a ring of four.
+    using GG = GeoOf<FMT, MODE, BT>;
+    constexpr int NS = GG::NS;
+    constexpr int SUB = GG::MX ? GG::BK / GBK : 1;     // 64-value MFMA K steps per MXFP8 stage
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
@@ -482,8 +504,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     constexpr bool A_MN = BF && WG, B_MN = BF && MODE != BSP_GEMM_FPROP;
     constexpr int RP = BT * 2;                         // bytes of an MN-major K row in LDS
     constexpr int SEEK = 1, FIN = 2;
-    // Ring of four K stages.
-    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * SLOT_BYTES];
+    // Ring of NS K stages.
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SLOT_BYTES];
     // Per tile (ordinal mod 8) and tile row: the A row read (-1: the row
     // reads as zero) and, for NVFP4, the row's outer scale times the expert's.
     // The producer runs at most 3 stages, hence at most 4 tiles, ahead.
@@ -528,20 +550,24 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     // code chunks and scale dwords this lane feeds to the MFMA.
     // Rows 32 apart share the swizzle, so one offset per operand serves all
     // of the wavefront's blocks (plus 32 * ROWB bytes per block).
-    uint32_t fa0, fa1, fb0, fb1, fsa, fsb;
+    uint32_t fa0[SUB], fa1[SUB], fb0[SUB], fb1[SUB], fsa, fsb;
     // MN-major operands: base offset of this lane's transposed reads for each
     // 32-wide block (see mn_frag).
     uint32_t tra[A_MN ? TI : 1], trb[B_MN ? 2 : 1];
     {
         const int ra = wm * (BT / 2) + lr, rb = wn * 64 + lr;
         if (MX || BF) {
-            fa0 = ra * 64 + 16 * (lh ^ swz<FMT>(ra));
-            fa1 = ra * 64 + 16 * ((2 + lh) ^ swz<FMT>(ra));
-            fb0 = GG::CODE + rb * 64 + 16 * (lh ^ swz<FMT>(rb));
-            fb1 = GG::CODE + rb * 64 + 16 * ((2 + lh) ^ swz<FMT>(rb));
+            // MFMA K step s of the stage: chunks 4 s + h and 4 s + 2 + h
+#pragma unroll
+            for (int s = 0; s < SUB; s++) {
+                fa0[s] = ra * GG::ROWB + 16 * ((4 * s + lh) ^ swz<GG::CH>(ra));
+                fa1[s] = ra * GG::ROWB + 16 * ((4 * s + 2 + lh) ^ swz<GG::CH>(ra));
+                fb0[s] = GG::CODE + rb * GG::ROWB + 16 * ((4 * s + lh) ^ swz<GG::CH>(rb));
+                fb1[s] = GG::CODE + rb * GG::ROWB + 16 * ((4 * s + 2 + lh) ^ swz<GG::CH>(rb));
+            }
         } else {
-            fa0 = fa1 = ra * 32 + 16 * (lh ^ swz<FMT>(ra));
-            fb0 = fb1 = GG::CODE + rb * 32 + 16 * (lh ^ swz<FMT>(rb));
+            fa0[0] = fa1[0] = ra * GG::ROWB + 16 * (lh ^ swz<GG::CH>(ra));
+            fb0[0] = fb1[0] = GG::CODE + rb * GG::ROWB + 16 * (lh ^ swz<GG::CH>(rb));
         }
         // MXFP8 lane half h reads block h's byte; NVFP4 blocks 2h and 2h + 1
         fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
@@ -603,7 +629,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < GG::CIW; j++) {
             const int u = 64 * (w * GG::CIW + j) + l;
-            const int r = u / GG::CH, cp = u % GG::CH, c = cp ^ swz<FMT>(r);
+            const int r = u / GG::CH, cp = u % GG::CH, c = cp ^ swz<GG::CH>(r);
             const int kr = u / (BT / 8), cm = (u % (BT / 8)) ^ swz_mn(kr);
             if constexpr (A_MN) {
                 const int col = PT.row0 + 8 * cm < p.M - 8 ? PT.row0 + 8 * cm : p.M - 8;
@@ -657,7 +683,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         for (int j = 0; j < GG::CIW; j++) {
             const int u = 64 * (w * GG::CIW + j) + l;
             const int r = u / GG::CH, cp = u % GG::CH;
-            const int c = cp ^ swz<FMT>(r);
+            const int c = cp ^ swz<GG::CH>(r);
             int ar;
             if (WG) {
                 ar = PT.row0 + r < p.M ? PT.row0 + r : PT.row0;
@@ -696,7 +722,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < GG::CIW; j++) {
                     const int u = 64 * (w * GG::CIW + j) + l;
-                    const int c = (u % GG::CH) ^ swz<FMT>(u / GG::CH);
+                    const int c = (u % GG::CH) ^ swz<GG::CH>(u / GG::CH);
                     dma16v(k0 + 8 * c >= kend ? kZeroChunk : base + kb + off[j], dst + (w * GG::CIW + j) * 1024);
                 }
             }
@@ -760,23 +786,23 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             bf_issue(m0);
             return;
         }
-        const int k0 = PT.kbeg + p_kt * GBK;
+        const int k0 = PT.kbeg + p_kt * GG::BK;
         const uint32_t kb = p_kt * GG::ROWB, so = p_kt * GG::SPS;
-        if (k0 + GBK / 2 < PT.kend) {
+        if (k0 + GG::BK <= PT.kend) {
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) dma16(pca + kb, poa[j], m0 + (w * GG::CIW + j) * 1024);
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) dma16(pcb + kb, pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
         } else {
-            // The stage's second half lies past the K end: its chunks load
-            // zeros, and their scales (plane padding, or the next group's
-            // columns in the weight-gradient form) are finite, so they add
-            // nothing and the consumer needs no special case.
+            // The stage runs past the K end: chunks past it load zeros, and
+            // their scales (plane padding, or the next group's columns in
+            // the weight-gradient form) are finite, so they add nothing and
+            // the consumer needs no special case.
 #pragma unroll
             for (int j = 0; j < GG::CIW; j++) {
                 const int u = 64 * (w * GG::CIW + j) + l;
-                const int c = (u % GG::CH) ^ swz<FMT>(u / GG::CH);
-                const bool past = c >= GG::CH / 2;
+                const int c = (u % GG::CH) ^ swz<GG::CH>(u / GG::CH);
+                const bool past = k0 + GG::VPC * c >= PT.kend;
                 dma16v(past ? kZeroChunk : pca + kb + poa[j], m0 + (w * GG::CIW + j) * 1024);
                 dma16v(past ? kZeroChunk : pcb + kb + pob[j], m0 + GG::CODE + (w * GG::CIW + j) * 1024);
             }
@@ -823,29 +849,33 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         const int nv = live_blocks();
         if (nv == 0) return;
         if constexpr (MX) {
-            // Lane half h supplies bytes [16h, 16h + 16) of K block 0, then of
-            // block 1 (chunks h and 2 + h), with block h's E8M0 byte (only the
-            // low byte of the scale operand is read).  Block i + 1's A
+            // Per 64-value MFMA K step s: lane half h supplies bytes
+            // [16h, 16h + 16) of K block 2s, then of block 2s + 1 (chunks
+            // 4s + h and 4s + 2 + h), with block (2s + h)'s E8M0 byte (only
+            // the low byte of the scale operand is read).  Block i + 1's A
             // fragment is read before block i's MFMAs are issued (the empty
             // asm keeps the order), so the LDS reads run under the matrix
             // work; blocks past the group's rows skip their MFMAs.
+#pragma unroll
+          for (int s = 0; s < SUB; s++) {
             uint4 b0[2], b1[2], a0[TI], a1[TI];
             uint32_t bs[2], as[TI];
+            const uint32_t sa = fsa + 2 * s * BT, sb = fsb + 2 * s * BT;
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 64 * j);
-                b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1 + 32 * 64 * j);
-                bs[j] = slot[fsb + 32 * j];
+                b0[j] = *reinterpret_cast<const uint4 *>(slot + fb0[s] + 32 * GG::ROWB * j);
+                b1[j] = *reinterpret_cast<const uint4 *>(slot + fb1[s] + 32 * GG::ROWB * j);
+                bs[j] = slot[sb + 32 * j];
             }
-            a0[0] = *reinterpret_cast<const uint4 *>(slot + fa0);
-            a1[0] = *reinterpret_cast<const uint4 *>(slot + fa1);
-            as[0] = slot[fsa];
+            a0[0] = *reinterpret_cast<const uint4 *>(slot + fa0[s]);
+            a1[0] = *reinterpret_cast<const uint4 *>(slot + fa1[s]);
+            as[0] = slot[sa];
 #pragma unroll
             for (int i = 0; i < TI; i++) {
                 if (i + 1 < TI) {
-                    a0[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 64 * (i + 1));
-                    a1[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa1 + 32 * 64 * (i + 1));
-                    as[i + 1] = slot[fsa + 32 * (i + 1)];
+                    a0[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa0[s] + 32 * GG::ROWB * (i + 1));
+                    a1[i + 1] = *reinterpret_cast<const uint4 *>(slot + fa1[s] + 32 * GG::ROWB * (i + 1));
+                    as[i + 1] = slot[sa + 32 * (i + 1)];
                 }
                 asm volatile("" ::: "memory");
                 if (i < nv) {
@@ -860,6 +890,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     }
                 }
             }
+          }
         } else if constexpr (BF) {
             // MFMA s covers K values 16 s + 0..15 of the stage, lane half h
             // supplying 16 s + 8 h + 0..7 of its row (A) or column (B):
@@ -879,13 +910,13 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 v8bf fa[TI], fb[2];
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    fb[j] = B_MN ? mfrag(trb[B_MN ? j : 0] + 16 * s2 * RP) : kfrag((s2 ? fb1 : fb0) + 32 * 64 * j);
-                fa[0] = A_MN ? mfrag(tra[0] + 16 * s2 * RP) : kfrag(s2 ? fa1 : fa0);
+                    fb[j] = B_MN ? mfrag(trb[B_MN ? j : 0] + 16 * s2 * RP) : kfrag((s2 ? fb1[0] : fb0[0]) + 32 * 64 * j);
+                fa[0] = A_MN ? mfrag(tra[0] + 16 * s2 * RP) : kfrag(s2 ? fa1[0] : fa0[0]);
 #pragma unroll
                 for (int i = 0; i < TI; i++) {
                     if (i + 1 < TI)
                         fa[i + 1] = A_MN ? mfrag(tra[A_MN ? i + 1 : 0] + 16 * s2 * RP)
-                                         : kfrag((s2 ? fa1 : fa0) + 32 * 64 * (i + 1));
+                                         : kfrag((s2 ? fa1[0] : fa0[0]) + 32 * 64 * (i + 1));
                     asm volatile("" ::: "memory");
                     if (i < nv) {
 #pragma unroll
@@ -903,7 +934,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < TI; i++) {
                 if (i >= nv) break;
-                ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0 + 32 * 32 * i);
+                ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0[0] + 32 * 32 * i);
                 const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + 32 * i], 0);
                 const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + BT + 32 * i], 0);
                 sa[i][0] = h2{s0, s0};
@@ -911,7 +942,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0 + 32 * 32 * j);
+                ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0[0] + 32 * 32 * j);
                 const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + 32 * j], 0);
                 const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + BT + 32 * j], 0);
                 sb[j][0] = h2{t0, t0};
@@ -1064,7 +1095,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         CT = decode_tile<FMT, MODE, BT>(p, c_lin);
         cons_begin();
     }
-    for (int s = 0; s < 3 && !p_done; s++) {
+    for (int s = 0; s < NS - 1 && !p_done; s++) {
         issue(s);
         p_q++;
         if (++p_kt == p_nk) {
@@ -1074,15 +1105,15 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         }
     }
 
-    // One pipeline step: the consumer's stage q sits in ring stage U = q % 4
-    // and the producer refills ring stage (U + 3) % 4, which held stage q - 1,
-    // so three stages stay in flight.
+    // One pipeline step: the consumer's stage q sits in ring stage U = q % NS
+    // and the producer refills ring stage (U + NS - 1) % NS, which held stage
+    // q - 1, so NS - 1 stages stay in flight.
     auto step = [&](auto U) __attribute__((always_inline)) -> int {
         wait_stage_w<GG::OPS>(p_q - c_q - 1, scl_w);
         barrier();   // stage q landed for every wavefront; the ring stage of q - 1 is free
         int fl = 0;
         if (!p_done) {
-            issue((decltype(U)::v + 3) & 3);
+            issue((decltype(U)::v + NS - 1) % NS);
             p_q++;
             if (++p_kt == p_nk) fl |= SEEK;
         }
@@ -1104,11 +1135,16 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         if (WG && CT.nk == 0) {
             fl = FIN;
         } else {
-            const int u0 = c_q & 3;
-            if (u0 == 0) fl = step(IC<0>{});
-            if (!fl && u0 <= 1) fl = step(IC<1>{});
-            if (!fl && u0 <= 2) fl = step(IC<2>{});
-            if (!fl) fl = step(IC<3>{});
+            const int u0 = c_q % NS;
+            if constexpr (NS == 4) {
+                if (u0 == 0) fl = step(IC<0>{});
+                if (!fl && u0 <= 1) fl = step(IC<1>{});
+                if (!fl && u0 <= 2) fl = step(IC<2>{});
+                if (!fl) fl = step(IC<3>{});
+            } else {
+                if (u0 == 0) fl = step(IC<0>{});
+                if (!fl) fl = step(IC<1>{});
+            }
         }
         if (fl & SEEK) {
             p_lin = next_tile(p_lin);
@@ -1118,7 +1154,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         if (fl & FIN) {
             waitcnt<63, 0>();
             barrier();   // every wavefront is done reading the stage
-            epilogue(ring + ((c_q + 3) & 3) * SLOT_BYTES);
+            epilogue(ring + ((c_q + NS - 1) % NS) * SLOT_BYTES);
             cons_next();
         }
     }
@@ -1138,7 +1174,12 @@ struct WsLayout {
 static int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 static WsLayout ws_layout(int fmt, int mode, int64_t M, int64_t N, int64_t K, int64_t G) {
     WsLayout L;
-    const int64_t sblk = fmt == BSP_FMT_MXFP8 ? 32 : 16, sps = 64 / sblk;
+    // scale blocks per stage, as the kernel's geometry stages them
+    const int64_t sblk = fmt == BSP_FMT_MXFP8 ? 32 : 16;
+    const int64_t sps = fmt == BSP_FMT_MXFP8
+                            ? (mode == BSP_GEMM_WGRAD ? GeoOf<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>::SPS
+                                                      : GeoOf<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>::SPS)
+                            : GeoOf<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>::SPS;
     const int64_t nblk = K / sblk;
     L.nbp = (int32_t)(up(nblk, sps) + sps);   // K-tail stages read one padded step past the end
     const int64_t entries = (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G)) + kGemmSchedSlots;
