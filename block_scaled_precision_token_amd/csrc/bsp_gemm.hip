@@ -19,22 +19,25 @@
 //
 // Data movement.  Operand tiles stream from global memory straight into LDS
 // with the gfx950 LDS-DMA loads (GLOBAL_LOAD_LDS_DWORDX4 for codes, _DWORD
-// for scales): no registers are spent on staging.  A ring of LDS stages
-// keeps the next stages in flight while one is multiplied: four stages of 64
-// K values (32 for BF16), or, for the MXFP8 forward and data-gradient forms,
-// two stages of 128 K values, whose loads fetch whole 128-byte lines of every
-// operand row (the per-CU count of outstanding memory requests is what bounds
-// these loads, so bytes per request matter; 8 % faster on the DeepSeek-V3
-// shapes than four stages of 64).  The ring runs across tile boundaries: the
-// first stages of a workgroup's next tile are fetched while the current tile
-// is finished and written back.  Completion is tracked with explicit vmcnt
+// or _DWORDX4 for scales): no registers are spent on staging.  A ring of LDS
+// stages keeps the next stages in flight while one is multiplied.  The
+// forward and data-gradient forms stage 128 K values (MXFP8: 128 bytes of
+// every operand row, whole 128-byte lines, in a ring of two stages; NVFP4: 64
+// bytes, in a ring of four): the per-CU count of outstanding memory requests
+// is what bounds these loads, so bytes per request matter (8 % faster than
+// 64-value stages on the DeepSeek-V3 MXFP8 shapes, 3 % on the Qwen3 NVFP4
+// ones).  The weight-gradient forms stage 64 K values (BF16 32) in a ring of
+// four.  The ring runs across tile boundaries: the first stages of a
+// workgroup's next tile are fetched while the current tile is finished and
+// written back.  Completion is tracked with explicit vmcnt
 // waits (loads retire in order, so "at most n stages outstanding" means the
 // oldest stage has landed) followed by a workgroup barrier; the epilogue's
 // stores are issued so that the compiler's own counter model stays exact.
 //
-// LDS layout of a stage: per operand BT rows of 64 or 128 (MXFP8) or 32
-// (NVFP4) code bytes, the 16-byte chunks of row r stored at position chunk ^ swz(r)
-// so that the 32 rows read by one fragment load hit distinct banks; then the
+// LDS layout of a stage: per operand BT rows of code bytes (128 or 64 for
+// MXFP8, 64 or 32 for NVFP4), the 16-byte chunks of row r stored at position
+// chunk ^ swz(r) so that the 32 rows read by one fragment load hit distinct
+// banks; then the
 // stage's scale bytes, block-major ([scale block][row]) as copied from the
 // scale planes a setup kernel builds in the workspace.
 //
@@ -292,7 +295,10 @@ struct Geo {
     static constexpr int SCLB = SPS * BT;              // scale bytes per operand per stage: [SPS][BT]
     static constexpr int A_SCL = 2 * CODE;
     static constexpr int B_SCL = 2 * CODE + SCLB;
-    static constexpr int SCI = 2 * SCLB / 256;         // 256-byte scale DMA loads per stage (both operands)
+    // scale DMA loads: one dword per lane (256 bytes) where the stage's scale
+    // bytes fit one such load per wavefront, else 16 bytes per lane (1 KB)
+    static constexpr int SCW = 2 * SCLB / 256 <= NW ? 4 : 16;
+    static constexpr int SCI = 2 * SCLB / (64 * SCW);  // scale DMA loads per stage (both operands)
     static constexpr int OPS = 2 * CIW;                // code DMA loads per wavefront per stage (+1 for w < SCI)
     // a ring stage also serves as the epilogue's transpose patch (32 x 144 bytes per wavefront)
     static constexpr int SLOT = (2 * CODE + 2 * SCLB) > NW * 4608 ? (2 * CODE + 2 * SCLB) : NW * 4608;
@@ -302,13 +308,14 @@ struct Geo {
     static_assert(CIW >= 1 && SCI <= NW && SCI % 2 == 0, "DMA split over the wavefronts");
 };
 
-// The geometry of each GEMM form: MXFP8 row-grouped forms (forward, data
-// gradient) stage 128 K values, every other form 64 (BF16: 32).  Every use
+// The geometry of each GEMM form: the block-scaled row-grouped forms
+// (forward, data gradient) stage 128 K values, the weight-gradient form 64,
+// BF16 32.  Every use
 // (tile decoding, the kernel, the workspace layout) goes through this one
 // definition, so the stage count of a tile and the stages the kernel loads
 // agree.
 template <int FMT, int MODE, int BT>
-using GeoOf = Geo<FMT, BT, FMT == BSP_FMT_MXFP8 && MODE != BSP_GEMM_WGRAD>;
+using GeoOf = Geo<FMT, BT, FMT != FMT_BF16 && MODE != BSP_GEMM_WGRAD>;
 
 // Chunk position of chunk c of row r is c ^ swz(r): a fragment load reads one
 // chunk from each of 32 consecutive rows, and with this swizzle every group
@@ -486,14 +493,15 @@ struct IC {
 
 template <int FMT, int MODE, bool BF16OUT, int BT>
 __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
-    // MXFP8 row-grouped forms stage 128 K values (128 bytes of every operand
-    // row, whole 128-byte L2 lines: half the memory requests per byte of a
-    // 64-value stage, and the per-CU count of outstanding requests is what
-    // bounds these loads) in a ring of two stages; the other forms stage 64
-    // (32 for BF16) in a ring of four.
+    // The block-scaled row-grouped forms stage 128 K values (MXFP8: 128
+    // bytes of every operand row, whole 128-byte L2 lines; NVFP4: 64 bytes):
+    // fewer memory requests per byte than a 64-value stage, and the per-CU
+    // count of outstanding requests is what bounds these loads.  MXFP8 then
+    // needs a ring of two stages, NVFP4 keeps four; the weight-gradient forms
+    // stage 64 (BF16 32) in a ring of four.
     using GG = GeoOf<FMT, MODE, BT>;
     constexpr int NS = GG::NS;
-    constexpr int SUB = GG::MX ? GG::BK / GBK : 1;     // 64-value MFMA K steps per MXFP8 stage
+    constexpr int SUB = GG::BF ? 1 : GG::BK / GBK;     // 64-value K steps per block-scaled stage
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
@@ -566,8 +574,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 fb1[s] = GG::CODE + rb * GG::ROWB + 16 * ((4 * s + 2 + lh) ^ swz<GG::CH>(rb));
             }
         } else {
-            fa0[0] = fa1[0] = ra * GG::ROWB + 16 * (lh ^ swz<GG::CH>(ra));
-            fb0[0] = fb1[0] = GG::CODE + rb * GG::ROWB + 16 * (lh ^ swz<GG::CH>(rb));
+            // NVFP4 K step s of the stage: chunk 2 s + h
+#pragma unroll
+            for (int s = 0; s < SUB; s++) {
+                fa0[s] = fa1[s] = ra * GG::ROWB + 16 * ((2 * s + lh) ^ swz<GG::CH>(ra));
+                fb0[s] = fb1[s] = GG::CODE + rb * GG::ROWB + 16 * ((2 * s + lh) ^ swz<GG::CH>(rb));
+            }
         }
         // MXFP8 lane half h reads block h's byte; NVFP4 blocks 2h and 2h + 1
         fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
@@ -597,12 +609,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     Tile PT;
     const uint8_t *pca = nullptr, *pcb = nullptr;     // code bases of the tile (uniform)
     uint32_t poa[GG::CIW], pob[GG::CIW];              // this lane's code chunk offsets
-    // Scale DMA (wavefronts w < SCI): operand and 256-byte piece of its
+    // Scale DMA (wavefronts w < SCI): operand and 64 SCW-byte piece of its
     // [SPS][BT] stage region; this lane covers block sbl, rows sr0..sr0+3.
     constexpr int SCH = GG::SCI > 0 ? GG::SCI / 2 : 1;
     const bool scl_w = GG::SCI > 0 && w < GG::SCI;
     const bool scl_b = w >= GG::SCI / 2;
-    const int scl_o = 256 * (w % SCH) + 4 * l;
+    const int scl_o = 64 * GG::SCW * (w % SCH) + GG::SCW * l;
     const int sbl = scl_o / BT, sr0 = scl_o % BT;
     const uint32_t psv = (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;   // lane offset in the plane
     const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
@@ -808,9 +820,12 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             }
         }
         // scale bytes of the stage: SPS plane rows (padded past the K end)
-        if (scl_w)
-            dma4(uniform_ptr(psbase + (size_t)so * (scl_b ? p.b_rp : p.a_rp)), psv,
-                 m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 256 * (w % SCH));
+        if (scl_w) {
+            const uint8_t *sbase = uniform_ptr(psbase + (size_t)so * (scl_b ? p.b_rp : p.a_rp));
+            const uint32_t sdst = m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 64 * GG::SCW * (w % SCH);
+            if constexpr (GG::SCW == 4) dma4(sbase, psv, sdst);
+            else dma16(sbase, psv, sdst);
+        }
     };
 
     // ---- consumer state ----
@@ -926,25 +941,29 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 }
             }
         } else {
-            // K order inside a stage: lane half h, MFMA step q and element e
-            // take K = 32 h + 8 q + e, the same on both operands, so each lane
-            // reads one 16-byte chunk (32 values, scale blocks 2h and 2h + 1).
+            // K order inside a 64-value step s of the stage: lane half h,
+            // MFMA step q and element e take K = 64 s + 32 h + 8 q + e, the
+            // same on both operands, so each lane reads one 16-byte chunk
+            // (32 values, scale blocks 4s + 2h and 4s + 2h + 1).
+#pragma unroll
+          for (int s = 0; s < SUB; s++) {
             uint4 ua[TI], ub[2];
             h2 sa[TI][2], sb[2][2];
+            const uint32_t ssa = fsa + 4 * s * BT, ssb = fsb + 4 * s * BT;
 #pragma unroll
             for (int i = 0; i < TI; i++) {
                 if (i >= nv) break;
-                ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0[0] + 32 * 32 * i);
-                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + 32 * i], 0);
-                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsa + BT + 32 * i], 0);
+                ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0[s] + 32 * GG::ROWB * i);
+                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + 32 * i], 0);
+                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + BT + 32 * i], 0);
                 sa[i][0] = h2{s0, s0};
                 sa[i][1] = h2{s1, s1};
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
-                ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0[0] + 32 * 32 * j);
-                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + 32 * j], 0);
-                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[fsb + BT + 32 * j], 0);
+                ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0[s] + 32 * GG::ROWB * j);
+                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + 32 * j], 0);
+                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + BT + 32 * j], 0);
                 sb[j][0] = h2{t0, t0};
                 sb[j][1] = h2{t1, t1};
             }
@@ -982,6 +1001,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
                 }
             }
+          }
         }
     };
 
@@ -1176,10 +1196,12 @@ static WsLayout ws_layout(int fmt, int mode, int64_t M, int64_t N, int64_t K, in
     WsLayout L;
     // scale blocks per stage, as the kernel's geometry stages them
     const int64_t sblk = fmt == BSP_FMT_MXFP8 ? 32 : 16;
+    const bool wg = mode == BSP_GEMM_WGRAD;
     const int64_t sps = fmt == BSP_FMT_MXFP8
-                            ? (mode == BSP_GEMM_WGRAD ? GeoOf<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>::SPS
-                                                      : GeoOf<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>::SPS)
-                            : GeoOf<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>::SPS;
+                            ? (wg ? GeoOf<BSP_FMT_MXFP8, BSP_GEMM_WGRAD, 256>::SPS
+                                  : GeoOf<BSP_FMT_MXFP8, BSP_GEMM_FPROP, 256>::SPS)
+                            : (wg ? GeoOf<BSP_FMT_NVFP4, BSP_GEMM_WGRAD, 256>::SPS
+                                  : GeoOf<BSP_FMT_NVFP4, BSP_GEMM_FPROP, 256>::SPS);
     const int64_t nblk = K / sblk;
     L.nbp = (int32_t)(up(nblk, sps) + sps);   // K-tail stages read one padded step past the end
     const int64_t entries = (mode == BSP_GEMM_WGRAD ? G + 1 : gemm_tile_count(M, G)) + kGemmSchedSlots;

@@ -50,14 +50,20 @@ def test_size_helpers():
     assert (c.value, s.value) == (4096 * 7168, 4096 * 224)
     assert L.bsp_mxfp8_grouped_cols(100, 4) == 224          # roundup32(100 + 31*4)
     # tile list + counters (256-byte aligned), then block-major scale planes:
-    # blocks padded to whole K steps plus one, rows padded to 256
+    # blocks padded to whole K stages plus one stage (128 K values, 8 NVFP4
+    # blocks, in the forward form; 64 in the weight-gradient form), rows
+    # padded to 256
     def up(x, a):
         return (x + a - 1) // a * a
     head = up((512 + 128 + 16) * 8, 256)
-    nbp = 2048 // 16 + 4
+    nbp = up(2048 // 16, 8) + 8
     a_plane = nbp * ((65536 + 255) // 256 + 128) * 256
     b_plane = 128 * nbp * up(1536, 256)
     assert L.bsp_gemm_workspace_size(0, 0, 65536, 1536, 2048, 128) == head + up(a_plane, 256) + up(b_plane, 256)
+    nbp = up(7168 // 32, 4) + 4
+    head = up(((36864 + 127) // 128 + 257 + 16) * 8, 256)
+    a_plane = nbp * ((36864 + 255) // 256 + 257) * 256
+    assert L.bsp_gemm_workspace_size(1, 0, 36864, 4096, 7168, 257) == head + up(a_plane, 256) + 257 * nbp * 4096
     # unknown modes size to 0
     assert L.bsp_gemm_workspace_size(0, 3, 65536, 1536, 2048, 128) == 0
     assert L.bsp_gemm_workspace_size(0, 7, 65536, 1536, 2048, 128) == 0
