@@ -51,9 +51,13 @@ BSP_EXPORT bsp_status bsp_mxfp8_sizes(int64_t M, int64_t K, size_t *codes_bytes,
     return BSP_OK;
 }
 
+// Smallest accepted column count of a grouped transposed copy: the padded
+// total sum_g roundup32(n_g) never exceeds roundup32(M + 31 G).
+static int64_t grouped_cols_min(int64_t M, int64_t G) { return (M + 31 * G + 31) / 32 * 32; }
+
 BSP_EXPORT int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G) {
     if (M < 0 || G < 1) return -1;
-    return (M + 31 * G + 31) / 32 * 32;
+    return (M + 31 * G + 255) / 256 * 256;
 }
 
 BSP_EXPORT size_t bsp_requant_workspace_size(int64_t M) {
@@ -134,7 +138,7 @@ BSP_EXPORT bsp_status bsp_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int6
         if (ld_colT <= 0 || ld_colT % 32) return BSP_ERR_SHAPE;
         if (group_offsets) {
             if (G < 1 || G > 2048) return BSP_ERR_SHAPE;
-            if (ld_colT < bsp_mxfp8_grouped_cols(M, G)) return BSP_ERR_SHAPE;
+            if (ld_colT < grouped_cols_min(M, G)) return BSP_ERR_SHAPE;
         } else {
             if (M % 32 || ld_colT < M) return BSP_ERR_SHAPE;
         }
@@ -192,7 +196,7 @@ BSP_EXPORT bsp_status bsp_requant_transpose_sr_grouped(const uint8_t *codes, con
     if (G < 1 || G > 2048 || R <= 0 || K <= 0 || K % 16 || src_rows <= 0) return BSP_ERR_SHAPE;
     if (src_rows >= (1ll << 31) || R >= (1ll << 40)) return BSP_ERR_SHAPE;
     if (!gather && src_rows != R) return BSP_ERR_SHAPE;
-    if (ldT % 32 || ldT < bsp_mxfp8_grouped_cols(R, G)) return BSP_ERR_SHAPE;
+    if (ldT % 32 || ldT < grouped_cols_min(R, G)) return BSP_ERR_SHAPE;
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(outer) || !aligned16(group_offsets) ||
         !aligned16(codesT) || !aligned16(scalesT) || !aligned16(outerT) || !aligned16_or_null(gather))
         return BSP_ERR_ALIGNMENT;

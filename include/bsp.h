@@ -125,7 +125,8 @@ bsp_status bsp_quantize_nvfp4_per_token(const uint16_t *x, int64_t M, int64_t K,
  *   scales_colT  device u8 [K, ld_colT/32] or NULL (both NULL or both set)
  *   ld_colT      columns of the transposed copy; ld_colT % 32 == 0.
  *                Ungrouped: ld_colT >= M and M % 32 == 0.
- *                Grouped: ld_colT >= bsp_mxfp8_grouped_cols(M, G).
+ *                Grouped: ld_colT >= roundup32(M + 31 G) (the value of
+ *                bsp_mxfp8_grouped_cols(M, G) keeps rows line-aligned).
  *   group_offsets  device int64 [G+1] or NULL.  Rows [off[g], off[g+1]) form
  *                group g (0 = off[0] <= ... <= off[G] = M).  Columnwise blocks
  *                then stay inside a group: group g occupies transposed columns
@@ -228,7 +229,8 @@ bsp_status bsp_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
  *            group g in columns [P[g], P[g] + pad32(n_g)), P the running sum
  *            of the 32-padded group sizes; padding columns hold zero codes
  *            and zero scales; columns from P[G] to ldT are left untouched
- *   ldT      multiple of 32, >= bsp_mxfp8_grouped_cols(R, G)
+ *   ldT      multiple of 32, >= roundup32(R + 31 G) (bsp_mxfp8_grouped_cols
+ *            gives a line-aligned value)
  *   outerT   device f32 [G] (out): G_g = max outer scale over group g's rows
  *   K % 16 == 0
  * Each group is requantized exactly as by bsp_requant_transpose_sr with its
@@ -431,8 +433,13 @@ bsp_status bsp_swiglu_quantize(const void *h13, int in_dtype, int64_t R, int64_t
 bsp_status bsp_nvfp4_sizes(int64_t M, int64_t K, int64_t rows_per_scale, size_t *codes_bytes,
                            size_t *scales_bytes, size_t *outer_count);
 bsp_status bsp_mxfp8_sizes(int64_t M, int64_t K, size_t *codes_bytes, size_t *scales_bytes);
-/* Upper bound of the padded column count of a grouped columnwise copy:
- * sum over groups of roundup32(n_g) <= roundup32(M + 31 * G). */
+/* Column count to allocate for a grouped columnwise copy (MXFP8 ld_colT, or
+ * ldT of the grouped requant): roundup256(M + 31 * G).  Any multiple of 32 of
+ * at least roundup32(M + 31 * G), an upper bound of the padded total
+ * sum_g roundup32(n_g), is accepted; the multiple of 256 starts every row of
+ * the transposed codes (ld bytes for MXFP8, ld / 2 for NVFP4) on a 128-byte
+ * line, which the quantizers' row stores and the weight-gradient GEMM's
+ * loads need to stay whole-line.  -1 for M < 0 or G < 1. */
 int64_t bsp_mxfp8_grouped_cols(int64_t M, int64_t G);
 /* Bytes of requant workspace for M rows: one f32 partial maximum of the outer
  * scales per 2048 rows (at most 1024 partials); 0 for M <= 0. */

@@ -48,7 +48,8 @@ def test_size_helpers():
     assert L.bsp_nvfp4_sizes(8192, 2040, 1, ctypes.byref(c), ctypes.byref(s), ctypes.byref(o)) == 2
     assert L.bsp_mxfp8_sizes(4096, 7168, ctypes.byref(c), ctypes.byref(s)) == 0
     assert (c.value, s.value) == (4096 * 7168, 4096 * 224)
-    assert L.bsp_mxfp8_grouped_cols(100, 4) == 224          # roundup32(100 + 31*4)
+    assert L.bsp_mxfp8_grouped_cols(100, 4) == 256          # roundup256(100 + 31*4)
+    assert L.bsp_mxfp8_grouped_cols(36864, 257) == 45056    # rows of the copy start on 128-byte lines
     # tile list + counters (256-byte aligned), then block-major scale planes:
     # blocks padded to whole K stages plus one stage (128 K values, 8 NVFP4
     # blocks, in the forward form; 64 in the weight-gradient form), rows
