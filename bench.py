@@ -1086,51 +1086,21 @@ def time_graphed(wl, steps, dev):
     return wall * 1e3 / steps, e_start.elapsed_time(e_end) / steps
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the requant size sweep")
-    ap.add_argument("--only", default=None, help="time just this op of the workload (for profiler runs)")
-    ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
-                    help="time HIP-graph replays instead of Python launches (auto: for the short-step workloads)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is not implemented)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(wl, steps, warmup, use_graph, dev):
+    """Warm up, time `steps` steps of workload `wl` and summarize: (ms per
+    step, per-op components, roofline object of the dominant op)."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    from block_scaled_precision_token_amd import ops
-    ops.lib()      # fails loudly when the HIP library is missing
-
-    wl = WORKLOADS[args.workload](dev)
-    if args.only:
-        sel = [op for op in wl.ops if op.name == args.only]
-        if not sel:
-            print(f"bench.py: no op {args.only!r} in {wl.name}; ops: {[op.name for op in wl.ops]}", file=sys.stderr)
-            sys.exit(2)
-        wl.ops = sel
     torch.cuda.synchronize()
     print(f"[bench] workload {wl.name} ready; {len(wl.ops)} ops per step", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         for op in wl.ops:
             op.fn()
     torch.cuda.synchronize()
-
-    use_graph = {"auto": getattr(wl, "graph", False), "on": True, "off": False}[args.graph]
     if use_graph:
-        ms_per_step, ev_ms_per_step = time_graphed(wl, args.steps, dev)
+        ms_per_step, ev_ms_per_step = time_graphed(wl, steps, dev)
     else:
-        ms_per_step, ev_ms_per_step = time_eager(wl, args.steps, dev)
-    print(f"[bench] timed {args.steps} steps{' (HIP graph replay)' if use_graph else ''}: "
+        ms_per_step, ev_ms_per_step = time_eager(wl, steps, dev)
+    print(f"[bench] timed {steps} steps{' (HIP graph replay)' if use_graph else ''}: "
           f"{ms_per_step:.3f} ms/step (events {ev_ms_per_step:.3f})", file=sys.stderr, flush=True)
 
     comps = {}
@@ -1165,11 +1135,77 @@ def main():
         ach = dom.nbytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom.name}
+    return ms_per_step, comps, roof
+
+
+# Workloads the default run measures after the headline one, each in a few
+# steps on the same GPU, so that every configuration's figures come from the
+# same run (reported beside the headline, never folded into it).
+SECONDARY = ("qwen3_moe_nvfp4", "qwen3_moe_nvfp4_bwd_fp4", "qwen3_moe_nvfp4_bwd_hp", "mxfp8_quant", "requant_sr")
+
+
+def secondary_workloads(dev, steps=5, warmup=2):
+    import torch
+    out = {}
+    for name in SECONDARY:
+        wl = WORKLOADS[name](dev)
+        ms, comps, roof = measure(wl, steps, warmup, getattr(wl, "graph", False), dev)
+        out[name] = {"ms_per_step": round(ms, 4), "value": round(wl.value(ms), 3), "unit": wl.unit,
+                     "config": wl.config(), "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved",
+                                                                               "unit", "frac")},
+                     "steps": steps, "warmup": warmup}
+        del wl, comps
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv3_moe_mxfp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the requant size sweep")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workloads the default run measures after the headline one")
+    ap.add_argument("--only", default=None, help="time just this op of the workload (for profiler runs)")
+    ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
+                    help="time HIP-graph replays instead of Python launches (auto: for the short-step workloads)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    from block_scaled_precision_token_amd import ops
+    ops.lib()      # fails loudly when the HIP library is missing
+
+    wl = WORKLOADS[args.workload](dev)
+    if args.only:
+        sel = [op for op in wl.ops if op.name == args.only]
+        if not sel:
+            print(f"bench.py: no op {args.only!r} in {wl.name}; ops: {[op.name for op in wl.ops]}", file=sys.stderr)
+            sys.exit(2)
+        wl.ops = sel
+    use_graph = {"auto": getattr(wl, "graph", False), "on": True, "off": False}[args.graph]
+    ms_per_step, comps, roof = measure(wl, args.steps, args.warmup, use_graph, dev)
 
     sweep = None
     if not args.no_sweep and not args.only and wl.name in ("dsv3_moe_mxfp8", "requant_sr"):
         print("[bench] requant size sweep", file=sys.stderr, flush=True)
         sweep = requant_size_sweep(dev)
+
+    secondary = None
+    if not args.no_secondary and not args.only and wl.name == "dsv3_moe_mxfp8":
+        print("[bench] other workloads, a few steps each", file=sys.stderr, flush=True)
+        secondary = secondary_workloads(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -1191,6 +1227,8 @@ def main():
     }
     if sweep is not None:
         line["requant_size_sweep"] = sweep
+    if secondary is not None:
+        line["other_workloads"] = secondary
     print(json.dumps(line), flush=True)
 
 

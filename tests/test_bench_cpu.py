@@ -25,6 +25,9 @@ def test_workload_registry():
     for name in ("dsv3_moe_mxfp8", "qwen3_moe_nvfp4", "qwen3_moe_nvfp4_bwd_hp", "qwen3_moe_nvfp4_bwd_deq",
                  "qwen3_moe_nvfp4_bwd_fp4", "mxfp8_quant", "requant_sr", "roundtrip", "hbm_copy"):
         assert name in bench.WORKLOADS, name
+    # the default run also measures these, after the headline workload
+    assert set(bench.SECONDARY) <= set(bench.WORKLOADS)
+    assert "dsv3_moe_mxfp8" not in bench.SECONDARY
 
 
 def test_kernel_source_digest_ignores_comments_and_layout(tmp_path, monkeypatch):
