@@ -23,11 +23,11 @@
 // stages keeps the next stages in flight while one is multiplied.  The
 // forward and data-gradient forms stage 128 K values (MXFP8: 128 bytes of
 // every operand row, whole 128-byte lines, in a ring of two stages; NVFP4: 64
-// bytes, in a ring of four): the per-CU count of outstanding memory requests
-// is what bounds these loads, so bytes per request matter (8 % faster than
-// 64-value stages on the DeepSeek-V3 MXFP8 shapes, 3 % on the Qwen3 NVFP4
-// ones).  The weight-gradient forms stage 64 K values (BF16 32) in a ring of
-// four.  The ring runs across tile boundaries: the first stages of a
+// bytes, in a ring of four; BF16 64 values, 128 bytes, two stages): the
+// per-CU count of outstanding memory requests is what bounds these loads, so
+// bytes per request matter (8 % faster than 64-value stages on the
+// DeepSeek-V3 MXFP8 shapes, 1-3 % on the Qwen3 NVFP4 and BF16 ones).  The
+// weight-gradient forms stage half as many (64, BF16 32) in a ring of four.  The ring runs across tile boundaries: the first stages of a
 // workgroup's next tile are fetched while the current tile is finished and
 // written back.  Completion is tracked with explicit vmcnt
 // waits (loads retire in order, so "at most n stages outstanding" means the
@@ -281,10 +281,10 @@ template <int FMT, int BT, bool WIDE = false>
 struct Geo {
     static constexpr bool MX = FMT == BSP_FMT_MXFP8;
     static constexpr bool BF = FMT == FMT_BF16;
-    static constexpr int BK = BF ? 32 : WIDE ? 2 * GBK : GBK;   // K values per stage
+    static constexpr int BK = (BF ? 32 : GBK) * (WIDE ? 2 : 1);   // K values per stage
     static constexpr int NW = BT / 32;                 // wavefronts
     static constexpr int TI = BT / 64;                 // 32-row MFMA blocks per wavefront
-    static constexpr int ROWB = MX ? BK : BF ? 64 : BK / 2;     // code bytes per row per stage
+    static constexpr int ROWB = MX ? BK : BF ? 2 * BK : BK / 2;   // code bytes per row per stage
     static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
     static constexpr int CODE = BT * ROWB;             // one operand's codes per stage
     static constexpr int CIW = CODE / 1024 / NW;       // 1 KB DMA loads per wavefront per operand
@@ -308,14 +308,14 @@ struct Geo {
     static_assert(CIW >= 1 && SCI <= NW && SCI % 2 == 0, "DMA split over the wavefronts");
 };
 
-// The geometry of each GEMM form: the block-scaled row-grouped forms
-// (forward, data gradient) stage 128 K values, the weight-gradient form 64,
-// BF16 32.  Every use
+// The geometry of each GEMM form: the row-grouped forms (forward, data
+// gradient) stage twice the K values of the weight-gradient form: 128 for
+// the block-scaled formats (64 in the weight gradient), 64 for BF16 (32).  Every use
 // (tile decoding, the kernel, the workspace layout) goes through this one
 // definition, so the stage count of a tile and the stages the kernel loads
 // agree.
 template <int FMT, int MODE, int BT>
-using GeoOf = Geo<FMT, BT, FMT != FMT_BF16 && MODE != BSP_GEMM_WGRAD>;
+using GeoOf = Geo<FMT, BT, MODE != BSP_GEMM_WGRAD>;
 
 // Chunk position of chunk c of row r is c ^ swz(r): a fragment load reads one
 // chunk from each of 32 consecutive rows, and with this swizzle every group
@@ -497,11 +497,13 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     // bytes of every operand row, whole 128-byte L2 lines; NVFP4: 64 bytes):
     // fewer memory requests per byte than a 64-value stage, and the per-CU
     // count of outstanding requests is what bounds these loads.  MXFP8 then
-    // needs a ring of two stages, NVFP4 keeps four; the weight-gradient forms
-    // stage 64 (BF16 32) in a ring of four.
+    // needs a ring of two stages, NVFP4 keeps four (BF16 row-grouped forms: 64
+    // values, 128 bytes, two stages); the weight-gradient forms stage half as
+    // many (64, BF16 32) in a ring of four.
     using GG = GeoOf<FMT, MODE, BT>;
     constexpr int NS = GG::NS;
-    constexpr int SUB = GG::BF ? 1 : GG::BK / GBK;     // 64-value K steps per block-scaled stage
+    // fragment-offset sets per stage: 64-value K steps (block-scaled), 32-value ones (BF16)
+    constexpr int SUB = GG::BF ? GG::BK / 32 : GG::BK / GBK;
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
@@ -921,17 +923,20 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             };
 #pragma unroll
-            for (int s2 = 0; s2 < 2; s2++) {
+            for (int st = 0; st < GG::BK / 16; st++) {
+                // MFMA step st = 2 sub + s2: K-major chunk 4 sub + 2 s2 + h
+                const int sub = st >> 1, s2 = st & 1;
                 v8bf fa[TI], fb[2];
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    fb[j] = B_MN ? mfrag(trb[B_MN ? j : 0] + 16 * s2 * RP) : kfrag((s2 ? fb1[0] : fb0[0]) + 32 * 64 * j);
-                fa[0] = A_MN ? mfrag(tra[0] + 16 * s2 * RP) : kfrag(s2 ? fa1[0] : fa0[0]);
+                    fb[j] = B_MN ? mfrag(trb[B_MN ? j : 0] + 16 * st * RP)
+                                 : kfrag((s2 ? fb1[sub] : fb0[sub]) + 32 * GG::ROWB * j);
+                fa[0] = A_MN ? mfrag(tra[0] + 16 * st * RP) : kfrag(s2 ? fa1[sub] : fa0[sub]);
 #pragma unroll
                 for (int i = 0; i < TI; i++) {
                     if (i + 1 < TI)
-                        fa[i + 1] = A_MN ? mfrag(tra[A_MN ? i + 1 : 0] + 16 * s2 * RP)
-                                         : kfrag((s2 ? fa1[0] : fa0[0]) + 32 * 64 * (i + 1));
+                        fa[i + 1] = A_MN ? mfrag(tra[A_MN ? i + 1 : 0] + 16 * st * RP)
+                                         : kfrag((s2 ? fa1[sub] : fa0[sub]) + 32 * GG::ROWB * (i + 1));
                     asm volatile("" ::: "memory");
                     if (i < nv) {
 #pragma unroll
