@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
     // the identity (groups or a gather); the plain form then needs 32 KB of
     // LDS in all, so five workgroups fit a compute unit.
     constexpr bool MAP = GROUPED || GATHER;
-    __shared__ __attribute__((aligned(16))) uint16_t tile[MX_TR][MX_TC];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[COL ? MX_TR : 1][MX_TC];
     __shared__ int64_t rsrc[ROW && MAP ? MX_TR : 1];   // destination row of each tile row in codes_row (-1: none)
     __shared__ int64_t xsrc[MAP ? MX_TR : 1];           // row of x of each tile row (-1: zeros)
     __shared__ int64_t blk_src0[GROUPED ? MX_TR / 32 : 1], blk_end[GROUPED ? MX_TR / 32 : 1];
@@ -459,8 +459,10 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             codes_row += b * M * K;
             scales_row += b * M * (K / 32);
         }
-        codes_colT += b * K * ld_colT;
-        scales_colT += b * K * (ld_colT / 32);
+        if (COL) {
+            codes_colT += b * K * ld_colT;
+            scales_colT += b * K * (ld_colT / 32);
+        }
     }
 
     if (GROUPED) {
@@ -575,6 +577,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_tile(const uint16_t *__restrict__
             }
         }
     }
+    if constexpr (!COL) return;   // rowwise copy only
 #pragma unroll
     for (int i = 0; i < 8; i++) *reinterpret_cast<uint4 *>(&tile[32 * wv + 4 * i + rq][8 * ch]) = raw[i];
     __syncthreads();
@@ -683,12 +686,26 @@ hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t x_rows, int64_t K, i
                                  uint8_t *scales_colT, int64_t ld_colT, const int64_t *group_offsets, int64_t G,
                                  int64_t batch, hipStream_t s) {
     const bool row = codes_row != nullptr, col = codes_colT != nullptr;
-    if (!col) {
-        const int gx = grid_for(M * (K / 32), 256, batch > 1 ? 4096 : (1 << 20));
-        k_mxfp8_row<<<dim3(gx, 1, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row, gather, x_rows);
+    const unsigned gx = (unsigned)((K + MX_TC - 1) / MX_TC);
+    if (!col && M * K * batch < (int64_t(1) << 26)) {
+        // a short rowwise-only tensor (less than one pass of 128 x 128 tiles
+        // over the GPU's workgroup slots): one lane per block, more and
+        // shorter work units
+        const int gxr = grid_for(M * (K / 32), 256, batch > 1 ? 4096 : (1 << 20));
+        k_mxfp8_row<<<dim3(gxr, 1, (unsigned)batch), 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row, gather,
+                                                                   x_rows);
         return hipGetLastError();
     }
-    const unsigned gx = (unsigned)((K + MX_TC - 1) / MX_TC);
+    if (!col) {   // rowwise only: the tile kernel without its column pass (whole-row loads and stores)
+        const dim3 grid(gx, (unsigned)((M + MX_TR - 1) / MX_TR), (unsigned)batch);
+        if (gather)
+            k_mxfp8_tile<true, false, false, true><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row, nullptr,
+                                                                       nullptr, 0, nullptr, 1, gather, x_rows);
+        else
+            k_mxfp8_tile<true, false, false, false><<<grid, 256, 0, s>>>(x, M, K, ldx, codes_row, scales_row, nullptr,
+                                                                        nullptr, 0, nullptr, 1, nullptr, x_rows);
+        return hipGetLastError();
+    }
     if (group_offsets) {
         // 1-D XCD-aware grid: 8 runs of ceil(tiles / 8) workgroups
         const int64_t tiles = (int64_t)gx * ((ld_colT + MX_TR - 1) / MX_TR);

@@ -16,6 +16,10 @@ branches cheaply:
     groups, empty groups, with and without a gather;
   - per-token NVFP4 of rows with 1537..2048 values once M > 8188 (one row per
     wavefront), both modes, at the 4-bit backward's 65,536 x 2048;
+  - rowwise-only MXFP8 of tensors of at least 2^26 values (the tile kernel
+    without its column pass; smaller ones take the lane-per-block kernel):
+    the MXFP8 quantization workload's 128 expert weights [2048, 768], and a
+    gathered rowwise copy of 65,536 routed rows of 2048;
   - the Qwen3-shaped NVFP4 down GEMM and the 4-bit backward's NVFP4 data- and
     weight-gradient GEMMs at full size on sampled rows and groups.
 """
@@ -129,6 +133,32 @@ def test_nvfp4_per_token_one_row_per_wavefront(M, K, mode46):
 T_D, H_D, I_D, E_D, TOPK_D = 4096, 7168, 2048, 256, 8
 N13_D = 2 * I_D
 SEED = 20261301
+
+
+def test_mxfp8_rowwise_only_large_batched_weights():
+    E, N, K = 128, 2048, 768        # the MXFP8 quantization workload's weights: 2^27.6 values
+    w = synth.device_weights(SEED + 41, E, N, K, device=DEV)
+    q = ops.quantize_mxfp8(w.view(E, N, K), True, False)
+    for e in (0, 1, 63, 127):
+        rc, rs = oracle.quantize_mxfp8_rowwise(bits(w[e * N:(e + 1) * N]))
+        assert_bytes_equal(host(q["codes_row"][e]), rc, f"expert {e} row codes")
+        assert_bytes_equal(host(q["scales_row"][e]), rs, f"expert {e} row scales")
+
+
+def test_mxfp8_rowwise_only_large_gathered():
+    T, K, R = 8192, 2048, 65536     # 2^27 gathered values
+    x = synth.device_activations(SEED + 42, T, K, device=DEV)
+    rng = np.random.default_rng(SEED + 43)
+    src = rng.integers(0, T, R).astype(np.int32)
+    src[::1000] = -1                # out-of-range indices read as zero rows
+    src[7] = T
+    q = ops.quantize_mxfp8(x, True, False, row_gather=to_dev(src))
+    xh = bits(x)
+    rows = np.r_[0:64, 7, 1000, 2000, R - 64:R, rng.integers(0, R, 256)]
+    xs = np.where(((src[rows] >= 0) & (src[rows] < T))[:, None], xh[np.clip(src[rows], 0, T - 1)], 0).astype(np.uint16)
+    rc, rs = oracle.quantize_mxfp8_rowwise(xs)
+    assert_bytes_equal(host(q["codes_row"])[rows], rc, "gathered row codes")
+    assert_bytes_equal(host(q["scales_row"])[rows], rs, "gathered row scales")
 
 
 @pytest.fixture(scope="module")
