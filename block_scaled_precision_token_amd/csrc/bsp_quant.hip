@@ -860,6 +860,9 @@ constexpr int RQ_TK = 128;            // input columns (k) per tile: 16 groups o
 constexpr int RQ_CS = RQ_TM + 4;      // word stride of the transposed code tile in LDS
 constexpr int RQ_MAXPART = 1024;      // partial maxima of the outer scales
 constexpr int RQ_PCHUNK = 2048;       // outer scales per partial-max block
+// outer scales per tensor reduced inside the requant kernel (one load per
+// thread; with 16384 the separate partial-maximum pass measured faster)
+constexpr int64_t RQ_FUSE = 256;
 
 // Partial maxima of the outer scales of each tensor of a batch (G_e = max
 // over tensor e's partials, starting from 0).  Tensor e = blockIdx.y has rows
@@ -1063,8 +1066,19 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t *__restrict__ cod
     const int64_t m0 = (int64_t)(tile / ntk) * RQ_TM, k0 = (int64_t)(tile % ntk) * RQ_TK;
 
     {
+        // G: the maximum of the tensor's partial maxima, or (a short outer
+        // array) of its outer scales themselves, four at a time where aligned
         float g = 0.0f;
-        for (int i = t; i < npart; i += 256) g = fmaxf(g, part[i]);
+        int i0 = 0;
+        if ((reinterpret_cast<uintptr_t>(part) & 15) == 0) {
+            const int n4 = npart >> 2;
+            for (int i = t; i < n4; i += 256) {
+                const float4 v = reinterpret_cast<const float4 *>(part)[i];
+                g = fmaxf(g, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+            }
+            i0 = 4 * n4;
+        }
+        for (int i = i0 + t; i < npart; i += 256) g = fmaxf(g, part[i]);
         g = wave_max(g);
         if ((t & 63) == 0) red[t >> 6] = g;
     }
@@ -1394,19 +1408,30 @@ int64_t requant_workspace_floats(int64_t E, int64_t M, int64_t rps) {
 hipError_t launch_requant(const uint8_t *codes, const uint8_t *scales, const float *outer, int64_t rps, int64_t E,
                           int64_t M, int64_t K, uint8_t *codesT, uint8_t *scalesT, float *outerT, uint64_t seed,
                           bool sr, float *part, hipStream_t s) {
-    const int np = requant_partials(requant_scales_per_tensor(M, rps));
-    k_outer_partial_max<<<dim3(np, (unsigned)E), 256, 0, s>>>(outer, M, rps, part);
+    // Up to RQ_FUSE outer scales per tensor (M / rps of them, contiguous per
+    // tensor), each workgroup reduces them itself; beyond, a first kernel
+    // reduces them to at most RQ_MAXPART partial maxima in the workspace.
+    int np;
+    const float *red_src;
+    if (M % rps == 0 && M / rps <= RQ_FUSE) {
+        np = (int)(M / rps);
+        red_src = outer;
+    } else {
+        np = requant_partials(requant_scales_per_tensor(M, rps));
+        k_outer_partial_max<<<dim3(np, (unsigned)E), 256, 0, s>>>(outer, M, rps, part);
+        red_src = part;
+    }
     const int64_t ntk = (K + RQ_TK - 1) / RQ_TK, ntm = (M + RQ_TM - 1) / RQ_TM;
     if (ntk * ntm > INT32_MAX) return hipErrorInvalidValue;
     const int nt = (int)(ntk * ntm);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const dim3 grid((unsigned)nt, (unsigned)E);
     if (sr)
-        k_requant<true><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, part, np, k0,
-                                             k1, (int)ntk, nt);
+        k_requant<true><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, red_src, np,
+                                             k0, k1, (int)ntk, nt);
     else
-        k_requant<false><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, part, np, k0,
-                                              k1, (int)ntk, nt);
+        k_requant<false><<<grid, 256, 0, s>>>(codes, scales, outer, rps, M, K, codesT, scalesT, outerT, red_src, np,
+                                              k0, k1, (int)ntk, nt);
     return hipGetLastError();
 }
 
