@@ -27,12 +27,13 @@
 // per-CU count of outstanding memory requests is what bounds these loads, so
 // bytes per request matter (8 % faster than 64-value stages on the
 // DeepSeek-V3 MXFP8 shapes, 1-3 % on the Qwen3 NVFP4 and BF16 ones).  The
-// weight-gradient forms stage half as many (64, BF16 32) in a ring of four.  The ring runs across tile boundaries: the first stages of a
-// workgroup's next tile are fetched while the current tile is finished and
-// written back.  Completion is tracked with explicit vmcnt
-// waits (loads retire in order, so "at most n stages outstanding" means the
-// oldest stage has landed) followed by a workgroup barrier; the epilogue's
-// stores are issued so that the compiler's own counter model stays exact.
+// weight-gradient forms stage half as many (64, BF16 32) in a ring of four.
+// The ring runs across tile boundaries: the first stages of a workgroup's
+// next tile are fetched while the current tile is finished and written back.
+// Completion is tracked with explicit vmcnt waits (loads retire in order, so
+// "at most n stages outstanding" means the oldest stage has landed) followed
+// by a workgroup barrier; the epilogue's stores are issued so that the
+// compiler's own counter model stays exact.
 //
 // LDS layout of a stage: per operand BT rows of code bytes (128 or 64 for
 // MXFP8, 64 or 32 for NVFP4), the 16-byte chunks of row r stored at position
@@ -73,7 +74,7 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int GBK = 64;    // K values per stage (block-scaled formats)
+constexpr int GBK = 64;    // K values per MFMA step of the block-scaled formats (a stage holds one or two)
 constexpr int FMT_BF16 = 2;   // plain bf16 operands (internal format tag of the BF16 GEMM)
 constexpr int NXCD = 8;
 constexpr int kMaxDevices = 64;
@@ -1111,7 +1112,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         cons_begin();
     };
 
-    // ---- prologue: first tiles, first three stages ----
+    // ---- prologue: first tiles, first NS - 1 stages ----
     int p_q = 0, c_q = 0;   // stages issued / consumed
     prod_seek();
     waitcnt<63, 0>();
