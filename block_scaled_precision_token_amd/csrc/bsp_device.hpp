@@ -131,35 +131,19 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
 // 2^k as an f32 for k in [-126, 127].
 __device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
 
-// exp(x) in f32 by one fixed sequence: n = rint(x / ln 2), r = x - n ln 2 with
-// ln 2 split in a 16-bit head (n * head is exact) and a tail, e^r by its
-// degree-7 Taylor polynomial in Horner form (reduction and Horner steps one
-// fused multiply-add each), then the exact scaling by 2^n.  Results are inf
-// from x = 89 and 0 up to x = -104; the sequence itself gives exactly those
-// at both ends, so the argument is clamped to [-104, 89] (one V_MED3_F32, no
-// branch) instead of testing the two cut-offs (finite x).
-__device__ __forceinline__ float exp_cw(float x) {
-    x = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
-    const float n = rintf(x * 1.44269504088896341f);
-    float r = __builtin_fmaf(-n, 0.693145751953125f, x);
-    r = __builtin_fmaf(-n, 1.428606765330187e-06f, r);
-    float p = 1.0f / 5040.0f;
-    p = __builtin_fmaf(p, r, 1.0f / 720.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 120.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 24.0f);
-    p = __builtin_fmaf(p, r, 1.0f / 6.0f);
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    return ldexpf(p, (int)n);
-}
-
-// SwiGLU of one element: bf16 bits of silu(gate) * up with silu(z) =
-// z / (1 + exp(-z)) (correctly rounded division), product rounded to bf16
-// (nearest even).  Within a few f32 units of the exact value before the
-// final rounding, so h is within one bf16 unit of the exactly rounded one.
+// SwiGLU of one element: bf16 bits of silu(gate) * up, silu(z) =
+// z / (1 + exp(-z)), the product rounded to bf16 (nearest even).  exp(-z) is
+// the hardware base-2 exponential (V_EXP_F32) of -z log2(e) and the division
+// the hardware reciprocal (V_RCP_F32) and a multiply: the argument's rounding
+// (at most |z log2 e| units of 2^-24, |z| < 89 where it matters) and the two
+// approximations keep silu(z) * up within 2^-16 of its exact value relative
+// to it, far inside the half bf16 unit (2^-9) of the final rounding, so h is
+// the correctly rounded bf16 value or its neighbour: within one bf16 unit.
+// From z < -88.7 the exponential is inf and h is -0 times up (the exact value
+// there is at most 3e-37 |up|).
 __device__ __forceinline__ uint32_t swiglu_bf16(float gate, float up) {
-    const float silu = gate / (1.0f + exp_cw(-gate));
+    const float e = __builtin_amdgcn_exp2f(gate * -1.44269504088896341f);
+    const float silu = gate * __builtin_amdgcn_rcpf(1.0f + e);
     return f32_to_bf16(silu * up);
 }
 
