@@ -107,38 +107,56 @@ struct GemmArgs {
 };
 
 // Row-tile list for the row-grouped form: tiles[i] = (g << 40) | first row, or -1.
-// One workgroup of 256 threads: per pass of 1024 groups each thread counts
-// the row tiles of four groups and a workgroup scan places them.
+// One workgroup of 256 threads, per pass of 1024 groups: each thread counts
+// the row tiles of four groups (the five offsets it needs loaded before any
+// is used; the tile edge bm = 2^lbm makes the count a shift), a workgroup
+// scan places the groups, and the pass's tiles are then written by all
+// threads, each finding its tile's group by a binary search over the
+// groups' first tiles in LDS (an expert with many row tiles would otherwise
+// leave one thread writing all of them).
 __global__ __launch_bounds__(256) void k_tile_list(const int64_t *__restrict__ off, int64_t G, int64_t M,
-                                                   int64_t bm, int64_t ntile_max, int64_t *__restrict__ tiles,
+                                                   int lbm, int64_t ntile_max, int64_t *__restrict__ tiles,
                                                    int64_t *__restrict__ sched) {
     __shared__ int64_t wsum[4];
+    __shared__ int64_t first[1024], row0[1024];
     const int t = threadIdx.x;
+    const int64_t bm = (int64_t)1 << lbm;
     int64_t carry = 0;
     for (int64_t g0 = 0; g0 < G; g0 += 1024) {
-        int64_t cnt[4], r0[4], local = 0;
+        int64_t o[5];
+#pragma unroll
+        for (int q = 0; q < 5; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            o[q] = g <= G ? off[g] : 0;
+        }
+        int64_t cnt[4], local = 0;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int64_t g = g0 + 4 * t + q;
-            cnt[q] = 0;
-            r0[q] = 0;
-            if (g < G) {
-                int64_t lo = off[g], hi = off[g + 1];
-                r0[q] = lo;
-                lo = lo < M ? lo : M;
-                hi = hi < M ? hi : M;
-                cnt[q] = hi > lo ? (hi - lo + bm - 1) / bm : 0;
-            }
+            const int64_t lo = o[q] < M ? o[q] : M, hi = o[q + 1] < M ? o[q + 1] : M;
+            cnt[q] = g < G && hi > lo ? (hi - lo + bm - 1) >> lbm : 0;
             local += cnt[q];
         }
         int64_t total;
-        int64_t base = carry + block256_excl_scan(local, wsum, total);
+        int64_t base = block256_excl_scan(local, wsum, total);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const int64_t g = g0 + 4 * t + q;
-            for (int64_t i = 0; i < cnt[q] && base + i < ntile_max; i++) tiles[base + i] = (g << 40) | (r0[q] + i * bm);
+            first[4 * t + q] = base;
+            row0[4 * t + q] = o[q];
             base += cnt[q];
         }
+        __syncthreads();
+        // tile i of the pass: group k = the last with first[k] <= i (it has tiles)
+        for (int64_t i = t; i < total && carry + i < ntile_max; i += blockDim.x) {
+            int lo = 0, hi = 1024;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (first[mid] <= i) lo = mid;
+                else hi = mid;
+            }
+            tiles[carry + i] = ((g0 + lo) << 40) | (row0[lo] + (i - first[lo]) * bm);
+        }
+        __syncthreads();   // first / row0 are rewritten by the next pass
         carry += total;
     }
     for (int64_t i = carry + t; i < ntile_max; i += blockDim.x) tiles[i] = -1;
@@ -177,11 +195,16 @@ __global__ __launch_bounds__(256) void k_padded_starts(const int64_t *__restrict
     if (t < NXCD) sched[t] = 0;
     int64_t carry = 0;
     for (int64_t g0 = 0; g0 < G; g0 += 1024) {
-        int64_t pn[4], local = 0;
+        int64_t o[5], pn[4], local = 0;
+#pragma unroll
+        for (int q = 0; q < 5; q++) {
+            const int64_t g = g0 + 4 * t + q;
+            o[q] = g <= G ? off[g] : 0;
+        }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int64_t g = g0 + 4 * t + q;
-            pn[q] = g < G ? (off[g + 1] - off[g] + 31) / 32 * 32 : 0;
+            pn[q] = g < G ? (o[q + 1] - o[q] + 31) / 32 * 32 : 0;
             local += pn[q];
         }
         int64_t total;
@@ -1320,7 +1343,7 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     const int bt = pick_tile(((M + 255) / 256 + G / 2) * ((N + 255) / 256), tile);
     p.ntn = (int32_t)((N + bt - 1) / bt);
     p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
-    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt == 256 ? 8 : 7, p.ntm, ws, p.sched);
     PlaneArgs pa = {};
     pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
     pa.tiles = ws; pa.sched = p.sched + NXCD; pa.off = group_offsets; pa.gather = a_gather;
@@ -1401,7 +1424,7 @@ hipError_t launch_gemm_bf16(int mode, const uint16_t *a, int64_t lda, const uint
     p.ntm = (int32_t)((M + bt - 1) / bt + G);   // upper bound of the row-tile count
     p.tiles = ws;
     p.sched = ws + gemm_tile_count(M, G);
-    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt, p.ntm, ws, p.sched);
+    k_tile_list<<<1, 256, 0, s>>>(group_offsets, G, M, bt == 256 ? 8 : 7, p.ntm, ws, p.sched);
     if (mode == BSP_GEMM_DGRAD) {
         if (bt == 256) launch_k<FMT_BF16, BSP_GEMM_DGRAD, 256>(p, bf, s);
         else launch_k<FMT_BF16, BSP_GEMM_DGRAD, 128>(p, bf, s);
