@@ -237,6 +237,9 @@ struct PlaneArgs {
     const int64_t *tiles, *sched, *off;
     const int32_t *gather;
     int32_t bt, M, a_rows;
+    // 0: block-major as above; 1: lane order of the NVFP4 row-grouped GEMM
+    // with tile edge bt (see k_scale_plane)
+    int32_t lane;
 };
 
 template <bool TILE_MAP>
@@ -275,6 +278,35 @@ __global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
         }
     }
     __syncthreads();
+    if (a.lane) {
+        // Lane order (NVFP4 row-grouped GEMM): per tile of bt rows and stage
+        // of 8 blocks, the stage's bt * 8 bytes hold one 8-byte chunk per
+        // (64-row window w, lane row lr, lane half h), chunk (32 w + lr) 2 + h,
+        // byte 4 s + 2 ii + e = scale of row 64 w + 32 ii + lr, block
+        // 4 s + 2 h + e of the stage: a GEMM lane reads its scales of a stage
+        // as whole chunks.  This block's 64 rows are one window: thread
+        // (stage, lr) writes the two chunks of lr, 16 contiguous bytes.
+        const int rt = r0 / a.bt, w = (r0 - rt * a.bt) / 64;
+        const int lr = t & 31, stl = t >> 5;
+        const int st = b0 / 8 + stl;
+        if (st * 8 >= a.nbp) return;
+        uint32_t v[4];
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                uint32_t d = 0;
+#pragma unroll
+                for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+                    for (int e = 0; e < 2; e++)
+                        d |= (uint32_t)tr[32 * ii + lr][8 * stl + 4 * s + 2 * h + e] << (8 * (2 * ii + e));
+                v[2 * h + s] = d;
+            }
+        const int64_t o = (int64_t)z * a.nbp * a.rp + ((int64_t)rt * (a.nbp / 8) + st) * 8 * a.bt + (w * 32 + lr) * 16;
+        *reinterpret_cast<uint4 *>(a.plane + o) = make_uint4(v[0], v[1], v[2], v[3]);
+        return;
+    }
     {
         const int bl = t >> 2, part = t & 3;
         const int b = b0 + bl;
@@ -442,6 +474,13 @@ __device__ __forceinline__ v8h nv_frag(uint32_t w, h2 s) {
     return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// The E4M3 pair in the low (HI false) or high half of w as two fp16 values,
+// exactly (every E4M3 value is an fp16 value; scale 1).
+template <bool HI>
+__device__ __forceinline__ h2 e4m3_pair(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
 // One output tile: expert, rows [row0, row_end), columns from col0, K range.
 struct Tile {
     int g, row0, row_end, col0, kbeg, kend;
@@ -531,6 +570,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
+    // NVFP4 row-grouped forms read scale planes in lane order (k_scale_plane)
+    constexpr bool NVL = NV && !WG;
     // BF16 operand layouts: the forward form takes both operands K-major; the
     // data-gradient form takes B as the forward weight is stored ([K, N] per
     // expert, N contiguous); the weight-gradient form reduces over rows, so
@@ -608,8 +649,15 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             }
         }
         // MXFP8 lane half h reads block h's byte; NVFP4 blocks 2h and 2h + 1
-        fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
-        fsb = GG::B_SCL + (MX ? lh : 2 * lh) * BT + rb;
+        // (row-grouped forms: the lane's chunk of the stage, k_scale_plane)
+        if constexpr (NVL) {
+            // the chunks of the lane's 64-row windows (A: TI / 2 of them, 512 bytes apart)
+            fsa = GG::A_SCL + ((wm * (TI / 2)) * 32 + lr) * 16 + lh * 8;
+            fsb = GG::B_SCL + (wn * 32 + lr) * 16 + lh * 8;
+        } else {
+            fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
+            fsb = GG::B_SCL + (MX ? lh : 2 * lh) * BT + rb;
+        }
         // A transposed read (DS_READ_B64_TR_B16) works on groups of 16 lanes:
         // in-group lane 4 e + c gives the address of 4 consecutive elements
         // (piece c) of K row e, and in-group lane j receives element j of the
@@ -642,7 +690,8 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     const bool scl_b = w >= GG::SCI / 2;
     const int scl_o = 64 * GG::SCW * (w % SCH) + GG::SCW * l;
     const int sbl = scl_o / BT, sr0 = scl_o % BT;
-    const uint32_t psv = (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;   // lane offset in the plane
+    // lane offset in the plane (lane order: the stage's bytes are contiguous)
+    const uint32_t psv = NVL ? (uint32_t)scl_o : (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;
     const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
 
     // A row of tile row r for the row-grouped form: its source row (or -1).
@@ -739,8 +788,14 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         }
         {
             const int b0 = WG ? PT.kbeg / GG::SBLK : 0;
-            if (scl_b) psbase = p.b_plane + ((size_t)(WG ? 0 : PT.g) * p.nbp + b0) * p.b_rp + PT.col0;
-            else psbase = p.a_plane + (size_t)b0 * p.a_rp + (WG ? PT.row0 : PT.slot * BT);
+            if constexpr (NVL) {
+                // lane order: tiles of BT rows, each nbp / SPS stages of SPS * BT bytes
+                if (scl_b) psbase = p.b_plane + (size_t)PT.g * p.nbp * p.b_rp + (size_t)PT.col0 * p.nbp;
+                else psbase = p.a_plane + (size_t)PT.slot * BT * p.nbp;
+            } else {
+                if (scl_b) psbase = p.b_plane + ((size_t)(WG ? 0 : PT.g) * p.nbp + b0) * p.b_rp + PT.col0;
+                else psbase = p.a_plane + (size_t)b0 * p.a_rp + (WG ? PT.row0 : PT.slot * BT);
+            }
         }
     };
 
@@ -847,7 +902,7 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
         }
         // scale bytes of the stage: SPS plane rows (padded past the K end)
         if (scl_w) {
-            const uint8_t *sbase = uniform_ptr(psbase + (size_t)so * (scl_b ? p.b_rp : p.a_rp));
+            const uint8_t *sbase = uniform_ptr(psbase + (size_t)so * (NVL ? BT : scl_b ? p.b_rp : p.a_rp));
             const uint32_t sdst = m0 + (scl_b ? GG::B_SCL : GG::A_SCL) + 64 * GG::SCW * (w % SCH);
             if constexpr (GG::SCW == 4) dma4(sbase, psv, sdst);
             else dma16(sbase, psv, sdst);
@@ -974,6 +1029,22 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             // MFMA step q and element e take K = 64 s + 32 h + 8 q + e, the
             // same on both operands, so each lane reads one 16-byte chunk
             // (32 values, scale blocks 4s + 2h and 4s + 2h + 1).
+            // Row-grouped forms: the lane's scales of the whole stage in
+            // whole chunks (lane-ordered planes): dword s of the chunk of A's
+            // window i / 2 (half i & 1) and of B's (half j) holds the E4M3
+            // pair of blocks 4s + 2h + e.
+            static_assert(!NVL || GG::SPS == 8, "lane-ordered planes hold stages of 8 blocks");
+            uint32_t wsa[NVL ? TI : 1], wsb[2];
+            if constexpr (NVL) {
+#pragma unroll
+                for (int ih = 0; ih < TI / 2; ih++) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(slot + fsa + 512 * ih);
+                    wsa[2 * ih] = v.x;
+                    wsa[2 * ih + 1] = v.y;
+                }
+                const uint2 v = *reinterpret_cast<const uint2 *>(slot + fsb);
+                wsb[0] = v.x; wsb[1] = v.y;
+            }
 #pragma unroll
           for (int s = 0; s < SUB; s++) {
             uint4 ua[TI], ub[2];
@@ -983,18 +1054,31 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             for (int i = 0; i < TI; i++) {
                 if (i >= nv) break;
                 ua[i] = *reinterpret_cast<const uint4 *>(slot + fa0[s] + 32 * GG::ROWB * i);
-                const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + 32 * i], 0);
-                const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + BT + 32 * i], 0);
-                sa[i][0] = h2{s0, s0};
-                sa[i][1] = h2{s1, s1};
+                if constexpr (NVL) {
+                    const uint32_t wv = wsa[2 * (i / 2) + s];
+                    const h2 pr = (i & 1) ? e4m3_pair<true>(wv) : e4m3_pair<false>(wv);
+                    sa[i][0] = h2{pr.x, pr.x};
+                    sa[i][1] = h2{pr.y, pr.y};
+                } else {
+                    const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + 32 * i], 0);
+                    const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + BT + 32 * i], 0);
+                    sa[i][0] = h2{s0, s0};
+                    sa[i][1] = h2{s1, s1};
+                }
             }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0[s] + 32 * GG::ROWB * j);
-                const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + 32 * j], 0);
-                const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + BT + 32 * j], 0);
-                sb[j][0] = h2{t0, t0};
-                sb[j][1] = h2{t1, t1};
+                if constexpr (NVL) {
+                    const h2 pr = j ? e4m3_pair<true>(wsb[s]) : e4m3_pair<false>(wsb[s]);
+                    sb[j][0] = h2{pr.x, pr.x};
+                    sb[j][1] = h2{pr.y, pr.y};
+                } else {
+                    const _Float16 t0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + 32 * j], 0);
+                    const _Float16 t1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssb + BT + 32 * j], 0);
+                    sb[j][0] = h2{t0, t0};
+                    sb[j][1] = h2{t1, t1};
+                }
             }
             auto word = [](const uint4 &u, int q) __attribute__((always_inline)) -> uint32_t {
                 return q == 0 ? u.x : q == 1 ? u.y : q == 2 ? u.z : u.w;
@@ -1348,6 +1432,11 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
     pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
     pa.tiles = ws; pa.sched = p.sched + NXCD; pa.off = group_offsets; pa.gather = a_gather;
     pa.bt = bt; pa.M = (int32_t)M; pa.a_rows = (int32_t)a_rows;
+    if (fmt == BSP_FMT_NVFP4) {
+        pa.lane = 1;
+        pb.lane = 1;
+        pb.bt = bt;
+    }
     k_scale_plane<true><<<dim3((unsigned)((int64_t)p.ntm * bt / 64), gy, 1), 256, 0, s>>>(pa);
     k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, (unsigned)G), 256, 0, s>>>(pb);
     if (bt == 256) {
