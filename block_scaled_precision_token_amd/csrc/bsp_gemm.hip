@@ -238,7 +238,8 @@ struct PlaneArgs {
     const int32_t *gather;
     int32_t bt, M, a_rows;
     // 0: block-major as above; 1: lane order of the NVFP4 row-grouped GEMM
-    // with tile edge bt (see k_scale_plane)
+    // with tile edge bt; 2: block pairs of the NVFP4 weight-gradient GEMM
+    // (see k_scale_plane)
     int32_t lane;
 };
 
@@ -278,6 +279,25 @@ __global__ __launch_bounds__(256) void k_scale_plane(PlaneArgs a) {
         }
     }
     __syncthreads();
+    if (a.lane == 2) {
+        // Block pairs (NVFP4 weight-gradient GEMM): plane[(b / 2) 2 rp + 2 r +
+        // (b & 1)], so a row's scales of blocks 2p and 2p + 1 are one 16-bit
+        // word (groups start on even blocks, so a stage of 4 blocks is 2
+        // whole pairs).  Thread (pair, 8-row piece) writes 16 bytes.
+        const int pp = t >> 3, piece = t & 7;
+        const int b = b0 + 2 * pp;
+        if (b >= a.nbp) return;
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int rr = 8 * piece + 2 * k;
+            v[k] = (uint32_t)tr[rr][2 * pp] | ((uint32_t)tr[rr][2 * pp + 1] << 8) |
+                   ((uint32_t)tr[rr + 1][2 * pp] << 16) | ((uint32_t)tr[rr + 1][2 * pp + 1] << 24);
+        }
+        uint8_t *dst = a.plane + (int64_t)z * a.nbp * a.rp + (int64_t)(b / 2) * 2 * a.rp + 2 * (r0 + 8 * piece);
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(v[0], v[1], v[2], v[3]);
+        return;
+    }
     if (a.lane) {
         // Lane order (NVFP4 row-grouped GEMM): per tile of bt rows and stage
         // of 8 blocks, the stage's bt * 8 bytes hold one 8-byte chunk per
@@ -570,8 +590,9 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     constexpr int TI = GG::TI, SLOT_BYTES = GG::SLOT;
     constexpr bool MX = GG::MX, BF = GG::BF, NV = FMT == BSP_FMT_NVFP4;
     constexpr bool WG = MODE == BSP_GEMM_WGRAD;
-    // NVFP4 row-grouped forms read scale planes in lane order (k_scale_plane)
-    constexpr bool NVL = NV && !WG;
+    // NVFP4 row-grouped forms read scale planes in lane order, the weight-
+    // gradient form in block pairs (k_scale_plane)
+    constexpr bool NVL = NV && !WG, NVP = NV && WG;
     // BF16 operand layouts: the forward form takes both operands K-major; the
     // data-gradient form takes B as the forward weight is stored ([K, N] per
     // expert, N contiguous); the weight-gradient form reduces over rows, so
@@ -654,6 +675,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
             // the chunks of the lane's 64-row windows (A: TI / 2 of them, 512 bytes apart)
             fsa = GG::A_SCL + ((wm * (TI / 2)) * 32 + lr) * 16 + lh * 8;
             fsb = GG::B_SCL + (wn * 32 + lr) * 16 + lh * 8;
+        } else if constexpr (NVP) {
+            // the 16-bit word of block pair h of the lane's row
+            fsa = GG::A_SCL + lh * 2 * BT + 2 * ra;
+            fsb = GG::B_SCL + lh * 2 * BT + 2 * rb;
         } else {
             fsa = GG::A_SCL + (MX ? lh : 2 * lh) * BT + ra;
             fsb = GG::B_SCL + (MX ? lh : 2 * lh) * BT + rb;
@@ -689,9 +714,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
     const bool scl_w = GG::SCI > 0 && w < GG::SCI;
     const bool scl_b = w >= GG::SCI / 2;
     const int scl_o = 64 * GG::SCW * (w % SCH) + GG::SCW * l;
-    const int sbl = scl_o / BT, sr0 = scl_o % BT;
+    // plane piece (block, or block pair for NVP) and offset in it of this lane's load
+    const int sbl = scl_o / (NVP ? 2 * BT : BT), sr0 = scl_o % (NVP ? 2 * BT : BT);
     // lane offset in the plane (lane order: the stage's bytes are contiguous)
-    const uint32_t psv = NVL ? (uint32_t)scl_o : (uint32_t)sbl * (scl_b ? p.b_rp : p.a_rp) + sr0;
+    const uint32_t psv = NVL ? (uint32_t)scl_o : (uint32_t)sbl * (NVP ? 2 : 1) * (scl_b ? p.b_rp : p.a_rp) + sr0;
     const uint8_t *psbase = nullptr;                   // plane at the tile's first block and row
 
     // A row of tile row r for the row-grouped form: its source row (or -1).
@@ -792,6 +818,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 // lane order: tiles of BT rows, each nbp / SPS stages of SPS * BT bytes
                 if (scl_b) psbase = p.b_plane + (size_t)PT.g * p.nbp * p.b_rp + (size_t)PT.col0 * p.nbp;
                 else psbase = p.a_plane + (size_t)PT.slot * BT * p.nbp;
+            } else if constexpr (NVP) {
+                // block pairs: b0 is even (groups start on 32-token boundaries)
+                if (scl_b) psbase = p.b_plane + (size_t)b0 * p.b_rp + 2 * PT.col0;
+                else psbase = p.a_plane + (size_t)b0 * p.a_rp + 2 * PT.row0;
             } else {
                 if (scl_b) psbase = p.b_plane + ((size_t)(WG ? 0 : PT.g) * p.nbp + b0) * p.b_rp + PT.col0;
                 else psbase = p.a_plane + (size_t)b0 * p.a_rp + (WG ? PT.row0 : PT.slot * BT);
@@ -1059,6 +1089,11 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                     const h2 pr = (i & 1) ? e4m3_pair<true>(wv) : e4m3_pair<false>(wv);
                     sa[i][0] = h2{pr.x, pr.x};
                     sa[i][1] = h2{pr.y, pr.y};
+                } else if constexpr (NVP) {
+                    static_assert(!NVP || SUB == 1, "block-pair planes: one 64-value step per stage");
+                    const h2 pr = e4m3_pair<false>(*reinterpret_cast<const uint16_t *>(slot + fsa + 64 * i));
+                    sa[i][0] = h2{pr.x, pr.x};
+                    sa[i][1] = h2{pr.y, pr.y};
                 } else {
                     const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + 32 * i], 0);
                     const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)slot[ssa + BT + 32 * i], 0);
@@ -1071,6 +1106,10 @@ __global__ __launch_bounds__(BT * 2) void k_gemm(GemmArgs p) {
                 ub[j] = *reinterpret_cast<const uint4 *>(slot + fb0[s] + 32 * GG::ROWB * j);
                 if constexpr (NVL) {
                     const h2 pr = j ? e4m3_pair<true>(wsb[s]) : e4m3_pair<false>(wsb[s]);
+                    sb[j][0] = h2{pr.x, pr.x};
+                    sb[j][1] = h2{pr.y, pr.y};
+                } else if constexpr (NVP) {
+                    const h2 pr = e4m3_pair<false>(*reinterpret_cast<const uint16_t *>(slot + fsb + 64 * j));
                     sb[j][0] = h2{pr.x, pr.x};
                     sb[j][1] = h2{pr.y, pr.y};
                 } else {
@@ -1413,6 +1452,10 @@ hipError_t launch_gemm(int fmt, int mode, const uint8_t *a_codes, const uint8_t 
         PlaneArgs pa = {};
         pa.src = a_scales; pa.sr = sr; pa.plane = wsb + L.a_off; pa.nbp = L.nbp; pa.rp = L.a_rp;
         pa.rows_z = (int32_t)M;
+        if (fmt == BSP_FMT_NVFP4) {
+            pa.lane = 2;
+            pb.lane = 2;
+        }
         k_scale_plane<false><<<dim3((unsigned)(L.a_rp / 64), gy, 1), 256, 0, s>>>(pa);
         k_scale_plane<false><<<dim3((unsigned)(L.b_rp / 64), gy, 1), 256, 0, s>>>(pb);
         if (fmt == BSP_FMT_MXFP8) {
