@@ -39,8 +39,11 @@
 // MXFP8, 64 or 32 for NVFP4), the 16-byte chunks of row r stored at position
 // chunk ^ swz(r) so that the 32 rows read by one fragment load hit distinct
 // banks; then the
-// stage's scale bytes, block-major ([scale block][row]) as copied from the
-// scale planes a setup kernel builds in the workspace.
+// stage's scale bytes as copied from the scale planes a setup kernel builds
+// in the workspace: block-major ([scale block][row]) for MXFP8, in block
+// pairs (a row's two scales of one lane half as a 16-bit word) for the NVFP4
+// weight gradient, and in the order the lanes read them (one 8-byte chunk per
+// lane and 32-row pair) for the NVFP4 row-grouped forms.
 //
 // Tiling: output tiles of BT x BT (256 on eight wavefronts, or 128 on four),
 // each wavefront (BT / 2) x 64 outputs; wavefronts skip
@@ -95,7 +98,8 @@ struct GemmArgs {
     int32_t G, M, N, K, ldc, a_rows;
     int32_t ntm;              // row tiles (row-grouped form: upper bound; WGRAD: G * ceil(M / BT))
     int32_t ntn;              // column tiles
-    // Scale planes in the workspace: plane[(z * nbp + block) * rp + row],
+    // Scale planes in the workspace: plane[(z * nbp + block) * rp + row]
+    // (NVFP4 forms: the same bytes in block pairs or lane order, k_scale_plane),
     // one byte per (block, row), rows of the A plane in tile-list order.
     const uint8_t *a_plane, *b_plane;
     int32_t a_rp, b_rp, nbp;
@@ -225,7 +229,8 @@ __global__ __launch_bounds__(256) void k_padded_starts(const int64_t *__restrict
 // one cache line per row.  Transposed to block-major planes, the bytes of a
 // K step for the tile's rows are contiguous: a few lines per operand.
 // plane[(z * nbp + b) * rp + r] = scale b of the source row of (z, r), or 0
-// where (z, r) has no source row or b is past the row's blocks.
+// where (z, r) has no source row or b is past the row's blocks (the NVFP4
+// forms place the same bytes in block pairs or lane order, below).
 struct PlaneArgs {
     const uint8_t *src;
     int64_t src_rows;          // rows of src
