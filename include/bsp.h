@@ -23,11 +23,13 @@
  * Conventions shared by every call:
  *   - Pointers named in the comments as "device" point to GPU memory; sizes
  *     and scalars are host values.  The caller allocates and owns every buffer;
- *     the library allocates nothing.  Its one piece of state is a per-device
- *     cache of the grouped GEMM kernels' occupancy (workgroups per compute
- *     unit), a property of the device and the compiled code filled on first
- *     use and stored atomically: results never depend on it, and concurrent
- *     callers may share the library.
+ *     the library allocates nothing.  Its state is a per-device cache of the
+ *     grouped GEMM kernels' occupancy (workgroups per compute unit), a
+ *     property of the device and the compiled code filled on first use and
+ *     stored atomically: results never depend on it, and concurrent callers
+ *     may share the library; and the static device scratch array of the
+ *     allocation-free GEMM entry point (bsp_moe_grouped_gemm_blockscaled_noalloc,
+ *     below), with its per-device address.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and never synchronize; results are ready when the
  *     stream reaches that point.  Calls on one stream are ordered.
